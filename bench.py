@@ -1,0 +1,276 @@
+"""Benchmark of the hot path on one MI355X.
+
+A step is one pass of every hot-path call over one batch of synthetic input, in the
+configuration the headline metric is quoted on (Qwen-3-8B-like single layer: B=16,
+H=4096, 32 Q / 8 KV heads, d=128, T=32768 including the decode token, bf16 KV in
+16-token pages, MLP scorer 4096->512->8, tau at the 75th percentile (25% kept),
+recent 128 kept):
+    prefill compression:  kvp_score (MLP over 16 x 32767 hidden states)
+                          -> kvp_select -> kvp_compact (pool + 128-slot ring)
+    decode step:          kvp_score (new token) -> kvp_step_delayed -> kvp_decode_attn
+Inputs are resident in HBM before timing.  `value` is kept-KV decode-attention
+token-heads per second of whole step time; the per-call breakdown, the decode-only
+rate and an isolated (cache-flushed) decode-attention rate are reported beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_layer")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU sample")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); this path has no "
+              "cross-GPU work to measure", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import kvp_workloads as W
+    import sparse_decode_attention_kvzap_amd as K
+    from sparse_decode_attention_kvzap_amd.pipeline import PrunedKVCache
+
+    torch.cuda.set_device(0)
+    dev = "cuda:0"
+    K.load()
+    wl = W.BY_NAME[args.workload]
+    if wl.steps:
+        raise SystemExit("bench.py times single-step workloads; use the DMS test for the loop")
+    T = wl.T
+    T0 = T - 1  # prompt positions 0..T-2, the decode token is position T-1
+    B, Hkv, Hq, d, H = wl.B, wl.Hkv, wl.Hq, wl.d, wl.H
+    log(f"[bench] workload {wl.name}: B={B} H={H} Hq={Hq} Hkv={Hkv} d={d} T={T} "
+        f"scorer={wl.scorer}")
+
+    t0 = time.perf_counter()
+    hidden = W.hidden_states(wl, T0, dev)
+    kd, vd = W.kv_dense(wl, T0, dev)
+    sw = W.scorer_weights(wl, dev)
+    h_new, k_new, v_new, q = W.step_inputs(wl, 0, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.perf_counter() - t0:.1f}s")
+
+    if wl.scorer == "mlp":
+        scorer = K.Scorer(K.KVP_SCORER_MLP, sw.W1, sw.b1, sw.W2, sw.b2)
+    else:
+        scorer = K.Scorer(K.KVP_SCORER_LINEAR, sw.W1, sw.b1)
+    q_keep = wl.keep_quantiles[0]
+    cache = PrunedKVCache(B, Hkv, Hq, d, T, wl.kv_dtype, scorer, wl.R, 0.0, device=dev,
+                          max_prompt=T0)
+    # threshold calibration (setup, untimed): quantile of this context's scores
+    cache.score(hidden)
+    torch.cuda.synchronize()
+    tau = float(torch.quantile(cache.scores.flatten()[:: max(1, cache.scores.numel() // (1 << 24))],
+                               q_keep).item())
+    tau = float(np.float32(tau))
+    cache.tau = tau
+    log(f"[bench] tau = {tau:.6f} (quantile {q_keep})")
+
+    calls = ["score_prefill", "select", "compact", "score_new", "step_delayed", "decode_attn"]
+
+    def one_step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record()
+        mark(0)
+        cache.score(hidden)
+        mark(1)
+        cache.select(T0)
+        mark(2)
+        cache.compact(kd, vd)
+        mark(3)
+        K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
+        mark(4)
+        K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, tau, T0, 1)
+        mark(5)
+        cache.attend(q)
+        mark(6)
+
+    for i in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    st = cache.check()
+    assert st == 0, f"capacity error {st}"
+    visible = cache.visible_token_heads()
+    total_th = B * Hkv * T
+    log(f"[bench] warmup done; visible token-heads {visible} of {total_th} "
+        f"({visible / total_th:.3f})")
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for s in range(args.steps):
+        one_step(evs[s])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    per_call = {c: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, c in enumerate(calls)}
+    log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.3f}s); "
+        + ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
+
+    # isolated decode attention, cache flushed between repetitions (256 MB MALL)
+    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    iso = []
+    for r in range(12):
+        flush.fill_(r)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        cache.attend(q)
+        e1.record()
+        torch.cuda.synchronize()
+        if r >= 2:
+            iso.append(e0.elapsed_time(e1))
+    attn_iso_ms = float(np.median(iso))
+    del flush
+
+    # algorithmic work per call
+    elt = 2 if wl.kv_dtype == torch.bfloat16 else 4
+    kv_bytes_attn = visible * 2 * d * elt + B * Hq * d * (elt + 4)
+    ntok = B * T0
+    if wl.scorer == "mlp":
+        score_flops = 2.0 * ntok * H * wl.inner + 2.0 * ntok * wl.inner * Hkv
+    else:
+        score_flops = 2.0 * ntok * H * Hkv
+    score_bytes = ntok * H * elt + ntok * Hkv * 4
+    kept_prefill = int(cache.kept_count.sum())
+    select_bytes = ntok * Hkv * 4 + B * Hkv * T0 * 4 + B * Hkv * ((T0 + 31) // 32) * 4 * 2
+    compact_bytes = kept_prefill * 2 * d * elt * 2 + kept_prefill * 4
+    step_bytes = B * Hkv * d * elt * 2 * 3
+    gbs = lambda b, ms: b / (ms * 1e-3) / 1e9  # noqa: E731
+    kernels = {
+        "score_prefill": {"ms": per_call["score_prefill"],
+                          "tflops": score_flops / (per_call["score_prefill"] * 1e-3) / 1e12,
+                          "gbs": gbs(score_bytes, per_call["score_prefill"])},
+        "select": {"ms": per_call["select"], "gbs": gbs(select_bytes, per_call["select"])},
+        "compact": {"ms": per_call["compact"], "gbs": gbs(compact_bytes, per_call["compact"])},
+        "score_new": {"ms": per_call["score_new"]},
+        "step_delayed": {"ms": per_call["step_delayed"], "gbs": gbs(step_bytes, per_call["step_delayed"])},
+        "decode_attn": {"ms": per_call["decode_attn"], "gbs": gbs(kv_bytes_attn, per_call["decode_attn"]),
+                        "token_heads_per_s": visible / (per_call["decode_attn"] * 1e-3)},
+        "decode_attn_isolated": {"ms": attn_iso_ms, "gbs": gbs(kv_bytes_attn, attn_iso_ms),
+                                 "frac_of_peak": gbs(kv_bytes_attn, attn_iso_ms) / PEAK_HBM_GBS,
+                                 "token_heads_per_s": visible / (attn_iso_ms * 1e-3)},
+    }
+    decode_ms = per_call["score_new"] + per_call["step_delayed"] + per_call["decode_attn"]
+    dominant = max(("score_prefill", "select", "compact", "decode_attn"), key=lambda c: per_call[c])
+    if dominant == "score_prefill" and wl.scorer == "mlp":
+        achieved = score_flops / (per_call[dominant] * 1e-3) / 1e12
+        roofline = {"kernel": "kvp_score (MLP: score_mlp_bf16 + score_mlp_finish)",
+                    "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                    "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                    "per_launch_work": score_flops}
+    else:
+        b = {"score_prefill": score_bytes, "select": select_bytes, "compact": compact_bytes,
+             "decode_attn": kv_bytes_attn}[dominant]
+        achieved = gbs(b, per_call[dominant])
+        roofline = {"kernel": dominant, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                    "per_launch_work": b}
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(wl, hidden, kd, vd, q, h_new, k_new, v_new, sw, tau, T0, args.cpu_rows)
+
+    line = {
+        "metric": "kept-KV decode attention tokens/s + achieved HBM GB/s (% of peak), 1 GPU",
+        "value": visible / (ms_per_step * 1e-3),
+        "unit": "kept token-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "hidden": H, "q_heads": Hq, "kv_heads": Hkv,
+                   "head_dim": d, "context": T, "scorer": wl.scorer, "keep_quantile": q_keep,
+                   "recent": wl.R, "page": 16, "visible_token_heads": visible,
+                   "total_token_heads": total_th},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "decode_step": {"ms": decode_ms, "token_heads_per_s": visible / (decode_ms * 1e-3)},
+        "kernels": kernels,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(wl, hidden, kd, vd, q, h_new, k_new, v_new, sw, tau, T0, rows):
+    """The oracle as it stands, on a bounded sample: the whole path for `rows` batch
+    rows (all KV heads), timed on this host's cores."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    def host(t):
+        t = t.detach().cpu().contiguous()
+        if t.dtype == torch.bfloat16:
+            return oracle.bf16_bits_to_f64(t.view(torch.int16).numpy().view(np.uint16))
+        return t.numpy().astype(np.float64)
+
+    log(f"[bench] cpu baseline: oracle on {rows} batch row(s)")
+    x = host(hidden[:rows])
+    xn = host(h_new[:rows])
+    Kd = host(kd[:rows])
+    Vd = host(vd[:rows])
+    kn = host(k_new[:rows])
+    vn = host(v_new[:rows])
+    qq = host(q[:rows])
+    W1, b1 = host(sw.W1), host(sw.b1)
+    W2 = host(sw.W2) if sw.W2 is not None else None
+    b2 = host(sw.b2) if sw.b2 is not None else None
+    t0 = time.perf_counter()
+    xa = np.concatenate([x, xn], axis=1)
+    if wl.scorer == "mlp":
+        s = oracle.score_mlp(xa, W1, b1, W2, b2)
+    else:
+        s = oracle.score_linear(xa, W1, b1)
+    vis = oracle.keep_mask(s, tau, wl.R)
+    Ka = np.concatenate([Kd, kn[:, :, None]], axis=2)
+    Va = np.concatenate([Vd, vn[:, :, None]], axis=2)
+    out = oracle.decode_attention(qq, Ka, Va, vis, oracle.sm_scale(wl.d))
+    dt = time.perf_counter() - t0
+    kept = int(vis.sum())
+    assert np.isfinite(out).all()
+    return {"value": kept / dt, "unit": "kept token-heads/s",
+            "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "threads": int(os.environ.get("OMP_NUM_THREADS", "0")) or None,
+            "sample": f"whole path (score, threshold, mask, compact, attend) for {rows} of "
+                      f"{wl.B} batch rows, all {wl.Hkv} KV heads; {dt:.2f}s"}
+
+
+if __name__ == "__main__":
+    main()

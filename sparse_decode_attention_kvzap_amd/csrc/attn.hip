@@ -1,0 +1,740 @@
+// GQA decode attention over the kept entries of the paged cache (gfx950).
+//
+// Method: KVzap digest (max5.ai), key points -- pruning shortens the sequence axis,
+// which GQA alone does not; the attention reads only the kept entries.  BeaconKV
+// briefing (jiinsi.com), body -- beacon entries at full precision and the others at
+// low precision are read in one attention.
+//
+// Work decomposition (split-K, evenly balanced):
+//   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages,
+//   then its ring pages, padded to an even count) and, when an int8 pool exists, a
+//   "region B" (its int8 pages, padded to even).  All regions are concatenated and
+//   the sequence is cut into NWAVES equal, even-length ranges; each wave walks its
+//   range 32 tokens (two pages) at a time and emits one partial (m, l, o) record per
+//   region it touches.  The last wave to finish a pair (atomic arrival counter)
+//   merges that pair's records with a log-sum-exp combine in a fixed order, writes
+//   the output and resets the counter, so the result is deterministic.
+//
+// Per 32-token step (bf16, head dim D, g query heads of one KV head):
+//   S^T[32 tok x 16 heads] = K . Q^T on 16x16x32 bf16 MFMA (exact products, fp32
+//   accumulation).  The K rows given to the two 16-row MFMA tiles are interleaved
+//   so that each lane ends up holding the scores of 8 consecutive tokens of one head,
+//   which is exactly the B-operand layout of the P.V MFMA that follows.
+//   O^T[D x 16 heads] += V^T . P^T on MFMA, with P split into bf16 hi + lo parts so
+//   the probabilities keep ~16 significant bits (V is exact in bf16).
+//   V pages are stored dim-major ([d][16]) so V^T fragments are plain 16-byte loads.
+#include "kvp_internal.h"
+
+namespace kvp {
+
+constexpr int ATTN_WG_WAVES = 4;
+constexpr int ATTN_GRID = 512;  // two work-groups per CU on a 256-CU part
+constexpr int ATTN_NWAVES = ATTN_GRID * ATTN_WG_WAVES;
+
+struct AttnArgs {
+  const void* q;
+  float* out;
+  int B, Hkv, Hq, g, D;
+  kvp_paged_kv kv;
+  kvp_ring ring;
+  int has_ring;
+  float scale_log2;  // sm_scale * log2(e)
+  float* part;       // partial records
+  int* counters;     // [num_pairs] arrival counters
+  int rec_floats;    // g * (D + 2)
+};
+
+// -------------------------------------------------------------------------------
+// Plan: page prefix P[] over the 2*num_pairs regions and partial-slot prefix C[].
+// Every work-group recomputes it into LDS (num_pairs lengths, a few KB of L2 reads).
+// -------------------------------------------------------------------------------
+__device__ __forceinline__ int region_pages(const AttnArgs& a, int s) {
+  const int np = a.kv.num_pairs;
+  int n;
+  if (s < np) {
+    n = cdiv(a.kv.length[s], PAGE) + (a.has_ring ? a.ring.window / PAGE : 0);
+  } else {
+    n = (a.kv.num_pages8 > 0) ? cdiv(a.kv.length8[s - np], PAGE) : 0;
+  }
+  return (n + 1) & ~1;
+}
+
+struct Plan {
+  int* P;  // [nseg + 1]
+  int* C;  // [nseg + 1]
+  int total;
+  int per;
+};
+
+__device__ Plan build_plan(const AttnArgs& a, int* lds) {
+  const int nseg = 2 * a.kv.num_pairs;
+  Plan pl;
+  pl.P = lds;
+  pl.C = lds + nseg + 1;
+  int* tmp = pl.C + nseg + 1;
+  for (int s = threadIdx.x; s <= nseg; s += blockDim.x) pl.P[s] = (s < nseg) ? region_pages(a, s) : 0;
+  __syncthreads();
+  pl.total = block_excl_scan_lds(pl.P, nseg + 1, tmp);
+  int per = (pl.total + ATTN_NWAVES - 1) / ATTN_NWAVES;
+  per = max(2, (per + 1) & ~1);
+  pl.per = per;
+  for (int s = threadIdx.x; s <= nseg; s += blockDim.x) {
+    int c = 0;
+    if (s < nseg) {
+      int p0 = pl.P[s], p1 = pl.P[s + 1];
+      if (p1 > p0) c = (p1 - 1) / per - p0 / per + 1;
+    }
+    pl.C[s] = c;
+  }
+  __syncthreads();
+  block_excl_scan_lds(pl.C, nseg + 1, tmp);
+  return pl;
+}
+
+// -------------------------------------------------------------------------------
+// Merge of a pair's partial records by one wave (fixed order => deterministic).
+// -------------------------------------------------------------------------------
+__device__ void combine_pair(const AttnArgs& a, const Plan& pl, int pair) {
+  const int lane = threadIdx.x & 63;
+  const int np = a.kv.num_pairs;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  const int r0 = pl.C[pair], r1 = pl.C[pair + 1];
+  const int s0 = pl.C[np + pair], s1 = pl.C[np + pair + 1];
+  const int nrec = (r1 - r0) + (s1 - s0);
+  for (int n = 0; n < a.g; ++n) {
+    float* o = a.out + ((int64_t)b * a.Hq + h * a.g + n) * a.D;
+    float M = neg_inf();
+    for (int k = 0; k < nrec; ++k) {
+      int slot = (k < r1 - r0) ? r0 + k : s0 + (k - (r1 - r0));
+      const float* rec = a.part + (int64_t)slot * a.rec_floats;
+      M = fmaxf(M, rec[a.g * a.D + n]);
+    }
+    for (int d = lane; d < a.D; d += 64) {
+      float num = 0.f, den = 0.f;
+      if (M != neg_inf()) {
+        for (int k = 0; k < nrec; ++k) {
+          int slot = (k < r1 - r0) ? r0 + k : s0 + (k - (r1 - r0));
+          const float* rec = a.part + (int64_t)slot * a.rec_floats;
+          float m = rec[a.g * a.D + n];
+          float wgt = (m == neg_inf()) ? 0.f : exp2f(m - M);
+          num += wgt * rec[n * a.D + d];
+          den += wgt * rec[a.g * a.D + a.g + n];
+        }
+      }
+      o[d] = (den > 0.f) ? num / den : 0.f;
+    }
+  }
+}
+
+// Arrival: called by the whole wave after its partial record is stored.
+__device__ __forceinline__ void arrive(const AttnArgs& a, const Plan& pl, int pair) {
+  const int np = a.kv.num_pairs;
+  const int expected = (pl.C[pair + 1] - pl.C[pair]) + (pl.C[np + pair + 1] - pl.C[np + pair]);
+  __threadfence();
+  int old = 0;
+  if ((threadIdx.x & 63) == 0) old = atomicAdd(a.counters + pair, 1);
+  old = __shfl(old, 0);
+  if (old == expected - 1) {
+    __threadfence();
+    combine_pair(a, pl, pair);
+    if ((threadIdx.x & 63) == 0) a.counters[pair] = 0;
+  }
+}
+
+// -------------------------------------------------------------------------------
+// bf16 region-A step machinery
+// -------------------------------------------------------------------------------
+template <int D>
+struct Bf16Frags {
+  u32x4 kA[D / 32];  // K rows for score tile A (this lane's row, D/4 elements)
+  u32x4 kB[D / 32];  // K rows for score tile B
+  u32x4 v[D / 16];   // V^T fragments, one per 16-wide output tile
+};
+
+struct PageRef {
+  const uint16_t* k;  // K page base
+  const uint16_t* v;  // V^T page base
+  int kind;           // 0 main, 1 ring, 2 padding
+  int nvalid;         // main: valid slots; ring: ring page index
+};
+
+template <int D>
+__device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, int vp, int npm,
+                                                 int len) {
+  PageRef r;
+  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
+  if (vp < npm) {
+    int pg = __builtin_amdgcn_readfirstlane(
+        a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + vp]);
+    r.k = reinterpret_cast<const uint16_t*>(a.kv.k_pages) + (int64_t)pg * PAGE * D;
+    r.v = reinterpret_cast<const uint16_t*>(a.kv.v_pages) + (int64_t)pg * PAGE * D;
+    r.kind = 0;
+    r.nvalid = min(PAGE, len - vp * PAGE);
+  } else if (vp < npm + nring) {
+    int rp = vp - npm;
+    int64_t off = ((int64_t)pair * nring + rp) * PAGE * D;
+    r.k = reinterpret_cast<const uint16_t*>(a.ring.k) + off;
+    r.v = reinterpret_cast<const uint16_t*>(a.ring.v) + off;
+    r.kind = 1;
+    r.nvalid = rp;
+  } else {
+    r.k = nullptr;
+    r.v = nullptr;
+    r.kind = 2;
+    r.nvalid = 0;
+  }
+  return r;
+}
+
+// Validity bits of this lane's 8 tokens (8j .. 8j+7 of the 32-token step).
+__device__ __forceinline__ uint32_t lane_valid_bits(const AttnArgs& a, int pair, const PageRef& X,
+                                                    const PageRef& Y, int j) {
+  const PageRef& P = (j < 2) ? X : Y;
+  const int s0 = 8 * (j & 1);
+  if (P.kind == 0) {
+    int n = P.nvalid - s0;
+    n = max(0, min(8, n));
+    return (1u << n) - 1u;
+  }
+  if (P.kind == 1) {
+    const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + P.nvalid * PAGE + s0;
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m |= (pos[i] >= 0 ? 1u : 0u) << i;
+    return m;
+  }
+  return 0u;
+}
+
+template <int D>
+__device__ __forceinline__ void load_step(Bf16Frags<D>& f, const PageRef& X, const PageRef& Y,
+                                          int lane) {
+  const int m = lane & 15, j = lane >> 4;
+  // Score tile A rows: token 8*(m/4) + m%4; tile B rows: token 8*(m/4) + 4 + m%4.
+  const int tA = 8 * (m >> 2) + (m & 3);
+  const int tB = tA + 4;
+  const PageRef& PA = (tA < 16) ? X : Y;  // tA < 16 <=> tB < 16
+  const uint16_t* kbase = (PA.k != nullptr) ? PA.k : X.k;
+  const uint16_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
+  const uint16_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    f.kA[kk] = *reinterpret_cast<const u32x4*>(rowA + 8 * kk);
+    f.kB[kk] = *reinterpret_cast<const u32x4*>(rowB + 8 * kk);
+  }
+  const PageRef& PV = (j < 2) ? X : Y;
+  const uint16_t* vbase = (PV.v != nullptr) ? PV.v : X.v;
+  const uint16_t* vcol = vbase + m * PAGE + 8 * (j & 1);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const u32x4*>(vcol + t * 16 * PAGE);
+}
+
+template <int D>
+struct SoftmaxState {
+  f32x4 o[D / 16];
+  float m;  // running max (log2 domain), this lane's head
+  float l;  // running sum of p over this lane's tokens
+};
+
+// Zero the bf16 elements of a fragment whose token bit is clear (keeps 0*garbage out
+// of the MFMA when a slot of a partly filled page holds stale bits).
+__device__ __forceinline__ u32x4 mask_tokens(u32x4 x, uint32_t vb) {
+  u32x4 r;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t lo = (vb >> (2 * w)) & 1u ? 0x0000ffffu : 0u;
+    uint32_t hi = (vb >> (2 * w + 1)) & 1u ? 0xffff0000u : 0u;
+    r[w] = x[w] & (lo | hi);
+  }
+  return r;
+}
+
+template <int D>
+__device__ __forceinline__ void compute_step(const AttnArgs& a, const Bf16Frags<D>& f,
+                                             const bf16x8 (&qf)[D / 32], SoftmaxState<D>& st,
+                                             uint32_t vbits, bool all_valid) {
+  f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    sA = mfma16x16x32(as_bf16x8(f.kA[kk]), qf[kk], sA);
+    sB = mfma16x16x32(as_bf16x8(f.kB[kk]), qf[kk], sB);
+  }
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = sA[i] * a.scale_log2;
+    s[i + 4] = sB[i] * a.scale_log2;
+  }
+  if (!all_valid) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = ((vbits >> i) & 1u) ? s[i] : neg_inf();
+  }
+  float mx = s[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mnew = fmaxf(st.m, mx);
+  if (mnew == neg_inf()) return;  // nothing visible yet (uniform across the wave)
+  const float alpha = exp2f(st.m - mnew);
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    p[i] = exp2f(s[i] - mnew);
+    psum += p[i];
+  }
+  st.l = st.l * alpha + psum;
+  st.m = mnew;
+  if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
+  }
+  u32x4 hi, lo;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint16_t h0 = f32_to_bf16(p[2 * w]), h1 = f32_to_bf16(p[2 * w + 1]);
+    float r0 = p[2 * w] - bf16_to_f32(h0), r1 = p[2 * w + 1] - bf16_to_f32(h1);
+    hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[w] = pack_bf16x2(r0, r1);
+  }
+  const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) {
+    const bf16x8 vt = as_bf16x8(all_valid ? f.v[t] : mask_tokens(f.v[t], vbits));
+    st.o[t] = mfma16x16x32(vt, phi, st.o[t]);
+    st.o[t] = mfma16x16x32(vt, plo, st.o[t]);
+  }
+}
+
+// Store this wave's partial record for one region and arrive at the pair.
+template <int D>
+__device__ __forceinline__ void emit_partial(const AttnArgs& a, const Plan& pl, int pair, int slot,
+                                             SoftmaxState<D>& st) {
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  float* rec = a.part + (int64_t)slot * a.rec_floats;
+  if (n < a.g) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t)
+      *reinterpret_cast<f32x4*>(rec + n * D + 16 * t + 4 * j) = st.o[t];
+    if (j == 0) {
+      rec[a.g * D + n] = st.m;
+      rec[a.g * D + a.g + n] = l;
+    }
+  }
+  arrive(a, pl, pair);
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const AttnArgs& a, int pair, bf16x8 (&qf)[D / 32]) {
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.g + n) * D +
+                      (D / 4) * j;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (n < a.g) v = *reinterpret_cast<const u32x4*>(q + 8 * kk);
+    qf[kk] = as_bf16x8(v);
+  }
+}
+
+template <int D>
+__device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
+                                  int slot) {
+  const int lane = threadIdx.x & 63, j = lane >> 4;
+  bf16x8 qf[D / 32];
+  load_q<D>(a, pair, qf);
+  SoftmaxState<D> st;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = neg_inf();
+  st.l = 0.f;
+  const int len = __builtin_amdgcn_readfirstlane(a.kv.length[pair]);
+  const int npm = cdiv(len, PAGE);
+
+  Bf16Frags<D> fa, fb;
+  PageRef xa = region_a_page<D>(a, pair, v0, npm, len);
+  PageRef ya = region_a_page<D>(a, pair, v0 + 1, npm, len);
+  if (xa.k == nullptr) {
+    // a fully padded step cannot start a range (regions are padded by at most one page)
+  }
+  load_step<D>(fa, xa, ya, lane);
+  for (int v = v0; v < v1; v += 4) {
+    // stage A: step at v (in fa); prefetch v + 2 into fb
+    PageRef xb, yb;
+    const bool hasb = (v + 2 < v1);
+    if (hasb) {
+      xb = region_a_page<D>(a, pair, v + 2, npm, len);
+      yb = region_a_page<D>(a, pair, v + 3, npm, len);
+      load_step<D>(fb, xb, yb, lane);
+    }
+    {
+      uint32_t vb = lane_valid_bits(a, pair, xa, ya, j);
+      bool allv = __ballot(vb != 0xffu) == 0;
+      compute_step<D>(a, fa, qf, st, vb, allv);
+    }
+    if (!hasb) break;
+    const bool hasa = (v + 4 < v1);
+    if (hasa) {
+      xa = region_a_page<D>(a, pair, v + 4, npm, len);
+      ya = region_a_page<D>(a, pair, v + 5, npm, len);
+      load_step<D>(fa, xa, ya, lane);
+    }
+    {
+      uint32_t vb = lane_valid_bits(a, pair, xb, yb, j);
+      bool allv = __ballot(vb != 0xffu) == 0;
+      compute_step<D>(a, fb, qf, st, vb, allv);
+    }
+  }
+  emit_partial<D>(a, pl, pair, slot, st);
+}
+
+// -------------------------------------------------------------------------------
+// int8 region (BeaconKV demoted tokens): codes -> bf16 exactly, per-token scales.
+// -------------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t word, int byte0) {
+  float f0 = (float)(int)(int8_t)((word >> (8 * byte0)) & 0xffu);
+  float f1 = (float)(int)(int8_t)((word >> (8 * (byte0 + 1))) & 0xffu);
+  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+}
+
+// 8 int8 codes (two dwords) -> 8 bf16 (exact: |code| <= 127).
+__device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  r[0] = i8pair_to_bf16x2(w0, 0);
+  r[1] = i8pair_to_bf16x2(w0, 2);
+  r[2] = i8pair_to_bf16x2(w1, 0);
+  r[3] = i8pair_to_bf16x2(w1, 2);
+  return r;
+}
+
+template <int D>
+__device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
+                                  int slot) {
+  const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
+  bf16x8 qf[D / 32];
+  load_q<D>(a, pair, qf);
+  SoftmaxState<D> st;
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = neg_inf();
+  st.l = 0.f;
+  const int len = __builtin_amdgcn_readfirstlane(a.kv.length8[pair]);
+  const int npm = cdiv(len, PAGE);
+  const int tA = 8 * (m >> 2) + (m & 3);
+  const int tB = tA + 4;
+  for (int v = v0; v < v1; v += 2) {
+    int pgX = -1, pgY = -1;
+    if (v < npm)
+      pgX = __builtin_amdgcn_readfirstlane(a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + v]);
+    if (v + 1 < npm)
+      pgY = __builtin_amdgcn_readfirstlane(a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + v + 1]);
+    if (pgY < 0) pgY = pgX;
+    const int nvX = max(0, min(PAGE, len - v * PAGE));
+    const int nvY = max(0, min(PAGE, len - (v + 1) * PAGE));
+    // K rows (int8) -> bf16 fragments
+    const int pgK = (tA < 16) ? pgX : pgY;
+    const int8_t* kbase = a.kv.k8_pages + (int64_t)pgK * PAGE * D;
+    const int8_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
+    const int8_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
+    f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      u32x2 ka = *reinterpret_cast<const u32x2*>(rowA + 8 * kk);
+      u32x2 kb = *reinterpret_cast<const u32x2*>(rowB + 8 * kk);
+      sA = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(ka[0], ka[1])), qf[kk], sA);
+      sB = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(kb[0], kb[1])), qf[kk], sB);
+    }
+    // this lane's 8 tokens: 8j .. 8j+7 -> page (j<2 ? X : Y), slots 8(j&1) ..
+    const int pgT = (j < 2) ? pgX : pgY;
+    const int nvT = (j < 2) ? nvX : nvY;
+    const int s0 = 8 * (j & 1);
+    const float* ksc = a.kv.k8_scale + (int64_t)pgT * PAGE + s0;
+    const float* vsc = a.kv.v8_scale + (int64_t)pgT * PAGE + s0;
+    float s[8], vs[8];
+    uint32_t vb = (uint32_t)((1 << max(0, min(8, nvT - s0))) - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[i] = sA[i] * ksc[i] * a.scale_log2;
+      s[i + 4] = sB[i] * ksc[i + 4] * a.scale_log2;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      vs[i] = vsc[i];
+      if (!((vb >> i) & 1u)) {
+        s[i] = neg_inf();
+        vs[i] = 0.f;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(st.m, mx);
+    if (mnew == neg_inf()) continue;
+    const float alpha = exp2f(st.m - mnew);
+    float p[8], psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      p[i] = exp2f(s[i] - mnew);
+      psum += p[i];
+    }
+    st.l = st.l * alpha + psum;
+    st.m = mnew;
+    if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
+    }
+    // fold the V scale into the probabilities: sum_t p_t (scale_t code_t)
+    u32x4 hi, lo;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      float q0 = p[2 * w] * vs[2 * w], q1 = p[2 * w + 1] * vs[2 * w + 1];
+      uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
+      hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      lo[w] = pack_bf16x2(q0 - bf16_to_f32(h0), q1 - bf16_to_f32(h1));
+    }
+    const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+    const int8_t* vcol = a.kv.v8_pages + (int64_t)pgT * PAGE * D + m * PAGE + s0;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      u32x2 vv = *reinterpret_cast<const u32x2*>(vcol + t * 16 * PAGE);
+      u32x4 vt = i8x8_to_bf16x8(vv[0], vv[1]);
+      if (vb != 0xffu) vt = mask_tokens(vt, vb);
+      st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
+      st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
+    }
+  }
+  emit_partial<D>(a, pl, pair, slot, st);
+}
+
+// -------------------------------------------------------------------------------
+// fp32 region A (VALU; small head dims / tiny workloads)
+// -------------------------------------------------------------------------------
+template <int D>
+__device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
+                                 int slot, float* wlds) {
+  // wlds: this wave's LDS area: q [16][D] then p [16][32]
+  const int lane = threadIdx.x & 63;
+  const int g = a.g;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  float* qs = wlds;
+  float* ps = wlds + 16 * D;
+  const float* q = reinterpret_cast<const float*>(a.q) + ((int64_t)b * a.Hq + h * g) * D;
+  for (int i = lane; i < g * D; i += 64) qs[i] = q[i];
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  float mrun[16], lrun[16];
+  float o[16][D / 64 > 0 ? D / 64 : 1];
+  for (int n = 0; n < 16; ++n) {
+    mrun[n] = neg_inf();
+    lrun[n] = 0.f;
+    for (int e = 0; e < D / 64; ++e) o[n][e] = 0.f;
+  }
+  const int len = a.kv.length[pair];
+  const int npm = cdiv(len, PAGE);
+  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
+  const int tok = lane & 31, half = lane >> 5;
+  for (int v = v0; v < v1; v += 2) {
+    const float* kp[2];
+    const float* vp[2];
+    int nvalid[2];
+    int ringp[2];
+    for (int u = 0; u < 2; ++u) {
+      int vv = v + u;
+      kp[u] = nullptr;
+      vp[u] = nullptr;
+      nvalid[u] = 0;
+      ringp[u] = -1;
+      if (vv < npm) {
+        int pg = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + vv];
+        kp[u] = reinterpret_cast<const float*>(a.kv.k_pages) + (int64_t)pg * PAGE * D;
+        vp[u] = reinterpret_cast<const float*>(a.kv.v_pages) + (int64_t)pg * PAGE * D;
+        nvalid[u] = min(PAGE, len - vv * PAGE);
+      } else if (vv < npm + nring) {
+        int rp = vv - npm;
+        int64_t off = ((int64_t)pair * nring + rp) * PAGE * D;
+        kp[u] = reinterpret_cast<const float*>(a.ring.k) + off;
+        vp[u] = reinterpret_cast<const float*>(a.ring.v) + off;
+        ringp[u] = rp;
+      }
+    }
+    // validity of token `tok` (and of every token, for the PV loop below)
+    auto valid_of = [&](int t) -> bool {
+      int u = t >> 4, sl = t & 15;
+      if (kp[u] == nullptr) return false;
+      if (ringp[u] < 0) return sl < nvalid[u];
+      return a.ring.pos[(int64_t)pair * a.ring.window + ringp[u] * PAGE + sl] >= 0;
+    };
+    const bool myvalid = valid_of(tok);
+    float sc[16];
+    for (int n = 0; n < 16; ++n) sc[n] = 0.f;
+    if (myvalid) {
+      const float* krow = kp[tok >> 4] + (tok & 15) * D + half * (D / 2);
+      for (int d = 0; d < D / 2; ++d) {
+        float kv = krow[d];
+        for (int n = 0; n < g; ++n) sc[n] += kv * qs[n * D + half * (D / 2) + d];
+      }
+    }
+    for (int n = 0; n < g; ++n) {
+      float s = sc[n] + __shfl_xor(sc[n], 32);
+      s = myvalid ? s * a.scale_log2 : neg_inf();
+      float mx = wave_max(s);
+      float mnew = fmaxf(mrun[n], mx);
+      float p = (mnew == neg_inf()) ? 0.f : exp2f(s - mnew);
+      float alpha = (mnew == neg_inf()) ? 1.f : exp2f(mrun[n] - mnew);
+      float psum = p;
+      for (int off = 16; off > 0; off >>= 1) psum += __shfl_xor(psum, off);  // within 32 lanes
+      lrun[n] = lrun[n] * alpha + psum;
+      mrun[n] = mnew;
+      for (int e = 0; e < D / 64; ++e) o[n][e] *= alpha;
+      if (half == 0) ps[n * 32 + tok] = p;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int t = 0; t < 32; ++t) {
+      int u = t >> 4, sl = t & 15;
+      if (!valid_of(t)) continue;
+      for (int e = 0; e < D / 64; ++e) {
+        int d = lane + 64 * e;
+        float vv = vp[u][d * PAGE + sl];
+        for (int n = 0; n < g; ++n) o[n][e] += ps[n * 32 + t] * vv;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+  float* rec = a.part + (int64_t)slot * a.rec_floats;
+  for (int n = 0; n < g; ++n) {
+    for (int e = 0; e < D / 64; ++e) rec[n * D + lane + 64 * e] = o[n][e];
+    if (lane == 0) {
+      rec[g * D + n] = mrun[n];
+      rec[g * D + g + n] = lrun[n];
+    }
+  }
+  arrive(a, pl, pair);
+}
+
+// -------------------------------------------------------------------------------
+// The kernel
+// -------------------------------------------------------------------------------
+template <int D, bool F32>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_kernel(AttnArgs a) {
+  extern __shared__ int lds[];
+  Plan pl = build_plan(a, lds);
+  const int np = a.kv.num_pairs;
+  const int nseg = 2 * np;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * ATTN_WG_WAVES + wid;
+
+  // pairs with nothing visible: zero output (one work-group does it)
+  if (blockIdx.x == 0) {
+    for (int p = threadIdx.x; p < np; p += blockDim.x) {
+      int n = (pl.C[p + 1] - pl.C[p]) + (pl.C[np + p + 1] - pl.C[np + p]);
+      if (n == 0) {
+        const int b = p / a.Hkv, h = p % a.Hkv;
+        float* o = a.out + ((int64_t)b * a.Hq + h * a.g) * D;
+        for (int i = 0; i < a.g * D; ++i) o[i] = 0.f;
+      }
+    }
+  }
+
+  pl.total = __builtin_amdgcn_readfirstlane(pl.total);
+  pl.per = __builtin_amdgcn_readfirstlane(pl.per);
+  int start = gw * pl.per;
+  const int end = min(start + pl.per, pl.total);
+  if (start >= end) return;
+  int s = __builtin_amdgcn_readfirstlane(upper_segment(pl.P, nseg, start));
+  float* wlds = nullptr;
+  if constexpr (F32) {
+    wlds = reinterpret_cast<float*>(lds + 2 * (nseg + 1) + 16) + wid * (16 * D + 16 * 32);
+  }
+  while (start < end) {
+    while (__builtin_amdgcn_readfirstlane(pl.P[s + 1]) <= start) ++s;
+    const int ps = __builtin_amdgcn_readfirstlane(pl.P[s]);
+    const int stop = min(end, __builtin_amdgcn_readfirstlane(pl.P[s + 1]));
+    const int slot = __builtin_amdgcn_readfirstlane(pl.C[s]) + (gw - ps / pl.per);
+    const int v0 = start - ps, v1 = stop - ps;
+    if (s < np) {
+      if constexpr (F32) {
+        run_region_a_f32<D>(a, pl, s, v0, v1, slot, wlds);
+      } else {
+        run_region_a_bf16<D>(a, pl, s, v0, v1, slot);
+      }
+    } else {
+      if constexpr (!F32) run_region_b_int8<D>(a, pl, s - np, v0, v1, slot);
+    }
+    start = stop;
+  }
+}
+
+size_t attn_lds_bytes(int num_pairs, int D, bool f32) {
+  size_t b = (size_t)(2 * (2 * num_pairs + 1) + 16) * sizeof(int);
+  if (f32) b += (size_t)ATTN_WG_WAVES * (16 * D + 16 * 32) * sizeof(float);
+  return b;
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+extern "C" size_t kvp_decode_attn_counter_bytes(int32_t num_pairs) {
+  if (num_pairs <= 0) return 0;
+  return (((size_t)num_pairs * sizeof(int)) + 255) & ~(size_t)255;
+}
+
+extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
+                                                 int32_t head_dim) {
+  if (B <= 0 || Hq <= 0 || num_pairs <= 0 || head_dim <= 0 || num_pairs % B != 0) return 0;
+  const int Hkv = num_pairs / B;
+  if (Hq % Hkv != 0) return 0;
+  const int g = Hq / Hkv;
+  const size_t recs = (size_t)ATTN_NWAVES + 2 * (size_t)num_pairs;
+  return kvp_decode_attn_counter_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
+}
+
+kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
+                                  const kvp_ring* ring, float sm_scale, float* out, void* ws,
+                                  hipStream_t stream) {
+  AttnArgs a;
+  a.q = q;
+  a.out = out;
+  a.B = B;
+  a.Hkv = kv->num_pairs / B;
+  a.Hq = Hq;
+  a.g = Hq / a.Hkv;
+  a.D = kv->head_dim;
+  a.kv = *kv;
+  a.has_ring = ring != nullptr;
+  if (ring) a.ring = *ring;
+  else a.ring = kvp_ring{};
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.counters = reinterpret_cast<int*>(ws);
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                    kvp_decode_attn_counter_bytes(kv->num_pairs));
+  a.rec_floats = a.g * (a.D + 2);
+  const bool f32 = kv->dtype == KVP_F32;
+  const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32);
+  if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
+  if (f32) {
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, true>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+  } else {
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+  }
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
+}
+
+size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32) {
+  return attn_lds_bytes(num_pairs, D, f32);
+}

@@ -1,0 +1,338 @@
+// Compaction of the kept entries into the paged cache (gfx950).
+//
+// Method: DeInfer summary (gist.science, arXiv 2604.17709), method part (b) -- a
+// preparation pass builds a remapping index list, then a copy pass moves the blocks
+// into a compact, fixed-address KV buffer.  Here the index list is kvp_select's
+// ordered kept_idx, the preparation pass is compact_plan_kernel (page counts, page
+// bases by exclusive scan, lengths, capacity checks) and the copy pass is
+// compact_gather_kernel.  KVzap practical application: only kept entries (plus the
+// recent window) remain.  BeaconKV body: in DEMOTE_INT8 mode the other entries are
+// kept at low precision instead (absmax int8 per (token, head), K and V separately).
+//
+// Work units are destination pages of 16 slots: a pair's pool pages, then its ring
+// pages, then its int8 pages.  The gather kernel is persistent (grid-stride over the
+// flattened unit list) and finds a unit's pair by binary search in the unit prefix.
+#include "kvp_internal.h"
+
+namespace kvp {
+
+constexpr int CMP_THREADS = 256;
+constexpr int CMP_GRID = 2048;
+constexpr int PLAN_THREADS = 1024;
+
+struct CompactArgs {
+  const void* k;
+  const void* v;
+  int T, d, num_pairs;
+  const int* kept_idx;
+  const int* kept_count;
+  const float* scores;
+  int64_t ld_s;
+  int demote;
+  kvp_paged_kv kv;
+  kvp_ring ring;
+  int has_ring;
+  int* ws;  // npool | pbase | nring | n8 | p8base | wbase (np+1) | tmp
+};
+
+__device__ __forceinline__ int* ws_npool(const CompactArgs& a) { return a.ws; }
+__device__ __forceinline__ int* ws_pbase(const CompactArgs& a) { return a.ws + a.num_pairs; }
+__device__ __forceinline__ int* ws_nring(const CompactArgs& a) { return a.ws + 2 * a.num_pairs; }
+__device__ __forceinline__ int* ws_n8(const CompactArgs& a) { return a.ws + 3 * a.num_pairs; }
+__device__ __forceinline__ int* ws_p8base(const CompactArgs& a) { return a.ws + 4 * a.num_pairs; }
+__device__ __forceinline__ int* ws_wbase(const CompactArgs& a) { return a.ws + 5 * a.num_pairs; }
+__device__ __forceinline__ int* ws_tmp(const CompactArgs& a) { return a.ws + 6 * a.num_pairs + 1; }
+
+// first index i in [lo, hi) with arr[i] >= x (arr ascending), hi if none
+__device__ __forceinline__ int lower_bound_i(const int* arr, int lo, int hi, int x) {
+  while (lo < hi) {
+    int mid = (lo + hi) >> 1;
+    if (arr[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(PLAN_THREADS) void compact_plan_kernel(CompactArgs a) {
+  const int np = a.num_pairs;
+  int* npool = ws_npool(a);
+  int* pbase = ws_pbase(a);
+  int* nring = ws_nring(a);
+  int* n8 = ws_n8(a);
+  int* p8base = ws_p8base(a);
+  int* wbase = ws_wbase(a);
+  __shared__ int tmp[PLAN_THREADS / 64];
+  const int w = a.has_ring ? a.ring.window : 0;
+  int errbits = 0;
+  for (int p = threadIdx.x; p < np; p += blockDim.x) {
+    const int cnt = a.kept_count[p];
+    const int* idx = a.kept_idx + (int64_t)p * a.T;
+    int nr = 0;
+    if (a.has_ring) nr = cnt - lower_bound_i(idx, 0, cnt, a.T - w);
+    int npl = cnt - nr;
+    int pages = cdiv(npl, PAGE);
+    if (pages > a.kv.max_pages_per_pair) {
+      errbits |= KVP_ERR_TABLE_FULL;
+      pages = a.kv.max_pages_per_pair;
+      npl = pages * PAGE;
+    }
+    int ne = a.demote ? (a.T - cnt) : 0;
+    int pages8 = cdiv(ne, PAGE);
+    if (a.demote && pages8 > a.kv.max_pages8_per_pair) {
+      errbits |= KVP_ERR_POOL8_FULL;
+      pages8 = a.kv.max_pages8_per_pair;
+      ne = pages8 * PAGE;
+    }
+    npool[p] = npl;
+    nring[p] = nr;
+    n8[p] = ne;
+    pbase[p] = pages;
+    p8base[p] = pages8;
+  }
+  __syncthreads();
+  const int total = block_excl_scan_lds(pbase, np, tmp);
+  const int total8 = block_excl_scan_lds(p8base, np, tmp);
+  const int rpages = w / PAGE;
+  for (int p = threadIdx.x; p <= np; p += blockDim.x) {
+    if (p == np) {
+      wbase[np] = 0;
+      continue;
+    }
+    int pages = cdiv(npool[p], PAGE);
+    if (pbase[p] + pages > a.kv.num_pages) {
+      errbits |= KVP_ERR_POOL_FULL;
+      pages = max(0, a.kv.num_pages - pbase[p]);
+      npool[p] = min(npool[p], pages * PAGE);
+    }
+    int pages8 = cdiv(n8[p], PAGE);
+    if (a.demote && p8base[p] + pages8 > a.kv.num_pages8) {
+      errbits |= KVP_ERR_POOL8_FULL;
+      pages8 = max(0, a.kv.num_pages8 - p8base[p]);
+      n8[p] = min(n8[p], pages8 * PAGE);
+    }
+    a.kv.length[p] = npool[p];
+    if (a.kv.num_pages8 > 0) a.kv.length8[p] = a.demote ? n8[p] : 0;
+    wbase[p] = pages + rpages + pages8;
+  }
+  __syncthreads();
+  block_excl_scan_lds(wbase, np + 1, tmp);
+  if (threadIdx.x == 0) {
+    a.kv.page_top[0] = min(total, a.kv.num_pages);
+    if (a.kv.num_pages8 > 0) a.kv.page8_top[0] = a.demote ? min(total8, a.kv.num_pages8) : 0;
+  }
+  if (errbits) atomicOr(a.kv.err, errbits);
+}
+
+template <typename E>
+__device__ __forceinline__ float elem_to_f32(E x);
+template <>
+__device__ __forceinline__ float elem_to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+template <>
+__device__ __forceinline__ float elem_to_f32<float>(float x) { return x; }
+
+// Copy 16 source rows (src[i] < 0 -> zeros) of K and V into a K page [16][d] and a
+// V^T page [d][16].
+template <typename E>
+__device__ void copy_page(const E* ksrc, const E* vsrc, int d, const int* src, E* kdst, E* vdst,
+                          E* vbuf) {
+  const int tid = threadIdx.x;
+  constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
+  const int cpr = d / EPC;             // chunks per row
+  for (int c = tid; c < PAGE * cpr; c += blockDim.x) {
+    const int row = c / cpr, col = (c % cpr) * EPC;
+    const int s = src[row];
+    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
+    if (s >= 0) {
+      kx = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)s * d + col);
+      vx = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)s * d + col);
+    }
+    *reinterpret_cast<u32x4*>(kdst + row * d + col) = kx;
+    *reinterpret_cast<u32x4*>(vbuf + row * d + col) = vx;
+  }
+  __syncthreads();
+  // V^T: row dd holds the 16 slots of dim dd
+  constexpr int CPT = 16 / EPC;  // chunks per V^T row
+  for (int c = tid; c < d * CPT; c += blockDim.x) {
+    const int dd = c / CPT, t0 = (c % CPT) * EPC;
+    E tmp[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) tmp[e] = vbuf[(t0 + e) * d + dd];
+    *reinterpret_cast<u32x4*>(vdst + dd * PAGE + t0) = *reinterpret_cast<u32x4*>(tmp);
+  }
+  __syncthreads();
+}
+
+// Quantize 16 source rows into an int8 K page [16][d] and an int8 V^T page [d][16]
+// with one fp32 absmax scale per slot for K and for V.
+template <typename E>
+__device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, int8_t* kdst,
+                           int8_t* vdst, float* ksc, float* vsc, int8_t* cbuf) {
+  const int tid = threadIdx.x;
+  constexpr int EPC = 16 / sizeof(E);
+  const int cpr = d / EPC;  // threads per row (power of two, <= 16)
+  for (int c = tid; c < PAGE * cpr; c += blockDim.x) {
+    const int row = c / cpr, col = (c % cpr) * EPC;
+    const int s = src[row];
+    float kf[EPC], vf[EPC];
+    if (s >= 0) {
+      u32x4 kx = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)s * d + col);
+      u32x4 vx = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)s * d + col);
+      const E* ke = reinterpret_cast<const E*>(&kx);
+      const E* ve = reinterpret_cast<const E*>(&vx);
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        kf[e] = elem_to_f32<E>(ke[e]);
+        vf[e] = elem_to_f32<E>(ve[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) kf[e] = vf[e] = 0.f;
+    }
+    float ka = 0.f, va = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      ka = fmaxf(ka, fabsf(kf[e]));
+      va = fmaxf(va, fabsf(vf[e]));
+    }
+    for (int o = 1; o < cpr; o <<= 1) {
+      ka = fmaxf(ka, __shfl_xor(ka, o));
+      va = fmaxf(va, __shfl_xor(va, o));
+    }
+    const float kscale = ka / 127.0f, vscale = va / 127.0f;
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      kdst[row * d + col + e] = static_cast<int8_t>(quant_code(kf[e], kscale));
+      cbuf[row * d + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale));
+    }
+    if ((c % cpr) == 0) {
+      ksc[row] = kscale;
+      vsc[row] = vscale;
+    }
+  }
+  __syncthreads();
+  for (int dd = tid; dd < d; dd += blockDim.x) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t x = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        x |= (static_cast<uint32_t>(static_cast<uint8_t>(cbuf[(4 * q + e) * d + dd]))) << (8 * e);
+      w[q] = x;
+    }
+    *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+  __syncthreads();
+}
+
+template <typename E>
+__global__ __launch_bounds__(CMP_THREADS) void compact_gather_kernel(CompactArgs a) {
+  __shared__ int src[PAGE];
+  __shared__ __attribute__((aligned(16))) E vbuf[PAGE * 128];
+  const int np = a.num_pairs;
+  const int* wbase = ws_wbase(a);
+  const int total = wbase[np];
+  const int d = a.d;
+  const int w = a.has_ring ? a.ring.window : 0;
+  const int rpages = w / PAGE;
+  for (int wp = blockIdx.x; wp < total; wp += gridDim.x) {
+    const int p = upper_segment(wbase, np, wp);
+    const int local = wp - wbase[p];
+    const int npl = ws_npool(a)[p];
+    const int pages = cdiv(npl, PAGE);
+    const int cnt = a.kept_count[p];
+    const int* idx = a.kept_idx + (int64_t)p * a.T;
+    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * d;
+    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * d;
+    if (local < pages) {
+      const int j = local;
+      const int dst = ws_pbase(a)[p] + j;
+      if (threadIdx.x < PAGE) {
+        const int i = threadIdx.x;
+        const int s = (j * PAGE + i < npl) ? idx[j * PAGE + i] : -1;
+        src[i] = s;
+        a.kv.page_pos[(int64_t)dst * PAGE + i] = s;
+      }
+      if (threadIdx.x == 0) a.kv.block_table[(int64_t)p * a.kv.max_pages_per_pair + j] = dst;
+      __syncthreads();
+      copy_page<E>(ksrc, vsrc, d, src, reinterpret_cast<E*>(a.kv.k_pages) + (int64_t)dst * PAGE * d,
+                   reinterpret_cast<E*>(a.kv.v_pages) + (int64_t)dst * PAGE * d, vbuf);
+    } else if (local < pages + rpages) {
+      const int r = local - pages;
+      if (threadIdx.x < PAGE) {
+        const int i = threadIdx.x;
+        const int slot = r * PAGE + i;
+        const int base = a.T - w;
+        int t = base + (((slot - base) % w) + w) % w;
+        int s = -1;
+        if (t >= 0) {
+          const int nr = ws_nring(a)[p];
+          const int lo = cnt - nr;
+          const int at = lower_bound_i(idx, lo, cnt, t);
+          if (at < cnt && idx[at] == t) s = t;
+        }
+        src[i] = s;
+        a.ring.pos[(int64_t)p * w + slot] = s;
+        a.ring.score[(int64_t)p * w + slot] = (s >= 0) ? a.scores[(int64_t)p * a.ld_s + s] : 0.f;
+      }
+      __syncthreads();
+      const int64_t off = ((int64_t)p * rpages + r) * PAGE * d;
+      copy_page<E>(ksrc, vsrc, d, src, reinterpret_cast<E*>(a.ring.k) + off,
+                   reinterpret_cast<E*>(a.ring.v) + off, vbuf);
+    } else {
+      const int j8 = local - pages - rpages;
+      const int ne = ws_n8(a)[p];
+      const int dst = ws_p8base(a)[p] + j8;
+      if (threadIdx.x < PAGE) {
+        const int i = threadIdx.x;
+        const int s = (j8 * PAGE + i < ne) ? idx[cnt + j8 * PAGE + i] : -1;
+        src[i] = s;
+        a.kv.page8_pos[(int64_t)dst * PAGE + i] = s;
+      }
+      if (threadIdx.x == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = dst;
+      __syncthreads();
+      quant_page<E>(ksrc, vsrc, d, src, a.kv.k8_pages + (int64_t)dst * PAGE * d,
+                    a.kv.v8_pages + (int64_t)dst * PAGE * d, a.kv.k8_scale + (int64_t)dst * PAGE,
+                    a.kv.v8_scale + (int64_t)dst * PAGE, reinterpret_cast<int8_t*>(vbuf));
+    }
+  }
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+extern "C" size_t kvp_compact_workspace_size(int32_t B, int32_t Hkv) {
+  if (B <= 0 || Hkv <= 0) return 0;
+  const size_t np = (size_t)B * Hkv;
+  return ((6 * np + 1 + 64) * sizeof(int) + 255) & ~(size_t)255;
+}
+
+kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T, int d,
+                              const int* kept_idx, const int* kept_count, const float* scores,
+                              int64_t ld_s, int demote, const kvp_paged_kv* kv,
+                              const kvp_ring* ring, void* ws, hipStream_t stream) {
+  CompactArgs a;
+  a.k = k;
+  a.v = v;
+  a.T = T;
+  a.d = d;
+  a.num_pairs = num_pairs;
+  a.kept_idx = kept_idx;
+  a.kept_count = kept_count;
+  a.scores = scores;
+  a.ld_s = ld_s;
+  a.demote = demote;
+  a.kv = *kv;
+  a.has_ring = ring != nullptr;
+  if (ring) a.ring = *ring;
+  else a.ring = kvp_ring{};
+  a.ws = reinterpret_cast<int*>(ws);
+  hipLaunchKernelGGL(compact_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a);
+  KVP_LAUNCH_CHECK();
+  if (kv->dtype == KVP_BF16)
+    hipLaunchKernelGGL(compact_gather_kernel<uint16_t>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+  else
+    hipLaunchKernelGGL(compact_gather_kernel<float>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
+}

@@ -1,0 +1,184 @@
+// extern "C" entry points of libkvp: argument validation on the host, then the
+// stream-ordered kernel launches in the per-step translation units.  Nothing here
+// allocates or synchronises (except kvp_check), and no exception escapes.
+#include <string.h>
+
+#include "kvp_internal.h"
+
+// launchers (defined next to their kernels)
+kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int T, float* scores,
+                            int64_t ld_s, void* ws, hipStream_t stream);
+kvp_status kvp_launch_select(const float* scores, int num_pairs, int T, int64_t ld_s, float tau,
+                             int recent, uint32_t* bits, int* kept_idx, int* kept_count, void* ws,
+                             hipStream_t stream);
+kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T, int d,
+                              const int* kept_idx, const int* kept_count, const float* scores,
+                              int64_t ld_s, int demote, const kvp_paged_kv* kv, const kvp_ring* ring,
+                              void* ws, hipStream_t stream);
+kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                   const void* v_new, const float* s_new, int64_t ld_s, float tau,
+                                   int p, hipStream_t stream);
+kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
+                                  const kvp_ring* ring, float sm_scale, float* out, void* ws,
+                                  hipStream_t stream);
+kvp_status kvp_launch_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream);
+kvp_status kvp_launch_clear_error(const kvp_paged_kv* kv, hipStream_t stream);
+size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32);
+
+namespace {
+
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
+bool is_kv_dtype(int32_t dt) { return dt == KVP_F32 || dt == KVP_BF16; }
+
+kvp_status check_kv(const kvp_paged_kv* kv) {
+  if (!kv) return KVP_E_ARG;
+  if (!is_kv_dtype(kv->dtype)) return KVP_E_DTYPE;
+  if (kv->num_pairs <= 0 || kv->num_pairs > 65535) return KVP_E_ARG;
+  if (kv->head_dim != 64 && kv->head_dim != 128) return KVP_E_UNSUPPORTED;
+  if (kv->num_pages < 0 || kv->max_pages_per_pair <= 0) return KVP_E_ARG;
+  if (!kv->k_pages || !kv->v_pages || !kv->page_pos || !kv->block_table || !kv->length ||
+      !kv->page_top || !kv->err)
+    return KVP_E_ARG;
+  if (kv->num_pages8 < 0) return KVP_E_ARG;
+  if (kv->num_pages8 > 0) {
+    if (kv->max_pages8_per_pair <= 0) return KVP_E_ARG;
+    if (!kv->k8_pages || !kv->v8_pages || !kv->k8_scale || !kv->v8_scale || !kv->page8_pos ||
+        !kv->block_table8 || !kv->length8 || !kv->page8_top)
+      return KVP_E_ARG;
+  }
+  return KVP_OK;
+}
+
+kvp_status check_ring(const kvp_ring* r) {
+  if (!r) return KVP_OK;
+  if (r->window <= 0 || r->window % KVP_PAGE != 0) return KVP_E_ARG;
+  if (!r->k || !r->v || !r->score || !r->pos) return KVP_E_ARG;
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" const char* kvp_status_str(kvp_status s) {
+  switch (s) {
+    case KVP_OK: return "KVP_OK";
+    case KVP_E_ARG: return "KVP_E_ARG: invalid argument";
+    case KVP_E_DTYPE: return "KVP_E_DTYPE: unsupported dtype combination";
+    case KVP_E_WORKSPACE: return "KVP_E_WORKSPACE: workspace missing or too small";
+    case KVP_E_CAPACITY: return "KVP_E_CAPACITY: page pool or block table exhausted";
+    case KVP_E_HIP: return "KVP_E_HIP: HIP runtime error";
+    case KVP_E_UNSUPPORTED: return "KVP_E_UNSUPPORTED: not implemented for these sizes";
+  }
+  return "KVP_E_UNKNOWN";
+}
+
+extern "C" const char* kvp_version(void) { return "libkvp 0.1.0 gfx950"; }
+
+extern "C" kvp_status kvp_score(const kvp_scorer* sc, const void* hidden, int32_t hdtype, int32_t B,
+                                int32_t T, float* scores, int64_t ld_s, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  if (!sc || !hidden || !scores || !sc->w1) return KVP_E_ARG;
+  if (B <= 0 || T <= 0 || ld_s < T || sc->hidden <= 0) return KVP_E_ARG;
+  if ((int64_t)B * T > kMaxTokens) return KVP_E_ARG;
+  if (sc->n_kv_heads <= 0 || sc->n_kv_heads > 16) return KVP_E_UNSUPPORTED;
+  if (!is_kv_dtype(hdtype) || hdtype != sc->wdtype) return KVP_E_DTYPE;
+  if (sc->kind == KVP_SCORER_LINEAR) {
+    if (hdtype == KVP_BF16 && sc->hidden % 32 != 0) return KVP_E_UNSUPPORTED;
+  } else if (sc->kind == KVP_SCORER_MLP) {
+    if (hdtype != KVP_BF16) return KVP_E_DTYPE;
+    if (!sc->w2) return KVP_E_ARG;
+    if (sc->inner <= 0 || sc->inner % 256 != 0 || sc->hidden % 64 != 0) return KVP_E_UNSUPPORTED;
+    const size_t need = kvp_score_workspace_size(sc, B, T);
+    if (!ws || ws_bytes < need) return KVP_E_WORKSPACE;
+  } else {
+    return KVP_E_ARG;
+  }
+  return kvp_launch_score(sc, hidden, B, T, scores, ld_s, ws, stream);
+}
+
+extern "C" kvp_status kvp_select(const float* scores, int32_t B, int32_t Hkv, int32_t T,
+                                 int64_t ld_s, float tau, int32_t recent, uint32_t* keep_bits,
+                                 int32_t* kept_idx, int32_t* kept_count, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (!scores || !keep_bits || !kept_idx || !kept_count) return KVP_E_ARG;
+  if (B <= 0 || Hkv <= 0 || T <= 0 || ld_s < T || recent < 0) return KVP_E_ARG;
+  if ((int64_t)B * Hkv > 65535 || T > kMaxTokens) return KVP_E_ARG;
+  if (!ws || ws_bytes < kvp_select_workspace_size(B, Hkv, T)) return KVP_E_WORKSPACE;
+  return kvp_launch_select(scores, B * Hkv, T, ld_s, tau, recent, keep_bits, kept_idx, kept_count,
+                           ws, stream);
+}
+
+extern "C" kvp_status kvp_compact(const void* k, const void* v, int32_t dtype, int32_t B,
+                                  int32_t Hkv, int32_t T, int32_t d, const int32_t* kept_idx,
+                                  const int32_t* kept_count, const float* scores, int64_t ld_s,
+                                  int32_t mode, const kvp_paged_kv* kv, const kvp_ring* ring, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  kvp_status st = check_kv(kv);
+  if (st != KVP_OK) return st;
+  if ((st = check_ring(ring)) != KVP_OK) return st;
+  if (!k || !v || !kept_idx || !kept_count) return KVP_E_ARG;
+  if (B <= 0 || Hkv <= 0 || T <= 0 || T > kMaxTokens) return KVP_E_ARG;
+  if ((int64_t)B * Hkv != kv->num_pairs) return KVP_E_ARG;
+  if (d != kv->head_dim) return KVP_E_ARG;
+  if (dtype != kv->dtype) return KVP_E_DTYPE;
+  if (mode != KVP_COMPACT_EVICT && mode != KVP_COMPACT_DEMOTE_INT8) return KVP_E_ARG;
+  if (mode == KVP_COMPACT_DEMOTE_INT8 && kv->num_pages8 <= 0) return KVP_E_ARG;
+  if (ring && (!scores || ld_s < T)) return KVP_E_ARG;
+  if (!ws || ws_bytes < kvp_compact_workspace_size(B, Hkv)) return KVP_E_WORKSPACE;
+  return kvp_launch_compact(k, v, kv->num_pairs, T, d, kept_idx, kept_count, scores, ld_s,
+                            mode == KVP_COMPACT_DEMOTE_INT8, kv, ring, ws, stream);
+}
+
+extern "C" kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
+                                       const void* k_new, const void* v_new, int32_t dtype,
+                                       const float* s_new, int64_t ld_s, float tau, int32_t p,
+                                       hipStream_t stream) {
+  kvp_status st = check_kv(kv);
+  if (st != KVP_OK) return st;
+  if (!ring) return KVP_E_ARG;
+  if ((st = check_ring(ring)) != KVP_OK) return st;
+  if (!k_new || !v_new || !s_new || ld_s < 1 || p < 0) return KVP_E_ARG;
+  if (dtype != kv->dtype) return KVP_E_DTYPE;
+  return kvp_launch_step_delayed(kv, ring, k_new, v_new, s_new, ld_s, tau, p, stream);
+}
+
+extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
+                                      const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
+                                      float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  kvp_status st = check_kv(kv);
+  if (st != KVP_OK) return st;
+  if ((st = check_ring(ring)) != KVP_OK) return st;
+  if (!q || !out) return KVP_E_ARG;
+  if (B <= 0 || Hq <= 0 || kv->num_pairs % B != 0) return KVP_E_ARG;
+  const int Hkv = kv->num_pairs / B;
+  if (Hq % Hkv != 0) return KVP_E_ARG;
+  if (Hq / Hkv > 16) return KVP_E_UNSUPPORTED;
+  if (qdtype != kv->dtype) return KVP_E_DTYPE;
+  if (kv->num_pages8 > 0 && kv->dtype != KVP_BF16) return KVP_E_DTYPE;
+  if (kvp_attn_lds_bytes_host(kv->num_pairs, kv->head_dim, kv->dtype == KVP_F32) > 160 * 1024)
+    return KVP_E_UNSUPPORTED;
+  if (!ws || ws_bytes < kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs, kv->head_dim))
+    return KVP_E_WORKSPACE;
+  return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream);
+}
+
+extern "C" kvp_status kvp_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream) {
+  kvp_status st = check_kv(kv);
+  if (st != KVP_OK) return st;
+  if ((st = check_ring(ring)) != KVP_OK) return st;
+  return kvp_launch_reset(kv, ring, stream);
+}
+
+extern "C" kvp_status kvp_clear_error(const kvp_paged_kv* kv, hipStream_t stream) {
+  if (!kv || !kv->err) return KVP_E_ARG;
+  return kvp_launch_clear_error(kv, stream);
+}
+
+extern "C" kvp_status kvp_check(const kvp_paged_kv* kv, hipStream_t stream) {
+  if (!kv || !kv->err) return KVP_E_ARG;
+  if (hipStreamSynchronize(stream) != hipSuccess) return KVP_E_HIP;
+  int host_err = 0;
+  if (hipMemcpy(&host_err, kv->err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+    return KVP_E_HIP;
+  return host_err ? KVP_E_CAPACITY : KVP_OK;
+}

@@ -1,0 +1,130 @@
+// Internal helpers shared by the libkvp translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "kvp.h"
+
+namespace kvp {
+
+constexpr int PAGE = KVP_PAGE;
+constexpr int WAVE = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 16x16x32 bf16 MFMA, fp32 accumulate.  Operand A: lane l holds row (l % 16) and 8
+// K-slots of group (l / 16); operand B: column (l % 16), same K-slot group; the result
+// C[r][c] sits in lane c + 16 * (r / 4), element r % 4.  K-slot order within a group
+// only has to agree between A and B, which every caller keeps.
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Inclusive scan of one int per lane across the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(v, o);
+    if (lane >= o) v += u;
+  }
+  return v;
+}
+
+// Number of set bits of a 64-bit wave mask below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0));
+}
+
+// Exclusive scan over n ints held in LDS, by the whole block (blockDim.x threads,
+// multiple of 64).  Returns the total.  `tmp` needs one int per wave.
+__device__ inline int block_excl_scan_lds(int* data, int n, int* tmp) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = nt >> 6;
+  int carry = 0;
+  for (int base = 0; base < n; base += nt) {
+    int i = base + tid;
+    int v = (i < n) ? data[i] : 0;
+    int inc = wave_incl_scan(v);
+    if (lane == 63) tmp[wid] = inc;
+    __syncthreads();
+    int woff = 0;
+    for (int w = 0; w < wid; ++w) woff += tmp[w];
+    int tot = 0;
+    for (int w = 0; w < nw; ++w) tot += tmp[w];
+    __syncthreads();
+    if (i < n) data[i] = carry + woff + inc - v;
+    carry += tot;
+  }
+  __syncthreads();
+  return carry;
+}
+
+// Binary search in an ascending array a[0..n]: largest s in [0, n) with a[s] <= x.
+__device__ __forceinline__ int upper_segment(const int* a, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Symmetric int8 code of x with the given fp32 scale: round half to even, clamp
+// to +-127; a zero scale gives code 0.
+__device__ __forceinline__ int quant_code(float x, float scale) {
+  if (scale == 0.0f) return 0;
+  float y = rintf(x / scale);
+  y = fminf(fmaxf(y, -127.0f), 127.0f);
+  return static_cast<int>(y);
+}
+
+}  // namespace kvp
+
+#define KVP_LAUNCH_CHECK()                                   \
+  do {                                                       \
+    hipError_t e_ = hipGetLastError();                       \
+    if (e_ != hipSuccess) return KVP_E_HIP;                  \
+  } while (0)

@@ -1,0 +1,340 @@
+// Surrogate importance scorers (gfx950).
+//
+// Method: KVzap digest (max5.ai), key points -- a small surrogate model predicts each
+// cache entry's importance directly from the hidden states, as a single linear layer
+// (KVzap-Linear) or a two-layer MLP (KVzap-MLP); the memory/compute bullet puts their
+// cost at ~0.02% and ~1.1% of the model's linear-projection FLOPs.
+//
+// Kernels:
+//   score_linear_f32   VALU, one thread per (token, head); small fp32 workloads.
+//   score_linear_bf16  16x16x32 bf16 MFMA: S[16 tok x 16 heads] per tile, HBM-bound
+//                      streaming of the hidden rows (W stays in L2).
+//   score_mlp_bf16     LDS-tiled bf16 MFMA GEMM computing A^T = W1 . X^T for a tile of
+//                      256 inner units x 256 tokens; the epilogue adds b1, applies the
+//                      exact erf GELU in fp32 and contracts with W2 on MFMA.  The GELU
+//                      output u is fed to that second MFMA straight from the
+//                      accumulator registers (the 16x16 result layout of two stacked
+//                      tiles is a valid B-operand layout under a K-slot permutation,
+//                      which W2's A operand follows), split into bf16 hi+lo parts, and
+//                      W2 likewise, so the 512-term sum keeps ~16 significant bits per
+//                      term.  Each 256-unit slice writes a partial score; a small finish
+//                      kernel adds the slices in a fixed order plus b2.
+#include "kvp_internal.h"
+
+namespace kvp {
+
+// ------------------------------------------------------------------ linear fp32
+__global__ __launch_bounds__(256) void score_linear_f32_kernel(const float* __restrict__ X,
+                                                               const float* __restrict__ W,
+                                                               const float* __restrict__ bias,
+                                                               int ntok, int H, int Hkv, int T,
+                                                               float* __restrict__ scores,
+                                                               int64_t ld_s) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)ntok * Hkv) return;
+  const int tok = static_cast<int>(idx / Hkv), h = static_cast<int>(idx % Hkv);
+  const float* x = X + (int64_t)tok * H;
+  const float* w = W + (int64_t)h * H;
+  float acc = 0.f;
+  for (int i = 0; i < H; ++i) acc = fmaf(x[i], w[i], acc);
+  if (bias) acc += bias[h];
+  const int b = tok / T, t = tok % T;
+  scores[((int64_t)b * Hkv + h) * ld_s + t] = acc;
+}
+
+// ------------------------------------------------------------------ linear bf16
+constexpr int LIN_TILES = 4;  // 16-token tiles per wave
+
+__global__ __launch_bounds__(256) void score_linear_bf16_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const float* __restrict__ bias,
+    int ntok, int H, int Hkv, int T, float* __restrict__ scores, int64_t ld_s) {
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  const int64_t gw = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t tok0 = gw * (16 * LIN_TILES);
+  if (tok0 >= ntok) return;
+  const uint16_t* xr[LIN_TILES];
+#pragma unroll
+  for (int tt = 0; tt < LIN_TILES; ++tt) {
+    int64_t tok = tok0 + 16 * tt + n;
+    if (tok >= ntok) tok = ntok - 1;
+    xr[tt] = X + tok * H + 8 * j;
+  }
+  const bool hv = n < Hkv;
+  const uint16_t* wr = W + (int64_t)(hv ? n : 0) * H + 8 * j;
+  f32x4 acc[LIN_TILES];
+#pragma unroll
+  for (int tt = 0; tt < LIN_TILES; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = H / 32;
+#pragma unroll 4
+  for (int kk = 0; kk < nk; ++kk) {
+    u32x4 wv = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
+    if (!hv) wv = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int tt = 0; tt < LIN_TILES; ++tt) {
+      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
+      acc[tt] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(wv), acc[tt]);
+    }
+  }
+  if (!hv) return;
+  const float bb = bias ? bias[n] : 0.f;
+#pragma unroll
+  for (int tt = 0; tt < LIN_TILES; ++tt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t tok = tok0 + 16 * tt + 4 * j + i;
+      if (tok < ntok) {
+        const int b = static_cast<int>(tok / T), t = static_cast<int>(tok % T);
+        scores[((int64_t)b * Hkv + n) * ld_s + t] = acc[tt][i] + bb;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ MLP bf16
+constexpr int MLP_BM = 256;  // inner units per work-group
+constexpr int MLP_BN = 256;  // tokens per work-group
+constexpr int MLP_BK = 64;
+constexpr int MLP_THREADS = 512;
+constexpr int MLP_ROWB = MLP_BK * 2;                // bytes per LDS row (128)
+constexpr int MLP_TILEB = MLP_BM * MLP_ROWB;        // 32 KB per operand tile
+constexpr int MLP_STAGEB = 2 * MLP_TILEB;           // A + B
+constexpr int MLP_LDSB = 2 * MLP_STAGEB;            // double buffered: 128 KB
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * MLP_ROWB + 16 * (chunk ^ (row & 7));
+}
+
+__device__ __forceinline__ float gelu_erf(float a) {
+  return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+}
+
+struct MlpArgs {
+  const uint16_t* X;   // [ntok][H]
+  const uint16_t* W1;  // [inner][H]
+  const float* b1;     // [inner] or null
+  const float* W2;     // [Hkv][inner]
+  float* part;         // [inner/256][ntok][16]
+  int ntok, H, inner, Hkv;
+};
+
+__global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[MLP_LDSB];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = lane & 15, j = lane >> 4;
+  const int wm = wid & 3, wn = wid >> 2;  // wave tile: inner [64wm,+64) x tokens [128wn,+128)
+  const int64_t tok0 = (int64_t)blockIdx.x * MLP_BN;
+  const int in0 = blockIdx.y * MLP_BM;
+  const int H = a.H;
+
+  // global -> LDS copy assignment: 4 A chunks + 4 B chunks (16 B each) per thread
+  const uint16_t* ga[4];
+  const uint16_t* gb[4];
+  int la[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int c = tid + MLP_THREADS * q;  // 0..2047
+    const int row = c >> 3, ch = c & 7;
+    ga[q] = a.W1 + (int64_t)(in0 + row) * H + 8 * ch;
+    int64_t tok = tok0 + row;
+    if (tok >= a.ntok) tok = a.ntok - 1;
+    gb[q] = a.X + tok * H + 8 * ch;
+    la[q] = swz(row, ch);
+  }
+  u32x4 ra[4], rb[4];
+  auto gload = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ra[q] = *reinterpret_cast<const u32x4*>(ga[q] + kt * MLP_BK);
+      rb[q] = *reinterpret_cast<const u32x4*>(gb[q] + kt * MLP_BK);
+    }
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* base = lds + buf * MLP_STAGEB;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *reinterpret_cast<u32x4*>(base + la[q]) = ra[q];
+      *reinterpret_cast<u32x4*>(base + MLP_TILEB + la[q]) = rb[q];
+    }
+  };
+
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nk = H / MLP_BK;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload(kt + 1);
+    const uint8_t* As = lds + cur * MLP_STAGEB;
+    const uint8_t* Bs = As + MLP_TILEB;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ch = 4 * ks + j;
+      bf16x8 af[4], bfr[8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int row = 64 * wm + 16 * mt + n;
+        af[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(As + swz(row, ch)));
+      }
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int row = 128 * wn + 16 * nt + n;
+        bfr[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(Bs + swz(row, ch)));
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma16x16x32(af[mt], bfr[nt], acc[mt][nt]);
+    }
+    if (kt + 1 < nk) lstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: u = GELU(acc + b1) (fp32), s_part = W2[:, slice] . u on MFMA
+  // acc[mt][nt][i] = A^T[inner 64wm + 16mt + 4j + i][token 128wn + 16nt + n]
+  // second-layer K-step kst uses M-tiles 2kst, 2kst+1; K-slot v of lane group j is
+  // inner row 32kst + 4j + v (v < 4) or 32kst + 16 + 4j + (v - 4) (v >= 4).
+  u32x4 w2hi[2], w2lo[2];
+#pragma unroll
+  for (int kst = 0; kst < 2; ++kst) {
+    float wv[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      const int r = 64 * wm + 32 * kst + (v < 4 ? 4 * j + v : 16 + 4 * j + (v - 4));
+      wv[v] = (n < a.Hkv) ? a.W2[(int64_t)n * a.inner + in0 + r] : 0.f;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint16_t h0 = f32_to_bf16(wv[2 * q]), h1 = f32_to_bf16(wv[2 * q + 1]);
+      w2hi[kst][q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+      w2lo[kst][q] = pack_bf16x2(wv[2 * q] - bf16_to_f32(h0), wv[2 * q + 1] - bf16_to_f32(h1));
+    }
+  }
+  float b1v[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = in0 + 64 * wm + 16 * mt + 4 * j + i;
+      b1v[mt][i] = a.b1 ? a.b1[r] : 0.f;
+    }
+  f32x4 sacc[8];
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt) {
+    sacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kst = 0; kst < 2; ++kst) {
+      float u[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        u[i] = gelu_erf(acc[2 * kst][nt][i] + b1v[2 * kst][i]);
+        u[i + 4] = gelu_erf(acc[2 * kst + 1][nt][i] + b1v[2 * kst + 1][i]);
+      }
+      u32x4 uhi, ulo;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint16_t h0 = f32_to_bf16(u[2 * q]), h1 = f32_to_bf16(u[2 * q + 1]);
+        uhi[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        ulo[q] = pack_bf16x2(u[2 * q] - bf16_to_f32(h0), u[2 * q + 1] - bf16_to_f32(h1));
+      }
+      sacc[nt] = mfma16x16x32(as_bf16x8(w2hi[kst]), as_bf16x8(uhi), sacc[nt]);
+      sacc[nt] = mfma16x16x32(as_bf16x8(w2lo[kst]), as_bf16x8(uhi), sacc[nt]);
+      sacc[nt] = mfma16x16x32(as_bf16x8(w2hi[kst]), as_bf16x8(ulo), sacc[nt]);
+    }
+  }
+  // sacc[nt][i] = partial s[head 4j+i][token 128wn + 16nt + n] over this wave's 64 units
+  __syncthreads();  // done with the GEMM tiles; reuse LDS for the cross-wave sum
+  float* red = reinterpret_cast<float*>(lds);  // [4 wm][256 tokens][16 heads]
+#pragma unroll
+  for (int nt = 0; nt < 8; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      red[(wm * MLP_BN + 128 * wn + 16 * nt + n) * 16 + 4 * j + i] = sacc[nt][i];
+  __syncthreads();
+  float* dst = a.part + ((int64_t)blockIdx.y * a.ntok) * 16;
+  for (int e = tid; e < MLP_BN * 16; e += MLP_THREADS) {
+    const int t = e >> 4, h = e & 15;
+    const int64_t tok = tok0 + t;
+    if (tok < a.ntok && h < a.Hkv) {
+      float s = red[(0 * MLP_BN + t) * 16 + h];
+      s += red[(1 * MLP_BN + t) * 16 + h];
+      s += red[(2 * MLP_BN + t) * 16 + h];
+      s += red[(3 * MLP_BN + t) * 16 + h];
+      dst[tok * 16 + h] = s;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void score_mlp_finish_kernel(const float* __restrict__ part,
+                                                               int nparts, int ntok, int Hkv,
+                                                               const float* __restrict__ b2, int T,
+                                                               float* __restrict__ scores,
+                                                               int64_t ld_s) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)ntok * Hkv) return;
+  // consecutive threads walk tokens of one (b, h) row so score stores coalesce
+  const int64_t bh = idx / T;
+  const int t = static_cast<int>(idx % T);
+  const int b = static_cast<int>(bh / Hkv), h = static_cast<int>(bh % Hkv);
+  const int64_t tok = (int64_t)b * T + t;
+  float s = part[tok * 16 + h];
+  for (int q = 1; q < nparts; ++q) s += part[((int64_t)q * ntok + tok) * 16 + h];
+  if (b2) s += b2[h];
+  scores[bh * ld_s + t] = s;
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+extern "C" size_t kvp_score_workspace_size(const kvp_scorer* sc, int32_t B, int32_t T) {
+  if (!sc || B <= 0 || T <= 0) return 0;
+  if (sc->kind != KVP_SCORER_MLP) return 0;
+  if (sc->inner <= 0 || sc->inner % MLP_BM != 0) return 0;
+  return (size_t)(sc->inner / MLP_BM) * (size_t)B * T * 16 * sizeof(float);
+}
+
+kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int T, float* scores,
+                            int64_t ld_s, void* ws, hipStream_t stream) {
+  const int ntok = B * T;
+  const int H = sc->hidden, Hkv = sc->n_kv_heads;
+  if (sc->kind == KVP_SCORER_LINEAR) {
+    if (sc->wdtype == KVP_F32) {
+      const int64_t n = (int64_t)ntok * Hkv;
+      hipLaunchKernelGGL(score_linear_f32_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, stream,
+                         reinterpret_cast<const float*>(hidden), reinterpret_cast<const float*>(sc->w1),
+                         sc->b1, ntok, H, Hkv, T, scores, ld_s);
+    } else {
+      const int64_t waves = cdiv64(ntok, 16 * LIN_TILES);
+      hipLaunchKernelGGL(score_linear_bf16_kernel, dim3((unsigned)cdiv64(waves, 4)), dim3(256), 0, stream,
+                         reinterpret_cast<const uint16_t*>(hidden),
+                         reinterpret_cast<const uint16_t*>(sc->w1), sc->b1, ntok, H, Hkv, T, scores, ld_s);
+    }
+    KVP_LAUNCH_CHECK();
+    return KVP_OK;
+  }
+  MlpArgs m;
+  m.X = reinterpret_cast<const uint16_t*>(hidden);
+  m.W1 = reinterpret_cast<const uint16_t*>(sc->w1);
+  m.b1 = sc->b1;
+  m.W2 = sc->w2;
+  m.part = reinterpret_cast<float*>(ws);
+  m.ntok = ntok;
+  m.H = H;
+  m.inner = sc->inner;
+  m.Hkv = Hkv;
+  const int nparts = sc->inner / MLP_BM;
+  hipLaunchKernelGGL(score_mlp_bf16_kernel, dim3((unsigned)cdiv64(ntok, MLP_BN), nparts), dim3(MLP_THREADS),
+                     0, stream, m);
+  KVP_LAUNCH_CHECK();
+  const int64_t n = (int64_t)ntok * Hkv;
+  hipLaunchKernelGGL(score_mlp_finish_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, stream, m.part,
+                     nparts, ntok, Hkv, sc->b2, T, scores, ld_s);
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
+}

@@ -1,0 +1,195 @@
+// One decode step of the recent-window ring with delayed eviction (gfx950).
+//
+// Method: DMS article (euno.news), "Delayed Eviction" -- a token flagged for eviction
+// is not removed at once but kept in a short buffer for a fixed number of steps and
+// deleted when that window expires; "How DMS works" step 3 -- the keep/evict signal
+// is binary per token.  KVzap digest (max5.ai), practical application -- the most
+// recent tokens are always kept and low-scoring ones are removed.
+//
+// The ring holds the last `window` positions of every pair (position t in slot
+// t mod window).  Appending position p evicts position p - window from its slot:
+// that token is appended to the retained pool iff its score >= tau, else dropped
+// (or demoted to the int8 pool when one exists).  One wave per pair; O(1) work.
+#include "kvp_internal.h"
+
+namespace kvp {
+
+struct StepArgs {
+  kvp_paged_kv kv;
+  kvp_ring ring;
+  const void* k_new;
+  const void* v_new;
+  const float* s_new;
+  int64_t ld_s;
+  float tau;
+  int p;
+};
+
+template <typename E>
+__device__ __forceinline__ float to_f32(E x);
+template <>
+__device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
+template <>
+__device__ __forceinline__ float to_f32<float>(float x) { return x; }
+
+template <typename E, int D>
+__global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= a.kv.num_pairs) return;
+  const int w = a.ring.window;
+  const int slot = a.p % w;
+  const int rp = slot / PAGE, rs = slot % PAGE;
+  const int64_t roff = ((int64_t)pair * (w / PAGE) + rp) * PAGE * D;
+  E* rk = reinterpret_cast<E*>(a.ring.k) + roff + rs * D;  // K row of the slot
+  E* rv = reinterpret_cast<E*>(a.ring.v) + roff + rs;      // V column, stride PAGE
+  const int old_pos = a.ring.pos[(int64_t)pair * w + slot];
+  const float old_s = a.ring.score[(int64_t)pair * w + slot];
+  constexpr int PER = (D + 63) / 64;
+  E ko[PER], vo[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int dd = lane + 64 * e;
+    if (dd < D) {
+      ko[e] = rk[dd];
+      vo[e] = rv[dd * PAGE];
+    }
+  }
+  if (old_pos >= 0) {
+    if (old_s >= a.tau) {
+      // retain: append to the pool (allocating a page when the last one is full)
+      const int len = a.kv.length[pair];
+      const int j = len / PAGE, sl = len % PAGE;
+      int pg = -1;
+      if (sl == 0) {
+        if (j >= a.kv.max_pages_per_pair) {
+          if (lane == 0) atomicOr(a.kv.err, KVP_ERR_TABLE_FULL);
+        } else {
+          int got = 0;
+          if (lane == 0) got = atomicAdd(a.kv.page_top, 1);
+          got = __shfl(got, 0);
+          if (got >= a.kv.num_pages) {
+            if (lane == 0) atomicOr(a.kv.err, KVP_ERR_POOL_FULL);
+          } else {
+            pg = got;
+            if (lane == 0) a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + j] = pg;
+          }
+        }
+      } else {
+        pg = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + j];
+      }
+      if (pg >= 0) {
+        E* kp = reinterpret_cast<E*>(a.kv.k_pages) + (int64_t)pg * PAGE * D + sl * D;
+        E* vp = reinterpret_cast<E*>(a.kv.v_pages) + (int64_t)pg * PAGE * D + sl;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int dd = lane + 64 * e;
+          if (dd < D) {
+            kp[dd] = ko[e];
+            vp[dd * PAGE] = vo[e];
+          }
+        }
+        if (lane == 0) {
+          a.kv.page_pos[(int64_t)pg * PAGE + sl] = old_pos;
+          a.kv.length[pair] = len + 1;
+        }
+      }
+    } else if (a.kv.num_pages8 > 0) {
+      // demote to the int8 pool (BeaconKV): absmax per row, K and V separately
+      float kf[PER], vf[PER];
+      float ka = 0.f, va = 0.f;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int dd = lane + 64 * e;
+        kf[e] = (dd < D) ? to_f32<E>(ko[e]) : 0.f;
+        vf[e] = (dd < D) ? to_f32<E>(vo[e]) : 0.f;
+        ka = fmaxf(ka, fabsf(kf[e]));
+        va = fmaxf(va, fabsf(vf[e]));
+      }
+      ka = wave_max(ka);
+      va = wave_max(va);
+      const float ks = ka / 127.0f, vs = va / 127.0f;
+      const int len = a.kv.length8[pair];
+      const int j = len / PAGE, sl = len % PAGE;
+      int pg = -1;
+      if (sl == 0) {
+        if (j >= a.kv.max_pages8_per_pair) {
+          if (lane == 0) atomicOr(a.kv.err, KVP_ERR_POOL8_FULL);
+        } else {
+          int got = 0;
+          if (lane == 0) got = atomicAdd(a.kv.page8_top, 1);
+          got = __shfl(got, 0);
+          if (got >= a.kv.num_pages8) {
+            if (lane == 0) atomicOr(a.kv.err, KVP_ERR_POOL8_FULL);
+          } else {
+            pg = got;
+            if (lane == 0) a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + j] = pg;
+          }
+        }
+      } else {
+        pg = a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + j];
+      }
+      if (pg >= 0) {
+        int8_t* kp = a.kv.k8_pages + (int64_t)pg * PAGE * D + sl * D;
+        int8_t* vp = a.kv.v8_pages + (int64_t)pg * PAGE * D + sl;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int dd = lane + 64 * e;
+          if (dd < D) {
+            kp[dd] = static_cast<int8_t>(quant_code(kf[e], ks));
+            vp[dd * PAGE] = static_cast<int8_t>(quant_code(vf[e], vs));
+          }
+        }
+        if (lane == 0) {
+          a.kv.k8_scale[(int64_t)pg * PAGE + sl] = ks;
+          a.kv.v8_scale[(int64_t)pg * PAGE + sl] = vs;
+          a.kv.page8_pos[(int64_t)pg * PAGE + sl] = old_pos;
+          a.kv.length8[pair] = len + 1;
+        }
+      }
+    }
+  }
+  // the new token enters the slot
+  const E* kn = reinterpret_cast<const E*>(a.k_new) + (int64_t)pair * D;
+  const E* vn = reinterpret_cast<const E*>(a.v_new) + (int64_t)pair * D;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int dd = lane + 64 * e;
+    if (dd < D) {
+      rk[dd] = kn[dd];
+      rv[dd * PAGE] = vn[dd];
+    }
+  }
+  if (lane == 0) {
+    a.ring.pos[(int64_t)pair * w + slot] = a.p;
+    a.ring.score[(int64_t)pair * w + slot] = a.s_new[(int64_t)pair * a.ld_s];
+  }
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                   const void* v_new, const float* s_new, int64_t ld_s, float tau,
+                                   int p, hipStream_t stream) {
+  StepArgs a;
+  a.kv = *kv;
+  a.ring = *ring;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.s_new = s_new;
+  a.ld_s = ld_s;
+  a.tau = tau;
+  a.p = p;
+  const dim3 grid(cdiv(kv->num_pairs, 4));
+  if (kv->dtype == KVP_BF16) {
+    if (kv->head_dim == 64) hipLaunchKernelGGL((step_delayed_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((step_delayed_kernel<uint16_t, 128>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (kv->head_dim == 64) hipLaunchKernelGGL((step_delayed_kernel<float, 64>), grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((step_delayed_kernel<float, 128>), grid, dim3(256), 0, stream, a);
+  }
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
+}

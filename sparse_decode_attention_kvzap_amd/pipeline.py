@@ -1,0 +1,104 @@
+"""One attention layer's pruned KV cache driven through the five C-ABI calls.
+
+Prefill (compress a context):  kvp_score -> kvp_select -> kvp_compact
+Decode step (one new token):   kvp_score -> kvp_step_delayed -> kvp_decode_attn
+
+KVzap (max5.ai digest, practical application): score every entry, drop low scores,
+always keep the most recent tokens.  DMS (euno.news, Delayed Eviction): with tau = 0
+and window w the same machinery keeps a flagged token for w steps.  BeaconKV
+(jiinsi.com, body): with demote=True evicted entries go to an int8 pool instead.
+
+This class only allocates device buffers (torch) and calls libkvp in stream order;
+all arithmetic runs in the HIP kernels.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+
+class PrunedKVCache:
+    def __init__(self, B: int, Hkv: int, Hq: int, d: int, T_max: int, dtype: torch.dtype,
+                 scorer: L.Scorer, window: int, tau: float, demote: bool = False,
+                 device="cuda", max_prompt: Optional[int] = None):
+        self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
+        self.P = B * Hkv
+        self.T_max = T_max
+        self.dtype = dtype
+        self.scorer = scorer
+        self.window = window
+        self.tau = float(tau)
+        self.demote = demote
+        self.device = torch.device(device)
+        dev = self.device
+        Tp = max_prompt or T_max
+        self.Tp = Tp
+        maxpp = -(-T_max // L.KVP_PAGE) + 1
+        kw = {}
+        if demote:
+            kw = dict(num_pages8=self.P * maxpp, max_pages8_per_pair=maxpp)
+        self.kv = L.PagedKV.allocate(self.P, d, self.P * maxpp, maxpp, dtype, dev, **kw)
+        self.ring = L.Ring.allocate(self.P, window, d, dtype, dev)
+        self.scores = torch.empty((B, Hkv, Tp), dtype=torch.float32, device=dev)
+        self.s_new = torch.empty((B, Hkv, 1), dtype=torch.float32, device=dev)
+        self.keep_bits = torch.empty((self.P, -(-Tp // 32)), dtype=torch.int32, device=dev)
+        self.kept_idx = torch.empty((self.P, Tp), dtype=torch.int32, device=dev)
+        self.kept_count = torch.empty((self.P,), dtype=torch.int32, device=dev)
+        self.ws_select = torch.empty(max(1, L.kvp_select_workspace_size(B, Hkv, Tp) // 4),
+                                     dtype=torch.int32, device=dev)
+        self.ws_compact = torch.empty(L.kvp_compact_workspace_size(B, Hkv) // 4,
+                                      dtype=torch.int32, device=dev)
+        nws = L.kvp_score_workspace_size(scorer, B, Tp)
+        self.ws_score = torch.empty(max(1, nws // 4), dtype=torch.float32, device=dev)
+        self.ws_attn = L.decode_attn_workspace(B, Hq, self.kv, dev)
+        self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        self.scale = L.sm_scale(d)
+        self.T0 = 0
+
+    # -- prefill -----------------------------------------------------------------
+    def score(self, hidden: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
+        return L.kvp_score(self.scorer, hidden, self.scores if out is None else out,
+                           self.ws_score, stream)
+
+    def select(self, T: int, stream=None):
+        L.kvp_select(self.scores, T, self.tau, self.window, self.keep_bits, self.kept_idx,
+                     self.kept_count, self.ws_select, stream)
+
+    def compact(self, k: torch.Tensor, v: torch.Tensor, stream=None):
+        L.kvp_compact(k, v, self.kept_idx, self.kept_count, self.kv, self.ws_compact,
+                      ring=self.ring, scores=self.scores,
+                      mode=L.KVP_COMPACT_DEMOTE_INT8 if self.demote else L.KVP_COMPACT_EVICT,
+                      stream=stream)
+
+    def prefill(self, hidden: torch.Tensor, k: torch.Tensor, v: torch.Tensor, stream=None):
+        """Compress a context of T = hidden.shape[1] tokens (positions 0..T-1)."""
+        T = hidden.shape[1]
+        self.score(hidden, stream=stream)
+        self.select(T, stream)
+        self.compact(k, v, stream)
+        self.T0 = T
+
+    # -- decode ------------------------------------------------------------------
+    def step(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             q: torch.Tensor, p: int, stream=None) -> torch.Tensor:
+        """Append position p and attend with q over the cache that now holds it."""
+        L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
+        L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau, p, 1, stream)
+        return self.attend(q, stream)
+
+    def attend(self, q: torch.Tensor, stream=None) -> torch.Tensor:
+        L.kvp_decode_attn(q, self.kv, self.ring, self.scale, self.out, self.ws_attn, stream)
+        return self.out
+
+    def visible_token_heads(self) -> int:
+        """Token-heads the next decode attention reads (pool + ring + int8 pool)."""
+        n = int(self.kv.length.sum()) + int((self.ring.pos >= 0).sum())
+        if self.demote:
+            n += int(self.kv.length8.sum())
+        return n
+
+    def check(self, stream=None) -> int:
+        return L.kvp_check(self.kv, stream)

@@ -1,0 +1,408 @@
+"""Kernel-level parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Sizes span several tiles and ragged tails; pools are poison-filled (NaN / sentinel
+ints) so unwritten or over-read elements show up.  Integer and byte results are
+compared bit-exactly; scores within a stated absolute bound; attention outputs with
+the benchmark spec's tolerances (max-abs 2e-3 for bf16 KV, 1e-5 relative per output vector
+for fp32 KV).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kvp_workloads as W
+import oracle
+from kvp_testlib import (band_mask, check_attention, f64, np_bits, read_pool, read_pool8,
+                         read_ring, unpack_bits, visible_positions)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+# fp32 score error bound: the band around tau is 1e-4, scores must agree well inside it
+SCORE_ATOL = 2.5e-5
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_decode_attention_kvzap_amd as K
+    K.load()
+    return K
+
+
+def seeded(shape, seed, dtype=torch.float32, scale=1.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    return (torch.randn(shape, generator=g, device=DEV) * scale).to(dtype)
+
+
+def upload_selection(keep: np.ndarray):
+    P, T = keep.shape
+    idx = np.zeros((P, T), np.int32)
+    cnt = np.zeros(P, np.int32)
+    for p in range(P):
+        k, e = oracle.partition_indices(keep[p])
+        idx[p] = np.concatenate([k, e])
+        cnt[p] = len(k)
+    return torch.from_numpy(idx).to(DEV), torch.from_numpy(cnt).to(DEV)
+
+
+def select_on_gpu(K, scores, T, tau, R):
+    B, Hkv, _ = scores.shape
+    P = B * Hkv
+    bits = torch.full((P, (T + 31) // 32), -1, dtype=torch.int32, device=DEV)
+    idx = torch.full((P, T), -5, dtype=torch.int32, device=DEV)
+    cnt = torch.full((P,), -5, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, K.kvp_select_workspace_size(B, Hkv, T) // 4), dtype=torch.int32,
+                     device=DEV)
+    K.kvp_select(scores, T, tau, R, bits, idx, cnt, ws)
+    return bits, idx, cnt
+
+
+def compact_ws(K, B, Hkv):
+    return torch.empty(K.kvp_compact_workspace_size(B, Hkv) // 4, dtype=torch.int32, device=DEV)
+
+
+# ---------------------------------------------------------------------------- score
+
+
+def test_score_linear_f32_tiny_workload(K):
+    wl = W.TINY
+    x = W.hidden_states(wl, wl.T, DEV)
+    sw = W.scorer_weights(wl, DEV)
+    sc = K.Scorer(K.KVP_SCORER_LINEAR, sw.W1, sw.b1)
+    s = torch.full((wl.B, wl.Hkv, wl.T), float("nan"), device=DEV)
+    K.kvp_score(sc, x, s)
+    ref = oracle.score_linear(f64(x), f64(sw.W1), f64(sw.b1))
+    err = np.abs(s.cpu().double().numpy() - ref).max()
+    assert err < SCORE_ATOL, err
+
+
+@pytest.mark.parametrize("B,T,H,Hkv,ld", [(2, 300, 512, 8, 300), (3, 77, 256, 2, 80),
+                                          (1, 1, 64, 1, 1), (2, 1000, 1024, 16, 1003)])
+def test_score_linear_bf16(K, B, T, H, Hkv, ld):
+    x = seeded((B, T, H), 1, torch.bfloat16)
+    Wt = seeded((Hkv, H), 2, torch.bfloat16, 1 / math.sqrt(H))
+    c = seeded((Hkv,), 3)
+    sc = K.Scorer(K.KVP_SCORER_LINEAR, Wt, c)
+    s = torch.full((B, Hkv, ld), float("nan"), device=DEV)
+    K.kvp_score(sc, x, s)
+    ref = oracle.score_linear(f64(x), f64(Wt), f64(c))
+    got = s[..., :T].cpu().double().numpy()
+    assert np.abs(got - ref).max() < SCORE_ATOL
+    if ld > T:
+        assert torch.isnan(s[..., T:]).all()  # padding untouched
+
+
+@pytest.mark.parametrize("B,T,H,inner,Hkv", [(2, 300, 256, 512, 8), (1, 513, 128, 256, 4),
+                                             (3, 17, 64, 512, 16)])
+def test_score_mlp_bf16(K, B, T, H, inner, Hkv):
+    x = seeded((B, T, H), 11, torch.bfloat16)
+    W1 = seeded((inner, H), 12, torch.bfloat16, 1 / math.sqrt(H))
+    b1 = seeded((inner,), 13, scale=0.5)
+    W2 = seeded((Hkv, inner), 14, scale=1 / math.sqrt(inner))
+    b2 = seeded((Hkv,), 15)
+    sc = K.Scorer(K.KVP_SCORER_MLP, W1, b1, W2, b2)
+    ws = torch.empty(K.kvp_score_workspace_size(sc, B, T) // 4, dtype=torch.float32, device=DEV)
+    s = torch.full((B, Hkv, T), float("nan"), device=DEV)
+    K.kvp_score(sc, x, s, ws)
+    ref = oracle.score_mlp(f64(x), f64(W1), f64(b1), f64(W2), f64(b2))
+    err = np.abs(s.cpu().double().numpy() - ref).max()
+    assert err < SCORE_ATOL, err
+
+
+# ---------------------------------------------------------------------------- select
+
+
+@pytest.mark.parametrize("B,Hkv,T,ld,q,R", [(3, 5, 5000, 5003, 0.6, 128), (1, 1, 1, 1, 0.5, 128),
+                                            (2, 2, 100, 100, 0.9, 128), (1, 4, 2048, 2048, 0.5, 0),
+                                            (2, 3, 2049, 2050, 0.25, 256), (1, 2, 131, 131, 0.5, 3)])
+def test_select_exact(K, B, Hkv, T, ld, q, R):
+    s = seeded((B, Hkv, ld), 21)
+    s[0, 0, T // 3] = float("nan")
+    tau = float(oracle.threshold_quantile(f64(s)[..., :T], q))
+    bits, idx, cnt = select_on_gpu(K, s, T, tau, R)
+    keep = oracle.keep_mask(f64(s)[..., :T], np.float32(tau), R).reshape(B * Hkv, T)
+    assert np.array_equal(unpack_bits(bits, T), keep)
+    words = np_bits(bits).astype(np.uint32)
+    if T % 32:
+        assert (words[:, -1] >> np.uint32(T % 32) == 0).all()  # tail bits zero
+    gi = np_bits(idx)
+    gc = np_bits(cnt)
+    for p in range(B * Hkv):
+        k, e = oracle.partition_indices(keep[p])
+        assert gc[p] == len(k)
+        assert np.array_equal(gi[p], np.concatenate([k, e]))
+
+
+@pytest.mark.parametrize("tau", [float("-inf"), float("inf")])
+def test_select_limits(K, tau):
+    B, Hkv, T = 2, 3, 700
+    s = seeded((B, Hkv, T), 22)
+    bits, idx, cnt = select_on_gpu(K, s, T, tau, 128)
+    c = np_bits(cnt)
+    if tau < 0:
+        assert (c == T).all()
+    else:
+        assert (c == 128).all()
+        assert (np_bits(idx)[:, :128] == np.arange(T - 128, T)).all()
+
+
+# ---------------------------------------------------------------------------- compact
+
+
+@pytest.mark.parametrize("dtype,d,ring_w", [(torch.bfloat16, 128, 0), (torch.bfloat16, 128, 128),
+                                            (torch.float32, 64, 128), (torch.bfloat16, 64, 32),
+                                            (torch.float32, 128, 0)])
+def test_compact_exact(K, dtype, d, ring_w):
+    B, Hkv, T = 2, 3, 700
+    P = B * Hkv
+    k = seeded((B, Hkv, T, d), 31, dtype)
+    v = seeded((B, Hkv, T, d), 32, dtype)
+    s = seeded((B, Hkv, T), 33)
+    R = ring_w if ring_w else 128
+    keep = oracle.keep_mask(f64(s), 0.3, R).reshape(P, T)
+    idx, cnt = upload_selection(keep)
+    kv = K.PagedKV.allocate(P, d, P * (T // 16 + 2), T // 16 + 2, dtype, DEV, poison=True)
+    ring = K.Ring.allocate(P, ring_w, d, dtype, DEV, poison=True) if ring_w else None
+    K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s)
+    assert K.kvp_check(kv) == 0
+    kb = np_bits(k).reshape(P, T, d)
+    vb = np_bits(v).reshape(P, T, d)
+    sb = np_bits(s).reshape(P, T)
+    for p in range(P):
+        kept = np.flatnonzero(keep[p])
+        pool_pos = kept[kept < T - ring_w] if ring_w else kept
+        pos, Kp, Vp = read_pool(kv, p)
+        assert np.array_equal(pos, pool_pos)
+        assert np.array_equal(Kp, kb[p, pool_pos]) and np.array_equal(Vp, vb[p, pool_pos])
+        if ring_w:
+            rpos, Kr, Vr, Sr = read_ring(ring, p)
+            want = kept[kept >= T - ring_w]
+            assert np.array_equal(np.sort(rpos), want)
+            assert ((rpos % ring_w) == np.flatnonzero(np_bits(ring.pos[p]) >= 0)).all()
+            assert np.array_equal(Kr, kb[p, rpos]) and np.array_equal(Vr, vb[p, rpos])
+            assert np.array_equal(Sr, sb[p, rpos])
+
+
+def test_compact_demote_int8_exact(K):
+    B, Hkv, T, d = 2, 2, 500, 128
+    P = B * Hkv
+    k = seeded((B, Hkv, T, d), 41, torch.bfloat16)
+    v = seeded((B, Hkv, T, d), 42, torch.bfloat16, 3.0)
+    k[0, 0, 7] = 0  # all-zero row -> scale 0, codes 0
+    s = seeded((B, Hkv, T), 43)
+    keep = oracle.keep_mask(f64(s), 0.8, 128).reshape(P, T)
+    idx, cnt = upload_selection(keep)
+    kv = K.PagedKV.allocate(P, d, P * 40, 40, torch.bfloat16, DEV, num_pages8=P * 40,
+                            max_pages8_per_pair=40, poison=True)
+    ring = K.Ring.allocate(P, 128, d, torch.bfloat16, DEV, poison=True)
+    K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s,
+                  mode=K.KVP_COMPACT_DEMOTE_INT8)
+    assert K.kvp_check(kv) == 0
+    kf = f64(k).reshape(P, T, d)
+    vf = f64(v).reshape(P, T, d)
+    for p in range(P):
+        ev = np.flatnonzero(~keep[p])
+        pos, Kc, Vc, ks, vs = read_pool8(kv, p)
+        assert np.array_equal(pos, ev)
+        for i, t in enumerate(ev):
+            c, sc = oracle.quantize_absmax_int8(kf[p, t])
+            assert ks[i] == sc and np.array_equal(Kc[i], c), (p, t)
+            c, sc = oracle.quantize_absmax_int8(vf[p, t])
+            assert vs[i] == sc and np.array_equal(Vc[i], c), (p, t)
+        # every position is held exactly once across bf16 pool, ring and int8 pool
+        allpos = visible_positions(kv, ring, p)
+        assert np.array_equal(allpos, np.arange(T))
+
+
+# ---------------------------------------------------------------------------- attention
+
+
+def build_cache(K, B, Hkv, T, d, dtype, keep, ring_w, seed, demote=False, poison=True):
+    P = B * Hkv
+    k = seeded((B, Hkv, T, d), seed, dtype)
+    v = seeded((B, Hkv, T, d), seed + 1, dtype)
+    s = seeded((B, Hkv, T), seed + 2)
+    idx, cnt = upload_selection(keep)
+    maxpp = T // 16 + 2
+    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp) if demote else {}
+    kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, dtype, DEV, poison=poison, **kw)
+    ring = K.Ring.allocate(P, ring_w, d, dtype, DEV, poison=poison) if ring_w else None
+    K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s,
+                  mode=K.KVP_COMPACT_DEMOTE_INT8 if demote else K.KVP_COMPACT_EVICT)
+    return k, v, kv, ring
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,T,d,dtype,ring_w,keepfrac", [
+    (2, 16, 4, 1000, 128, torch.bfloat16, 128, 0.3),
+    (1, 8, 1, 3000, 128, torch.bfloat16, 0, 0.5),
+    (3, 24, 3, 517, 64, torch.bfloat16, 64, 0.2),
+    (1, 4, 2, 512, 64, torch.float32, 128, 0.5),
+    (2, 8, 8, 300, 128, torch.float32, 0, 0.7),
+    (1, 64, 8, 2000, 128, torch.bfloat16, 128, 0.25),
+    (2, 4, 4, 40, 128, torch.bfloat16, 128, 0.5),
+])
+def test_decode_attn(K, B, Hq, Hkv, T, d, dtype, ring_w, keepfrac):
+    P = B * Hkv
+    g = torch.Generator().manual_seed(T + d)
+    keep = (torch.rand((P, T), generator=g) < keepfrac).numpy()
+    keep[:, T - (ring_w or 128):] = True
+    k, v, kv, ring = build_cache(K, B, Hkv, T, d, dtype, keep, ring_w, seed=51)
+    q = seeded((B, Hq, d), 54, dtype)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    ws = K.decode_attn_workspace(B, Hq, kv)
+    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
+    ref = oracle.decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
+                                  oracle.sm_scale(d))
+    check_attention(out, ref, dtype)
+    # deterministic: a rerun gives identical bits; counters were reset
+    out2 = torch.zeros_like(out)
+    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out2, ws)
+    assert torch.equal(out, out2)
+    cb = K.kvp_decode_attn_counter_bytes(P)
+    assert (ws.view(torch.uint8)[:cb] == 0).all()
+
+
+def test_decode_attn_empty_pairs(K):
+    B, Hq, Hkv, T, d = 2, 8, 2, 600, 128
+    P = B * Hkv
+    keep = np.zeros((P, T), bool)
+    keep[1, ::3] = True
+    keep[3, :] = True  # pair 0 and 2 have nothing visible -> zeros
+    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, 0, seed=61)
+    q = seeded((B, Hq, d), 64, torch.bfloat16)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    ws = K.decode_attn_workspace(B, Hq, kv)
+    K.kvp_decode_attn(q, kv, None, K.sm_scale(d), out, ws)
+    ref = oracle.decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T), oracle.sm_scale(d))
+    check_attention(out, ref, torch.bfloat16)
+    assert (out[0, :4] == 0).all() and (out[1, :4] == 0).all()
+
+
+def test_decode_attn_int8_pool(K):
+    B, Hq, Hkv, T, d = 2, 8, 2, 900, 128
+    P = B * Hkv
+    s = seeded((B, Hkv, T), 71)
+    keep = oracle.keep_mask(f64(s), 1.2, 128).reshape(P, T)
+    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, 128, seed=72, demote=True)
+    q = seeded((B, Hq, d), 75, torch.bfloat16)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    ws = K.decode_attn_workspace(B, Hq, kv)
+    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
+    ref = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
+                                         oracle.sm_scale(d))
+    check_attention(out, ref, torch.bfloat16)
+
+
+# ---------------------------------------------------------------------------- delayed step
+
+
+@pytest.mark.parametrize("dtype,d,w,demote", [(torch.bfloat16, 128, 64, False),
+                                              (torch.float32, 64, 32, False),
+                                              (torch.bfloat16, 128, 32, True)])
+def test_step_delayed_state_machine(K, dtype, d, w, demote):
+    """DMS: flagged tokens stay w steps; the visible set is re-derived from scratch by
+    the oracle at every step and compared with the ring + pool content."""
+    B, Hkv, Hq, T0, steps = 2, 3, 6, 200, 90
+    P = B * Hkv
+    total = T0 + steps
+    s_all = seeded((B, Hkv, total), 81) - 1.15
+    tau = 0.0
+    flags = oracle.dms_evict_flags(f64(s_all).reshape(P, total))
+    keep0 = oracle.dms_visible(flags[:, :T0], T0 - 1, w)
+    k_all = seeded((B, Hkv, total, d), 82, dtype)
+    v_all = seeded((B, Hkv, total, d), 83, dtype)
+    idx, cnt = upload_selection(keep0)
+    maxpp = total // 16 + 2
+    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp) if demote else {}
+    kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, dtype, DEV, poison=True, **kw)
+    ring = K.Ring.allocate(P, w, d, dtype, DEV, poison=True)
+    scores0 = s_all[..., :T0].contiguous()
+    K.kvp_compact(k_all[:, :, :T0].contiguous(), v_all[:, :, :T0].contiguous(), idx, cnt, kv,
+                  compact_ws(K, B, Hkv), ring=ring, scores=scores0,
+                  mode=K.KVP_COMPACT_DEMOTE_INT8 if demote else K.KVP_COMPACT_EVICT)
+    ws = K.decode_attn_workspace(B, Hq, kv)
+    kf, vf = f64(k_all), f64(v_all)
+    for i in range(steps):
+        p = T0 + i
+        k_new = k_all[:, :, p].contiguous()
+        v_new = v_all[:, :, p].contiguous()
+        s_new = s_all[:, :, p].contiguous()
+        K.kvp_step_delayed(kv, ring, k_new, v_new, s_new, tau, p)
+        want = oracle.dms_visible(flags, p, w)
+        for pr in range(P):
+            got = np.sort(np.concatenate([read_pool(kv, pr)[0], read_ring(ring, pr)[0]]))
+            assert np.array_equal(got, np.flatnonzero(want[pr])), (i, pr)
+            if demote:
+                assert np.array_equal(np.sort(np.concatenate([got, read_pool8(kv, pr)[0]])),
+                                      np.arange(p + 1))
+        if i in (0, 1, w - 1, w, w + 1, steps - 1):
+            q = seeded((B, Hq, d), 900 + i, dtype)
+            out = torch.full((B, Hq, d), float("nan"), device=DEV)
+            K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
+            vis = want.reshape(B, Hkv, -1)
+            if demote:
+                ref = oracle.beacon_decode_attention(f64(q), kf[:, :, :p + 1], vf[:, :, :p + 1],
+                                                     vis, oracle.sm_scale(d))
+            else:
+                ref = oracle.decode_attention(f64(q), kf[:, :, :p + 1], vf[:, :, :p + 1], vis,
+                                              oracle.sm_scale(d))
+            check_attention(out, ref, dtype)
+    assert K.kvp_check(kv) == 0
+
+
+# ---------------------------------------------------------------------------- errors
+
+
+def test_capacity_overflow_reported(K):
+    B, Hkv, T, d = 1, 2, 400, 128
+    P = B * Hkv
+    keep = np.ones((P, T), bool)
+    idx, cnt = upload_selection(keep)
+    k = seeded((B, Hkv, T, d), 91, torch.bfloat16)
+    kv = K.PagedKV.allocate(P, d, 30, 30, torch.bfloat16, DEV)  # needs 2 * 25 pages
+    K.kvp_compact(k, k, idx, cnt, kv, compact_ws(K, B, Hkv))
+    assert K.kvp_check(kv) == 4  # KVP_E_CAPACITY
+    assert int(kv.err[0]) & K.ERR_POOL_FULL
+    assert int(kv.length.sum()) <= 30 * 16
+    K.kvp_clear_error(kv)
+    assert K.kvp_check(kv) == 0
+    # table overflow
+    kv2 = K.PagedKV.allocate(P, d, 100, 10, torch.bfloat16, DEV)
+    K.kvp_compact(k, k, idx, cnt, kv2, compact_ws(K, B, Hkv))
+    assert K.kvp_check(kv2) == 4 and int(kv2.err[0]) & K.ERR_TABLE_FULL
+    # attention still runs on what fits
+    q = seeded((B, 4, d), 92, torch.bfloat16)
+    out = torch.zeros((B, 4, d), device=DEV)
+    K.kvp_decode_attn(q, kv2, None, K.sm_scale(d), out, K.decode_attn_workspace(B, 4, kv2))
+    assert torch.isfinite(out).all()
+
+
+def test_argument_errors(K):
+    B, Hkv, T, d = 1, 2, 64, 128
+    kv = K.PagedKV.allocate(B * Hkv, d, 16, 8, torch.bfloat16, DEV)
+    q = torch.zeros((B, 3, d), dtype=torch.bfloat16, device=DEV)  # 3 % 2 != 0
+    out = torch.zeros((B, 3, d), device=DEV)
+    with pytest.raises(K.KvpError) as e:
+        K.kvp_decode_attn(q, kv, None, 0.1, out, K.decode_attn_workspace(B, 4, kv))
+    assert e.value.status == 1
+    q = torch.zeros((B, 4, d), dtype=torch.float32, device=DEV)  # dtype mismatch
+    with pytest.raises(K.KvpError) as e:
+        K.kvp_decode_attn(q, kv, None, 0.1, torch.zeros((B, 4, d), device=DEV),
+                          K.decode_attn_workspace(B, 4, kv))
+    assert e.value.status == 2
+    q = torch.zeros((B, 4, d), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(K.KvpError) as e:  # undersized workspace
+        K.kvp_decode_attn(q, kv, None, 0.1, torch.zeros((B, 4, d), device=DEV),
+                          torch.zeros(4, dtype=torch.int32, device=DEV))
+    assert e.value.status == 3
+    s10 = torch.zeros((B, Hkv, 10), device=DEV)
+    with pytest.raises(K.KvpError):  # ld_s < T
+        K.kvp_select(s10, T, 0.0, 128, torch.zeros(4, dtype=torch.int32, device=DEV),
+                     torch.zeros(4, dtype=torch.int32, device=DEV),
+                     torch.zeros(4, dtype=torch.int32, device=DEV),
+                     torch.zeros(16, dtype=torch.int32, device=DEV))
