@@ -40,8 +40,20 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen3_8b_layer")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=1, help="batch rows in the CPU sample")
+    ap.add_argument("--cpu-rows", type=int, default=16, help="batch rows in the CPU sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
+    if args.calibrate_copy:
+        import torch
+        src = torch.ones(1 << 28, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "launches": 5}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); this path has no "
               "cross-GPU work to measure", file=sys.stderr)
@@ -138,11 +150,14 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.3f}s); "
         + ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
 
-    # isolated decode attention, cache flushed between repetitions (256 MB MALL)
-    flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    # isolated decode attention; between repetitions the 256 MB MALL is flushed by
+    # READING 1 GiB (a write flush would leave dirty lines draining into the timed run)
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    fsum = torch.zeros(1, dtype=torch.int64, device=dev)
     iso = []
     for r in range(12):
-        flush.fill_(r)
+        fsum.add_(flush.sum())
+        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()

@@ -133,7 +133,7 @@ typedef struct kvp_paged_kv {
  * layout: k [num_pairs][window/16][16][d], v [num_pairs][window/16][d][16];
  * score [num_pairs][window] is the slot's score, pos [num_pairs][window] its
  * absolute position or -1 when empty.  Element type = kv->dtype.
- * window must be a positive multiple of 16.
+ * window must be a positive multiple of 16, at most 1024.
  * -------------------------------------------------------------------------- */
 typedef struct kvp_ring {
   int32_t window;
@@ -241,16 +241,15 @@ kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const 
  *   out [B][Hq][d] fp32: softmax(sm_scale * K q) V over the pair's pool tokens, its
  *       non-empty ring slots and (if present) its int8 tokens, all in one softmax.
  *       A pair with no visible token yields zeros.
- *   ws  >= kvp_decode_attn_workspace_size(...) bytes.  Its first
- *       kvp_decode_attn_counter_bytes(...) bytes must be zero before the first call
- *       with that workspace; every call leaves them zero again.
+ *   ws  >= kvp_decode_attn_workspace_size(...) bytes of scratch (any contents);
+ *       it holds the split plan and the per-range partial (max, sum, output)
+ *       records between the attention kernel and the merge kernel.
  * -------------------------------------------------------------------------- */
 kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
                            const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
                            float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                       int32_t head_dim);
-size_t kvp_decode_attn_counter_bytes(int32_t num_pairs);
 
 /* ----------------------------------------------------------------------------
  * Helpers.

@@ -8,7 +8,7 @@ from ._lib import (  # noqa: F401
     KVP_BF16, KVP_COMPACT_DEMOTE_INT8, KVP_COMPACT_EVICT, KVP_F32, KVP_PAGE,
     KVP_SCORER_LINEAR, KVP_SCORER_MLP, ERR_POOL8_FULL, ERR_POOL_FULL, ERR_TABLE_FULL,
     KvpError, PagedKV, Ring, Scorer, decode_attn_workspace, kvp_check, kvp_clear_error,
-    kvp_compact, kvp_compact_workspace_size, kvp_decode_attn, kvp_decode_attn_counter_bytes,
+    kvp_compact, kvp_compact_workspace_size, kvp_decode_attn,
     kvp_decode_attn_workspace_size, kvp_reset, kvp_score, kvp_score_workspace_size,
     kvp_select, kvp_select_workspace_size, kvp_status_str, kvp_step_delayed, kvp_version,
     load, sm_scale, LIB_PATH,

@@ -87,7 +87,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
         "kvp_decode_attn_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
-        "kvp_decode_attn_counter_bytes": (c_size_t, [c_int32]),
         "kvp_reset": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p]),
         "kvp_clear_error": (c_int32, [P(KvpPagedKV), c_void_p]),
         "kvp_check": (c_int32, [P(KvpPagedKV), c_void_p]),
@@ -315,14 +314,10 @@ def kvp_decode_attn_workspace_size(B: int, Hq: int, num_pairs: int, head_dim: in
     return load().kvp_decode_attn_workspace_size(B, Hq, num_pairs, head_dim)
 
 
-def kvp_decode_attn_counter_bytes(num_pairs: int) -> int:
-    return load().kvp_decode_attn_counter_bytes(num_pairs)
-
-
 def decode_attn_workspace(B: int, Hq: int, kv: PagedKV, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace for kvp_decode_attn (its counters must start at zero)."""
+    """A workspace of the size kvp_decode_attn needs (contents are scratch)."""
     n = kvp_decode_attn_workspace_size(B, Hq, kv.c.num_pairs, kv.c.head_dim)
-    return torch.zeros(max(n, 4) // 4 + 1, dtype=torch.int32, device=device)
+    return torch.empty(max(n, 4) // 4 + 1, dtype=torch.int32, device=device)
 
 
 def kvp_decode_attn(q: torch.Tensor, kv: PagedKV, ring: Optional[Ring], sm_scale: float,

@@ -11,9 +11,10 @@
 //   "region B" (its int8 pages, padded to even).  All regions are concatenated and
 //   the sequence is cut into NWAVES equal, even-length ranges; each wave walks its
 //   range 32 tokens (two pages) at a time and emits one partial (m, l, o) record per
-//   region it touches.  The last wave to finish a pair (atomic arrival counter)
-//   merges that pair's records with a log-sum-exp combine in a fixed order, writes
-//   the output and resets the counter, so the result is deterministic.
+//   region it touches.  A second kernel (one wave per pair and query head) merges a
+//   pair's records with a log-sum-exp combine in a fixed order, so the result is
+//   deterministic.  The kernel boundary makes the records visible: no atomics and no
+//   device-scope fences (each of which writes back an XCD's L2) in the hot kernel.
 //
 // Per 32-token step (bf16, head dim D, g query heads of one KV head):
 //   S^T[32 tok x 16 heads] = K . Q^T on 16x16x32 bf16 MFMA (exact products, fp32
@@ -40,7 +41,7 @@ struct AttnArgs {
   int has_ring;
   float scale_log2;  // sm_scale * log2(e)
   float* part;       // partial records
-  int* counters;     // [num_pairs] arrival counters
+  int* plan_c;       // [2 * num_pairs + 1] partial-slot prefix, written by work-group 0
   int rec_floats;    // g * (D + 2)
 };
 
@@ -74,7 +75,7 @@ __device__ Plan build_plan(const AttnArgs& a, int* lds) {
   int* tmp = pl.C + nseg + 1;
   for (int s = threadIdx.x; s <= nseg; s += blockDim.x) pl.P[s] = (s < nseg) ? region_pages(a, s) : 0;
   __syncthreads();
-  pl.total = block_excl_scan_lds(pl.P, nseg + 1, tmp);
+  pl.total = block_scan_excl(pl.P, nseg + 1, tmp);
   int per = (pl.total + ATTN_NWAVES - 1) / ATTN_NWAVES;
   per = max(2, (per + 1) & ~1);
   pl.per = per;
@@ -87,58 +88,8 @@ __device__ Plan build_plan(const AttnArgs& a, int* lds) {
     pl.C[s] = c;
   }
   __syncthreads();
-  block_excl_scan_lds(pl.C, nseg + 1, tmp);
+  block_scan_excl(pl.C, nseg + 1, tmp);
   return pl;
-}
-
-// -------------------------------------------------------------------------------
-// Merge of a pair's partial records by one wave (fixed order => deterministic).
-// -------------------------------------------------------------------------------
-__device__ void combine_pair(const AttnArgs& a, const Plan& pl, int pair) {
-  const int lane = threadIdx.x & 63;
-  const int np = a.kv.num_pairs;
-  const int b = pair / a.Hkv, h = pair % a.Hkv;
-  const int r0 = pl.C[pair], r1 = pl.C[pair + 1];
-  const int s0 = pl.C[np + pair], s1 = pl.C[np + pair + 1];
-  const int nrec = (r1 - r0) + (s1 - s0);
-  for (int n = 0; n < a.g; ++n) {
-    float* o = a.out + ((int64_t)b * a.Hq + h * a.g + n) * a.D;
-    float M = neg_inf();
-    for (int k = 0; k < nrec; ++k) {
-      int slot = (k < r1 - r0) ? r0 + k : s0 + (k - (r1 - r0));
-      const float* rec = a.part + (int64_t)slot * a.rec_floats;
-      M = fmaxf(M, rec[a.g * a.D + n]);
-    }
-    for (int d = lane; d < a.D; d += 64) {
-      float num = 0.f, den = 0.f;
-      if (M != neg_inf()) {
-        for (int k = 0; k < nrec; ++k) {
-          int slot = (k < r1 - r0) ? r0 + k : s0 + (k - (r1 - r0));
-          const float* rec = a.part + (int64_t)slot * a.rec_floats;
-          float m = rec[a.g * a.D + n];
-          float wgt = (m == neg_inf()) ? 0.f : exp2f(m - M);
-          num += wgt * rec[n * a.D + d];
-          den += wgt * rec[a.g * a.D + a.g + n];
-        }
-      }
-      o[d] = (den > 0.f) ? num / den : 0.f;
-    }
-  }
-}
-
-// Arrival: called by the whole wave after its partial record is stored.
-__device__ __forceinline__ void arrive(const AttnArgs& a, const Plan& pl, int pair) {
-  const int np = a.kv.num_pairs;
-  const int expected = (pl.C[pair + 1] - pl.C[pair]) + (pl.C[np + pair + 1] - pl.C[np + pair]);
-  __threadfence();
-  int old = 0;
-  if ((threadIdx.x & 63) == 0) old = atomicAdd(a.counters + pair, 1);
-  old = __shfl(old, 0);
-  if (old == expected - 1) {
-    __threadfence();
-    combine_pair(a, pl, pair);
-    if ((threadIdx.x & 63) == 0) a.counters[pair] = 0;
-  }
 }
 
 // -------------------------------------------------------------------------------
@@ -158,21 +109,29 @@ struct PageRef {
   int nvalid;         // main: valid slots; ring: ring page index
 };
 
+// Segment context for region A: block-table entries of the pages this wave walks are
+// fetched once into a VGPR (lane i holds page base+i) and read back with readlane, so
+// no memory access sits between a step's loads and their use; the ring's slot
+// occupancy is summarised once into 16-bit masks in this wave's LDS area.
+struct SegA {
+  int pair, npm, len, nring;
+  int bt_base;   // virtual page index held by lane 0 of bt
+  int bt;        // this lane's block-table entry
+  const int* ringmask;  // LDS: 16-bit occupancy of each ring page
+};
+
 template <int D>
-__device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, int vp, int npm,
-                                                 int len) {
+__device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, const SegA& sg, int vp) {
   PageRef r;
-  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
-  if (vp < npm) {
-    int pg = __builtin_amdgcn_readfirstlane(
-        a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + vp]);
+  if (vp < sg.npm) {
+    const int pg = __builtin_amdgcn_readlane(sg.bt, vp - sg.bt_base);
     r.k = reinterpret_cast<const uint16_t*>(a.kv.k_pages) + (int64_t)pg * PAGE * D;
     r.v = reinterpret_cast<const uint16_t*>(a.kv.v_pages) + (int64_t)pg * PAGE * D;
     r.kind = 0;
-    r.nvalid = min(PAGE, len - vp * PAGE);
-  } else if (vp < npm + nring) {
-    int rp = vp - npm;
-    int64_t off = ((int64_t)pair * nring + rp) * PAGE * D;
+    r.nvalid = min(PAGE, sg.len - vp * PAGE);
+  } else if (vp < sg.npm + sg.nring) {
+    const int rp = vp - sg.npm;
+    const int64_t off = ((int64_t)sg.pair * sg.nring + rp) * PAGE * D;
     r.k = reinterpret_cast<const uint16_t*>(a.ring.k) + off;
     r.v = reinterpret_cast<const uint16_t*>(a.ring.v) + off;
     r.kind = 1;
@@ -187,7 +146,7 @@ __device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, in
 }
 
 // Validity bits of this lane's 8 tokens (8j .. 8j+7 of the 32-token step).
-__device__ __forceinline__ uint32_t lane_valid_bits(const AttnArgs& a, int pair, const PageRef& X,
+__device__ __forceinline__ uint32_t lane_valid_bits(const SegA& sg, const PageRef& X,
                                                     const PageRef& Y, int j) {
   const PageRef& P = (j < 2) ? X : Y;
   const int s0 = 8 * (j & 1);
@@ -196,19 +155,12 @@ __device__ __forceinline__ uint32_t lane_valid_bits(const AttnArgs& a, int pair,
     n = max(0, min(8, n));
     return (1u << n) - 1u;
   }
-  if (P.kind == 1) {
-    const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + P.nvalid * PAGE + s0;
-    uint32_t m = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m |= (pos[i] >= 0 ? 1u : 0u) << i;
-    return m;
-  }
+  if (P.kind == 1) return (static_cast<uint32_t>(sg.ringmask[P.nvalid]) >> s0) & 0xffu;
   return 0u;
 }
 
 template <int D>
-__device__ __forceinline__ void load_step(Bf16Frags<D>& f, const PageRef& X, const PageRef& Y,
-                                          int lane) {
+__device__ __forceinline__ void load_k(Bf16Frags<D>& f, const PageRef& X, const PageRef& Y, int lane) {
   const int m = lane & 15, j = lane >> 4;
   // Score tile A rows: token 8*(m/4) + m%4; tile B rows: token 8*(m/4) + 4 + m%4.
   const int tA = 8 * (m >> 2) + (m & 3);
@@ -222,6 +174,11 @@ __device__ __forceinline__ void load_step(Bf16Frags<D>& f, const PageRef& X, con
     f.kA[kk] = *reinterpret_cast<const u32x4*>(rowA + 8 * kk);
     f.kB[kk] = *reinterpret_cast<const u32x4*>(rowB + 8 * kk);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(Bf16Frags<D>& f, const PageRef& X, const PageRef& Y, int lane) {
+  const int m = lane & 15, j = lane >> 4;
   const PageRef& PV = (j < 2) ? X : Y;
   const uint16_t* vbase = (PV.v != nullptr) ? PV.v : X.v;
   const uint16_t* vcol = vbase + m * PAGE + 8 * (j & 1);
@@ -250,15 +207,23 @@ __device__ __forceinline__ u32x4 mask_tokens(u32x4 x, uint32_t vb) {
 }
 
 template <int D>
-__device__ __forceinline__ void compute_step(const AttnArgs& a, const Bf16Frags<D>& f,
-                                             const bf16x8 (&qf)[D / 32], SoftmaxState<D>& st,
-                                             uint32_t vbits, bool all_valid) {
-  f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ void qk_step(const Bf16Frags<D>& f, const bf16x8 (&qf)[D / 32], f32x4& sA,
+                                        f32x4& sB) {
+  sA = f32x4{0.f, 0.f, 0.f, 0.f};
+  sB = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     sA = mfma16x16x32(as_bf16x8(f.kA[kk]), qf[kk], sA);
     sB = mfma16x16x32(as_bf16x8(f.kB[kk]), qf[kk], sB);
   }
+}
+
+// Online-softmax update for this step's 8 scores per lane; returns false when nothing
+// is visible yet.  phi/plo receive the bf16 hi/lo split of the probabilities.
+template <int D>
+__device__ __forceinline__ bool softmax_step(const AttnArgs& a, f32x4 sA, f32x4 sB,
+                                             SoftmaxState<D>& st, uint32_t vbits, bool all_valid,
+                                             bf16x8& phi, bf16x8& plo) {
   float s[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -275,7 +240,7 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Bf16Frags<
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
   const float mnew = fmaxf(st.m, mx);
-  if (mnew == neg_inf()) return;  // nothing visible yet (uniform across the wave)
+  if (mnew == neg_inf()) return false;  // nothing visible yet (uniform across the wave)
   const float alpha = exp2f(st.m - mnew);
   float p[8];
   float psum = 0.f;
@@ -298,7 +263,14 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Bf16Frags<
     hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
     lo[w] = pack_bf16x2(r0, r1);
   }
-  const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+  phi = as_bf16x8(hi);
+  plo = as_bf16x8(lo);
+  return true;
+}
+
+template <int D>
+__device__ __forceinline__ void pv_step(const Bf16Frags<D>& f, SoftmaxState<D>& st, bf16x8 phi,
+                                        bf16x8 plo, uint32_t vbits, bool all_valid) {
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     const bf16x8 vt = as_bf16x8(all_valid ? f.v[t] : mask_tokens(f.v[t], vbits));
@@ -307,7 +279,7 @@ __device__ __forceinline__ void compute_step(const AttnArgs& a, const Bf16Frags<
   }
 }
 
-// Store this wave's partial record for one region and arrive at the pair.
+// Store this wave's partial record for one region.
 template <int D>
 __device__ __forceinline__ void emit_partial(const AttnArgs& a, const Plan& pl, int pair, int slot,
                                              SoftmaxState<D>& st) {
@@ -325,7 +297,6 @@ __device__ __forceinline__ void emit_partial(const AttnArgs& a, const Plan& pl, 
       rec[a.g * D + a.g + n] = l;
     }
   }
-  arrive(a, pl, pair);
 }
 
 template <int D>
@@ -344,7 +315,7 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int pair, bf16x8 (&qf)
 
 template <int D>
 __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
-                                  int slot) {
+                                  int slot, int* wlds) {
   const int lane = threadIdx.x & 63, j = lane >> 4;
   bf16x8 qf[D / 32];
   load_q<D>(a, pair, qf);
@@ -353,41 +324,55 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
   for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = neg_inf();
   st.l = 0.f;
-  const int len = __builtin_amdgcn_readfirstlane(a.kv.length[pair]);
-  const int npm = cdiv(len, PAGE);
-
-  Bf16Frags<D> fa, fb;
-  PageRef xa = region_a_page<D>(a, pair, v0, npm, len);
-  PageRef ya = region_a_page<D>(a, pair, v0 + 1, npm, len);
-  if (xa.k == nullptr) {
-    // a fully padded step cannot start a range (regions are padded by at most one page)
+  SegA sg;
+  sg.pair = pair;
+  sg.len = __builtin_amdgcn_readfirstlane(a.kv.length[pair]);
+  sg.npm = cdiv(sg.len, PAGE);
+  sg.nring = a.has_ring ? a.ring.window / PAGE : 0;
+  sg.ringmask = wlds;
+  // ring occupancy masks (only when this range reaches the ring pages)
+  if (v1 > sg.npm && sg.nring > 0) {
+    for (int rp = lane; rp < sg.nring; rp += 64) {
+      const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + rp * PAGE;
+      int m = 0;
+#pragma unroll
+      for (int i = 0; i < PAGE; ++i) m |= (pos[i] >= 0 ? 1 : 0) << i;
+      wlds[rp] = m;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  load_step<D>(fa, xa, ya, lane);
-  for (int v = v0; v < v1; v += 4) {
-    // stage A: step at v (in fa); prefetch v + 2 into fb
-    PageRef xb, yb;
-    const bool hasb = (v + 2 < v1);
-    if (hasb) {
-      xb = region_a_page<D>(a, pair, v + 2, npm, len);
-      yb = region_a_page<D>(a, pair, v + 3, npm, len);
-      load_step<D>(fb, xb, yb, lane);
-    }
-    {
-      uint32_t vb = lane_valid_bits(a, pair, xa, ya, j);
-      bool allv = __ballot(vb != 0xffu) == 0;
-      compute_step<D>(a, fa, qf, st, vb, allv);
-    }
-    if (!hasb) break;
-    const bool hasa = (v + 4 < v1);
-    if (hasa) {
-      xa = region_a_page<D>(a, pair, v + 4, npm, len);
-      ya = region_a_page<D>(a, pair, v + 5, npm, len);
-      load_step<D>(fa, xa, ya, lane);
-    }
-    {
-      uint32_t vb = lane_valid_bits(a, pair, xb, yb, j);
-      bool allv = __ballot(vb != 0xffu) == 0;
-      compute_step<D>(a, fb, qf, st, vb, allv);
+  for (int c0 = v0; c0 < v1; c0 += 64) {
+    // block-table chunk: pages [c0, c0 + 64) of this range
+    const int c1 = min(v1, c0 + 64);
+    sg.bt_base = c0;
+    sg.bt = 0;
+    if (c0 + lane < min(c1, sg.npm))
+      sg.bt = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + c0 + lane];
+    // One register buffer: the next step's K is loaded as soon as this step's QK
+    // MFMAs have consumed K, and its V right after the PV MFMAs, so a full step of loads
+    // is in flight behind the math.  The last step re-loads its own pages (in range)
+    // instead of branching, which keeps the wait counts exact.
+    Bf16Frags<D> f;
+    PageRef x = region_a_page<D>(a, sg, c0);
+    PageRef y = region_a_page<D>(a, sg, c0 + 1);
+    load_k<D>(f, x, y, lane);
+    load_v<D>(f, x, y, lane);
+    for (int v = c0; v < c1; v += 2) {
+      const int vn = (v + 2 < c1) ? v + 2 : v;
+      const PageRef xn = region_a_page<D>(a, sg, vn);
+      const PageRef yn = region_a_page<D>(a, sg, vn + 1);
+      const uint32_t vb = lane_valid_bits(sg, x, y, j);
+      const bool allv = __ballot(vb != 0xffu) == 0;
+      f32x4 sA, sB;
+      qk_step<D>(f, qf, sA, sB);
+      load_k<D>(f, xn, yn, lane);
+      bf16x8 phi, plo;
+      if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv);
+      load_v<D>(f, xn, yn, lane);
+      x = xn;
+      y = yn;
     }
   }
   emit_partial<D>(a, pl, pair, slot, st);
@@ -413,9 +398,49 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
 }
 
 template <int D>
+struct I8Frags {
+  u32x2 kA[D / 32];  // 8 int8 K codes per MFMA K-step, score tile A row
+  u32x2 kB[D / 32];
+  u32x2 v[D / 16];   // 8 int8 V^T codes per output tile
+  f32x4 ks[2];       // K scales of this lane's 8 tokens
+  f32x4 vs[2];       // V scales of this lane's 8 tokens
+};
+
+template <int D>
+__device__ __forceinline__ void load_i8_k(const AttnArgs& a, I8Frags<D>& f, int pgX, int pgY, int lane) {
+  const int m = lane & 15, j = lane >> 4;
+  const int tA = 8 * (m >> 2) + (m & 3), tB = tA + 4;
+  const int pgK = (tA < 16) ? pgX : pgY;
+  const int8_t* kbase = a.kv.k8_pages + (int64_t)pgK * PAGE * D;
+  const int8_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
+  const int8_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
+#pragma unroll
+  for (int kk = 0; kk < D / 32; ++kk) {
+    f.kA[kk] = *reinterpret_cast<const u32x2*>(rowA + 8 * kk);
+    f.kB[kk] = *reinterpret_cast<const u32x2*>(rowB + 8 * kk);
+  }
+  const int pgT = (j < 2) ? pgX : pgY;
+  const float* ksc = a.kv.k8_scale + (int64_t)pgT * PAGE + 8 * (j & 1);
+  f.ks[0] = *reinterpret_cast<const f32x4*>(ksc);
+  f.ks[1] = *reinterpret_cast<const f32x4*>(ksc + 4);
+}
+
+template <int D>
+__device__ __forceinline__ void load_i8_v(const AttnArgs& a, I8Frags<D>& f, int pgX, int pgY, int lane) {
+  const int m = lane & 15, j = lane >> 4;
+  const int pgT = (j < 2) ? pgX : pgY;
+  const int8_t* vcol = a.kv.v8_pages + (int64_t)pgT * PAGE * D + m * PAGE + 8 * (j & 1);
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const u32x2*>(vcol + t * 16 * PAGE);
+  const float* vsc = a.kv.v8_scale + (int64_t)pgT * PAGE + 8 * (j & 1);
+  f.vs[0] = *reinterpret_cast<const f32x4*>(vsc);
+  f.vs[1] = *reinterpret_cast<const f32x4*>(vsc + 4);
+}
+
+template <int D>
 __device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
                                   int slot) {
-  const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
+  const int lane = threadIdx.x & 63, j = lane >> 4;
   bf16x8 qf[D / 32];
   load_q<D>(a, pair, qf);
   SoftmaxState<D> st;
@@ -424,90 +449,94 @@ __device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, i
   st.m = neg_inf();
   st.l = 0.f;
   const int len = __builtin_amdgcn_readfirstlane(a.kv.length8[pair]);
-  const int npm = cdiv(len, PAGE);
-  const int tA = 8 * (m >> 2) + (m & 3);
-  const int tB = tA + 4;
-  for (int v = v0; v < v1; v += 2) {
-    int pgX = -1, pgY = -1;
-    if (v < npm)
-      pgX = __builtin_amdgcn_readfirstlane(a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + v]);
-    if (v + 1 < npm)
-      pgY = __builtin_amdgcn_readfirstlane(a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + v + 1]);
-    if (pgY < 0) pgY = pgX;
-    const int nvX = max(0, min(PAGE, len - v * PAGE));
-    const int nvY = max(0, min(PAGE, len - (v + 1) * PAGE));
-    // K rows (int8) -> bf16 fragments
-    const int pgK = (tA < 16) ? pgX : pgY;
-    const int8_t* kbase = a.kv.k8_pages + (int64_t)pgK * PAGE * D;
-    const int8_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
-    const int8_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
-    f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
+  const int npm = cdiv(len, PAGE);  // v1 <= npm rounded up to even; the pad page is never loaded
+  for (int c0 = v0; c0 < v1; c0 += 64) {
+    const int c1 = min(v1, c0 + 64);
+    int bt = 0;
+    if (c0 + lane < min(c1, npm))
+      bt = a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + c0 + lane];
+    auto page = [&](int vp) -> int {
+      // the pad page of an odd page count re-uses the previous page (all slots masked)
+      return __builtin_amdgcn_readlane(bt, min(vp, npm - 1) - c0);
+    };
+    I8Frags<D> f;
+    int pgX = page(c0), pgY = page(c0 + 1);
+    load_i8_k<D>(a, f, pgX, pgY, lane);
+    load_i8_v<D>(a, f, pgX, pgY, lane);
+    for (int v = c0; v < c1; v += 2) {
+      const int vn = (v + 2 < c1) ? v + 2 : v;
+      const int pgXn = page(vn), pgYn = page(vn + 1);
+      const int nvT = max(0, min(PAGE, len - (v + (j >> 1)) * PAGE));
+      const int s0 = 8 * (j & 1);
+      const uint32_t vb = (uint32_t)((1 << max(0, min(8, nvT - s0))) - 1);
+      const bool allv = __ballot(vb != 0xffu) == 0;
+      f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-      u32x2 ka = *reinterpret_cast<const u32x2*>(rowA + 8 * kk);
-      u32x2 kb = *reinterpret_cast<const u32x2*>(rowB + 8 * kk);
-      sA = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(ka[0], ka[1])), qf[kk], sA);
-      sB = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(kb[0], kb[1])), qf[kk], sB);
-    }
-    // this lane's 8 tokens: 8j .. 8j+7 -> page (j<2 ? X : Y), slots 8(j&1) ..
-    const int pgT = (j < 2) ? pgX : pgY;
-    const int nvT = (j < 2) ? nvX : nvY;
-    const int s0 = 8 * (j & 1);
-    const float* ksc = a.kv.k8_scale + (int64_t)pgT * PAGE + s0;
-    const float* vsc = a.kv.v8_scale + (int64_t)pgT * PAGE + s0;
-    float s[8], vs[8];
-    uint32_t vb = (uint32_t)((1 << max(0, min(8, nvT - s0))) - 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[i] = sA[i] * ksc[i] * a.scale_log2;
-      s[i + 4] = sB[i] * ksc[i + 4] * a.scale_log2;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      vs[i] = vsc[i];
-      if (!((vb >> i) & 1u)) {
-        s[i] = neg_inf();
-        vs[i] = 0.f;
+      for (int kk = 0; kk < D / 32; ++kk) {
+        sA = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(f.kA[kk][0], f.kA[kk][1])), qf[kk], sA);
+        sB = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(f.kB[kk][0], f.kB[kk][1])), qf[kk], sB);
       }
-    }
-    float mx = s[0];
+      // per-token K scale folds into the logits; V scale into the probabilities
+      const f32x4 ks0 = f.ks[0], ks1 = f.ks[1];
+      const f32x4 vs0 = f.vs[0], vs1 = f.vs[1];
+      sA = sA * ks0;
+      sB = sB * ks1;
+      load_i8_k<D>(a, f, pgXn, pgYn, lane);
+      float s[8], vsc[8];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(st.m, mx);
-    if (mnew == neg_inf()) continue;
-    const float alpha = exp2f(st.m - mnew);
-    float p[8], psum = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        s[i] = sA[i] * a.scale_log2;
+        s[i + 4] = sB[i] * a.scale_log2;
+        vsc[i] = vs0[i];
+        vsc[i + 4] = vs1[i];
+      }
+      if (!allv) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(s[i] - mnew);
-      psum += p[i];
-    }
-    st.l = st.l * alpha + psum;
-    st.m = mnew;
-    if (__ballot(alpha != 1.0f) != 0) {
+        for (int i = 0; i < 8; ++i) {
+          const bool ok = (vb >> i) & 1u;
+          s[i] = ok ? s[i] : neg_inf();
+          vsc[i] = ok ? vsc[i] : 0.f;
+        }
+      }
+      float mx = s[0];
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
-    }
-    // fold the V scale into the probabilities: sum_t p_t (scale_t code_t)
-    u32x4 hi, lo;
+      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(st.m, mx);
+      if (mnew != neg_inf()) {
+        const float alpha = exp2f(st.m - mnew);
+        float p[8], psum = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      float q0 = p[2 * w] * vs[2 * w], q1 = p[2 * w + 1] * vs[2 * w + 1];
-      uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
-      hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      lo[w] = pack_bf16x2(q0 - bf16_to_f32(h0), q1 - bf16_to_f32(h1));
-    }
-    const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
-    const int8_t* vcol = a.kv.v8_pages + (int64_t)pgT * PAGE * D + m * PAGE + s0;
+        for (int i = 0; i < 8; ++i) {
+          p[i] = exp2f(s[i] - mnew);
+          psum += p[i];
+        }
+        st.l = st.l * alpha + psum;
+        st.m = mnew;
+        if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) {
-      u32x2 vv = *reinterpret_cast<const u32x2*>(vcol + t * 16 * PAGE);
-      u32x4 vt = i8x8_to_bf16x8(vv[0], vv[1]);
-      if (vb != 0xffu) vt = mask_tokens(vt, vb);
-      st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
-      st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
+          for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
+        }
+        // sum_t p_t (scale_t code_t) = sum_t (p_t scale_t) code_t
+        u32x4 hi, lo;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float q0 = p[2 * w] * vsc[2 * w], q1 = p[2 * w + 1] * vsc[2 * w + 1];
+          const uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
+          hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          lo[w] = pack_bf16x2(q0 - bf16_to_f32(h0), q1 - bf16_to_f32(h1));
+        }
+        const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+#pragma unroll
+        for (int t = 0; t < D / 16; ++t) {
+          u32x4 vt = i8x8_to_bf16x8(f.v[t][0], f.v[t][1]);
+          if (!allv) vt = mask_tokens(vt, vb);
+          st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
+          st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
+        }
+      }
+      load_i8_v<D>(a, f, pgXn, pgYn, lane);
     }
   }
   emit_partial<D>(a, pl, pair, slot, st);
@@ -620,7 +649,6 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
       rec[g * D + g + n] = lrun[n];
     }
   }
-  arrive(a, pl, pair);
 }
 
 // -------------------------------------------------------------------------------
@@ -635,17 +663,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * ATTN_WG_WAVES + wid;
 
-  // pairs with nothing visible: zero output (one work-group does it)
-  if (blockIdx.x == 0) {
-    for (int p = threadIdx.x; p < np; p += blockDim.x) {
-      int n = (pl.C[p + 1] - pl.C[p]) + (pl.C[np + p + 1] - pl.C[np + p]);
-      if (n == 0) {
-        const int b = p / a.Hkv, h = p % a.Hkv;
-        float* o = a.out + ((int64_t)b * a.Hq + h * a.g) * D;
-        for (int i = 0; i < a.g * D; ++i) o[i] = 0.f;
-      }
-    }
-  }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= nseg; i += blockDim.x) a.plan_c[i] = pl.C[i];
 
   pl.total = __builtin_amdgcn_readfirstlane(pl.total);
   pl.per = __builtin_amdgcn_readfirstlane(pl.per);
@@ -654,8 +673,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   if (start >= end) return;
   int s = __builtin_amdgcn_readfirstlane(upper_segment(pl.P, nseg, start));
   float* wlds = nullptr;
+  int* wmask = lds + 2 * (nseg + 1) + 16 + wid * 64;
   if constexpr (F32) {
-    wlds = reinterpret_cast<float*>(lds + 2 * (nseg + 1) + 16) + wid * (16 * D + 16 * 32);
+    wlds = reinterpret_cast<float*>(lds + 2 * (nseg + 1) + 16 + ATTN_WG_WAVES * 64) + wid * (16 * D + 16 * 32);
   }
   while (start < end) {
     while (__builtin_amdgcn_readfirstlane(pl.P[s + 1]) <= start) ++s;
@@ -667,7 +687,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       if constexpr (F32) {
         run_region_a_f32<D>(a, pl, s, v0, v1, slot, wlds);
       } else {
-        run_region_a_bf16<D>(a, pl, s, v0, v1, slot);
+        run_region_a_bf16<D>(a, pl, s, v0, v1, slot, wmask);
       }
     } else {
       if constexpr (!F32) run_region_b_int8<D>(a, pl, s - np, v0, v1, slot);
@@ -676,8 +696,63 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// -------------------------------------------------------------------------------
+// Merge: one wave per (pair, query head).  Lanes first cover the records to find the
+// running-max reference M and the normaliser sum_k 2^(m_k - M) l_k, then walk the
+// records in order accumulating 2^(m_k - M) o_k for their D/64 output elements.
+// A pair with no visible token (no records) gets zeros.
+// -------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int np = a.kv.num_pairs, g = a.g;
+  if (w >= np * g) return;
+  const int pair = w / g, n = w % g;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  const int r0 = a.plan_c[pair], na = a.plan_c[pair + 1] - r0;
+  const int s0 = a.plan_c[np + pair];
+  const int nrec = na + (a.plan_c[np + pair + 1] - s0);
+  auto rec = [&](int k) {
+    const int slot = (k < na) ? r0 + k : s0 + (k - na);
+    return a.part + (int64_t)slot * a.rec_floats;
+  };
+  float M = neg_inf();
+  for (int k = lane; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
+  M = wave_max(M);
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  if (M != neg_inf()) {
+    for (int k0 = 0; k0 < nrec; k0 += 64) {
+      const int k = k0 + lane;
+      float wk = 0.f, lk = 0.f;
+      if (k < nrec) {
+        const float m = rec(k)[g * D + n];
+        wk = (m == neg_inf()) ? 0.f : exp2f(m - M);
+        lk = rec(k)[g * D + g + n];
+      }
+      den += wk * lk;
+      const int kn = min(64, nrec - k0);
+#pragma unroll 8
+      for (int kk = 0; kk < kn; ++kk) {
+        const float wb = __shfl(wk, kk);
+        const float* o = rec(k0 + kk) + n * D;
+#pragma unroll
+        for (int e = 0; e < D / 64; ++e) acc[e] += wb * o[lane + 64 * e];
+      }
+    }
+    den = wave_sum(den);
+  }
+  float* out = a.out + ((int64_t)b * a.Hq + h * g + n) * D;
+  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] * inv;
+}
+
 size_t attn_lds_bytes(int num_pairs, int D, bool f32) {
-  size_t b = (size_t)(2 * (2 * num_pairs + 1) + 16) * sizeof(int);
+  size_t b = (size_t)(2 * (2 * num_pairs + 1) + 16 + ATTN_WG_WAVES * 64) * sizeof(int);
   if (f32) b += (size_t)ATTN_WG_WAVES * (16 * D + 16 * 32) * sizeof(float);
   return b;
 }
@@ -686,9 +761,8 @@ size_t attn_lds_bytes(int num_pairs, int D, bool f32) {
 
 using namespace kvp;
 
-extern "C" size_t kvp_decode_attn_counter_bytes(int32_t num_pairs) {
-  if (num_pairs <= 0) return 0;
-  return (((size_t)num_pairs * sizeof(int)) + 255) & ~(size_t)255;
+static size_t attn_plan_bytes(int num_pairs) {
+  return (((size_t)(2 * num_pairs + 1) * sizeof(int)) + 255) & ~(size_t)255;
 }
 
 extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
@@ -698,7 +772,7 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   if (Hq % Hkv != 0) return 0;
   const int g = Hq / Hkv;
   const size_t recs = (size_t)ATTN_NWAVES + 2 * (size_t)num_pairs;
-  return kvp_decode_attn_counter_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
+  return attn_plan_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
 }
 
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
@@ -717,9 +791,8 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
   if (ring) a.ring = *ring;
   else a.ring = kvp_ring{};
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.counters = reinterpret_cast<int*>(ws);
-  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
-                                    kvp_decode_attn_counter_bytes(kv->num_pairs));
+  a.plan_c = reinterpret_cast<int*>(ws);
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_plan_bytes(kv->num_pairs));
   a.rec_floats = a.g * (a.D + 2);
   const bool f32 = kv->dtype == KVP_F32;
   const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32);
@@ -731,6 +804,10 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
   }
+  KVP_LAUNCH_CHECK();
+  const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
+  if (a.D == 64) hipLaunchKernelGGL((decode_attn_combine_kernel<64>), cgrid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((decode_attn_combine_kernel<128>), cgrid, dim3(256), 0, stream, a);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
 }

@@ -53,6 +53,7 @@ kvp_status check_kv(const kvp_paged_kv* kv) {
 kvp_status check_ring(const kvp_ring* r) {
   if (!r) return KVP_OK;
   if (r->window <= 0 || r->window % KVP_PAGE != 0) return KVP_E_ARG;
+  if (r->window > 1024) return KVP_E_UNSUPPORTED;
   if (!r->k || !r->v || !r->score || !r->pos) return KVP_E_ARG;
   return KVP_OK;
 }
@@ -88,11 +89,11 @@ extern "C" kvp_status kvp_score(const kvp_scorer* sc, const void* hidden, int32_
     if (hdtype != KVP_BF16) return KVP_E_DTYPE;
     if (!sc->w2) return KVP_E_ARG;
     if (sc->inner <= 0 || sc->inner % 256 != 0 || sc->hidden % 64 != 0) return KVP_E_UNSUPPORTED;
-    const size_t need = kvp_score_workspace_size(sc, B, T);
-    if (!ws || ws_bytes < need) return KVP_E_WORKSPACE;
   } else {
     return KVP_E_ARG;
   }
+  const size_t need = kvp_score_workspace_size(sc, B, T);
+  if (need > 0 && (!ws || ws_bytes < need)) return KVP_E_WORKSPACE;
   return kvp_launch_score(sc, hidden, B, T, scores, ld_s, ws, stream);
 }
 

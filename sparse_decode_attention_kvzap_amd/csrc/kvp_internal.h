@@ -99,6 +99,35 @@ __device__ inline int block_excl_scan_lds(int* data, int n, int* tmp) {
   return carry;
 }
 
+// Exclusive scan over n ints held in LDS by the whole block: each thread scans a
+// contiguous chunk serially, the chunk totals are scanned across the wave with
+// shuffles and across waves through `wtot` (one int per wave).  Returns the total.
+__device__ inline int block_scan_excl(int* data, int n, int* wtot) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & 63, wid = tid >> 6;
+  const int nw = nt >> 6;
+  const int per = (n + nt - 1) / nt;
+  const int b0 = min(n, tid * per), b1 = min(n, b0 + per);
+  int sum = 0;
+  for (int i = b0; i < b1; ++i) sum += data[i];
+  const int inc = wave_incl_scan(sum);
+  if (lane == 63) wtot[wid] = inc;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = wtot[w];
+    off += (w < wid) ? t : 0;
+    tot += t;
+  }
+  int run = off + inc - sum;
+  for (int i = b0; i < b1; ++i) {
+    const int v = data[i];
+    data[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return tot;
+}
+
 // Binary search in an ascending array a[0..n]: largest s in [0, n) with a[s] <= x.
 __device__ __forceinline__ int upper_segment(const int* a, int n, int x) {
   int lo = 0, hi = n - 1;

@@ -104,8 +104,25 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * MLP_ROWB + 16 * (chunk ^ (row & 7));
 }
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1/(1 + p x),
+// x >= 0, |error| <= 1.5e-7; odd extension for x < 0.  Branch-free (the GELU runs on
+// every unit of every token), and its error moves a score by ~1e-6 at most here.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  poly *= t;
+  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
+  return copysignf(fmaf(-poly, e, 1.0f), x);
+}
+
+// Exact-form GELU: 0.5 a (1 + erf(a / sqrt 2)) (not the tanh approximation).
 __device__ __forceinline__ float gelu_erf(float a) {
-  return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
+  return 0.5f * a * (1.0f + erf_as7126(a * 0.70710678118654752f));
 }
 
 struct MlpArgs {
@@ -122,8 +139,16 @@ __global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = lane & 15, j = lane >> 4;
   const int wm = wid & 3, wn = wid >> 2;  // wave tile: inner [64wm,+64) x tokens [128wn,+128)
-  const int64_t tok0 = (int64_t)blockIdx.x * MLP_BN;
-  const int in0 = blockIdx.y * MLP_BM;
+  // XCD-aware order: work-groups are dispatched round-robin over the 8 XCDs, so the
+  // nparts slices of one token tile get ids b, b+8, ... (same XCD, adjacent in time)
+  // and share that tile's hidden states through the XCD's L2.
+  const int nparts = a.inner / MLP_BM;
+  const int grp = blockIdx.x / (8 * nparts), r8 = blockIdx.x % (8 * nparts);
+  const int64_t tile = (int64_t)grp * 8 + (r8 % 8);
+  const int part = r8 / 8;
+  const int64_t tok0 = tile * MLP_BN;
+  if (tok0 >= a.ntok) return;
+  const int in0 = part * MLP_BM;
   const int H = a.H;
 
   // global -> LDS copy assignment: 4 A chunks + 4 B chunks (16 B each) per thread
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) 
     for (int i = 0; i < 4; ++i)
       red[(wm * MLP_BN + 128 * wn + 16 * nt + n) * 16 + 4 * j + i] = sacc[nt][i];
   __syncthreads();
-  float* dst = a.part + ((int64_t)blockIdx.y * a.ntok) * 16;
+  float* dst = a.part + ((int64_t)part * a.ntok) * 16;
   for (int e = tid; e < MLP_BN * 16; e += MLP_THREADS) {
     const int t = e >> 4, h = e & 15;
     const int64_t tok = tok0 + t;
@@ -288,21 +313,145 @@ __global__ __launch_bounds__(256) void score_mlp_finish_kernel(const float* __re
   scores[bh * ld_s + t] = s;
 }
 
+// ------------------------------------------------------------------ small batches
+// Decode steps score only a handful of tokens (one per sequence).  The big-tile GEMM
+// would leave all but a few CUs idle and walk the whole K loop serially, so small
+// batches split K instead: wave (r, ks) contracts rows [16r, 16r+16) of W (zero past
+// `rows`) with every token over K slice ks (256 wide) on MFMA, straight from global
+// memory, into part[ks][token][row]; a per-token epilogue adds the slices in a fixed
+// order and finishes the scorer.
+constexpr int SMALL_MAX_TOK = 64;
+constexpr int SMALL_KSLICE = 256;
+
+__global__ __launch_bounds__(256) void score_small_gemm_kernel(
+    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int rows, int ntok, int H,
+    int rtiles, int ksplit, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= rtiles * ksplit) return;
+  const int rt = w % rtiles, ks = w / rtiles;
+  const int row = rt * 16 + n;
+  const bool rv = row < rows;
+  const uint16_t* wr = W + (int64_t)(rv ? row : 0) * H + ks * SMALL_KSLICE + 8 * j;
+  const int ntt = (ntok + 15) / 16;
+  const uint16_t* xr[SMALL_MAX_TOK / 16];
+#pragma unroll
+  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
+    const int tok = min(tt * 16 + n, ntok - 1);
+    xr[tt] = X + (int64_t)tok * H + ks * SMALL_KSLICE + 8 * j;
+  }
+  f32x4 acc[SMALL_MAX_TOK / 16];
+#pragma unroll
+  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < SMALL_KSLICE / 32; ++kk) {
+    u32x4 wv = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
+    if (!rv) wv = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
+      if (tt < ntt) {
+        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
+        acc[tt] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(xv), acc[tt]);
+      }
+    }
+  }
+  // acc[tt][i] = C[row 16rt + 4j + i][token 16tt + n]
+  const int rpad = rtiles * 16;
+#pragma unroll
+  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
+    const int tok = tt * 16 + n;
+    if (tt < ntt && tok < ntok) {
+      float* dst = part + ((int64_t)ks * ntok + tok) * rpad + rt * 16 + 4 * j;
+      *reinterpret_cast<f32x4*>(dst) = acc[tt];
+    }
+  }
+}
+
+// MLP epilogue: one work-group per token, one thread per inner unit (inner <= 1024).
+__global__ __launch_bounds__(1024) void score_small_mlp_epi_kernel(
+    const float* __restrict__ part, int ksplit, int ntok, int inner, const float* __restrict__ b1,
+    const float* __restrict__ W2, const float* __restrict__ b2, int Hkv, int T,
+    float* __restrict__ scores, int64_t ld_s) {
+  __shared__ float red[16][16];
+  const int tok = blockIdx.x, u = threadIdx.x;
+  const int lane = u & 63, wid = u >> 6;
+  float a = 0.f;
+  for (int ks = 0; ks < ksplit; ++ks) a += part[((int64_t)ks * ntok + tok) * inner + u];
+  if (b1) a += b1[u];
+  const float g = gelu_erf(a);
+  for (int h = 0; h < Hkv; ++h) {
+    const float v = wave_sum(g * W2[(int64_t)h * inner + u]);
+    if (lane == 0) red[h][wid] = v;
+  }
+  __syncthreads();
+  if (u < Hkv) {
+    float sacc = 0.f;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) sacc += red[u][w];
+    if (b2) sacc += b2[u];
+    const int b = tok / T, t = tok % T;
+    scores[((int64_t)b * Hkv + u) * ld_s + t] = sacc;
+  }
+}
+
+// Linear epilogue: sum the K slices of each (token, head) and add the bias.
+__global__ __launch_bounds__(256) void score_small_linear_epi_kernel(
+    const float* __restrict__ part, int ksplit, int ntok, int Hkv, const float* __restrict__ bias,
+    int T, float* __restrict__ scores, int64_t ld_s) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= ntok * Hkv) return;
+  const int tok = idx / Hkv, h = idx % Hkv;
+  float a = 0.f;
+  for (int ks = 0; ks < ksplit; ++ks) a += part[((int64_t)ks * ntok + tok) * 16 + h];
+  if (bias) a += bias[h];
+  const int b = tok / T, t = tok % T;
+  scores[((int64_t)b * Hkv + h) * ld_s + t] = a;
+}
+
 }  // namespace kvp
 
 using namespace kvp;
 
+static bool small_path(const kvp_scorer* sc, int64_t ntok) {
+  return sc->wdtype == KVP_BF16 && ntok <= SMALL_MAX_TOK && sc->hidden % SMALL_KSLICE == 0 &&
+         (sc->kind == KVP_SCORER_LINEAR || sc->inner <= 1024);
+}
+
 extern "C" size_t kvp_score_workspace_size(const kvp_scorer* sc, int32_t B, int32_t T) {
   if (!sc || B <= 0 || T <= 0) return 0;
+  const int64_t ntok = (int64_t)B * T;
+  if (sc->kind == KVP_SCORER_MLP && (sc->inner <= 0 || sc->inner % MLP_BM != 0)) return 0;
+  if (small_path(sc, ntok)) {
+    const int rows = sc->kind == KVP_SCORER_MLP ? sc->inner : 16;
+    return (size_t)(sc->hidden / SMALL_KSLICE) * ntok * cdiv(rows, 16) * 16 * sizeof(float);
+  }
   if (sc->kind != KVP_SCORER_MLP) return 0;
-  if (sc->inner <= 0 || sc->inner % MLP_BM != 0) return 0;
-  return (size_t)(sc->inner / MLP_BM) * (size_t)B * T * 16 * sizeof(float);
+  return (size_t)(sc->inner / MLP_BM) * (size_t)ntok * 16 * sizeof(float);
 }
 
 kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int T, float* scores,
                             int64_t ld_s, void* ws, hipStream_t stream) {
   const int ntok = B * T;
   const int H = sc->hidden, Hkv = sc->n_kv_heads;
+  if (small_path(sc, ntok)) {
+    const int ksplit = H / SMALL_KSLICE;
+    const bool mlp = sc->kind == KVP_SCORER_MLP;
+    const int rows = mlp ? sc->inner : Hkv;
+    const int rtiles = cdiv(rows, 16);
+    float* part = reinterpret_cast<float*>(ws);
+    hipLaunchKernelGGL(score_small_gemm_kernel, dim3(cdiv(rtiles * ksplit, 4)), dim3(256), 0, stream,
+                       reinterpret_cast<const uint16_t*>(hidden),
+                       reinterpret_cast<const uint16_t*>(sc->w1), rows, ntok, H, rtiles, ksplit, part);
+    KVP_LAUNCH_CHECK();
+    if (mlp) {
+      hipLaunchKernelGGL(score_small_mlp_epi_kernel, dim3(ntok), dim3(sc->inner), 0, stream, part, ksplit,
+                         ntok, sc->inner, sc->b1, sc->w2, sc->b2, Hkv, T, scores, ld_s);
+    } else {
+      hipLaunchKernelGGL(score_small_linear_epi_kernel, dim3(cdiv(ntok * Hkv, 256)), dim3(256), 0, stream,
+                         part, ksplit, ntok, Hkv, sc->b1, T, scores, ld_s);
+    }
+    KVP_LAUNCH_CHECK();
+    return KVP_OK;
+  }
   if (sc->kind == KVP_SCORER_LINEAR) {
     if (sc->wdtype == KVP_F32) {
       const int64_t n = (int64_t)ntok * Hkv;
@@ -329,8 +478,9 @@ kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int
   m.inner = sc->inner;
   m.Hkv = Hkv;
   const int nparts = sc->inner / MLP_BM;
-  hipLaunchKernelGGL(score_mlp_bf16_kernel, dim3((unsigned)cdiv64(ntok, MLP_BN), nparts), dim3(MLP_THREADS),
-                     0, stream, m);
+  const int64_t tiles = cdiv64(ntok, MLP_BN);
+  hipLaunchKernelGGL(score_mlp_bf16_kernel, dim3((unsigned)(cdiv64(tiles, 8) * 8 * nparts)),
+                     dim3(MLP_THREADS), 0, stream, m);
   KVP_LAUNCH_CHECK();
   const int64_t n = (int64_t)ntok * Hkv;
   hipLaunchKernelGGL(score_mlp_finish_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, stream, m.part,

@@ -51,7 +51,7 @@ class PrunedKVCache:
                                      dtype=torch.int32, device=dev)
         self.ws_compact = torch.empty(L.kvp_compact_workspace_size(B, Hkv) // 4,
                                       dtype=torch.int32, device=dev)
-        nws = L.kvp_score_workspace_size(scorer, B, Tp)
+        nws = max(L.kvp_score_workspace_size(scorer, B, Tp), L.kvp_score_workspace_size(scorer, B, 1))
         self.ws_score = torch.empty(max(1, nws // 4), dtype=torch.float32, device=dev)
         self.ws_attn = L.decode_attn_workspace(B, Hq, self.kv, dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)

@@ -99,7 +99,7 @@ def test_workspace_sizes(L):
     assert L.kvp_select_workspace_size(0, 8, 10) == 0
     assert L.kvp_compact_workspace_size(16, 8) >= (6 * 128 + 1) * 4
     n = L.kvp_decode_attn_workspace_size(16, 32, 128, 128)
-    assert n >= L.kvp_decode_attn_counter_bytes(128) + 128 * 4 * 130 * 4
+    assert n >= 128 * 4 * 130 * 4
     assert L.kvp_decode_attn_workspace_size(16, 30, 128, 128) == 0  # Hq % Hkv != 0
     sc = L.KvpScorer(L.KVP_SCORER_MLP, 4096, 512, 8, L.KVP_BF16, 0, 1, 0, 1, 0)
     assert L.load().kvp_score_workspace_size(ctypes.byref(sc), 16, 100) == 2 * 16 * 100 * 16 * 4
