@@ -29,7 +29,7 @@
 namespace kvp {
 
 constexpr int ATTN_WG_WAVES = 4;
-constexpr int ATTN_GRID = 512;  // two work-groups per CU on a 256-CU part
+constexpr int ATTN_GRID = 256;  // one work-group (4 waves) per CU on a 256-CU part
 constexpr int ATTN_NWAVES = ATTN_GRID * ATTN_WG_WAVES;
 
 struct AttnArgs {
@@ -326,13 +326,26 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
   st.l = 0.f;
   SegA sg;
   sg.pair = pair;
-  sg.len = __builtin_amdgcn_readfirstlane(a.kv.length[pair]);
-  sg.npm = cdiv(sg.len, PAGE);
   sg.nring = a.has_ring ? a.ring.window / PAGE : 0;
   sg.ringmask = wlds;
-  // ring occupancy masks (only when this range reaches the ring pages)
-  if (v1 > sg.npm && sg.nring > 0) {
-    for (int rp = lane; rp < sg.nring; rp += 64) {
+  // Issue the segment's independent loads together (length, first block-table chunk,
+  // ring occupancy) so their latencies overlap with the q load above.
+  const int len_raw = a.kv.length[pair];
+  const int bt_first = (v0 + lane < v1) ? a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair +
+                                                           min(v0 + lane, a.kv.max_pages_per_pair - 1)]
+                                        : 0;
+  int ring_m = 0;
+  const bool need_ring = sg.nring > 0 && lane < sg.nring;
+  if (need_ring) {
+    const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + lane * PAGE;
+#pragma unroll
+    for (int i = 0; i < PAGE; ++i) ring_m |= (pos[i] >= 0 ? 1 : 0) << i;
+  }
+  sg.len = __builtin_amdgcn_readfirstlane(len_raw);
+  sg.npm = cdiv(sg.len, PAGE);
+  if (sg.nring > 0) {
+    if (need_ring) wlds[lane] = ring_m;
+    for (int rp = lane + 64; rp < sg.nring; rp += 64) {
       const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + rp * PAGE;
       int m = 0;
 #pragma unroll
@@ -347,9 +360,13 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
     // block-table chunk: pages [c0, c0 + 64) of this range
     const int c1 = min(v1, c0 + 64);
     sg.bt_base = c0;
-    sg.bt = 0;
-    if (c0 + lane < min(c1, sg.npm))
-      sg.bt = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + c0 + lane];
+    if (c0 == v0) {
+      sg.bt = bt_first;  // entries past npm are never read (those pages are ring/pad)
+    } else {
+      sg.bt = 0;
+      if (c0 + lane < min(c1, sg.npm))
+        sg.bt = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + c0 + lane];
+    }
     // One register buffer: the next step's K is loaded as soon as this step's QK
     // MFMAs have consumed K, and its V right after the PV MFMAs, so a full step of loads
     // is in flight behind the math.  The last step re-loads its own pages (in range)
@@ -717,6 +734,7 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
     const int slot = (k < na) ? r0 + k : s0 + (k - na);
     return a.part + (int64_t)slot * a.rec_floats;
   };
+  // lane k < 64 holds record k's (m, l); records beyond 64 are folded in serially
   float M = neg_inf();
   for (int k = lane; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
   M = wave_max(M);
@@ -735,12 +753,22 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
       }
       den += wk * lk;
       const int kn = min(64, nrec - k0);
-#pragma unroll 8
-      for (int kk = 0; kk < kn; ++kk) {
-        const float wb = __shfl(wk, kk);
-        const float* o = rec(k0 + kk) + n * D;
+      // batches of 16 records: all loads issued before the accumulation
+      for (int kb = 0; kb < kn; kb += 16) {
+        float ov[16][D / 64];
 #pragma unroll
-        for (int e = 0; e < D / 64; ++e) acc[e] += wb * o[lane + 64 * e];
+        for (int i = 0; i < 16; ++i) {
+          const int kk = min(kb + i, kn - 1);
+          const float* o = rec(k0 + kk) + n * D;
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) ov[i][e] = o[lane + 64 * e];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float wb = (kb + i < kn) ? __shfl(wk, kb + i) : 0.f;
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) acc[e] += wb * ov[i][e];
+        }
       }
     }
     den = wave_sum(den);
