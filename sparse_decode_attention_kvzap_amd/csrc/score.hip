@@ -93,16 +93,24 @@ __global__ __launch_bounds__(256) void score_linear_bf16_kernel(
 // ------------------------------------------------------------------ MLP bf16
 constexpr int MLP_BM = 256;  // inner units per work-group
 constexpr int MLP_BN = 256;  // tokens per work-group
-constexpr int MLP_BK = 64;
-constexpr int MLP_THREADS = 512;
+constexpr int MLP_BK = 64;   // K per stage: 128-byte row segments, two MFMA K-steps
+constexpr int MLP_THREADS = 512;                    // 8 waves: 4 (units) x 2 (tokens)
 constexpr int MLP_ROWB = MLP_BK * 2;                // bytes per LDS row (128)
-constexpr int MLP_TILEB = MLP_BM * MLP_ROWB;        // 32 KB per operand tile
-constexpr int MLP_STAGEB = 2 * MLP_TILEB;           // A + B
-constexpr int MLP_LDSB = 2 * MLP_STAGEB;            // double buffered: 128 KB
+constexpr int MLP_TILEB = 256 * MLP_ROWB;           // 32 KB: one stage of one operand
+constexpr int MLP_WSLOTS = 2;                       // W1 ring (L2-resident operand)
+constexpr int MLP_XSLOTS = 3;                       // hidden-state ring (streamed from HBM)
+constexpr int MLP_LDSB = (MLP_WSLOTS + MLP_XSLOTS) * MLP_TILEB;  // 160 KB: all of a CU's LDS
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return row * MLP_ROWB + 16 * (chunk ^ (row & 7));
-}
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// LDS row r holds the 64 K-values of one row as eight 16-byte chunks; chunk c is stored
+// in slot c ^ (r & 7).  A ds_read_b128 is served eight lanes (128 bytes, all banks) at
+// a time; the eight lanes of a fragment read read eight consecutive rows at one logical
+// chunk, and the swizzle puts them in eight distinct 16-byte bank groups (conflict-free;
+// measured on gfx950 as fast as a linear read).
+__device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ (row & 7); }
+__device__ __forceinline__ int swz(int row, int chunk) { return row * MLP_ROWB + 16 * swz_slot(row, chunk); }
 
 // erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
 // erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1/(1 + p x),
@@ -130,13 +138,14 @@ struct MlpArgs {
   const uint16_t* W1;  // [inner][H]
   const float* b1;     // [inner] or null
   const float* W2;     // [Hkv][inner]
-  float* part;         // [inner/256][ntok][16]
+  float* part;         // [inner/MLP_BM][ntok][16]
   int ntok, H, inner, Hkv;
 };
 
-__global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) {
+__global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void score_mlp_bf16_kernel(MlpArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[MLP_LDSB];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, j = lane >> 4;
   const int wm = wid & 3, wn = wid >> 2;  // wave tile: inner [64wm,+64) x tokens [128wn,+128)
   // XCD-aware order: work-groups are dispatched round-robin over the 8 XCDs, so the
@@ -151,35 +160,62 @@ __global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) 
   const int in0 = part * MLP_BM;
   const int H = a.H;
 
-  // global -> LDS copy assignment: 4 A chunks + 4 B chunks (16 B each) per thread
-  const uint16_t* ga[4];
-  const uint16_t* gb[4];
-  int la[4];
+  // Direct global->LDS copies: one global_load_lds_dwordx4 writes a wave's 64 lanes x
+  // 16 B to 1 KB of contiguous LDS (lane i at +16 i), i.e. 8 rows of a stage.  A stage
+  // of either operand is 32 such blocks; wave w fills blocks 4w .. 4w+3 of both.  Lane i
+  // covers row 8 blk + i/8, slot i%8, and fetches the chunk the swizzle maps to that
+  // slot, so each instruction reads eight whole 128-byte row segments.
+  // Copies go through buffer resources based at this tile's first row: a per-lane 32-bit
+  // offset in one VGPR plus a uniform offset (block, K-step) in an SGPR, so the
+  // 128-entry accumulator still fits in 256 VGPRs.  Every address is in bounds by
+  // construction (tail rows are clamped), the resource range is only a backstop.  Row
+  // 8 blk + i/8 has row & 7 == i/8 for every block, so the swizzled chunk is the same
+  // for all of a wave's blocks.
+  const int chunk = swz_slot(lane >> 3, lane & 7);  // the swizzle is an involution
+  const int rowb = 2 * H;                            // bytes per row
+  const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W1 + (int64_t)in0 * H), (short)0, MLP_BM * rowb, 0x00020000);
+  const int64_t xrows = min((int64_t)MLP_BN, (int64_t)a.ntok - tok0);
+  const __amdgpu_buffer_rsrc_t xres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + tok0 * H), (short)0, (int)(xrows * rowb), 0x00020000);
+  const uint32_t woff = (uint32_t)((lane >> 3) * rowb + 16 * chunk);
+  uint32_t xoff[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const int c = tid + MLP_THREADS * q;  // 0..2047
-    const int row = c >> 3, ch = c & 7;
-    ga[q] = a.W1 + (int64_t)(in0 + row) * H + 8 * ch;
-    int64_t tok = tok0 + row;
-    if (tok >= a.ntok) tok = a.ntok - 1;
-    gb[q] = a.X + tok * H + 8 * ch;
-    la[q] = swz(row, ch);
+    const int row = min(8 * (4 * wid + q) + (lane >> 3), (int)xrows - 1);  // tail: duplicate rows, results dropped
+    xoff[q] = (uint32_t)(row * rowb + 16 * chunk);
   }
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int kt) {
+  uint8_t* const wring = lds;
+  uint8_t* const xring = lds + MLP_WSLOTS * MLP_TILEB;
+  auto issue_w = [&](int kt, int slot) {
+    uint8_t* st = wring + slot * MLP_TILEB + 4 * wid * 1024;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      ra[q] = *reinterpret_cast<const u32x4*>(ga[q] + kt * MLP_BK);
-      rb[q] = *reinterpret_cast<const u32x4*>(gb[q] + kt * MLP_BK);
-    }
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(st + q * 1024), 16, woff,
+                                               (8 * (4 * wid + q)) * rowb + kt * MLP_ROWB, 0, 0);
   };
-  auto lstore = [&](int buf) {
-    uint8_t* base = lds + buf * MLP_STAGEB;
+  auto issue_x = [&](int kt, int slot) {
+    uint8_t* st = xring + slot * MLP_TILEB + 4 * wid * 1024;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      *reinterpret_cast<u32x4*>(base + la[q]) = ra[q];
-      *reinterpret_cast<u32x4*>(base + MLP_TILEB + la[q]) = rb[q];
-    }
+    for (int q = 0; q < 4; ++q)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(st + q * 1024), 16, xoff[q],
+                                               kt * MLP_ROWB, 0, 0);
+  };
+  // fragment of K-step ks (0/1) of the stage in slot kt % ring: 16 rows x 32 K, lane
+  // (n, j) holds row n, logical chunk 4 ks + j (eight consecutive K-values)
+  auto lds_a = [&](int kt, int ks, int mt) {
+    const uint8_t* s = wring + (kt % MLP_WSLOTS) * MLP_TILEB;
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(s + swz(64 * wm + 16 * mt + n, 4 * ks + j)));
+  };
+  auto lds_b = [&](int kt, int ks, int nt) {
+    const uint8_t* s = xring + (kt % MLP_XSLOTS) * MLP_TILEB;
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(s + swz(128 * wn + 16 * nt + n, 4 * ks + j)));
+  };
+  // a plain barrier after this wave's LDS reads: __syncthreads() would also wait for
+  // every copy still in flight
+  auto barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) (vmcnt/expcnt max)
+    __builtin_amdgcn_s_barrier();
   };
 
   f32x4 acc[4][8];
@@ -189,36 +225,90 @@ __global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) 
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nk = H / MLP_BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint8_t* As = lds + cur * MLP_STAGEB;
-    const uint8_t* Bs = As + MLP_TILEB;
+  // Pipeline.  Stage s of W1 lives in W slot s % 2, stage s of the hidden states in X
+  // slot s % 3.  Step kt runs the MFMAs of stage kt in two K-steps; fragments are read
+  // one K-step ahead (A into a second register set, B refilled in place right after its
+  // last use).  Half-way through step kt, after the MFMAs of K-step 0 are issued:
+  //   1. wait for this wave's copies of W1 stage kt+1 and X stage kt+1 (X stage kt+2
+  //      may still fly)
+  //   2. barrier: stage kt+1 is complete for every wave, and every wave has read all of
+  //      stage kt into registers (its K-step 1 fragments were read during K-step 0), so
+  //      both of stage kt's slots are free
+  //   3. copy W1 stage kt+2 into W slot kt % 2, X stage kt+3 into X slot kt % 3
+  // W1 (4 MB, shared by every work-group, L2-resident) gets one step to arrive, the
+  // hidden states (HBM) two.  Copies past the last stage are clamped to it (same bytes,
+  // still into the free slot) so every step issues the same instructions and the wait
+  // counts stay exact; the fragments read in the last step (for a stage nk that does
+  // not exist) come from a slot whose copy has landed and that no copy targets, and are
+  // never used.  sched_barrier(0) pins the order against the instruction scheduler.
+  // prologue: [W0 X0] [X1] [W1 X2]
+  issue_w(0, 0);
+  issue_x(0, 0);
+  issue_x(min(1, nk - 1), 1);
+  issue_w(min(1, nk - 1), 1);
+  issue_x(min(2, nk - 1), 2);
+  __builtin_amdgcn_s_waitcnt(0x0F7C);  // vmcnt(12): W0, X0 landed (expcnt/lgkmcnt max)
+  barrier();
+  bf16x8 fa0[4], fa1[4], fb[8];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int ch = 4 * ks + j;
-      bf16x8 af[4], bfr[8];
+  for (int mt = 0; mt < 4; ++mt) fa0[mt] = lds_a(0, 0, mt);
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int row = 64 * wm + 16 * mt + n;
-        af[mt] = as_bf16x8(*reinterpret_cast<const u32x4*>(As + swz(row, ch)));
+  for (int nt = 0; nt < 8; ++nt) fb[nt] = lds_b(0, 0, nt);
+
+  // The next A fragments are read after the first column of MFMAs, when the oldest B
+  // reads have returned, so at most 12 LDS reads are ever outstanding.  The loop is
+  // rotated so that its back edge sits at the mid-step barrier, which waits for every
+  // LDS read anyway: the compiler's conservative wait at a loop header costs nothing
+  // there, and inside the body it waits only for the fragment the next MFMA needs.
+  auto kstep0 = [&](int kt) {  // K-step 0 of stage kt; reads K-step 1 of stage kt
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma16x16x32(fa0[mt], fb[nt], acc[mt][nt]);
+      if (nt == 0) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) fa1[mt] = lds_a(kt, 1, mt);
       }
-#pragma unroll
-      for (int nt = 0; nt < 8; ++nt) {
-        const int row = 128 * wn + 16 * nt + n;
-        bfr[nt] = as_bf16x8(*reinterpret_cast<const u32x4*>(Bs + swz(row, ch)));
-      }
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = mfma16x16x32(af[mt], bfr[nt], acc[mt][nt]);
+      fb[nt] = lds_b(kt, 1, nt);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
+  };
+  auto kstep1 = [&](int kt, bool next) {  // K-step 1 of stage kt; reads K-step 0 of kt+1
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma16x16x32(fa1[mt], fb[nt], acc[mt][nt]);
+      if (next) {
+        if (nt == 0) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) fa0[mt] = lds_a(kt + 1, 0, mt);
+        }
+        fb[nt] = lds_b(kt + 1, 0, nt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto mid = [&](int kt) {  // stage kt+1 ready, stage kt's slots refilled
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only X stage kt+2 may still fly
+    barrier();
+    issue_w(min(kt + 2, nk - 1), kt % MLP_WSLOTS);
+    issue_x(min(kt + 3, nk - 1), kt % MLP_XSLOTS);
+  };
+  kstep0(0);
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    mid(kt);
+    kstep1(kt, true);
+    kstep0(kt + 1);
   }
+  kstep1(nk - 1, false);
+  // the clamped copies of the last steps are still in flight: drain them before the
+  // epilogue reuses LDS
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: u = GELU(acc + b1) (fp32), s_part = W2[:, slice] . u on MFMA
   // acc[mt][nt][i] = A^T[inner 64wm + 16mt + 4j + i][token 128wn + 16nt + n]
@@ -286,11 +376,11 @@ __global__ __launch_bounds__(MLP_THREADS) void score_mlp_bf16_kernel(MlpArgs a) 
     const int t = e >> 4, h = e & 15;
     const int64_t tok = tok0 + t;
     if (tok < a.ntok && h < a.Hkv) {
-      float s = red[(0 * MLP_BN + t) * 16 + h];
-      s += red[(1 * MLP_BN + t) * 16 + h];
-      s += red[(2 * MLP_BN + t) * 16 + h];
-      s += red[(3 * MLP_BN + t) * 16 + h];
-      dst[tok * 16 + h] = s;
+      float sum = red[(0 * MLP_BN + t) * 16 + h];
+      sum += red[(1 * MLP_BN + t) * 16 + h];
+      sum += red[(2 * MLP_BN + t) * 16 + h];
+      sum += red[(3 * MLP_BN + t) * 16 + h];
+      dst[tok * 16 + h] = sum;
     }
   }
 }
