@@ -187,6 +187,14 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   }
   uint8_t* const wring = lds;
   uint8_t* const xring = lds + MLP_WSLOTS * MLP_TILEB;
+  auto issue_w1 = [&](int kt, int slot, int q) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(wres, (lds_void_t*)(wring + slot * MLP_TILEB + (4 * wid + q) * 1024),
+                                             16, woff, (8 * (4 * wid + q)) * rowb + kt * MLP_ROWB, 0, 0);
+  };
+  auto issue_x1 = [&](int kt, int slot, int q) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(xres, (lds_void_t*)(xring + slot * MLP_TILEB + (4 * wid + q) * 1024),
+                                             16, xoff[q], kt * MLP_ROWB, 0, 0);
+  };
   auto issue_w = [&](int kt, int slot) {
     uint8_t* st = wring + slot * MLP_TILEB + 4 * wid * 1024;
 #pragma unroll
@@ -234,7 +242,8 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   //   2. barrier: stage kt+1 is complete for every wave, and every wave has read all of
   //      stage kt into registers (its K-step 1 fragments were read during K-step 0), so
   //      both of stage kt's slots are free
-  //   3. copy W1 stage kt+2 into W slot kt % 2, X stage kt+3 into X slot kt % 3
+  //   3. copy W1 stage kt+2 into W slot kt % 2, X stage kt+3 into X slot kt % 3, one
+  //      copy per MFMA column of K-step 1 so the matrix pipe never waits on the issue
   // W1 (4 MB, shared by every work-group, L2-resident) gets one step to arrive, the
   // hidden states (HBM) two.  Copies past the last stage are clamped to it (same bytes,
   // still into the free slot) so every step issues the same instructions and the wait
@@ -275,13 +284,20 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto kstep1 = [&](int kt, bool next) {  // K-step 1 of stage kt; reads K-step 0 of kt+1
+  // K-step 1 of stage kt; reads K-step 0 of kt+1 and spreads the copies of W1 stage
+  // kt+2 and X stage kt+3 over its MFMA columns (all W1 copies before all X copies, so
+  // the in-order vmcnt waits above stay exact)
+  auto kstep1 = [&](int kt, bool next) {
+    const int ws = kt % MLP_WSLOTS, xs = kt % MLP_XSLOTS;
+    const int wk = min(kt + 2, nk - 1), xk = min(kt + 3, nk - 1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma16x16x32(fa1[mt], fb[nt], acc[mt][nt]);
       if (next) {
+        if (nt < 4) issue_w1(wk, ws, nt);
+        else issue_x1(xk, xs, nt - 4);
         if (nt == 0) {
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -292,16 +308,14 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto mid = [&](int kt) {  // stage kt+1 ready, stage kt's slots refilled
+  auto mid = [&]() {  // stage kt+1 ready; stage kt's slots free for the copies above
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only X stage kt+2 may still fly
     barrier();
-    issue_w(min(kt + 2, nk - 1), kt % MLP_WSLOTS);
-    issue_x(min(kt + 3, nk - 1), kt % MLP_XSLOTS);
   };
   kstep0(0);
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    mid(kt);
+    mid();
     kstep1(kt, true);
     kstep0(kt + 1);
   }
@@ -385,22 +399,28 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// One thread per token: the token's 16-float partial rows are contiguous (four 16-byte
+// loads per part), and for each head consecutive threads store consecutive positions.
 __global__ __launch_bounds__(256) void score_mlp_finish_kernel(const float* __restrict__ part,
                                                                int nparts, int ntok, int Hkv,
                                                                const float* __restrict__ b2, int T,
                                                                float* __restrict__ scores,
                                                                int64_t ld_s) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)ntok * Hkv) return;
-  // consecutive threads walk tokens of one (b, h) row so score stores coalesce
-  const int64_t bh = idx / T;
-  const int t = static_cast<int>(idx % T);
-  const int b = static_cast<int>(bh / Hkv), h = static_cast<int>(bh % Hkv);
-  const int64_t tok = (int64_t)b * T + t;
-  float s = part[tok * 16 + h];
-  for (int q = 1; q < nparts; ++q) s += part[((int64_t)q * ntok + tok) * 16 + h];
-  if (b2) s += b2[h];
-  scores[bh * ld_s + t] = s;
+  const int64_t tok = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (tok >= ntok) return;
+  f32x4 s[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s[c] = reinterpret_cast<const f32x4*>(part + tok * 16)[c];
+  for (int q = 1; q < nparts; ++q) {
+    const f32x4* pq = reinterpret_cast<const f32x4*>(part + ((int64_t)q * ntok + tok) * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c] += pq[c];
+  }
+  const int b = static_cast<int>(tok / T), t = static_cast<int>(tok % T);
+  float* dst = scores + (int64_t)b * Hkv * ld_s + t;
+#pragma unroll
+  for (int h = 0; h < 16; ++h)
+    if (h < Hkv) dst[(int64_t)h * ld_s] = s[h >> 2][h & 3] + (b2 ? b2[h] : 0.f);
 }
 
 // ------------------------------------------------------------------ small batches
@@ -572,8 +592,7 @@ kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int
   hipLaunchKernelGGL(score_mlp_bf16_kernel, dim3((unsigned)(cdiv64(tiles, 8) * 8 * nparts)),
                      dim3(MLP_THREADS), 0, stream, m);
   KVP_LAUNCH_CHECK();
-  const int64_t n = (int64_t)ntok * Hkv;
-  hipLaunchKernelGGL(score_mlp_finish_kernel, dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, stream, m.part,
+  hipLaunchKernelGGL(score_mlp_finish_kernel, dim3((unsigned)cdiv64(ntok, 256)), dim3(256), 0, stream, m.part,
                      nparts, ntok, Hkv, sc->b2, T, scores, ld_s);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
