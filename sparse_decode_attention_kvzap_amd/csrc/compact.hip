@@ -9,15 +9,19 @@
 // recent window) remain.  BeaconKV body: in DEMOTE_INT8 mode the other entries are
 // kept at low precision instead (absmax int8 per (token, head), K and V separately).
 //
-// Work units are destination pages of 16 slots: a pair's pool pages, then its ring
-// pages, then its int8 pages.  The gather kernel is persistent (grid-stride over the
-// flattened unit list) and finds a unit's pair by binary search in the unit prefix.
+// Work units are destination pages of 16 slots.  Copy units (a pair's pool pages, then
+// its ring pages) go to compact_copy_kernel: each wave owns one contiguous run of
+// units, so it finds its first pair once and then walks pairs in order; a page is
+// copied by one wave (K rows straight through, V transposed through the wave's own LDS
+// tile), with no work-group barrier.  int8 units (DEMOTE_INT8) go to
+// compact_quant_kernel, one work-group per page.
 #include "kvp_internal.h"
 
 namespace kvp {
 
 constexpr int CMP_THREADS = 256;
 constexpr int CMP_GRID = 2048;
+constexpr int CPY_WAVES = CMP_THREADS / 64;
 constexpr int PLAN_THREADS = 1024;
 
 struct CompactArgs {
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(PLAN_THREADS) void compact_plan_kernel(CompactArgs 
     }
     a.kv.length[p] = npool[p];
     if (a.kv.num_pages8 > 0) a.kv.length8[p] = a.demote ? n8[p] : 0;
-    wbase[p] = pages + rpages + pages8;
+    wbase[p] = pages + rpages;  // copy units; int8 pages are numbered by p8base
   }
   __syncthreads();
   block_excl_scan_lds(wbase, np + 1, tmp);
@@ -128,38 +132,6 @@ template <>
 __device__ __forceinline__ float elem_to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
 template <>
 __device__ __forceinline__ float elem_to_f32<float>(float x) { return x; }
-
-// Copy 16 source rows (src[i] < 0 -> zeros) of K and V into a K page [16][d] and a
-// V^T page [d][16].
-template <typename E>
-__device__ void copy_page(const E* ksrc, const E* vsrc, int d, const int* src, E* kdst, E* vdst,
-                          E* vbuf) {
-  const int tid = threadIdx.x;
-  constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
-  const int cpr = d / EPC;             // chunks per row
-  for (int c = tid; c < PAGE * cpr; c += blockDim.x) {
-    const int row = c / cpr, col = (c % cpr) * EPC;
-    const int s = src[row];
-    u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (s >= 0) {
-      kx = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)s * d + col);
-      vx = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)s * d + col);
-    }
-    *reinterpret_cast<u32x4*>(kdst + row * d + col) = kx;
-    *reinterpret_cast<u32x4*>(vbuf + row * d + col) = vx;
-  }
-  __syncthreads();
-  // V^T: row dd holds the 16 slots of dim dd
-  constexpr int CPT = 16 / EPC;  // chunks per V^T row
-  for (int c = tid; c < d * CPT; c += blockDim.x) {
-    const int dd = c / CPT, t0 = (c % CPT) * EPC;
-    E tmp[EPC];
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) tmp[e] = vbuf[(t0 + e) * d + dd];
-    *reinterpret_cast<u32x4*>(vdst + dd * PAGE + t0) = *reinterpret_cast<u32x4*>(tmp);
-  }
-  __syncthreads();
-}
 
 // Quantize 16 source rows into an int8 K page [16][d] and an int8 V^T page [d][16]
 // with one fp32 absmax scale per slot for K and for V.
@@ -224,76 +196,148 @@ __device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, 
   __syncthreads();
 }
 
-template <typename E>
-__global__ __launch_bounds__(CMP_THREADS) void compact_gather_kernel(CompactArgs a) {
-  __shared__ int src[PAGE];
-  __shared__ __attribute__((aligned(16))) E vbuf[PAGE * 128];
+// Slot of ring page r, lane i: the ring holds positions [T - w, T), position t in slot
+// t mod w.  Returns the source row (t if t was kept, else -1) for lanes < PAGE.
+__device__ __forceinline__ int ring_src(const CompactArgs& a, const int* idx, int cnt, int nr, int r,
+                                        int i, int w) {
+  const int slot = r * PAGE + i;
+  const int base = a.T - w;
+  const int t = base + (((slot - base) % w) + w) % w;
+  int s = -1;
+  if (t >= 0) {
+    const int lo = cnt - nr;
+    const int at = lower_bound_i(idx, lo, cnt, t);
+    if (at < cnt && idx[at] == t) s = t;
+  }
+  return s;
+}
+
+template <typename E, int D>
+__global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a) {
+  constexpr int EPC = 16 / sizeof(E);    // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;           // chunks per K row
+  constexpr int NCH = PAGE * CPR;        // chunks per page (128 .. 512)
+  constexpr int NPL = NCH / 64;          // chunks per lane
+  constexpr int TCH = PAGE / EPC;        // chunks per V^T row (one dim, 16 slots)
+  __shared__ __attribute__((aligned(16))) E tile[CPY_WAVES][PAGE * D];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  E* vt = tile[wid];
   const int np = a.num_pairs;
   const int* wbase = ws_wbase(a);
   const int total = wbase[np];
-  const int d = a.d;
+  const int nw = gridDim.x * CPY_WAVES;
+  const int per = cdiv(total, nw);
+  int u = (blockIdx.x * CPY_WAVES + wid) * per;
+  const int uend = min(total, u + per);
+  if (u >= uend) return;
   const int w = a.has_ring ? a.ring.window : 0;
   const int rpages = w / PAGE;
-  for (int wp = blockIdx.x; wp < total; wp += gridDim.x) {
-    const int p = upper_segment(wbase, np, wp);
-    const int local = wp - wbase[p];
+  int p = upper_segment(wbase, np, u);
+  int pb = wbase[p], pe = wbase[p + 1];
+  for (; u < uend; ++u) {
+    while (u >= pe) {  // next pair (units of a pair are contiguous)
+      ++p;
+      pb = pe;
+      pe = wbase[p + 1];
+    }
+    const int local = u - pb;
     const int npl = ws_npool(a)[p];
     const int pages = cdiv(npl, PAGE);
     const int cnt = a.kept_count[p];
     const int* idx = a.kept_idx + (int64_t)p * a.T;
-    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * d;
-    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * d;
+    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * D;
+    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * D;
+    E* kdst;
+    E* vdst;
+    int s = -1;  // lanes < PAGE: source row of slot `lane`
     if (local < pages) {
-      const int j = local;
-      const int dst = ws_pbase(a)[p] + j;
-      if (threadIdx.x < PAGE) {
-        const int i = threadIdx.x;
-        const int s = (j * PAGE + i < npl) ? idx[j * PAGE + i] : -1;
-        src[i] = s;
-        a.kv.page_pos[(int64_t)dst * PAGE + i] = s;
+      const int dst = ws_pbase(a)[p] + local;
+      if (lane < PAGE) {
+        if (local * PAGE + lane < npl) s = idx[local * PAGE + lane];
+        a.kv.page_pos[(int64_t)dst * PAGE + lane] = s;
       }
-      if (threadIdx.x == 0) a.kv.block_table[(int64_t)p * a.kv.max_pages_per_pair + j] = dst;
-      __syncthreads();
-      copy_page<E>(ksrc, vsrc, d, src, reinterpret_cast<E*>(a.kv.k_pages) + (int64_t)dst * PAGE * d,
-                   reinterpret_cast<E*>(a.kv.v_pages) + (int64_t)dst * PAGE * d, vbuf);
-    } else if (local < pages + rpages) {
+      if (lane == 0) a.kv.block_table[(int64_t)p * a.kv.max_pages_per_pair + local] = dst;
+      kdst = reinterpret_cast<E*>(a.kv.k_pages) + (int64_t)dst * PAGE * D;
+      vdst = reinterpret_cast<E*>(a.kv.v_pages) + (int64_t)dst * PAGE * D;
+    } else {
       const int r = local - pages;
-      if (threadIdx.x < PAGE) {
-        const int i = threadIdx.x;
-        const int slot = r * PAGE + i;
-        const int base = a.T - w;
-        int t = base + (((slot - base) % w) + w) % w;
-        int s = -1;
-        if (t >= 0) {
-          const int nr = ws_nring(a)[p];
-          const int lo = cnt - nr;
-          const int at = lower_bound_i(idx, lo, cnt, t);
-          if (at < cnt && idx[at] == t) s = t;
-        }
-        src[i] = s;
+      if (lane < PAGE) {
+        s = ring_src(a, idx, cnt, ws_nring(a)[p], r, lane, w);
+        const int slot = r * PAGE + lane;
         a.ring.pos[(int64_t)p * w + slot] = s;
         a.ring.score[(int64_t)p * w + slot] = (s >= 0) ? a.scores[(int64_t)p * a.ld_s + s] : 0.f;
       }
-      __syncthreads();
-      const int64_t off = ((int64_t)p * rpages + r) * PAGE * d;
-      copy_page<E>(ksrc, vsrc, d, src, reinterpret_cast<E*>(a.ring.k) + off,
-                   reinterpret_cast<E*>(a.ring.v) + off, vbuf);
-    } else {
-      const int j8 = local - pages - rpages;
-      const int ne = ws_n8(a)[p];
-      const int dst = ws_p8base(a)[p] + j8;
-      if (threadIdx.x < PAGE) {
-        const int i = threadIdx.x;
-        const int s = (j8 * PAGE + i < ne) ? idx[cnt + j8 * PAGE + i] : -1;
-        src[i] = s;
-        a.kv.page8_pos[(int64_t)dst * PAGE + i] = s;
-      }
-      if (threadIdx.x == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = dst;
-      __syncthreads();
-      quant_page<E>(ksrc, vsrc, d, src, a.kv.k8_pages + (int64_t)dst * PAGE * d,
-                    a.kv.v8_pages + (int64_t)dst * PAGE * d, a.kv.k8_scale + (int64_t)dst * PAGE,
-                    a.kv.v8_scale + (int64_t)dst * PAGE, reinterpret_cast<int8_t*>(vbuf));
+      const int64_t off = ((int64_t)p * rpages + r) * PAGE * D;
+      kdst = reinterpret_cast<E*>(a.ring.k) + off;
+      vdst = reinterpret_cast<E*>(a.ring.v) + off;
     }
+    // gather: chunk c = lane + 64 i is row c / CPR, columns (c % CPR) * EPC ..
+    u32x4 kx[NPL], vx[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i, row = c / CPR, col = (c % CPR) * EPC;
+      const int sr = __shfl(s, row);
+      kx[i] = u32x4{0u, 0u, 0u, 0u};
+      vx[i] = u32x4{0u, 0u, 0u, 0u};
+      if (sr >= 0) {
+        kx[i] = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)sr * D + col);
+        vx[i] = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)sr * D + col);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i;
+      *reinterpret_cast<u32x4*>(kdst + c * EPC) = kx[i];
+      *reinterpret_cast<u32x4*>(vt + c * EPC) = vx[i];  // V rows [16][D] in LDS
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // V^T: chunk c = lane + 64 i is dim c / TCH, slots (c % TCH) * EPC ..
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i, dd = c / TCH, t0 = (c % TCH) * EPC;
+      E tmp[EPC];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) tmp[e] = vt[(t0 + e) * D + dd];
+      *reinterpret_cast<u32x4*>(vdst + dd * PAGE + t0) = *reinterpret_cast<const u32x4*>(tmp);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+  }
+}
+
+// int8 pages: unit u is int8 page u of the pool; its pair is the last one whose page
+// base is <= u (pairs without int8 pages share the next pair's base).
+template <typename E>
+__global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs a) {
+  __shared__ int src[PAGE];
+  __shared__ __attribute__((aligned(16))) int8_t cbuf[PAGE * 128];
+  const int np = a.num_pairs;
+  const int d = a.d;
+  const int total8 = a.kv.page8_top[0];
+  for (int u = blockIdx.x; u < total8; u += gridDim.x) {
+    const int p = upper_segment(ws_p8base(a), np, u);
+    const int j8 = u - ws_p8base(a)[p];
+    const int ne = ws_n8(a)[p];
+    if (j8 >= cdiv(ne, PAGE)) continue;  // uniform across the work-group
+    const int cnt = a.kept_count[p];
+    const int* idx = a.kept_idx + (int64_t)p * a.T;
+    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * d;
+    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * d;
+    if (threadIdx.x < PAGE) {
+      const int i = threadIdx.x;
+      const int s = (j8 * PAGE + i < ne) ? idx[cnt + j8 * PAGE + i] : -1;
+      src[i] = s;
+      a.kv.page8_pos[(int64_t)u * PAGE + i] = s;
+    }
+    if (threadIdx.x == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = u;
+    __syncthreads();
+    quant_page<E>(ksrc, vsrc, d, src, a.kv.k8_pages + (int64_t)u * PAGE * d,
+                  a.kv.v8_pages + (int64_t)u * PAGE * d, a.kv.k8_scale + (int64_t)u * PAGE,
+                  a.kv.v8_scale + (int64_t)u * PAGE, cbuf);
   }
 }
 
@@ -329,10 +373,22 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
   a.ws = reinterpret_cast<int*>(ws);
   hipLaunchKernelGGL(compact_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a);
   KVP_LAUNCH_CHECK();
-  if (kv->dtype == KVP_BF16)
-    hipLaunchKernelGGL(compact_gather_kernel<uint16_t>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+  const bool bf = kv->dtype == KVP_BF16;
+  if (bf && d == 128)
+    hipLaunchKernelGGL((compact_copy_kernel<uint16_t, 128>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+  else if (bf)
+    hipLaunchKernelGGL((compact_copy_kernel<uint16_t, 64>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+  else if (d == 128)
+    hipLaunchKernelGGL((compact_copy_kernel<float, 128>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
   else
-    hipLaunchKernelGGL(compact_gather_kernel<float>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    hipLaunchKernelGGL((compact_copy_kernel<float, 64>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
   KVP_LAUNCH_CHECK();
+  if (demote) {
+    if (bf)
+      hipLaunchKernelGGL(compact_quant_kernel<uint16_t>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    else
+      hipLaunchKernelGGL(compact_quant_kernel<float>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    KVP_LAUNCH_CHECK();
+  }
   return KVP_OK;
 }
