@@ -197,6 +197,58 @@ def main():
             iso.append(e0.elapsed_time(e1))
     score_iso_ms = float(np.median(iso))
 
+    # End-to-end scaling with kept tokens: the decode step (score the new tokens ->
+    # delayed step -> attention) right after compressing the same context at several
+    # keep ratios (keep 1.0: tau = -inf keeps every token), and the attention alone after
+    # a read flush.  Compression is redone untimed before every repetition.
+    flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    sample = cache.scores.flatten()[:: max(1, cache.scores.numel() // (1 << 24))]
+    keep_scaling = []
+    for keep in (1.0, 0.5, 0.25):
+        tau_k = float("-inf") if keep >= 1.0 else float(np.float32(
+            torch.quantile(sample, 1.0 - keep).item()))
+        cache.tau = tau_k
+        dec, att = [], []
+        for r in range(6):
+            cache.select(T0)
+            cache.compact(kd, vd)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
+            ev[1].record()
+            K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, tau_k, T0, 1)
+            ev[2].record()
+            cache.attend(q)
+            ev[3].record()
+            fsum.add_(flush.sum())
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            cache.attend(q)
+            e1.record()
+            torch.cuda.synchronize()
+            if r >= 1:
+                dec.append(ev[0].elapsed_time(ev[3]))
+                att.append(e0.elapsed_time(e1))
+        vis_k = cache.visible_token_heads()
+        keep_scaling.append({"keep": keep, "tau": tau_k if keep < 1.0 else None,
+                             "visible_token_heads": vis_k,
+                             "decode_step_ms": float(np.median(dec)),
+                             "attn_isolated_ms": float(np.median(att))})
+    del flush
+    cache.tau = tau
+    base = keep_scaling[0]
+    for e in keep_scaling:
+        e["bytes_ratio_vs_keep1"] = e["visible_token_heads"] / base["visible_token_heads"]
+        e["decode_step_ratio_vs_keep1"] = e["decode_step_ms"] / base["decode_step_ms"]
+        e["attn_ratio_vs_keep1"] = e["attn_isolated_ms"] / base["attn_isolated_ms"]
+        e["attn_gbs"] = e["visible_token_heads"] * 2 * d * (2 if wl.kv_dtype == torch.bfloat16 else 4) \
+            / (e["attn_isolated_ms"] * 1e-3) / 1e9
+    log("[bench] keep scaling: " + "; ".join(
+        f"keep {e['keep']}: decode {e['decode_step_ms']:.3f} ms (x{e['decode_step_ratio_vs_keep1']:.2f}), "
+        f"attn {e['attn_isolated_ms']:.3f} ms (x{e['attn_ratio_vs_keep1']:.2f}), bytes x{e['bytes_ratio_vs_keep1']:.2f}"
+        for e in keep_scaling))
+
     # algorithmic work per call
     elt = 2 if wl.kv_dtype == torch.bfloat16 else 4
     kv_bytes_attn = visible * 2 * d * elt + B * Hq * d * (elt + 4)
@@ -275,6 +327,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_step": {"ms": decode_ms, "token_heads_per_s": visible / (decode_ms * 1e-3)},
         "kernels": kernels,
+        "keep_scaling": keep_scaling,
     }
     print(json.dumps(line), flush=True)
 
