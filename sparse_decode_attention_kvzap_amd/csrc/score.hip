@@ -44,6 +44,7 @@ __global__ __launch_bounds__(256) void score_linear_f32_kernel(const float* __re
 
 // ------------------------------------------------------------------ linear bf16
 constexpr int LIN_TILES = 4;  // 16-token tiles per wave
+constexpr int LIN_U = 4;      // K-steps per load batch
 
 __global__ __launch_bounds__(256) void score_linear_bf16_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, const float* __restrict__ bias,
@@ -64,17 +65,41 @@ __global__ __launch_bounds__(256) void score_linear_bf16_kernel(
   f32x4 acc[LIN_TILES];
 #pragma unroll
   for (int tt = 0; tt < LIN_TILES; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // K-steps in batches of LIN_U: a batch's loads (LIN_U x (LIN_TILES + 1) 16-byte
+  // fragments) are all issued before its MFMAs, and the next batch is issued before
+  // this one is consumed, so ~2 batches per wave are in flight (a plain loop makes the
+  // compiler wait for each load before its MFMA).
   const int nk = H / 32;
-#pragma unroll 4
-  for (int kk = 0; kk < nk; ++kk) {
-    u32x4 wv = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
-    if (!hv) wv = u32x4{0u, 0u, 0u, 0u};
+  u32x4 wv[2][LIN_U], xv[2][LIN_U][LIN_TILES];
+  auto load_batch = [&](int b, int kk) {
 #pragma unroll
-    for (int tt = 0; tt < LIN_TILES; ++tt) {
-      const u32x4 xv = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
-      acc[tt] = mfma16x16x32(as_bf16x8(xv), as_bf16x8(wv), acc[tt]);
+    for (int u = 0; u < LIN_U; ++u) {
+      const int k = min(kk + u, nk - 1);
+      wv[b][u] = *reinterpret_cast<const u32x4*>(wr + 32 * k);
+#pragma unroll
+      for (int tt = 0; tt < LIN_TILES; ++tt) xv[b][u][tt] = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * k);
     }
+  };
+  auto mma_batch = [&](int b, int kk) {
+#pragma unroll
+    for (int u = 0; u < LIN_U; ++u) {
+      if (kk + u < nk) {
+        const u32x4 w = hv ? wv[b][u] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int tt = 0; tt < LIN_TILES; ++tt)
+          acc[tt] = mfma16x16x32(as_bf16x8(xv[b][u][tt]), as_bf16x8(w), acc[tt]);
+      }
+    }
+  };
+  load_batch(0, 0);
+  int kk = 0;
+  for (; kk + LIN_U < nk; kk += 2 * LIN_U) {
+    load_batch(1, kk + LIN_U);
+    mma_batch(0, kk);
+    if (kk + 2 * LIN_U < nk) load_batch(0, kk + 2 * LIN_U);
+    mma_batch(1, kk + LIN_U);
   }
+  if (kk < nk) mma_batch(0, kk);
   if (!hv) return;
   const float bb = bias ? bias[n] : 0.f;
 #pragma unroll
@@ -433,6 +458,10 @@ __global__ __launch_bounds__(256) void score_mlp_finish_kernel(const float* __re
 constexpr int SMALL_MAX_TOK = 64;
 constexpr int SMALL_KSLICE = 256;
 
+// NTT = number of 16-token tiles.  Loads are unconditional (token rows clamped, rows of
+// W past `rows` read row 0 and are zeroed) so the compiler issues all of a wave's loads
+// before its MFMAs instead of waiting on each behind a branch.
+template <int NTT>
 __global__ __launch_bounds__(256) void score_small_gemm_kernel(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int rows, int ntok, int H,
     int rtiles, int ksplit, float* __restrict__ part) {
@@ -443,39 +472,44 @@ __global__ __launch_bounds__(256) void score_small_gemm_kernel(
   const int row = rt * 16 + n;
   const bool rv = row < rows;
   const uint16_t* wr = W + (int64_t)(rv ? row : 0) * H + ks * SMALL_KSLICE + 8 * j;
-  const int ntt = (ntok + 15) / 16;
-  const uint16_t* xr[SMALL_MAX_TOK / 16];
+  const uint16_t* xr[NTT];
 #pragma unroll
-  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
+  for (int tt = 0; tt < NTT; ++tt) {
     const int tok = min(tt * 16 + n, ntok - 1);
     xr[tt] = X + (int64_t)tok * H + ks * SMALL_KSLICE + 8 * j;
   }
-  f32x4 acc[SMALL_MAX_TOK / 16];
+  constexpr int NK = SMALL_KSLICE / 32;
+  u32x4 wv[NK], xv[NK][NTT];
 #pragma unroll
-  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kk = 0; kk < NK; ++kk) {
+    wv[kk] = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
 #pragma unroll
-  for (int kk = 0; kk < SMALL_KSLICE / 32; ++kk) {
-    u32x4 wv = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
-    if (!rv) wv = u32x4{0u, 0u, 0u, 0u};
+    for (int tt = 0; tt < NTT; ++tt) xv[kk][tt] = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
+  }
+  f32x4 acc[NTT];
 #pragma unroll
-    for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
-      if (tt < ntt) {
-        const u32x4 xv = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
-        acc[tt] = mfma16x16x32(as_bf16x8(wv), as_bf16x8(xv), acc[tt]);
-      }
-    }
+  for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kk = 0; kk < NK; ++kk) {
+    const u32x4 wk = rv ? wv[kk] : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma16x16x32(as_bf16x8(wk), as_bf16x8(xv[kk][tt]), acc[tt]);
   }
   // acc[tt][i] = C[row 16rt + 4j + i][token 16tt + n]
   const int rpad = rtiles * 16;
 #pragma unroll
-  for (int tt = 0; tt < SMALL_MAX_TOK / 16; ++tt) {
+  for (int tt = 0; tt < NTT; ++tt) {
     const int tok = tt * 16 + n;
-    if (tt < ntt && tok < ntok) {
+    if (tok < ntok) {
       float* dst = part + ((int64_t)ks * ntok + tok) * rpad + rt * 16 + 4 * j;
       *reinterpret_cast<f32x4*>(dst) = acc[tt];
     }
   }
 }
+
+// K slices are summed in a fixed order; loads of absent slices (ks >= ksplit) read the
+// last slice and contribute an exact zero, so every load is unconditional.
+constexpr int SMALL_MAX_KSPLIT = 32;  // hidden size <= 8192
 
 // MLP epilogue: one work-group per token, one thread per inner unit (inner <= 1024).
 __global__ __launch_bounds__(1024) void score_small_mlp_epi_kernel(
@@ -485,13 +519,25 @@ __global__ __launch_bounds__(1024) void score_small_mlp_epi_kernel(
   __shared__ float red[16][16];
   const int tok = blockIdx.x, u = threadIdx.x;
   const int lane = u & 63, wid = u >> 6;
+  float pv[SMALL_MAX_KSPLIT];
+#pragma unroll
+  for (int ks = 0; ks < SMALL_MAX_KSPLIT; ++ks)
+    pv[ks] = part[((int64_t)min(ks, ksplit - 1) * ntok + tok) * inner + u];
+  float w2v[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) w2v[h] = W2[(int64_t)min(h, Hkv - 1) * inner + u];
+  const float bias1 = b1 ? b1[u] : 0.f;
   float a = 0.f;
-  for (int ks = 0; ks < ksplit; ++ks) a += part[((int64_t)ks * ntok + tok) * inner + u];
-  if (b1) a += b1[u];
+#pragma unroll
+  for (int ks = 0; ks < SMALL_MAX_KSPLIT; ++ks) a += (ks < ksplit) ? pv[ks] : 0.f;
+  a += bias1;
   const float g = gelu_erf(a);
-  for (int h = 0; h < Hkv; ++h) {
-    const float v = wave_sum(g * W2[(int64_t)h * inner + u]);
-    if (lane == 0) red[h][wid] = v;
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    if (h < Hkv) {
+      const float v = wave_sum(g * w2v[h]);
+      if (lane == 0) red[h][wid] = v;
+    }
   }
   __syncthreads();
   if (u < Hkv) {
@@ -510,8 +556,12 @@ __global__ __launch_bounds__(256) void score_small_linear_epi_kernel(
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= ntok * Hkv) return;
   const int tok = idx / Hkv, h = idx % Hkv;
+  float pv[SMALL_MAX_KSPLIT];
+#pragma unroll
+  for (int ks = 0; ks < SMALL_MAX_KSPLIT; ++ks) pv[ks] = part[((int64_t)min(ks, ksplit - 1) * ntok + tok) * 16 + h];
   float a = 0.f;
-  for (int ks = 0; ks < ksplit; ++ks) a += part[((int64_t)ks * ntok + tok) * 16 + h];
+#pragma unroll
+  for (int ks = 0; ks < SMALL_MAX_KSPLIT; ++ks) a += (ks < ksplit) ? pv[ks] : 0.f;
   if (bias) a += bias[h];
   const int b = tok / T, t = tok % T;
   scores[((int64_t)b * Hkv + h) * ld_s + t] = a;
@@ -523,6 +573,7 @@ using namespace kvp;
 
 static bool small_path(const kvp_scorer* sc, int64_t ntok) {
   return sc->wdtype == KVP_BF16 && ntok <= SMALL_MAX_TOK && sc->hidden % SMALL_KSLICE == 0 &&
+         sc->hidden / SMALL_KSLICE <= SMALL_MAX_KSPLIT &&
          (sc->kind == KVP_SCORER_LINEAR || sc->inner <= 1024);
 }
 
@@ -548,9 +599,15 @@ kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int
     const int rows = mlp ? sc->inner : Hkv;
     const int rtiles = cdiv(rows, 16);
     float* part = reinterpret_cast<float*>(ws);
-    hipLaunchKernelGGL(score_small_gemm_kernel, dim3(cdiv(rtiles * ksplit, 4)), dim3(256), 0, stream,
-                       reinterpret_cast<const uint16_t*>(hidden),
-                       reinterpret_cast<const uint16_t*>(sc->w1), rows, ntok, H, rtiles, ksplit, part);
+    const uint16_t* xh = reinterpret_cast<const uint16_t*>(hidden);
+    const uint16_t* w1 = reinterpret_cast<const uint16_t*>(sc->w1);
+    const dim3 g(cdiv(rtiles * ksplit, 4));
+    switch (cdiv(ntok, 16)) {
+      case 1: hipLaunchKernelGGL(score_small_gemm_kernel<1>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+      case 2: hipLaunchKernelGGL(score_small_gemm_kernel<2>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+      case 3: hipLaunchKernelGGL(score_small_gemm_kernel<3>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+      default: hipLaunchKernelGGL(score_small_gemm_kernel<4>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+    }
     KVP_LAUNCH_CHECK();
     if (mlp) {
       hipLaunchKernelGGL(score_small_mlp_epi_kernel, dim3(ntok), dim3(sc->inner), 0, stream, part, ksplit,
