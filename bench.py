@@ -166,14 +166,15 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step:.3f} ms/step (wall {wall:.3f}s); "
         + ", ".join(f"{c} {v:.3f}" for c, v in per_call.items()))
 
-    # isolated decode attention; between repetitions the 256 MB MALL is flushed by
-    # READING 1 GiB (a write flush would leave dirty lines draining into the timed run)
+    # isolated decode attention; before each repetition the 256 MB MALL is flushed by
+    # READING 1 GiB (a write flush would leave dirty lines draining into the timed run).
+    # The flush runs on the same stream right before the timed call, with no host sync
+    # in between: an idle GPU takes several microseconds to start the next kernel.
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
     fsum = torch.zeros(1, dtype=torch.int64, device=dev)
     iso = []
     for r in range(12):
         fsum.add_(flush.sum())
-        torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
