@@ -6,6 +6,7 @@ H=4096, 32 Q / 8 KV heads, d=128, T=32768 including the decode token, bf16 KV in
 16-token pages, MLP scorer 4096->512->8, tau at the 75th percentile (25% kept),
 recent 128 kept):
     prefill compression:  kvp_score (MLP over 16 x 32767 hidden states)
+                          -> kvp_threshold (tau = 75th percentile, on the device)
                           -> kvp_select -> kvp_compact (pool + 128-slot ring)
     decode step:          kvp_score (new token) -> kvp_step_delayed -> kvp_decode_attn
 Inputs are resident in HBM before timing.  `value` is kept-KV decode-attention
@@ -109,16 +110,15 @@ def main():
     q_keep = wl.keep_quantiles[0]
     cache = PrunedKVCache(B, Hkv, Hq, d, T, wl.kv_dtype, scorer, wl.R, 0.0, device=dev,
                           max_prompt=T0)
-    # threshold calibration (setup, untimed): quantile of this context's scores
+    # tau is calibrated on the device inside every step (kvp_threshold: the exact
+    # q-quantile of the prompt's scores); its value is logged once here
     cache.score(hidden)
-    torch.cuda.synchronize()
-    tau = float(torch.quantile(cache.scores.flatten()[:: max(1, cache.scores.numel() // (1 << 24))],
-                               q_keep).item())
-    tau = float(np.float32(tau))
-    cache.tau = tau
-    log(f"[bench] tau = {tau:.6f} (quantile {q_keep})")
+    cache.calibrate(q_keep, T0)
+    tau = float(cache.tau_dev.item())
+    log(f"[bench] tau = {tau:.6f} (quantile {q_keep}, computed on the device)")
 
-    calls = ["score_prefill", "select", "compact", "score_new", "step_delayed", "decode_attn"]
+    calls = ["score_prefill", "threshold", "select", "compact", "score_new", "step_delayed",
+             "decode_attn"]
 
     def one_step(ev=None):
         def mark(i):
@@ -127,16 +127,18 @@ def main():
         mark(0)
         cache.score(hidden)
         mark(1)
-        cache.select(T0)
+        cache.calibrate(q_keep, T0)
         mark(2)
-        cache.compact(kd, vd)
+        cache.select(T0)
         mark(3)
-        K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
+        cache.compact(kd, vd)
         mark(4)
-        K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, tau, T0, 1)
+        K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
         mark(5)
-        cache.attend(q)
+        K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, cache.tau_dev, T0, 1)
         mark(6)
+        cache.attend(q)
+        mark(7)
 
     for i in range(args.warmup):
         one_step()
@@ -148,7 +150,8 @@ def main():
     log(f"[bench] warmup done; visible token-heads {visible} of {total_th} "
         f"({visible / total_th:.3f})")
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -203,11 +206,13 @@ def main():
     # keep ratios (keep 1.0: tau = -inf keeps every token), and the attention alone after
     # a read flush.  Compression is redone untimed before every repetition.
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
-    sample = cache.scores.flatten()[:: max(1, cache.scores.numel() // (1 << 24))]
     keep_scaling = []
     for keep in (1.0, 0.5, 0.25):
-        tau_k = float("-inf") if keep >= 1.0 else float(np.float32(
-            torch.quantile(sample, 1.0 - keep).item()))
+        if keep >= 1.0:
+            tau_k = float("-inf")
+        else:
+            cache.calibrate(1.0 - keep, T0)
+            tau_k = float(cache.tau_dev.item())
         cache.tau = tau_k
         dec, att = [], []
         for r in range(6):
@@ -237,7 +242,7 @@ def main():
                              "decode_step_ms": float(np.median(dec)),
                              "attn_isolated_ms": float(np.median(att))})
     del flush
-    cache.tau = tau
+    cache.calibrate(q_keep, T0)
     base = keep_scaling[0]
     for e in keep_scaling:
         e["bytes_ratio_vs_keep1"] = e["visible_token_heads"] / base["visible_token_heads"]
@@ -271,6 +276,8 @@ def main():
                           "traffic": pmc_traffic("score_mlp_bf16") if wl.scorer == "mlp" else None},
         "score_prefill_back_to_back": {"ms": score_iso_ms,
                                        "tflops": score_flops / (score_iso_ms * 1e-3) / 1e12},
+        "threshold": {"ms": per_call["threshold"], "gbs": gbs(ntok * Hkv * 4 * 3, per_call["threshold"]),
+                      "note": "exact radix select on the device, three passes over the scores"},
         "select": {"ms": per_call["select"], "gbs": gbs(select_bytes, per_call["select"])},
         "compact": {"ms": per_call["compact"], "gbs": gbs(compact_bytes, per_call["compact"]),
                     "traffic": pmc_traffic("compact_copy")},

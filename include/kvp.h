@@ -70,7 +70,10 @@ typedef enum kvp_dtype { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
  *           w1 [inner][H] (wdtype), b1 [inner] or NULL, w2 [Hkv][inner] fp32,
  *           b2 [Hkv] or NULL.
  * wdtype must equal the hidden-state dtype.  MLP requires bf16, H % 64 == 0,
- * inner == 512 and Hkv <= 16; LINEAR requires Hkv <= 16 (and H % 32 == 0 for bf16).
+ * inner % 256 == 0 and Hkv <= 16; LINEAR requires Hkv <= 16 (and H % 32 == 0 for
+ * bf16).  Both need a workspace for some shapes (see kvp_score_workspace_size):
+ * the MLP for its per-slice partial scores, and either kind for small batches
+ * (<= 64 tokens, H % 256 == 0, H <= 8192), which split the contraction over K.
  * -------------------------------------------------------------------------- */
 typedef enum kvp_scorer_kind { KVP_SCORER_LINEAR = 0, KVP_SCORER_MLP = 1 } kvp_scorer_kind;
 
@@ -188,6 +191,30 @@ kvp_status kvp_select(const float* scores, int32_t B, int32_t Hkv, int32_t T, in
                       int32_t* kept_count, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t kvp_select_workspace_size(int32_t B, int32_t Hkv, int32_t T);
 
+/* kvp_select_dev_tau - kvp_select with tau read from device memory (tau[0]), e.g.
+ * as written by kvp_threshold, so the prefill needs no host round trip.  Same
+ * arguments, rules and errors as kvp_select; tau == NULL is KVP_E_ARG. */
+kvp_status kvp_select_dev_tau(const float* scores, int32_t B, int32_t Hkv, int32_t T,
+                              int64_t ld_s, const float* tau, int32_t recent, uint32_t* keep_bits,
+                              int32_t* kept_idx, int32_t* kept_count, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
+ * kvp_threshold - on-device threshold for a keep ratio.
+ * Source: KVzap, key points (entries scoring below a threshold are removed):
+ * keeping a fraction k of the entries is thresholding at the (1 - k) quantile.
+ *   tau_out[0] (device memory) = fp32 rounding of the q-quantile of the N = B*Hkv*T
+ *   scores (the first T of each row of [B*Hkv][ld_s]) by numpy's default "linear"
+ *   rule: sorted ascending a[0..N-1], v = (N - 1) q, a[floor v] moved towards
+ *   a[floor v + 1] by v - floor v (a[N-1] when v >= N - 1), interpolated in fp64.
+ *   Any NaN score gives NaN.  q in [0, 1] (else KVP_E_ARG); N < 2^32 and
+ *   B*Hkv <= 65535 (else KVP_E_UNSUPPORTED).  Exact (radix select, not sampling).
+ *   ws >= kvp_threshold_workspace_size() bytes (scratch, any contents).
+ * -------------------------------------------------------------------------- */
+kvp_status kvp_threshold(const float* scores, int32_t B, int32_t Hkv, int32_t T, int64_t ld_s,
+                         double q, float* tau_out, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t kvp_threshold_workspace_size(void);
+
 /* ----------------------------------------------------------------------------
  * kvp_compact - rebuild the paged cache from a dense context and a selection.
  * Source: DeInfer method (b) (a remapping index list drives a copy into a compact,
@@ -231,6 +258,13 @@ size_t kvp_compact_workspace_size(int32_t B, int32_t Hkv);
 kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                             const void* v_new, int32_t dtype, const float* s_new,
                             int64_t ld_s, float tau, int32_t p, hipStream_t stream);
+
+/* kvp_step_delayed_dev_tau - kvp_step_delayed with tau read from device memory
+ * (tau[0]); tau == NULL is KVP_E_ARG. */
+kvp_status kvp_step_delayed_dev_tau(const kvp_paged_kv* kv, const kvp_ring* ring,
+                                    const void* k_new, const void* v_new, int32_t dtype,
+                                    const float* s_new, int64_t ld_s, const float* tau, int32_t p,
+                                    hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
  * kvp_decode_attn - GQA decode attention over the kept entries only.

@@ -77,12 +77,21 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvp_select": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int64, c_float, c_int32,
                                  c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "kvp_select_workspace_size": (c_size_t, [c_int32, c_int32, c_int32]),
+        "kvp_select_dev_tau": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int64, c_void_p,
+                                         c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t,
+                                         c_void_p]),
+        "kvp_threshold": (c_int32, [c_void_p, c_int32, c_int32, c_int32, c_int64, ctypes.c_double,
+                                    c_void_p, c_void_p, c_size_t, c_void_p]),
+        "kvp_threshold_workspace_size": (c_size_t, []),
         "kvp_compact": (c_int32, [c_void_p, c_void_p, c_int32, c_int32, c_int32, c_int32, c_int32,
                                   c_void_p, c_void_p, c_void_p, c_int64, c_int32, P(KvpPagedKV),
                                   P(KvpRing), c_void_p, c_size_t, c_void_p]),
         "kvp_compact_workspace_size": (c_size_t, [c_int32, c_int32]),
         "kvp_step_delayed": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p, c_void_p, c_int32,
                                        c_void_p, c_int64, c_float, c_int32, c_void_p]),
+        "kvp_step_delayed_dev_tau": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p, c_void_p,
+                                               c_int32, c_void_p, c_int64, c_void_p, c_int32,
+                                               c_void_p]),
         "kvp_decode_attn": (c_int32, [c_void_p, c_int32, c_int32, c_int32, P(KvpPagedKV),
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
@@ -270,17 +279,40 @@ def kvp_select_workspace_size(B: int, Hkv: int, T: int) -> int:
     return load().kvp_select_workspace_size(B, Hkv, T)
 
 
-def kvp_select(scores: torch.Tensor, T: int, tau: float, recent: int, keep_bits: torch.Tensor,
+def kvp_select(scores: torch.Tensor, T: int, tau, recent: int, keep_bits: torch.Tensor,
                kept_idx: torch.Tensor, kept_count: torch.Tensor, ws: torch.Tensor,
                stream=None):
     """scores [B, Hkv, ld_s] fp32 -> keep_bits [B*Hkv, ceil(T/32)] i32 (u32 bits),
-    kept_idx [B*Hkv, T] i32, kept_count [B*Hkv] i32."""
+    kept_idx [B*Hkv, T] i32, kept_count [B*Hkv] i32.  tau: a float, or a one-element
+    fp32 device tensor (kvp_select_dev_tau, e.g. written by kvp_threshold)."""
     _cuda(scores, keep_bits, kept_idx, kept_count, ws)
     B, Hkv, ld_s = scores.shape
-    _ok(load().kvp_select(scores.data_ptr(), B, Hkv, T, ld_s, float(tau), recent,
-                          keep_bits.data_ptr(), kept_idx.data_ptr(), kept_count.data_ptr(),
-                          ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
-        "kvp_select")
+    args = (keep_bits.data_ptr(), kept_idx.data_ptr(), kept_count.data_ptr(),
+            ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream))
+    if isinstance(tau, torch.Tensor):
+        _cuda(tau)
+        assert tau.dtype == torch.float32 and tau.numel() >= 1
+        _ok(load().kvp_select_dev_tau(scores.data_ptr(), B, Hkv, T, ld_s, tau.data_ptr(), recent,
+                                      *args), "kvp_select_dev_tau")
+    else:
+        _ok(load().kvp_select(scores.data_ptr(), B, Hkv, T, ld_s, float(tau), recent, *args),
+            "kvp_select")
+
+
+def kvp_threshold_workspace_size() -> int:
+    return load().kvp_threshold_workspace_size()
+
+
+def kvp_threshold(scores: torch.Tensor, T: int, q: float, tau_out: torch.Tensor,
+                  ws: torch.Tensor, stream=None) -> torch.Tensor:
+    """tau_out[0] = fp32 q-quantile (numpy "linear") of scores[:, :, :T], on the device."""
+    _cuda(scores, tau_out, ws)
+    assert tau_out.dtype == torch.float32 and tau_out.numel() >= 1
+    B, Hkv, ld_s = scores.shape
+    _ok(load().kvp_threshold(scores.data_ptr(), B, Hkv, T, ld_s, float(q), tau_out.data_ptr(),
+                             ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
+        "kvp_threshold")
+    return tau_out
 
 
 def kvp_compact_workspace_size(B: int, Hkv: int) -> int:
@@ -302,12 +334,21 @@ def kvp_compact(k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
 
 
 def kvp_step_delayed(kv: PagedKV, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor,
-                     s_new: torch.Tensor, tau: float, p: int, ld_s: int = 1, stream=None):
-    """Append position p: k_new, v_new [B, Hkv, d]; s_new holds pair i's score at i*ld_s."""
+                     s_new: torch.Tensor, tau, p: int, ld_s: int = 1, stream=None):
+    """Append position p: k_new, v_new [B, Hkv, d]; s_new holds pair i's score at i*ld_s.
+    tau: a float, or a one-element fp32 device tensor (kvp_step_delayed_dev_tau)."""
     _cuda(k_new, v_new, s_new)
-    _ok(load().kvp_step_delayed(_kvref(kv), _ringref(ring), k_new.data_ptr(), v_new.data_ptr(),
-                                _dt(k_new), s_new.data_ptr(), ld_s, float(tau), p,
-                                _stream(stream)), "kvp_step_delayed")
+    if isinstance(tau, torch.Tensor):
+        _cuda(tau)
+        assert tau.dtype == torch.float32 and tau.numel() >= 1
+        _ok(load().kvp_step_delayed_dev_tau(_kvref(kv), _ringref(ring), k_new.data_ptr(),
+                                            v_new.data_ptr(), _dt(k_new), s_new.data_ptr(), ld_s,
+                                            tau.data_ptr(), p, _stream(stream)),
+            "kvp_step_delayed_dev_tau")
+    else:
+        _ok(load().kvp_step_delayed(_kvref(kv), _ringref(ring), k_new.data_ptr(), v_new.data_ptr(),
+                                    _dt(k_new), s_new.data_ptr(), ld_s, float(tau), p,
+                                    _stream(stream)), "kvp_step_delayed")
 
 
 def kvp_decode_attn_workspace_size(B: int, Hq: int, num_pairs: int, head_dim: int) -> int:

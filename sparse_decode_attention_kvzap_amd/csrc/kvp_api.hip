@@ -9,15 +9,17 @@
 kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int T, float* scores,
                             int64_t ld_s, void* ws, hipStream_t stream);
 kvp_status kvp_launch_select(const float* scores, int num_pairs, int T, int64_t ld_s, float tau,
-                             int recent, uint32_t* bits, int* kept_idx, int* kept_count, void* ws,
-                             hipStream_t stream);
+                             const float* tau_dev, int recent, uint32_t* bits, int* kept_idx,
+                             int* kept_count, void* ws, hipStream_t stream);
+kvp_status kvp_launch_threshold(const float* scores, int rows, int T, int64_t ld_s, double q,
+                                float* tau_out, void* ws, hipStream_t stream);
 kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T, int d,
                               const int* kept_idx, const int* kept_count, const float* scores,
                               int64_t ld_s, int demote, const kvp_paged_kv* kv, const kvp_ring* ring,
                               void* ws, hipStream_t stream);
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   int p, hipStream_t stream);
+                                   const float* tau_dev, int p, hipStream_t stream);
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   hipStream_t stream);
@@ -97,16 +99,45 @@ extern "C" kvp_status kvp_score(const kvp_scorer* sc, const void* hidden, int32_
   return kvp_launch_score(sc, hidden, B, T, scores, ld_s, ws, stream);
 }
 
-extern "C" kvp_status kvp_select(const float* scores, int32_t B, int32_t Hkv, int32_t T,
-                                 int64_t ld_s, float tau, int32_t recent, uint32_t* keep_bits,
-                                 int32_t* kept_idx, int32_t* kept_count, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+static kvp_status select_common(const float* scores, int32_t B, int32_t Hkv, int32_t T, int64_t ld_s,
+                                float tau, const float* tau_dev, int32_t recent, uint32_t* keep_bits,
+                                int32_t* kept_idx, int32_t* kept_count, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
   if (!scores || !keep_bits || !kept_idx || !kept_count) return KVP_E_ARG;
   if (B <= 0 || Hkv <= 0 || T <= 0 || ld_s < T || recent < 0) return KVP_E_ARG;
   if ((int64_t)B * Hkv > 65535 || T > kMaxTokens) return KVP_E_ARG;
   if (!ws || ws_bytes < kvp_select_workspace_size(B, Hkv, T)) return KVP_E_WORKSPACE;
-  return kvp_launch_select(scores, B * Hkv, T, ld_s, tau, recent, keep_bits, kept_idx, kept_count,
-                           ws, stream);
+  return kvp_launch_select(scores, B * Hkv, T, ld_s, tau, tau_dev, recent, keep_bits, kept_idx,
+                           kept_count, ws, stream);
+}
+
+extern "C" kvp_status kvp_select(const float* scores, int32_t B, int32_t Hkv, int32_t T,
+                                 int64_t ld_s, float tau, int32_t recent, uint32_t* keep_bits,
+                                 int32_t* kept_idx, int32_t* kept_count, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  return select_common(scores, B, Hkv, T, ld_s, tau, nullptr, recent, keep_bits, kept_idx,
+                       kept_count, ws, ws_bytes, stream);
+}
+
+extern "C" kvp_status kvp_select_dev_tau(const float* scores, int32_t B, int32_t Hkv, int32_t T,
+                                         int64_t ld_s, const float* tau, int32_t recent,
+                                         uint32_t* keep_bits, int32_t* kept_idx,
+                                         int32_t* kept_count, void* ws, size_t ws_bytes,
+                                         hipStream_t stream) {
+  if (!tau) return KVP_E_ARG;
+  return select_common(scores, B, Hkv, T, ld_s, 0.0f, tau, recent, keep_bits, kept_idx, kept_count,
+                       ws, ws_bytes, stream);
+}
+
+extern "C" kvp_status kvp_threshold(const float* scores, int32_t B, int32_t Hkv, int32_t T,
+                                    int64_t ld_s, double q, float* tau_out, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+  if (!scores || !tau_out) return KVP_E_ARG;
+  if (B <= 0 || Hkv <= 0 || T <= 0 || ld_s < T) return KVP_E_ARG;
+  if (!(q >= 0.0 && q <= 1.0)) return KVP_E_ARG;  // also rejects NaN
+  if ((int64_t)B * Hkv > 65535 || (int64_t)B * Hkv * T > 0xffffffffLL) return KVP_E_UNSUPPORTED;
+  if (!ws || ws_bytes < kvp_threshold_workspace_size()) return KVP_E_WORKSPACE;
+  return kvp_launch_threshold(scores, B * Hkv, T, ld_s, q, tau_out, ws, stream);
 }
 
 extern "C" kvp_status kvp_compact(const void* k, const void* v, int32_t dtype, int32_t B,
@@ -130,17 +161,31 @@ extern "C" kvp_status kvp_compact(const void* k, const void* v, int32_t dtype, i
                             mode == KVP_COMPACT_DEMOTE_INT8, kv, ring, ws, stream);
 }
 
-extern "C" kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
-                                       const void* k_new, const void* v_new, int32_t dtype,
-                                       const float* s_new, int64_t ld_s, float tau, int32_t p,
-                                       hipStream_t stream) {
+static kvp_status step_common(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                              const void* v_new, int32_t dtype, const float* s_new, int64_t ld_s,
+                              float tau, const float* tau_dev, int32_t p, hipStream_t stream) {
   kvp_status st = check_kv(kv);
   if (st != KVP_OK) return st;
   if (!ring) return KVP_E_ARG;
   if ((st = check_ring(ring)) != KVP_OK) return st;
   if (!k_new || !v_new || !s_new || ld_s < 1 || p < 0) return KVP_E_ARG;
   if (dtype != kv->dtype) return KVP_E_DTYPE;
-  return kvp_launch_step_delayed(kv, ring, k_new, v_new, s_new, ld_s, tau, p, stream);
+  return kvp_launch_step_delayed(kv, ring, k_new, v_new, s_new, ld_s, tau, tau_dev, p, stream);
+}
+
+extern "C" kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
+                                       const void* k_new, const void* v_new, int32_t dtype,
+                                       const float* s_new, int64_t ld_s, float tau, int32_t p,
+                                       hipStream_t stream) {
+  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, tau, nullptr, p, stream);
+}
+
+extern "C" kvp_status kvp_step_delayed_dev_tau(const kvp_paged_kv* kv, const kvp_ring* ring,
+                                               const void* k_new, const void* v_new, int32_t dtype,
+                                               const float* s_new, int64_t ld_s, const float* tau,
+                                               int32_t p, hipStream_t stream) {
+  if (!tau) return KVP_E_ARG;
+  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, 0.0f, tau, p, stream);
 }
 
 extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,

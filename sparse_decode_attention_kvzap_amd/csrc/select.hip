@@ -20,9 +20,10 @@ constexpr int SEL_THREADS = 256;
 constexpr int SEL_GROUPS = SEL_TILE / SEL_THREADS;  // 64-token groups per wave
 
 __global__ __launch_bounds__(SEL_THREADS) void select_bits_kernel(
-    const float* __restrict__ scores, int T, int64_t ld_s, float tau, int recent,
-    uint32_t* __restrict__ bits, int nwords, int* __restrict__ tile_count, int ntiles) {
+    const float* __restrict__ scores, int T, int64_t ld_s, float tau_val, const float* tau_dev,
+    int recent, uint32_t* __restrict__ bits, int nwords, int* __restrict__ tile_count, int ntiles) {
   const int pair = blockIdx.y, tile = blockIdx.x;
+  const float tau = tau_dev ? tau_dev[0] : tau_val;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const float* s = scores + (int64_t)pair * ld_s;
   uint32_t* bw = bits + (int64_t)pair * nwords;
@@ -148,14 +149,14 @@ extern "C" size_t kvp_select_workspace_size(int32_t B, int32_t Hkv, int32_t T) {
 }
 
 kvp_status kvp_launch_select(const float* scores, int num_pairs, int T, int64_t ld_s, float tau,
-                             int recent, uint32_t* bits, int* kept_idx, int* kept_count,
-                             void* ws, hipStream_t stream) {
+                             const float* tau_dev, int recent, uint32_t* bits, int* kept_idx,
+                             int* kept_count, void* ws, hipStream_t stream) {
   const int ntiles = cdiv(T, SEL_TILE);
   const int nwords = cdiv(T, 32);
   int* tile_count = reinterpret_cast<int*>(ws);
   dim3 grid(ntiles, num_pairs);
   hipLaunchKernelGGL(select_bits_kernel, grid, dim3(SEL_THREADS), 0, stream, scores, T, ld_s, tau,
-                     recent, bits, nwords, tile_count, ntiles);
+                     tau_dev, recent, bits, nwords, tile_count, ntiles);
   KVP_LAUNCH_CHECK();
   hipLaunchKernelGGL(select_scatter_kernel, grid, dim3(SEL_THREADS), 0, stream, bits, T, nwords,
                      tile_count, ntiles, kept_idx, kept_count);

@@ -22,6 +22,7 @@ struct StepArgs {
   const float* s_new;
   int64_t ld_s;
   float tau;
+  const float* tau_dev;  // if set, tau is read from here
   int p;
 };
 
@@ -55,8 +56,9 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
       vo[e] = rv[dd * PAGE];
     }
   }
+  const float tau = a.tau_dev ? a.tau_dev[0] : a.tau;
   if (old_pos >= 0) {
-    if (old_s >= a.tau) {
+    if (old_s >= tau) {
       // retain: append to the pool (allocating a page when the last one is full)
       const int len = a.kv.length[pair];
       const int j = len / PAGE, sl = len % PAGE;
@@ -172,7 +174,7 @@ using namespace kvp;
 
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   int p, hipStream_t stream) {
+                                   const float* tau_dev, int p, hipStream_t stream) {
   StepArgs a;
   a.kv = *kv;
   a.ring = *ring;
@@ -181,6 +183,7 @@ kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
   a.s_new = s_new;
   a.ld_s = ld_s;
   a.tau = tau;
+  a.tau_dev = tau_dev;
   a.p = p;
   const dim3 grid(cdiv(kv->num_pairs, 4));
   if (kv->dtype == KVP_BF16) {

@@ -1,7 +1,11 @@
 """One attention layer's pruned KV cache driven through the five C-ABI calls.
 
-Prefill (compress a context):  kvp_score -> kvp_select -> kvp_compact
+Prefill (compress a context):  kvp_score -> [kvp_threshold] -> kvp_select -> kvp_compact
 Decode step (one new token):   kvp_score -> kvp_step_delayed -> kvp_decode_attn
+
+tau is either a fixed float or, after calibrate(q), a one-element device tensor holding
+the q-quantile of the prompt's scores (computed on the device), which select and the
+delayed step then read without a host round trip.
 
 KVzap (max5.ai digest, practical application): score every entry, drop low scores,
 always keep the most recent tokens.  DMS (euno.news, Delayed Eviction): with tau = 0
@@ -30,7 +34,7 @@ class PrunedKVCache:
         self.dtype = dtype
         self.scorer = scorer
         self.window = window
-        self.tau = float(tau)
+        self.tau = float(tau)  # or a device tensor after calibrate()
         self.demote = demote
         self.device = torch.device(device)
         dev = self.device
@@ -56,12 +60,21 @@ class PrunedKVCache:
         self.ws_attn = L.decode_attn_workspace(B, Hq, self.kv, dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         self.scale = L.sm_scale(d)
+        self.tau_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.ws_threshold = torch.empty(L.kvp_threshold_workspace_size() // 4 + 1,
+                                        dtype=torch.int32, device=dev)
         self.T0 = 0
 
     # -- prefill -----------------------------------------------------------------
     def score(self, hidden: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
         return L.kvp_score(self.scorer, hidden, self.scores if out is None else out,
                            self.ws_score, stream)
+
+    def calibrate(self, q: float, T: int, stream=None) -> torch.Tensor:
+        """tau := the q-quantile of scores[:, :, :T], on the device (keep ~ 1 - q)."""
+        L.kvp_threshold(self.scores, T, q, self.tau_dev, self.ws_threshold, stream)
+        self.tau = self.tau_dev
+        return self.tau_dev
 
     def select(self, T: int, stream=None):
         L.kvp_select(self.scores, T, self.tau, self.window, self.keep_bits, self.kept_idx,

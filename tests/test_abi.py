@@ -159,10 +159,26 @@ def test_host_validation_without_device(L):
                            None) == E_ARG
     assert lib.kvp_compact(fake, fake, L.KVP_BF16, 1, 3, 64, 128, fake, fake, None, 0,
                            L.KVP_COMPACT_EVICT, ctypes.byref(kv), None, fake, 1 << 16, None) == E_ARG
+    # threshold: null pointers, q outside [0, 1] or NaN, too many scores, workspace
+    thr_ws = L.kvp_threshold_workspace_size()
+    assert thr_ws == 64 + 3 * 8 * 2 * 2048 * 4
+    assert lib.kvp_threshold(None, 1, 1, 10, 10, 0.5, fake, fake, thr_ws, None) == E_ARG
+    assert lib.kvp_threshold(fake, 1, 1, 10, 10, 0.5, None, fake, thr_ws, None) == E_ARG
+    for q in (-0.1, 1.5, float("nan")):
+        assert lib.kvp_threshold(fake, 1, 1, 10, 10, q, fake, fake, thr_ws, None) == E_ARG
+    assert lib.kvp_threshold(fake, 1, 1, 10, 5, 0.5, fake, fake, thr_ws, None) == E_ARG  # ld_s < T
+    assert lib.kvp_threshold(fake, 65535, 1, 1 << 17, 1 << 17, 0.5, fake, fake, thr_ws,
+                             None) == E_UNSUP
+    assert lib.kvp_threshold(fake, 1, 1, 10, 10, 0.5, fake, fake, thr_ws - 1, None) == E_WS
+    # device-tau variants need the tau pointer
+    assert lib.kvp_select_dev_tau(fake, 1, 1, 10, 10, None, 128, fake, fake, fake, fake, 64,
+                                  None) == E_ARG
     # step: position must be >= 0
     ring = L.KvpRing(64, 0, fake, fake, fake, fake)
     assert lib.kvp_step_delayed(ctypes.byref(kv), ctypes.byref(ring), fake, fake, L.KVP_BF16, fake,
                                 1, 0.0, -1, None) == E_ARG
+    assert lib.kvp_step_delayed_dev_tau(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
+                                        L.KVP_BF16, fake, 1, None, 5, None) == E_ARG
 
 
 def test_missing_library_fails_loudly(L, tmp_path):

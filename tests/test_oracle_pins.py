@@ -141,6 +141,30 @@ def test_threshold_keep_count(q):
     assert float(tau) == float(np.float32(np.quantile(s.ravel(), q)))
 
 
+def _quantile_by_definition(values, q):
+    """The 'linear' sample quantile written out: sort, v = (n - 1) q, interpolate
+    between the order statistics at floor(v) and floor(v) + 1 (Hyndman & Fan's
+    definition 7)."""
+    a = sorted(float(x) for x in values)
+    v = (len(a) - 1) * q
+    i = math.floor(v)
+    if i >= len(a) - 1:
+        return a[-1]
+    return a[i] + (a[i + 1] - a[i]) * (v - i)
+
+
+@pytest.mark.parametrize("n,q", [(1, 0.3), (2, 0.5), (5, 0.0), (5, 1.0), (7, 0.25), (10, 0.9),
+                                 (101, 0.75), (1000, 0.333)])
+def test_threshold_is_the_linear_sample_quantile(n, q):
+    rng = np.random.default_rng(n)
+    s = np.round(rng.standard_normal(n) * 4) / 4  # ties included
+    tau = oracle.threshold_quantile(s, q)
+    want = _quantile_by_definition(s, q)
+    assert abs(float(tau) - want) <= 1e-6 * max(1.0, abs(want))
+    assert tau == np.float32(want) or abs(float(tau) - float(np.float32(want))) <= \
+        np.spacing(np.float32(want))
+
+
 # ------------------------------------------------------------------ mask
 
 
