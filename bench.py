@@ -58,6 +58,8 @@ def main():
     ap.add_argument("--workload", default="qwen3_8b_layer")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-rows", type=int, default=16, help="batch rows in the CPU sample")
+    ap.add_argument("--no-scaling", action="store_true",
+                    help="skip the keep-ratio sweep (profiling runs of the headline workload)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -207,7 +209,7 @@ def main():
     # a read flush.  Compression is redone untimed before every repetition.
     flush = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     keep_scaling = []
-    for keep in (1.0, 0.5, 0.25):
+    for keep in (() if args.no_scaling else (1.0, 0.5, 0.25)):
         if keep >= 1.0:
             tau_k = float("-inf")
         else:
@@ -243,7 +245,7 @@ def main():
                              "attn_isolated_ms": float(np.median(att))})
     del flush
     cache.calibrate(q_keep, T0)
-    base = keep_scaling[0]
+    base = keep_scaling[0] if keep_scaling else None
     for e in keep_scaling:
         e["bytes_ratio_vs_keep1"] = e["visible_token_heads"] / base["visible_token_heads"]
         e["decode_step_ratio_vs_keep1"] = e["decode_step_ms"] / base["decode_step_ms"]
