@@ -259,12 +259,16 @@ kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const 
                             const void* v_new, int32_t dtype, const float* s_new,
                             int64_t ld_s, float tau, int32_t p, hipStream_t stream);
 
-/* kvp_step_delayed_dev_tau - kvp_step_delayed with tau read from device memory
- * (tau[0]); tau == NULL is KVP_E_ARG. */
-kvp_status kvp_step_delayed_dev_tau(const kvp_paged_kv* kv, const kvp_ring* ring,
-                                    const void* k_new, const void* v_new, int32_t dtype,
-                                    const float* s_new, int64_t ld_s, const float* tau, int32_t p,
-                                    hipStream_t stream);
+/* kvp_step_delayed_dev - kvp_step_delayed with every per-step value in device memory,
+ * so the call can sit in a captured HIP graph and be replayed step after step (the
+ * fixed-address decode step of the DeInfer methodology, part (b)).
+ *   tau  device float: tau[0] (e.g. written by kvp_threshold)
+ *   pos  device int32[2]: pos[0] = absolute position of the new token; pos[1] must be 0
+ *        (arrival count).  On completion pos[0] has advanced by 1 and pos[1] is 0 again.
+ * tau == NULL or pos == NULL is KVP_E_ARG; otherwise as kvp_step_delayed. */
+kvp_status kvp_step_delayed_dev(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                const void* v_new, int32_t dtype, const float* s_new,
+                                int64_t ld_s, const float* tau, int32_t* pos, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
  * kvp_decode_attn - GQA decode attention over the kept entries only.

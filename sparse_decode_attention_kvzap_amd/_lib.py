@@ -89,9 +89,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "kvp_compact_workspace_size": (c_size_t, [c_int32, c_int32]),
         "kvp_step_delayed": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p, c_void_p, c_int32,
                                        c_void_p, c_int64, c_float, c_int32, c_void_p]),
-        "kvp_step_delayed_dev_tau": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p, c_void_p,
-                                               c_int32, c_void_p, c_int64, c_void_p, c_int32,
-                                               c_void_p]),
+        "kvp_step_delayed_dev": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p, c_void_p,
+                                           c_int32, c_void_p, c_int64, c_void_p, c_void_p,
+                                           c_void_p]),
         "kvp_decode_attn": (c_int32, [c_void_p, c_int32, c_int32, c_int32, P(KvpPagedKV),
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
@@ -334,17 +334,21 @@ def kvp_compact(k: torch.Tensor, v: torch.Tensor, kept_idx: torch.Tensor,
 
 
 def kvp_step_delayed(kv: PagedKV, ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor,
-                     s_new: torch.Tensor, tau, p: int, ld_s: int = 1, stream=None):
+                     s_new: torch.Tensor, tau, p, ld_s: int = 1, stream=None):
     """Append position p: k_new, v_new [B, Hkv, d]; s_new holds pair i's score at i*ld_s.
-    tau: a float, or a one-element fp32 device tensor (kvp_step_delayed_dev_tau)."""
+    tau float and p int: kvp_step_delayed.  tau a one-element fp32 device tensor and p an
+    int32[2] device tensor [position, 0]: kvp_step_delayed_dev, which reads both on the
+    device and advances p[0] (graph-replayable)."""
     _cuda(k_new, v_new, s_new)
-    if isinstance(tau, torch.Tensor):
-        _cuda(tau)
-        assert tau.dtype == torch.float32 and tau.numel() >= 1
-        _ok(load().kvp_step_delayed_dev_tau(_kvref(kv), _ringref(ring), k_new.data_ptr(),
-                                            v_new.data_ptr(), _dt(k_new), s_new.data_ptr(), ld_s,
-                                            tau.data_ptr(), p, _stream(stream)),
-            "kvp_step_delayed_dev_tau")
+    if isinstance(tau, torch.Tensor) or isinstance(p, torch.Tensor):
+        if not (isinstance(tau, torch.Tensor) and isinstance(p, torch.Tensor)):
+            raise ValueError("device tau and device position go together")
+        _cuda(tau, p)
+        assert tau.dtype == torch.float32 and p.dtype == torch.int32 and p.numel() >= 2
+        _ok(load().kvp_step_delayed_dev(_kvref(kv), _ringref(ring), k_new.data_ptr(),
+                                        v_new.data_ptr(), _dt(k_new), s_new.data_ptr(), ld_s,
+                                        tau.data_ptr(), p.data_ptr(), _stream(stream)),
+            "kvp_step_delayed_dev")
     else:
         _ok(load().kvp_step_delayed(_kvref(kv), _ringref(ring), k_new.data_ptr(), v_new.data_ptr(),
                                     _dt(k_new), s_new.data_ptr(), ld_s, float(tau), p,

@@ -19,7 +19,7 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
                               void* ws, hipStream_t stream);
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   const float* tau_dev, int p, hipStream_t stream);
+                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream);
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   hipStream_t stream);
@@ -163,29 +163,31 @@ extern "C" kvp_status kvp_compact(const void* k, const void* v, int32_t dtype, i
 
 static kvp_status step_common(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                               const void* v_new, int32_t dtype, const float* s_new, int64_t ld_s,
-                              float tau, const float* tau_dev, int32_t p, hipStream_t stream) {
+                              float tau, const float* tau_dev, int32_t p, int32_t* pos_dev,
+                              hipStream_t stream) {
   kvp_status st = check_kv(kv);
   if (st != KVP_OK) return st;
   if (!ring) return KVP_E_ARG;
   if ((st = check_ring(ring)) != KVP_OK) return st;
   if (!k_new || !v_new || !s_new || ld_s < 1 || p < 0) return KVP_E_ARG;
   if (dtype != kv->dtype) return KVP_E_DTYPE;
-  return kvp_launch_step_delayed(kv, ring, k_new, v_new, s_new, ld_s, tau, tau_dev, p, stream);
+  return kvp_launch_step_delayed(kv, ring, k_new, v_new, s_new, ld_s, tau, tau_dev, p, pos_dev,
+                                 stream);
 }
 
 extern "C" kvp_status kvp_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
                                        const void* k_new, const void* v_new, int32_t dtype,
                                        const float* s_new, int64_t ld_s, float tau, int32_t p,
                                        hipStream_t stream) {
-  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, tau, nullptr, p, stream);
+  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, tau, nullptr, p, nullptr, stream);
 }
 
-extern "C" kvp_status kvp_step_delayed_dev_tau(const kvp_paged_kv* kv, const kvp_ring* ring,
-                                               const void* k_new, const void* v_new, int32_t dtype,
-                                               const float* s_new, int64_t ld_s, const float* tau,
-                                               int32_t p, hipStream_t stream) {
-  if (!tau) return KVP_E_ARG;
-  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, 0.0f, tau, p, stream);
+extern "C" kvp_status kvp_step_delayed_dev(const kvp_paged_kv* kv, const kvp_ring* ring,
+                                           const void* k_new, const void* v_new, int32_t dtype,
+                                           const float* s_new, int64_t ld_s, const float* tau,
+                                           int32_t* pos, hipStream_t stream) {
+  if (!tau || !pos) return KVP_E_ARG;
+  return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, 0.0f, tau, 0, pos, stream);
 }
 
 extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,

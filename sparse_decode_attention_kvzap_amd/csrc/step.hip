@@ -24,6 +24,7 @@ struct StepArgs {
   float tau;
   const float* tau_dev;  // if set, tau is read from here
   int p;
+  int* pos_dev;  // if set: [position, arrivals]; the position is read from here and advanced
 };
 
 template <typename E>
@@ -39,7 +40,8 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (pair >= a.kv.num_pairs) return;
   const int w = a.ring.window;
-  const int slot = a.p % w;
+  const int p = a.pos_dev ? a.pos_dev[0] : a.p;
+  const int slot = p % w;
   const int rp = slot / PAGE, rs = slot % PAGE;
   const int64_t roff = ((int64_t)pair * (w / PAGE) + rp) * PAGE * D;
   E* rk = reinterpret_cast<E*>(a.ring.k) + roff + rs * D;  // K row of the slot
@@ -163,8 +165,17 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
     }
   }
   if (lane == 0) {
-    a.ring.pos[(int64_t)pair * w + slot] = a.p;
+    a.ring.pos[(int64_t)pair * w + slot] = p;
     a.ring.score[(int64_t)pair * w + slot] = a.s_new[(int64_t)pair * a.ld_s];
+  }
+  // Device-resident position: every pair's wave has read it (above) before it counts
+  // itself here; the last of the num_pairs arrivals advances it and clears the count, so
+  // the next call (or graph replay) appends the next position.
+  if (a.pos_dev && lane == 0) {
+    if (atomicAdd(&a.pos_dev[1], 1) == a.kv.num_pairs - 1) {
+      a.pos_dev[0] = p + 1;
+      a.pos_dev[1] = 0;
+    }
   }
 }
 
@@ -174,7 +185,7 @@ using namespace kvp;
 
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   const float* tau_dev, int p, hipStream_t stream) {
+                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream) {
   StepArgs a;
   a.kv = *kv;
   a.ring = *ring;
@@ -185,6 +196,7 @@ kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
   a.tau = tau;
   a.tau_dev = tau_dev;
   a.p = p;
+  a.pos_dev = pos_dev;
   const dim3 grid(cdiv(kv->num_pairs, 4));
   if (kv->dtype == KVP_BF16) {
     if (kv->head_dim == 64) hipLaunchKernelGGL((step_delayed_kernel<uint16_t, 64>), grid, dim3(256), 0, stream, a);

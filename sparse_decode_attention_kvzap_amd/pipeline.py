@@ -60,7 +60,8 @@ class PrunedKVCache:
         self.ws_attn = L.decode_attn_workspace(B, Hq, self.kv, dev)
         self.out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
         self.scale = L.sm_scale(d)
-        self.tau_dev = torch.zeros(1, dtype=torch.float32, device=dev)
+        self.tau_dev = torch.full((1,), float(tau), dtype=torch.float32, device=dev)
+        self.pos_dev = torch.zeros(2, dtype=torch.int32, device=dev)  # [next position, 0]
         self.ws_threshold = torch.empty(L.kvp_threshold_workspace_size() // 4 + 1,
                                         dtype=torch.int32, device=dev)
         self.T0 = 0
@@ -95,11 +96,28 @@ class PrunedKVCache:
         self.T0 = T
 
     # -- decode ------------------------------------------------------------------
+    def set_tau(self, tau: float):
+        """A fixed threshold (also mirrored to the device copy the decode step reads)."""
+        self.tau = float(tau)
+        self.tau_dev.fill_(self.tau)
+
+    def set_position(self, p: int):
+        """The absolute position the next decode step appends (kept on the device)."""
+        self.pos_dev[0] = p
+        self.pos_dev[1] = 0
+
     def step(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-             q: torch.Tensor, p: int, stream=None) -> torch.Tensor:
-        """Append position p and attend with q over the cache that now holds it."""
+             q: torch.Tensor, p: Optional[int] = None, stream=None) -> torch.Tensor:
+        """Append a position (p, or the device-held next position when p is None) and
+        attend with q over the cache that now holds it.  Every per-step value lives in
+        device memory, so this sequence can be captured in a HIP graph and replayed."""
+        if p is not None:
+            self.set_position(p)
+        if not isinstance(self.tau, torch.Tensor):
+            self.tau_dev.fill_(self.tau)
         L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
-        L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau, p, 1, stream)
+        L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau_dev, self.pos_dev,
+                           1, stream)
         return self.attend(q, stream)
 
     def attend(self, q: torch.Tensor, stream=None) -> torch.Tensor:

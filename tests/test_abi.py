@@ -177,8 +177,10 @@ def test_host_validation_without_device(L):
     ring = L.KvpRing(64, 0, fake, fake, fake, fake)
     assert lib.kvp_step_delayed(ctypes.byref(kv), ctypes.byref(ring), fake, fake, L.KVP_BF16, fake,
                                 1, 0.0, -1, None) == E_ARG
-    assert lib.kvp_step_delayed_dev_tau(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
-                                        L.KVP_BF16, fake, 1, None, 5, None) == E_ARG
+    assert lib.kvp_step_delayed_dev(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
+                                    L.KVP_BF16, fake, 1, None, fake, None) == E_ARG
+    assert lib.kvp_step_delayed_dev(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
+                                    L.KVP_BF16, fake, 1, fake, None, None) == E_ARG
 
 
 def test_missing_library_fails_loudly(L, tmp_path):

@@ -105,8 +105,8 @@ def test_threshold_repeated_calls_reuse_workspace(K):
 
 
 def test_select_and_step_with_device_tau(K):
-    """kvp_select_dev_tau / kvp_step_delayed_dev_tau give bit-identical results to the
-    host-tau calls with the same value."""
+    """kvp_select_dev_tau / kvp_step_delayed_dev (device tau and position) give
+    bit-identical results to the host-argument calls with the same values."""
     B, Hkv, T, d, w = 2, 4, 3000, 128, 64
     P = B * Hkv
     sc = scores_of("normal", (B, Hkv, T), 11, T)
@@ -131,16 +131,24 @@ def test_select_and_step_with_device_tau(K):
     ks = torch.randn((B, Hkv, 3 * w, d), generator=g, device=DEV).to(torch.bfloat16)
     vs = torch.randn((B, Hkv, 3 * w, d), generator=g, device=DEV).to(torch.bfloat16)
     ss = torch.randn((B, Hkv, 3 * w), generator=g, device=DEV)
+    # the device variant reads the position from device memory and advances it itself
+    pos_dev = torch.tensor([0, 0], dtype=torch.int32, device=DEV)
     states = []
-    for t in (tau, tau_dev):
+    for dev_side in (False, True):
         maxpp = 3 * w // 16 + 2
         kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, torch.bfloat16, DEV, poison=True)
         ring = K.Ring.allocate(P, w, d, torch.bfloat16, DEV, poison=True)
         K.kvp_reset(kv, ring)
         for p in range(3 * w):
-            K.kvp_step_delayed(kv, ring, ks[:, :, p].contiguous(), vs[:, :, p].contiguous(),
-                               ss[:, :, p].contiguous(), t, p)
+            args = (kv, ring, ks[:, :, p].contiguous(), vs[:, :, p].contiguous(),
+                    ss[:, :, p].contiguous())
+            if dev_side:
+                K.kvp_step_delayed(*args, tau_dev, pos_dev)
+            else:
+                K.kvp_step_delayed(*args, tau, p)
         states.append([np.concatenate([read_pool(kv, pr)[0], read_ring(ring, pr)[0]])
                        for pr in range(P)])
+        if dev_side:
+            assert pos_dev.tolist() == [3 * w, 0]
     for a, b in zip(*states):
         assert np.array_equal(np.sort(a), np.sort(b))
