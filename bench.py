@@ -151,6 +151,7 @@ def main():
     st = cache.check()
     assert st == 0, f"capacity error {st}"
     visible = cache.visible_token_heads()
+    kept_prefill = int(cache.kept_count.sum())  # before the keep sweep below re-selects
     total_th = B * Hkv * T
     log(f"[bench] warmup done; visible token-heads {visible} of {total_th} "
         f"({visible / total_th:.3f})")
@@ -269,7 +270,6 @@ def main():
     else:
         score_flops = 2.0 * ntok * H * Hkv
     score_bytes = ntok * H * elt + ntok * Hkv * 4
-    kept_prefill = int(cache.kept_count.sum())
     select_bytes = ntok * Hkv * 4 + B * Hkv * T0 * 4 + B * Hkv * ((T0 + 31) // 32) * 4 * 2
     compact_bytes = kept_prefill * 2 * d * elt * 2 + kept_prefill * 4
     step_bytes = B * Hkv * d * elt * 2 * 3
