@@ -31,6 +31,7 @@ namespace kvp {
 constexpr int ATTN_WG_WAVES = 4;
 constexpr int ATTN_GRID = 256;  // one work-group (4 waves) per CU on a 256-CU part
 constexpr int ATTN_NWAVES = ATTN_GRID * ATTN_WG_WAVES;
+static_assert(ATTN_GRID % 8 == 0, "ranges are numbered per XCD (8 XCDs)");
 
 struct AttnArgs {
   const void* q;
@@ -67,8 +68,13 @@ struct Plan {
   int per;
 };
 
+// Regions in the plan: the int8 regions only exist with an int8 pool.
+__device__ __forceinline__ int plan_regions(const AttnArgs& a) {
+  return (a.kv.num_pages8 > 0 ? 2 : 1) * a.kv.num_pairs;
+}
+
 __device__ Plan build_plan(const AttnArgs& a, int* lds) {
-  const int nseg = 2 * a.kv.num_pairs;
+  const int nseg = plan_regions(a);
   Plan pl;
   pl.P = lds;
   pl.C = lds + nseg + 1;
@@ -692,12 +698,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   extern __shared__ int lds[];
   Plan pl = build_plan(a, lds);
   const int np = a.kv.num_pairs;
-  const int nseg = 2 * np;
+  const int nseg = plan_regions(a);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int gw = blockIdx.x * ATTN_WG_WAVES + wid;
+  // Work-groups are dispatched round-robin over the 8 XCDs; numbering the ranges so that
+  // each XCD takes one contiguous eighth of the sequence evens out the XCDs' finish times
+  // (measured: 1-3 us off the call at the 361 MB and 543 MB shapes).
+  const int gw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * ATTN_WG_WAVES + wid;
 
+  // the merge reads 2 * num_pairs + 1 entries; absent int8 regions hold no records
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= nseg; i += blockDim.x) a.plan_c[i] = pl.C[i];
+    for (int i = threadIdx.x; i <= 2 * np; i += blockDim.x) a.plan_c[i] = pl.C[min(i, nseg)];
 
   pl.total = __builtin_amdgcn_readfirstlane(pl.total);
   pl.per = __builtin_amdgcn_readfirstlane(pl.per);
@@ -730,10 +740,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 }
 
 // -------------------------------------------------------------------------------
-// Merge: one wave per (pair, query head).  Lanes first cover the records to find the
-// running-max reference M and the normaliser sum_k 2^(m_k - M) l_k, then walk the
-// records in order accumulating 2^(m_k - M) o_k for their D/64 output elements.
-// A pair with no visible token (no records) gets zeros.
+// Merge: one wave per (pair, query head).  Right after the plan entries arrive, the wave
+// requests the (m, l) of the pair's first 64 records (one per lane) and the outputs of the
+// first 16 in one batch, so a pair with up to 16 records costs two memory round trips.
+// The reference max M covers every record; the normaliser is sum_k 2^(m_k - M) l_k and
+// the output sum_k 2^(m_k - M) o_k / normaliser, accumulated in record order, so the
+// result is deterministic.  A pair with no visible token (no records) gets zeros.
 // -------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
@@ -746,13 +758,32 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
   const int r0 = a.plan_c[pair], na = a.plan_c[pair + 1] - r0;
   const int s0 = a.plan_c[np + pair];
   const int nrec = na + (a.plan_c[np + pair + 1] - s0);
+  float* out = a.out + ((int64_t)b * a.Hq + h * g + n) * D;
+  if (nrec == 0) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = 0.f;
+    return;
+  }
   auto rec = [&](int k) {
     const int slot = (k < na) ? r0 + k : s0 + (k - na);
     return a.part + (int64_t)slot * a.rec_floats;
   };
-  // lane k < 64 holds record k's (m, l); records beyond 64 are folded in serially
-  float M = neg_inf();
-  for (int k = lane; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
+  // first batch: lane k < 64 holds record k's (m, l); outputs of records 0..15
+  const float* rl = rec(min(lane, nrec - 1));
+  float m0 = rl[g * D + n], l0 = rl[g * D + g + n];
+  float ov0[16][D / 64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float* o = rec(min(i, nrec - 1)) + n * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) ov0[i][e] = o[lane + 64 * e];
+  }
+  if (lane >= nrec) {
+    m0 = neg_inf();
+    l0 = 0.f;
+  }
+  float M = m0;
+  for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
   M = wave_max(M);
   float acc[D / 64];
 #pragma unroll
@@ -762,7 +793,10 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
     for (int k0 = 0; k0 < nrec; k0 += 64) {
       const int k = k0 + lane;
       float wk = 0.f, lk = 0.f;
-      if (k < nrec) {
+      if (k0 == 0) {
+        wk = (m0 == neg_inf()) ? 0.f : exp2f(m0 - M);
+        lk = l0;
+      } else if (k < nrec) {
         const float m = rec(k)[g * D + n];
         wk = (m == neg_inf()) ? 0.f : exp2f(m - M);
         lk = rec(k)[g * D + g + n];
@@ -772,12 +806,19 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
       // batches of 16 records: all loads issued before the accumulation
       for (int kb = 0; kb < kn; kb += 16) {
         float ov[16][D / 64];
+        if (k0 == 0 && kb == 0) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = min(kb + i, kn - 1);
-          const float* o = rec(k0 + kk) + n * D;
+          for (int i = 0; i < 16; ++i)
 #pragma unroll
-          for (int e = 0; e < D / 64; ++e) ov[i][e] = o[lane + 64 * e];
+            for (int e = 0; e < D / 64; ++e) ov[i][e] = ov0[i][e];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = min(kb + i, kn - 1);
+            const float* o = rec(k0 + kk) + n * D;
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) ov[i][e] = o[lane + 64 * e];
+          }
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -789,7 +830,6 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
     }
     den = wave_sum(den);
   }
-  float* out = a.out + ((int64_t)b * a.Hq + h * g + n) * D;
   const float inv = (den > 0.f) ? 1.0f / den : 0.f;
 #pragma unroll
   for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] * inv;
