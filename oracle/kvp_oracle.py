@@ -234,10 +234,17 @@ def dms_visible(flags: np.ndarray, p: int, w: int) -> np.ndarray:
 # ----------------------------------------------------------------------------------
 
 
-def quantize_absmax_int8(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
-    """Symmetric int8 with one fp32 absmax scale per row (token, head), computed from
-    the stored values.  scale = fp32(a / 127) with a = max |x|; code = clamp(round-
-    half-even(x / scale), -127, 127).  A zero row has scale 0 and zero codes.
+# The page names low-precision quantization of the non-beacon entries without fixing a
+# format.  Reading: symmetric integer codes with one fp32 absmax scale per (token, head)
+# row, in two widths: int8 (codes -127..127) and int4 (codes -7..7, the same rule with
+# 7 levels a side; -8 is not used, so the grid stays symmetric).
+LP_QMAX = {8: 127, 4: 7}
+
+
+def quantize_absmax(x: np.ndarray, qmax: int) -> Tuple[np.ndarray, np.float32]:
+    """Symmetric codes with one fp32 absmax scale per row (token, head), computed from
+    the stored values.  scale = fp32(a / qmax) with a = max |x|; code = clamp(round-
+    half-even(x / scale), -qmax, qmax).  A zero row has scale 0 and zero codes.
 
     Precision: the code is an integer decided by floating point, so it is decided in
     IEEE fp32 (the division of two fp32 values, correctly rounded), which is the
@@ -245,26 +252,37 @@ def quantize_absmax_int8(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
     """
     xf = np.asarray(x, dtype=np.float32)
     a = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0)
-    scale = np.float32(a / np.float32(127.0))
+    scale = np.float32(a / np.float32(qmax))
     if scale == 0:
         return np.zeros(xf.shape, dtype=np.int8), np.float32(0.0)
     y = xf / scale  # float32 / float32 -> float32, correctly rounded
-    codes = np.clip(np.rint(y), -127, 127).astype(np.int8)
+    codes = np.clip(np.rint(y), -qmax, qmax).astype(np.int8)
     return codes, scale
 
 
+def quantize_absmax_int8(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """int8 codes -127..127, scale fp32(a / 127) (see quantize_absmax)."""
+    return quantize_absmax(x, 127)
+
+
+def quantize_absmax_int4(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """int4 codes -7..7 (held in int8 here), scale fp32(a / 7) (see quantize_absmax)."""
+    return quantize_absmax(x, 7)
+
+
 def dequantize_int8(codes: np.ndarray, scale: np.float32) -> np.ndarray:
-    """x_hat = code * scale (exact in float64)."""
+    """x_hat = code * scale (exact in float64); any code width."""
     return codes.astype(np.float64) * np.float64(scale)
 
 
-def beacon_kv(K: np.ndarray, V: np.ndarray, beacon: np.ndarray):
+def beacon_kv(K: np.ndarray, V: np.ndarray, beacon: np.ndarray, bits: int = 8):
     """Beacon entries keep their exact values; every other (token, head) row of K and
-    of V (separately) is replaced by its int8 round trip.
+    of V (separately) is replaced by its round trip through `bits`-bit codes (8 or 4).
 
     K, V: [B,Hkv,T,d] float64 holding bf16 values; beacon: [B,Hkv,T] bool.
     Returns K_hat, V_hat float64, plus the codes and scales of the demoted rows.
     """
+    qmax = LP_QMAX[bits]
     Kh = np.array(K, dtype=np.float64, copy=True)
     Vh = np.array(V, dtype=np.float64, copy=True)
     B, Hkv, T, d = K.shape
@@ -275,10 +293,10 @@ def beacon_kv(K: np.ndarray, V: np.ndarray, beacon: np.ndarray):
     for b in range(B):
         for h in range(Hkv):
             for t in np.flatnonzero(~beacon[b, h]):
-                c, s = quantize_absmax_int8(K[b, h, t])
+                c, s = quantize_absmax(K[b, h, t], qmax)
                 kc[b, h, t], ks[b, h, t] = c, s
                 Kh[b, h, t] = dequantize_int8(c, s)
-                c, s = quantize_absmax_int8(V[b, h, t])
+                c, s = quantize_absmax(V[b, h, t], qmax)
                 vc[b, h, t], vs[b, h, t] = c, s
                 Vh[b, h, t] = dequantize_int8(c, s)
     return Kh, Vh, (kc, ks, vc, vs)
@@ -313,9 +331,9 @@ def kvzap_visible_at_decode(s: np.ndarray, tau: float, R: int, p: int) -> np.nda
     return keep_mask(s[..., :p + 1], tau, R)
 
 
-def beacon_decode_attention(q, K, V, beacon, scale):
-    """One softmax over all T tokens: exact values for beacon rows, int8 round trips
-    for the others."""
-    Kh, Vh, _ = beacon_kv(K, V, beacon)
+def beacon_decode_attention(q, K, V, beacon, scale, bits: int = 8):
+    """One softmax over all T tokens: exact values for beacon rows, round trips through
+    `bits`-bit codes for the others."""
+    Kh, Vh, _ = beacon_kv(K, V, beacon, bits)
     allvis = np.ones(beacon.shape, dtype=bool)
     return decode_attention(q, Kh, Vh, allvis, scale)

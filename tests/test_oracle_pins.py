@@ -399,6 +399,74 @@ def test_int8_on_grid_inputs_are_exact_and_round_half_even():
     assert s == 1.0 and c.tolist() == [127, 2, 4, 0, -2]
 
 
+def _nearest_code_brute(y: float, qmax: int) -> int:
+    """The code nearest to y among -qmax..qmax, ties to the even code (brute force)."""
+    best = None
+    for c in range(-qmax, qmax + 1):
+        key = (abs(y - c), c % 2)  # distance first, then prefer even
+        if best is None or key < best[0]:
+            best = (key, c)
+    return best[1]
+
+
+def test_int4_roundtrip_bound_extremes_and_brute_force():
+    rng = np.random.default_rng(15)
+    for trial in range(20):
+        x = (rng.standard_normal(64) * rng.uniform(0.01, 10)).astype(np.float32)
+        codes, scale = oracle.quantize_absmax_int4(x)
+        assert scale.dtype == np.float32 and scale == np.float32(np.abs(x).max() / np.float32(7))
+        assert np.abs(codes).max() == 7 and codes.min() >= -7
+        i = np.argmax(np.abs(x))
+        assert abs(int(codes[i])) == 7 and np.sign(codes[i]) == np.sign(x[i])
+        xh = oracle.dequantize_int8(codes, scale)
+        assert np.all(np.abs(x - xh) <= scale / 2 * (1 + 1e-6))
+        # every code is the nearest grid point of the fp32 quotient (brute force)
+        y = x / scale
+        assert [int(c) for c in codes] == [_nearest_code_brute(float(v), 7) for v in y]
+    zc, zs = oracle.quantize_absmax_int4(np.zeros(8, np.float32))
+    assert zs == 0 and not zc.any()
+
+
+def test_int4_on_grid_inputs_are_exact_and_round_half_even():
+    scale = np.float32(0.25)
+    codes = np.array([7, -3, 0, 1, -7, 5, -6], dtype=np.int8)
+    x = codes.astype(np.float32) * scale
+    c2, s2 = oracle.quantize_absmax_int4(x)
+    assert s2 == scale and np.array_equal(c2, codes)
+    # a = 7 -> scale 1; ties go to even: 2.5 -> 2, 3.5 -> 4, -0.5 -> 0, 6.5 -> 6
+    x = np.array([7.0, 2.5, 3.5, -0.5, 6.5, -4.5], dtype=np.float32)
+    c, s = oracle.quantize_absmax_int4(x)
+    assert s == 1.0 and c.tolist() == [7, 2, 4, 0, 6, -4]
+
+
+def test_int8_codes_match_brute_force():
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal(128) * 2).astype(np.float32)
+    codes, scale = oracle.quantize_absmax_int8(x)
+    y = x / scale
+    assert [int(c) for c in codes] == [_nearest_code_brute(float(v), 127) for v in y]
+
+
+def test_beacon_int4_is_coarser_than_int8_and_all_beacons_is_dense():
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, T, d = 1, 4, 2, 64, 16
+    q = rng.standard_normal((B, Hq, d))
+    K = rng.standard_normal((B, Hkv, T, d)).astype(np.float32).astype(np.float64)
+    V = rng.standard_normal((B, Hkv, T, d)).astype(np.float32).astype(np.float64)
+    scale = oracle.sm_scale(d)
+    allb = np.ones((B, Hkv, T), bool)
+    dense = oracle.decode_attention(q, K, V, allb, scale)
+    assert np.allclose(oracle.beacon_decode_attention(q, K, V, allb, scale, bits=4), dense, atol=1e-14)
+    none = np.zeros((B, Hkv, T), bool)
+    e8 = np.abs(oracle.beacon_decode_attention(q, K, V, none, scale, bits=8) - dense).max()
+    e4 = np.abs(oracle.beacon_decode_attention(q, K, V, none, scale, bits=4) - dense).max()
+    assert 1e-5 < e8 < e4 < 0.5
+    # the demoted rows of an int4 round trip are on the row's 15-level grid
+    Kh, Vh, (kc, ks, vc, vs) = oracle.beacon_kv(K, V, none, bits=4)
+    assert np.abs(kc).max() == 7 and np.abs(vc).max() == 7
+    assert np.array_equal(Kh, kc.astype(np.float64) * ks[..., None].astype(np.float64))
+
+
 def test_beacon_all_beacons_is_dense_and_demotion_changes_output():
     rng = np.random.default_rng(14)
     B, Hq, Hkv, T, d = 1, 4, 2, 64, 16
