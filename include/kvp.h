@@ -98,9 +98,14 @@ typedef struct kvp_scorer {
  *   page_pos [num_pages][16]     absolute position of each slot
  * block_table[pair][j] is the physical page of the pair's j-th page; the pair holds
  * length[pair] tokens in its pages, in ascending position order.  page_top[0] is a
- * bump allocator over the pool.  The optional int8 pool (BeaconKV demotion; all
- * fields NULL/0 when absent) has the same layout with int8 codes plus one fp32
- * absmax scale per slot for K and for V.
+ * bump allocator over the pool.  The optional low-precision pool (BeaconKV
+ * demotion; all fields NULL/0 when absent) has the same layout with symmetric
+ * integer codes plus one fp32 absmax scale per slot for K and for V: lp_bits = 8
+ * holds int8 codes (-127..127, scale = absmax/127), lp_bits = 4 int4 codes (-7..7,
+ * scale = absmax/7) two per byte, the even element in the low nibble (K rows: dims
+ * 2i, 2i+1; V^T rows: tokens 2i, 2i+1), so its pages are half the size.  Source:
+ * BeaconKV briefing (jiinsi.com), body and FAQ: non-beacon entries are kept at low
+ * precision; the format is not given there.
  * Physical page ids and the unused slots of partly filled pages are unspecified.
  * -------------------------------------------------------------------------- */
 typedef struct kvp_paged_kv {
@@ -109,9 +114,9 @@ typedef struct kvp_paged_kv {
   int32_t head_dim;           /* d: 64 or 128 */
   int32_t num_pages;          /* main pool capacity in pages */
   int32_t max_pages_per_pair; /* row stride of block_table */
-  int32_t num_pages8;         /* int8 pool capacity (0 = no int8 pool) */
+  int32_t num_pages8;         /* low-precision pool capacity (0 = no such pool) */
   int32_t max_pages8_per_pair;
-  int32_t _pad;
+  int32_t lp_bits;            /* code width of that pool: 8 (0 also means 8) or 4 */
   void* k_pages;
   void* v_pages;
   int32_t* page_pos;
@@ -119,8 +124,8 @@ typedef struct kvp_paged_kv {
   int32_t* length;      /* [num_pairs] */
   int32_t* page_top;    /* [1] */
   int32_t* err;         /* [1] KVP_ERR_* bits */
-  int8_t* k8_pages;     /* [num_pages8][16][d] */
-  int8_t* v8_pages;     /* [num_pages8][d][16] */
+  int8_t* k8_pages;     /* [num_pages8][16][d * lp_bits / 8] */
+  int8_t* v8_pages;     /* [num_pages8][d][16 * lp_bits / 8] */
   float* k8_scale;      /* [num_pages8][16] */
   float* v8_scale;      /* [num_pages8][16] */
   int32_t* page8_pos;   /* [num_pages8][16] */
@@ -149,7 +154,8 @@ typedef struct kvp_ring {
 
 typedef enum kvp_compact_mode {
   KVP_COMPACT_EVICT = 0,      /* evicted tokens are dropped */
-  KVP_COMPACT_DEMOTE_INT8 = 1 /* evicted tokens go to the int8 pool (BeaconKV) */
+  KVP_COMPACT_DEMOTE_INT8 = 1 /* evicted tokens go to the low-precision pool (BeaconKV;
+                                 int8 or int4 codes per kv->lp_bits) */
 } kvp_compact_mode;
 
 /* Human-readable name of a status code (static string, never NULL). */

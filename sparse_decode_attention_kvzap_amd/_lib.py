@@ -43,7 +43,7 @@ class KvpScorer(ctypes.Structure):
 class KvpPagedKV(ctypes.Structure):
     _fields_ = [("dtype", c_int32), ("num_pairs", c_int32), ("head_dim", c_int32),
                 ("num_pages", c_int32), ("max_pages_per_pair", c_int32),
-                ("num_pages8", c_int32), ("max_pages8_per_pair", c_int32), ("_pad", c_int32),
+                ("num_pages8", c_int32), ("max_pages8_per_pair", c_int32), ("lp_bits", c_int32),
                 ("k_pages", c_void_p), ("v_pages", c_void_p), ("page_pos", c_void_p),
                 ("block_table", c_void_p), ("length", c_void_p), ("page_top", c_void_p),
                 ("err", c_void_p), ("k8_pages", c_void_p), ("v8_pages", c_void_p),
@@ -173,7 +173,12 @@ class PagedKV:
     @staticmethod
     def allocate(num_pairs: int, head_dim: int, num_pages: int, max_pages_per_pair: int,
                  dtype=torch.bfloat16, device="cuda", num_pages8: int = 0,
-                 max_pages8_per_pair: int = 0, poison: bool = False) -> "PagedKV":
+                 max_pages8_per_pair: int = 0, poison: bool = False,
+                 lp_bits: int = 8) -> "PagedKV":
+        """lp_bits: code width of the low-precision pool (8: int8 codes; 4: int4 codes,
+        two per byte, so its K pages are [16][d/2] bytes and its V^T pages [d][8])."""
+        if lp_bits not in (4, 8):
+            raise ValueError("lp_bits must be 8 or 4")
         dev = torch.device(device)
         t = {}
         fill = float("nan") if poison else 0.0
@@ -185,8 +190,9 @@ class PagedKV:
         t["page_top"] = torch.zeros(1, dtype=torch.int32, device=dev)
         t["err"] = torch.zeros(1, dtype=torch.int32, device=dev)
         if num_pages8 > 0:
-            t["k8_pages"] = torch.full((num_pages8, KVP_PAGE, head_dim), 0x55, dtype=torch.int8, device=dev)
-            t["v8_pages"] = torch.full((num_pages8, head_dim, KVP_PAGE), 0x55, dtype=torch.int8, device=dev)
+            per = 8 // lp_bits  # codes per byte
+            t["k8_pages"] = torch.full((num_pages8, KVP_PAGE, head_dim // per), 0x55, dtype=torch.int8, device=dev)
+            t["v8_pages"] = torch.full((num_pages8, head_dim, KVP_PAGE // per), 0x55, dtype=torch.int8, device=dev)
             t["k8_scale"] = torch.full((num_pages8, KVP_PAGE), fill, dtype=torch.float32, device=dev)
             t["v8_scale"] = torch.full((num_pages8, KVP_PAGE), fill, dtype=torch.float32, device=dev)
             t["page8_pos"] = torch.full((num_pages8, KVP_PAGE), -7, dtype=torch.int32, device=dev)
@@ -198,6 +204,7 @@ class PagedKV:
         c.num_pairs, c.head_dim, c.num_pages = num_pairs, head_dim, num_pages
         c.max_pages_per_pair = max_pages_per_pair
         c.num_pages8, c.max_pages8_per_pair = num_pages8, max_pages8_per_pair
+        c.lp_bits = lp_bits
         for name, ten in t.items():
             setattr(c, name, ten.data_ptr())
         return PagedKV(c, t)

@@ -68,7 +68,7 @@ struct Plan {
   int per;
 };
 
-// Regions in the plan: the int8 regions only exist with an int8 pool.
+// Regions in the plan: the low-precision regions only exist with a low-precision pool.
 __device__ __forceinline__ int plan_regions(const AttnArgs& a) {
   return (a.kv.num_pages8 > 0 ? 2 : 1) * a.kv.num_pairs;
 }
@@ -412,7 +412,8 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
 }
 
 // -------------------------------------------------------------------------------
-// int8 region (BeaconKV demoted tokens): codes -> bf16 exactly, per-token scales.
+// Low-precision region (BeaconKV demoted tokens, int8 or int4 codes): codes -> bf16
+// exactly, per-token scales.
 // -------------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t word, int byte0) {
   float f0 = (float)(int)(int8_t)((word >> (8 * byte0)) & 0xffu);
@@ -430,27 +431,49 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-template <int D>
-struct I8Frags {
-  u32x2 kA[D / 32];  // 8 int8 K codes per MFMA K-step, score tile A row
-  u32x2 kB[D / 32];
-  u32x2 v[D / 16];   // 8 int8 V^T codes per output tile
-  f32x4 ks[2];       // K scales of this lane's 8 tokens
-  f32x4 vs[2];       // V scales of this lane's 8 tokens
+// 8 int4 codes (one dword, element e in nibble e) -> 8 bf16 (exact: |code| <= 8).
+__device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
+  u32x4 r;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float f0 = (float)(static_cast<int>(w << (28 - 8 * q)) >> 28);
+    const float f1 = (float)(static_cast<int>(w << (24 - 8 * q)) >> 28);
+    r[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  }
+  return r;
+}
+
+// 8 codes of a fragment: two dwords of int8 codes or one dword of int4 codes.
+template <int BITS> struct LpWord { typedef u32x2 T; };
+template <> struct LpWord<4> { typedef uint32_t T; };
+__device__ __forceinline__ u32x4 lp_to_bf16x8(u32x2 w) { return i8x8_to_bf16x8(w[0], w[1]); }
+__device__ __forceinline__ u32x4 lp_to_bf16x8(uint32_t w) { return i4x8_to_bf16x8(w); }
+
+template <int D, int BITS>
+struct LpFrags {
+  typedef typename LpWord<BITS>::T W;
+  W kA[D / 32];  // 8 K codes per MFMA K-step, score tile A row
+  W kB[D / 32];
+  W v[D / 16];   // 8 V^T codes per output tile
+  f32x4 ks[2];   // K scales of this lane's 8 tokens
+  f32x4 vs[2];   // V scales of this lane's 8 tokens
 };
 
-template <int D>
-__device__ __forceinline__ void load_i8_k(const AttnArgs& a, I8Frags<D>& f, int pgX, int pgY, int lane) {
+// Byte offsets scale with the code width: a K row is D * BITS / 8 bytes, a V^T row
+// 16 * BITS / 8.
+template <int D, int BITS>
+__device__ __forceinline__ void load_lp_k(const AttnArgs& a, LpFrags<D, BITS>& f, int pgX, int pgY, int lane) {
+  typedef typename LpWord<BITS>::T W;
   const int m = lane & 15, j = lane >> 4;
   const int tA = 8 * (m >> 2) + (m & 3), tB = tA + 4;
   const int pgK = (tA < 16) ? pgX : pgY;
-  const int8_t* kbase = a.kv.k8_pages + (int64_t)pgK * PAGE * D;
-  const int8_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
-  const int8_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
+  const int8_t* kbase = a.kv.k8_pages + (int64_t)pgK * PAGE * D * BITS / 8;
+  const int8_t* rowA = kbase + ((tA & 15) * D + (D / 4) * j) * BITS / 8;
+  const int8_t* rowB = kbase + ((tB & 15) * D + (D / 4) * j) * BITS / 8;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    f.kA[kk] = *reinterpret_cast<const u32x2*>(rowA + 8 * kk);
-    f.kB[kk] = *reinterpret_cast<const u32x2*>(rowB + 8 * kk);
+    f.kA[kk] = *reinterpret_cast<const W*>(rowA + kk * BITS);
+    f.kB[kk] = *reinterpret_cast<const W*>(rowB + kk * BITS);
   }
   const int pgT = (j < 2) ? pgX : pgY;
   const float* ksc = a.kv.k8_scale + (int64_t)pgT * PAGE + 8 * (j & 1);
@@ -458,21 +481,22 @@ __device__ __forceinline__ void load_i8_k(const AttnArgs& a, I8Frags<D>& f, int 
   f.ks[1] = *reinterpret_cast<const f32x4*>(ksc + 4);
 }
 
-template <int D>
-__device__ __forceinline__ void load_i8_v(const AttnArgs& a, I8Frags<D>& f, int pgX, int pgY, int lane) {
+template <int D, int BITS>
+__device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS>& f, int pgX, int pgY, int lane) {
+  typedef typename LpWord<BITS>::T W;
   const int m = lane & 15, j = lane >> 4;
   const int pgT = (j < 2) ? pgX : pgY;
-  const int8_t* vcol = a.kv.v8_pages + (int64_t)pgT * PAGE * D + m * PAGE + 8 * (j & 1);
+  const int8_t* vcol = a.kv.v8_pages + ((int64_t)pgT * PAGE * D + m * PAGE + 8 * (j & 1)) * BITS / 8;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const u32x2*>(vcol + t * 16 * PAGE);
+  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const W*>(vcol + t * 16 * PAGE * BITS / 8);
   const float* vsc = a.kv.v8_scale + (int64_t)pgT * PAGE + 8 * (j & 1);
   f.vs[0] = *reinterpret_cast<const f32x4*>(vsc);
   f.vs[1] = *reinterpret_cast<const f32x4*>(vsc + 4);
 }
 
-template <int D>
-__device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
-                                  int slot) {
+template <int D, int BITS>
+__device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
+                                int slot) {
   const int lane = threadIdx.x & 63, j = lane >> 4;
   bf16x8 qf[D / 32];
   load_q<D>(a, pair, qf);
@@ -495,12 +519,12 @@ __device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, i
       // the pad page of an odd page count re-uses the previous page (all slots masked)
       return __builtin_amdgcn_readlane(bt, min(vp, npm - 1) - c0);
     };
-    I8Frags<D> f;
+    LpFrags<D, BITS> f;
     const int nst = (c1 - c0) / 2;
     auto vat = [&](int i) { return c0 + 2 * (rev ? nst - 1 - i : i); };
     int pgX = page(vat(0)), pgY = page(vat(0) + 1);
-    load_i8_k<D>(a, f, pgX, pgY, lane);
-    load_i8_v<D>(a, f, pgX, pgY, lane);
+    load_lp_k<D, BITS>(a, f, pgX, pgY, lane);
+    load_lp_v<D, BITS>(a, f, pgX, pgY, lane);
     for (int i = 0; i < nst; ++i) {
       const int v = vat(i);
       const int vn = vat(i + 1 < nst ? i + 1 : i);
@@ -512,15 +536,15 @@ __device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, i
       f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
-        sA = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(f.kA[kk][0], f.kA[kk][1])), qf[kk], sA);
-        sB = mfma16x16x32(as_bf16x8(i8x8_to_bf16x8(f.kB[kk][0], f.kB[kk][1])), qf[kk], sB);
+        sA = mfma16x16x32(as_bf16x8(lp_to_bf16x8(f.kA[kk])), qf[kk], sA);
+        sB = mfma16x16x32(as_bf16x8(lp_to_bf16x8(f.kB[kk])), qf[kk], sB);
       }
       // per-token K scale folds into the logits; V scale into the probabilities
       const f32x4 ks0 = f.ks[0], ks1 = f.ks[1];
       const f32x4 vs0 = f.vs[0], vs1 = f.vs[1];
       sA = sA * ks0;
       sB = sB * ks1;
-      load_i8_k<D>(a, f, pgXn, pgYn, lane);
+      load_lp_k<D, BITS>(a, f, pgXn, pgYn, lane);
       float s[8], vsc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -569,13 +593,13 @@ __device__ void run_region_b_int8(const AttnArgs& a, const Plan& pl, int pair, i
         const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
 #pragma unroll
         for (int t = 0; t < D / 16; ++t) {
-          u32x4 vt = i8x8_to_bf16x8(f.v[t][0], f.v[t][1]);
+          u32x4 vt = lp_to_bf16x8(f.v[t]);
           if (!allv) vt = mask_tokens(vt, vb);
           st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
           st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
         }
       }
-      load_i8_v<D>(a, f, pgXn, pgYn, lane);
+      load_lp_v<D, BITS>(a, f, pgXn, pgYn, lane);
     }
   }
   emit_partial<D>(a, pl, pair, slot, st);
@@ -705,7 +729,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   // (measured: 1-3 us off the call at the 361 MB and 543 MB shapes).
   const int gw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * ATTN_WG_WAVES + wid;
 
-  // the merge reads 2 * num_pairs + 1 entries; absent int8 regions hold no records
+  // the merge reads 2 * num_pairs + 1 entries; absent low-precision regions hold no records
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= 2 * np; i += blockDim.x) a.plan_c[i] = pl.C[min(i, nseg)];
 
@@ -733,7 +757,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         run_region_a_bf16<D>(a, pl, s, v0, v1, slot, wmask);
       }
     } else {
-      if constexpr (!F32) run_region_b_int8<D>(a, pl, s - np, v0, v1, slot);
+      if constexpr (!F32) {
+        if (a.kv.lp_bits == 4) run_region_b_lp<D, 4>(a, pl, s - np, v0, v1, slot);
+        else run_region_b_lp<D, 8>(a, pl, s - np, v0, v1, slot);
+      }
     }
     start = stop;
   }

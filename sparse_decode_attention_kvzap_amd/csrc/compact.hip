@@ -133,11 +133,15 @@ __device__ __forceinline__ float elem_to_f32<uint16_t>(uint16_t x) { return bf16
 template <>
 __device__ __forceinline__ float elem_to_f32<float>(float x) { return x; }
 
-// Quantize 16 source rows into an int8 K page [16][d] and an int8 V^T page [d][16]
-// with one fp32 absmax scale per slot for K and for V.
-template <typename E>
+// Quantize 16 source rows into a K page [16][d] and a V^T page [d][16] of BITS-bit
+// codes with one fp32 absmax scale per slot for K and for V.  int8: one code per
+// byte.  int4: two codes per byte, the even element in the low nibble (K: dims 2i and
+// 2i+1 of a token; V^T: tokens 2i and 2i+1 of a dim), so a K row takes d/2 bytes and
+// a V^T row 8.
+template <typename E, int BITS>
 __device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, int8_t* kdst,
                            int8_t* vdst, float* ksc, float* vsc, int8_t* cbuf) {
+  constexpr float QMAX = BITS == 4 ? 7.0f : 127.0f;
   const int tid = threadIdx.x;
   constexpr int EPC = 16 / sizeof(E);
   const int cpr = d / EPC;  // threads per row (power of two, <= 16)
@@ -169,12 +173,19 @@ __device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, 
       ka = fmaxf(ka, __shfl_xor(ka, o));
       va = fmaxf(va, __shfl_xor(va, o));
     }
-    const float kscale = ka / 127.0f, vscale = va / 127.0f;
+    const float kscale = ka / QMAX, vscale = va / QMAX;
+    if constexpr (BITS == 4) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      kdst[row * d + col + e] = static_cast<int8_t>(quant_code(kf[e], kscale));
-      cbuf[row * d + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale));
+      for (int e = 0; e < EPC; e += 2) {
+        const int c0 = quant_code(kf[e], kscale, QMAX), c1 = quant_code(kf[e + 1], kscale, QMAX);
+        kdst[(row * d + col + e) / 2] = static_cast<int8_t>((c0 & 0xf) | (c1 << 4));
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) kdst[row * d + col + e] = static_cast<int8_t>(quant_code(kf[e], kscale, QMAX));
     }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) cbuf[row * d + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale, QMAX));
     if ((c % cpr) == 0) {
       ksc[row] = kscale;
       vsc[row] = vscale;
@@ -182,16 +193,29 @@ __device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, 
   }
   __syncthreads();
   for (int dd = tid; dd < d; dd += blockDim.x) {
-    uint32_t w[4];
+    if constexpr (BITS == 4) {
+      uint32_t w[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t x = 0;
+      for (int q = 0; q < 2; ++q) {
+        uint32_t x = 0;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        x |= (static_cast<uint32_t>(static_cast<uint8_t>(cbuf[(4 * q + e) * d + dd]))) << (8 * e);
-      w[q] = x;
+        for (int e = 0; e < 8; ++e)
+          x |= (static_cast<uint32_t>(cbuf[(8 * q + e) * d + dd]) & 0xfu) << (4 * e);
+        w[q] = x;
+      }
+      *reinterpret_cast<u32x2*>(vdst + dd * (PAGE / 2)) = u32x2{w[0], w[1]};
+    } else {
+      uint32_t w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint32_t x = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x |= (static_cast<uint32_t>(static_cast<uint8_t>(cbuf[(4 * q + e) * d + dd]))) << (8 * e);
+        w[q] = x;
+      }
+      *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
     }
-    *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
   }
   __syncthreads();
 }
@@ -311,7 +335,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a
 
 // int8 pages: unit u is int8 page u of the pool; its pair is the last one whose page
 // base is <= u (pairs without int8 pages share the next pair's base).
-template <typename E>
+template <typename E, int BITS>
 __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs a) {
   __shared__ int src[PAGE];
   __shared__ __attribute__((aligned(16))) int8_t cbuf[PAGE * 128];
@@ -335,9 +359,9 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs 
     }
     if (threadIdx.x == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = u;
     __syncthreads();
-    quant_page<E>(ksrc, vsrc, d, src, a.kv.k8_pages + (int64_t)u * PAGE * d,
-                  a.kv.v8_pages + (int64_t)u * PAGE * d, a.kv.k8_scale + (int64_t)u * PAGE,
-                  a.kv.v8_scale + (int64_t)u * PAGE, cbuf);
+    const int64_t page_bytes = (int64_t)PAGE * d * BITS / 8;
+    quant_page<E, BITS>(ksrc, vsrc, d, src, a.kv.k8_pages + u * page_bytes, a.kv.v8_pages + u * page_bytes,
+                        a.kv.k8_scale + (int64_t)u * PAGE, a.kv.v8_scale + (int64_t)u * PAGE, cbuf);
   }
 }
 
@@ -384,10 +408,15 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
     hipLaunchKernelGGL((compact_copy_kernel<float, 64>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
   KVP_LAUNCH_CHECK();
   if (demote) {
-    if (bf)
-      hipLaunchKernelGGL(compact_quant_kernel<uint16_t>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    const bool i4 = lp_bits_of(*kv) == 4;
+    if (bf && i4)
+      hipLaunchKernelGGL((compact_quant_kernel<uint16_t, 4>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    else if (bf)
+      hipLaunchKernelGGL((compact_quant_kernel<uint16_t, 8>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    else if (i4)
+      hipLaunchKernelGGL((compact_quant_kernel<float, 4>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
     else
-      hipLaunchKernelGGL(compact_quant_kernel<float>, dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+      hipLaunchKernelGGL((compact_quant_kernel<float, 8>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
     KVP_LAUNCH_CHECK();
   }
   return KVP_OK;

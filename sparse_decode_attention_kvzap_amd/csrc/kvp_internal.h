@@ -141,14 +141,17 @@ __device__ __forceinline__ int upper_segment(const int* a, int n, int x) {
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Symmetric int8 code of x with the given fp32 scale: round half to even, clamp
-// to +-127; a zero scale gives code 0.
-__device__ __forceinline__ int quant_code(float x, float scale) {
+// Symmetric code of x with the given fp32 scale: round half to even, clamp to
+// +-qmax (127 for int8 codes, 7 for int4); a zero scale gives code 0.
+__device__ __forceinline__ int quant_code(float x, float scale, float qmax = 127.0f) {
   if (scale == 0.0f) return 0;
   float y = rintf(x / scale);
-  y = fminf(fmaxf(y, -127.0f), 127.0f);
+  y = fminf(fmaxf(y, -qmax), qmax);
   return static_cast<int>(y);
 }
+
+// Low-precision pool code width (kvp_paged_kv::lp_bits; 0 means 8).
+__host__ __device__ inline int lp_bits_of(const kvp_paged_kv& kv) { return kv.lp_bits == 4 ? 4 : 8; }
 
 }  // namespace kvp
 

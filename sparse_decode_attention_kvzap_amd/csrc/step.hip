@@ -112,7 +112,9 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
       }
       ka = wave_max(ka);
       va = wave_max(va);
-      const float ks = ka / 127.0f, vs = va / 127.0f;
+      const bool i4 = lp_bits_of(a.kv) == 4;
+      const float qmax = i4 ? 7.0f : 127.0f;
+      const float ks = ka / qmax, vs = va / qmax;
       const int len = a.kv.length8[pair];
       const int j = len / PAGE, sl = len % PAGE;
       int pg = -1;
@@ -133,7 +135,26 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
       } else {
         pg = a.kv.block_table8[(int64_t)pair * a.kv.max_pages8_per_pair + j];
       }
-      if (pg >= 0) {
+      if (pg >= 0 && i4) {
+        // int4: K row of d/2 bytes (dims 2i, 2i+1 share byte i: even lanes write, the odd
+        // neighbour's code comes by shuffle); V^T rows of 8 bytes, this slot's nibble
+        // merged into the byte it shares with slot sl ^ 1 (written at another step)
+        int8_t* kp = a.kv.k8_pages + (int64_t)pg * PAGE * D / 2 + sl * (D / 2);
+        uint8_t* vp = reinterpret_cast<uint8_t*>(a.kv.v8_pages) + (int64_t)pg * PAGE * D / 2 + sl / 2;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+          const int dd = lane + 64 * e;
+          const int kc = quant_code(kf[e], ks, qmax);
+          const int kc1 = __shfl_down(kc, 1);
+          if (dd < D) {
+            if ((dd & 1) == 0) kp[dd / 2] = static_cast<int8_t>((kc & 0xf) | (kc1 << 4));
+            const uint32_t vc = static_cast<uint32_t>(quant_code(vf[e], vs, qmax)) & 0xfu;
+            uint8_t* vb = vp + dd * (PAGE / 2);
+            const uint32_t old_b = *vb;
+            *vb = static_cast<uint8_t>((sl & 1) ? ((old_b & 0x0fu) | (vc << 4)) : ((old_b & 0xf0u) | vc));
+          }
+        }
+      } else if (pg >= 0) {
         int8_t* kp = a.kv.k8_pages + (int64_t)pg * PAGE * D + sl * D;
         int8_t* vp = a.kv.v8_pages + (int64_t)pg * PAGE * D + sl;
 #pragma unroll
@@ -144,6 +165,8 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
             vp[dd * PAGE] = static_cast<int8_t>(quant_code(vf[e], vs));
           }
         }
+      }
+      if (pg >= 0) {
         if (lane == 0) {
           a.kv.k8_scale[(int64_t)pg * PAGE + sl] = ks;
           a.kv.v8_scale[(int64_t)pg * PAGE + sl] = vs;

@@ -10,7 +10,8 @@ delayed step then read without a host round trip.
 KVzap (max5.ai digest, practical application): score every entry, drop low scores,
 always keep the most recent tokens.  DMS (euno.news, Delayed Eviction): with tau = 0
 and window w the same machinery keeps a flagged token for w steps.  BeaconKV
-(jiinsi.com, body): with demote=True evicted entries go to an int8 pool instead.
+(jiinsi.com, body): with demote=True evicted entries go to a low-precision pool
+instead (int8 codes, or int4 with lp_bits=4).
 
 This class only allocates device buffers (torch) and calls libkvp in stream order;
 all arithmetic runs in the HIP kernels.
@@ -27,7 +28,7 @@ from . import _lib as L
 class PrunedKVCache:
     def __init__(self, B: int, Hkv: int, Hq: int, d: int, T_max: int, dtype: torch.dtype,
                  scorer: L.Scorer, window: int, tau: float, demote: bool = False,
-                 device="cuda", max_prompt: Optional[int] = None):
+                 device="cuda", max_prompt: Optional[int] = None, lp_bits: int = 8):
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
         self.P = B * Hkv
         self.T_max = T_max
@@ -43,7 +44,7 @@ class PrunedKVCache:
         maxpp = -(-T_max // L.KVP_PAGE) + 1
         kw = {}
         if demote:
-            kw = dict(num_pages8=self.P * maxpp, max_pages8_per_pair=maxpp)
+            kw = dict(num_pages8=self.P * maxpp, max_pages8_per_pair=maxpp, lp_bits=lp_bits)
         self.kv = L.PagedKV.allocate(self.P, d, self.P * maxpp, maxpp, dtype, dev, **kw)
         self.ring = L.Ring.allocate(self.P, window, d, dtype, dev)
         self.scores = torch.empty((B, Hkv, Tp), dtype=torch.float32, device=dev)
@@ -125,7 +126,7 @@ class PrunedKVCache:
         return self.out
 
     def visible_token_heads(self) -> int:
-        """Token-heads the next decode attention reads (pool + ring + int8 pool)."""
+        """Token-heads the next decode attention reads (pool + ring + low-precision pool)."""
         n = int(self.kv.length.sum()) + int((self.ring.pos >= 0).sum())
         if self.demote:
             n += int(self.kv.length8.sum())

@@ -50,6 +50,14 @@ def read_pool(kv, pair: int):
     return np_bits(pos).astype(np.int64), np_bits(K), np_bits(V)
 
 
+def unpack_int4(x: torch.Tensor) -> torch.Tensor:
+    """int8 bytes [..., n] -> int8 codes [..., 2n]: low nibble first, sign-extended."""
+    b = x.to(torch.int32) & 0xFF
+    lo = ((b & 0xF) ^ 8) - 8
+    hi = (((b >> 4) & 0xF) ^ 8) - 8
+    return torch.stack([lo, hi], dim=-1).reshape(*x.shape[:-1], 2 * x.shape[-1]).to(torch.int8)
+
+
 def read_pool8(kv, pair: int):
     n = int(kv.length8[pair])
     npg = (n + 15) // 16
@@ -59,8 +67,11 @@ def read_pool8(kv, pair: int):
         return np.zeros(0, np.int64), z, z, np.zeros(0, np.float32), np.zeros(0, np.float32)
     bt = kv.block_table8[pair, :npg].long()
     pos = kv.page8_pos[bt].reshape(-1)[:n]
-    K = kv.k8_pages[bt].reshape(-1, d)[:n]
-    V = kv.v8_pages[bt].transpose(1, 2).reshape(-1, d)[:n]
+    Kp, Vp = kv.k8_pages[bt], kv.v8_pages[bt]
+    if kv.c.lp_bits == 4:  # two codes per byte, the even element in the low nibble
+        Kp, Vp = unpack_int4(Kp), unpack_int4(Vp)
+    K = Kp.reshape(-1, d)[:n]
+    V = Vp.transpose(1, 2).reshape(-1, d)[:n]
     ks = kv.k8_scale[bt].reshape(-1)[:n]
     vs = kv.v8_scale[bt].reshape(-1)[:n]
     return (np_bits(pos).astype(np.int64), np_bits(K), np_bits(V), np_bits(ks), np_bits(vs))

@@ -59,6 +59,7 @@ int main(void) {
   printf("kvp_ring %zu\n", sizeof(kvp_ring));
   F(kvp_scorer, w1); F(kvp_scorer, b2);
   F(kvp_paged_kv, k_pages); F(kvp_paged_kv, err); F(kvp_paged_kv, k8_pages);
+  F(kvp_paged_kv, lp_bits);
   F(kvp_paged_kv, page8_top);
   F(kvp_ring, k); F(kvp_ring, pos);
   return 0;
@@ -153,6 +154,15 @@ def test_host_validation_without_device(L):
                                1 << 20, None) == E_DTYPE
     assert lib.kvp_decode_attn(fake, L.KVP_BF16, 1, 8, ctypes.byref(kv), None, 0.1, fake, fake,
                                16, None) == E_WS
+    # a low-precision pool with a code width other than 8 or 4
+    kv.num_pages8, kv.max_pages8_per_pair = 4, 4
+    for name in ("k8_pages", "v8_pages", "k8_scale", "v8_scale", "page8_pos", "block_table8",
+                 "length8", "page8_top"):
+        setattr(kv, name, fake)
+    kv.lp_bits = 3
+    assert lib.kvp_reset(ctypes.byref(kv), None, None) == E_ARG
+    kv.lp_bits = 4
+    kv.num_pages8, kv.max_pages8_per_pair = 0, 0
     # compact: demotion without an int8 pool, wrong pair count
     assert lib.kvp_compact(fake, fake, L.KVP_BF16, 1, 4, 64, 128, fake, fake, None, 0,
                            L.KVP_COMPACT_DEMOTE_INT8, ctypes.byref(kv), None, fake, 1 << 16,

@@ -196,8 +196,9 @@ def test_compact_exact(K, dtype, d, ring_w):
             assert np.array_equal(Sr, sb[p, rpos])
 
 
-def test_compact_demote_int8_exact(K):
-    B, Hkv, T, d = 2, 2, 500, 128
+@pytest.mark.parametrize("bits,d", [(8, 128), (4, 128), (4, 64)])
+def test_compact_demote_exact(K, bits, d):
+    B, Hkv, T = 2, 2, 500
     P = B * Hkv
     k = seeded((B, Hkv, T, d), 41, torch.bfloat16)
     v = seeded((B, Hkv, T, d), 42, torch.bfloat16, 3.0)
@@ -206,21 +207,22 @@ def test_compact_demote_int8_exact(K):
     keep = oracle.keep_mask(f64(s), 0.8, 128).reshape(P, T)
     idx, cnt = upload_selection(keep)
     kv = K.PagedKV.allocate(P, d, P * 40, 40, torch.bfloat16, DEV, num_pages8=P * 40,
-                            max_pages8_per_pair=40, poison=True)
+                            max_pages8_per_pair=40, poison=True, lp_bits=bits)
     ring = K.Ring.allocate(P, 128, d, torch.bfloat16, DEV, poison=True)
     K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s,
                   mode=K.KVP_COMPACT_DEMOTE_INT8)
     assert K.kvp_check(kv) == 0
     kf = f64(k).reshape(P, T, d)
     vf = f64(v).reshape(P, T, d)
+    qmax = oracle.LP_QMAX[bits]
     for p in range(P):
         ev = np.flatnonzero(~keep[p])
         pos, Kc, Vc, ks, vs = read_pool8(kv, p)
         assert np.array_equal(pos, ev)
         for i, t in enumerate(ev):
-            c, sc = oracle.quantize_absmax_int8(kf[p, t])
+            c, sc = oracle.quantize_absmax(kf[p, t], qmax)
             assert ks[i] == sc and np.array_equal(Kc[i], c), (p, t)
-            c, sc = oracle.quantize_absmax_int8(vf[p, t])
+            c, sc = oracle.quantize_absmax(vf[p, t], qmax)
             assert vs[i] == sc and np.array_equal(Vc[i], c), (p, t)
         # every position is held exactly once across bf16 pool, ring and int8 pool
         allpos = visible_positions(kv, ring, p)
@@ -230,14 +232,14 @@ def test_compact_demote_int8_exact(K):
 # ---------------------------------------------------------------------------- attention
 
 
-def build_cache(K, B, Hkv, T, d, dtype, keep, ring_w, seed, demote=False, poison=True):
+def build_cache(K, B, Hkv, T, d, dtype, keep, ring_w, seed, demote=False, poison=True, bits=8):
     P = B * Hkv
     k = seeded((B, Hkv, T, d), seed, dtype)
     v = seeded((B, Hkv, T, d), seed + 1, dtype)
     s = seeded((B, Hkv, T), seed + 2)
     idx, cnt = upload_selection(keep)
     maxpp = T // 16 + 2
-    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp) if demote else {}
+    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp, lp_bits=bits) if demote else {}
     kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, dtype, DEV, poison=poison, **kw)
     ring = K.Ring.allocate(P, ring_w, d, dtype, DEV, poison=poison) if ring_w else None
     K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s,
@@ -290,28 +292,36 @@ def test_decode_attn_empty_pairs(K):
     assert (out[0, :4] == 0).all() and (out[1, :4] == 0).all()
 
 
-def test_decode_attn_int8_pool(K):
-    B, Hq, Hkv, T, d = 2, 8, 2, 900, 128
+@pytest.mark.parametrize("bits,d,Hq,T", [(8, 128, 8, 900), (4, 128, 8, 900), (4, 64, 16, 777)])
+def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
+    B, Hkv = 2, 2
     P = B * Hkv
     s = seeded((B, Hkv, T), 71)
     keep = oracle.keep_mask(f64(s), 1.2, 128).reshape(P, T)
-    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, 128, seed=72, demote=True)
+    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, 128, seed=72, demote=True,
+                                 bits=bits)
     q = seeded((B, Hq, d), 75, torch.bfloat16)
     out = torch.full((B, Hq, d), float("nan"), device=DEV)
     ws = K.decode_attn_workspace(B, Hq, kv)
     K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
     ref = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
-                                         oracle.sm_scale(d))
+                                         oracle.sm_scale(d), bits=bits)
     check_attention(out, ref, torch.bfloat16)
+    if bits == 4:  # the coarser pool really is read: int8 codes would give another result
+        ref8 = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
+                                              oracle.sm_scale(d), bits=8)
+        assert np.abs(ref8 - ref).max() > 10 * 2e-3
 
 
 # ---------------------------------------------------------------------------- delayed step
 
 
-@pytest.mark.parametrize("dtype,d,w,demote", [(torch.bfloat16, 128, 64, False),
-                                              (torch.float32, 64, 32, False),
-                                              (torch.bfloat16, 128, 32, True)])
-def test_step_delayed_state_machine(K, dtype, d, w, demote):
+@pytest.mark.parametrize("dtype,d,w,demote,bits", [(torch.bfloat16, 128, 64, False, 8),
+                                                   (torch.float32, 64, 32, False, 8),
+                                                   (torch.bfloat16, 128, 32, True, 8),
+                                                   (torch.bfloat16, 128, 32, True, 4),
+                                                   (torch.bfloat16, 64, 48, True, 4)])
+def test_step_delayed_state_machine(K, dtype, d, w, demote, bits):
     """DMS: flagged tokens stay w steps; the visible set is re-derived from scratch by
     the oracle at every step and compared with the ring + pool content."""
     B, Hkv, Hq, T0, steps = 2, 3, 6, 200, 90
@@ -325,7 +335,7 @@ def test_step_delayed_state_machine(K, dtype, d, w, demote):
     v_all = seeded((B, Hkv, total, d), 83, dtype)
     idx, cnt = upload_selection(keep0)
     maxpp = total // 16 + 2
-    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp) if demote else {}
+    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp, lp_bits=bits) if demote else {}
     kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, dtype, DEV, poison=True, **kw)
     ring = K.Ring.allocate(P, w, d, dtype, DEV, poison=True)
     scores0 = s_all[..., :T0].contiguous()
@@ -354,12 +364,23 @@ def test_step_delayed_state_machine(K, dtype, d, w, demote):
             vis = want.reshape(B, Hkv, -1)
             if demote:
                 ref = oracle.beacon_decode_attention(f64(q), kf[:, :, :p + 1], vf[:, :, :p + 1],
-                                                     vis, oracle.sm_scale(d))
+                                                     vis, oracle.sm_scale(d), bits=bits)
             else:
                 ref = oracle.decode_attention(f64(q), kf[:, :, :p + 1], vf[:, :, :p + 1], vis,
                                               oracle.sm_scale(d))
             check_attention(out, ref, dtype)
     assert K.kvp_check(kv) == 0
+    if demote:  # every demoted row (by compaction or by a step) holds the oracle's codes
+        qmax = oracle.LP_QMAX[bits]
+        kr, vr = kf.reshape(P, total, d), vf.reshape(P, total, d)
+        for pr in range(P):
+            pos, Kc, Vc, ks, vs = read_pool8(kv, pr)
+            assert len(pos) > w // 2
+            for i, t in enumerate(pos):
+                c, sc = oracle.quantize_absmax(kr[pr, t], qmax)
+                assert ks[i] == sc and np.array_equal(Kc[i], c), (pr, t)
+                c, sc = oracle.quantize_absmax(vr[pr, t], qmax)
+                assert vs[i] == sc and np.array_equal(Vc[i], c), (pr, t)
 
 
 # ---------------------------------------------------------------------------- errors
