@@ -111,7 +111,7 @@ def main():
         scorer = K.Scorer(K.KVP_SCORER_LINEAR, sw.W1, sw.b1)
     q_keep = wl.keep_quantiles[0]
     cache = PrunedKVCache(B, Hkv, Hq, d, T, wl.kv_dtype, scorer, wl.R, 0.0, device=dev,
-                          max_prompt=T0)
+                          max_prompt=T0, demote=wl.int8_demote, lp_bits=wl.lp_bits)
     # tau is calibrated on the device inside every step (kvp_threshold: the exact
     # q-quantile of the prompt's scores); its value is logged once here
     cache.score(hidden)
@@ -152,6 +152,8 @@ def main():
     assert st == 0, f"capacity error {st}"
     visible = cache.visible_token_heads()
     kept_prefill = int(cache.kept_count.sum())  # before the keep sweep below re-selects
+    lp_visible = int(cache.kv.length8.sum()) if wl.int8_demote else 0
+    kv_bytes_attn = attn_bytes(cache, wl, B, Hq, d)
     total_th = B * Hkv * T
     log(f"[bench] warmup done; visible token-heads {visible} of {total_th} "
         f"({visible / total_th:.3f})")
@@ -245,17 +247,17 @@ def main():
         vis_k = cache.visible_token_heads()
         keep_scaling.append({"keep": keep, "tau": tau_k if keep < 1.0 else None,
                              "visible_token_heads": vis_k,
+                             "attn_bytes": attn_bytes(cache, wl, B, Hq, d),
                              "decode_step_ms": float(np.median(dec)),
                              "attn_isolated_ms": float(np.median(att))})
     del flush
     cache.calibrate(q_keep, T0)
     base = keep_scaling[0] if keep_scaling else None
     for e in keep_scaling:
-        e["bytes_ratio_vs_keep1"] = e["visible_token_heads"] / base["visible_token_heads"]
+        e["bytes_ratio_vs_keep1"] = e["attn_bytes"] / base["attn_bytes"]
         e["decode_step_ratio_vs_keep1"] = e["decode_step_ms"] / base["decode_step_ms"]
         e["attn_ratio_vs_keep1"] = e["attn_isolated_ms"] / base["attn_isolated_ms"]
-        e["attn_gbs"] = e["visible_token_heads"] * 2 * d * (2 if wl.kv_dtype == torch.bfloat16 else 4) \
-            / (e["attn_isolated_ms"] * 1e-3) / 1e9
+        e["attn_gbs"] = e["attn_bytes"] / (e["attn_isolated_ms"] * 1e-3) / 1e9
     log("[bench] keep scaling: " + "; ".join(
         f"keep {e['keep']}: decode {e['decode_step_ms']:.3f} ms (x{e['decode_step_ratio_vs_keep1']:.2f}), "
         f"attn {e['attn_isolated_ms']:.3f} ms (x{e['attn_ratio_vs_keep1']:.2f}), bytes x{e['bytes_ratio_vs_keep1']:.2f}"
@@ -263,7 +265,6 @@ def main():
 
     # algorithmic work per call
     elt = 2 if wl.kv_dtype == torch.bfloat16 else 4
-    kv_bytes_attn = visible * 2 * d * elt + B * Hq * d * (elt + 4)
     ntok = B * T0
     if wl.scorer == "mlp":
         score_flops = 2.0 * ntok * H * wl.inner + 2.0 * ntok * wl.inner * Hkv
@@ -272,6 +273,9 @@ def main():
     score_bytes = ntok * H * elt + ntok * Hkv * 4
     select_bytes = ntok * Hkv * 4 + B * Hkv * T0 * 4 + B * Hkv * ((T0 + 31) // 32) * 4 * 2
     compact_bytes = kept_prefill * 2 * d * elt * 2 + kept_prefill * 4
+    if wl.int8_demote:  # demoted tokens: read in full, written as codes + one scale per row
+        demoted = B * Hkv * T0 - kept_prefill
+        compact_bytes += demoted * (2 * d * elt + 2 * (d * wl.lp_bits // 8 + 4) + 4)
     step_bytes = B * Hkv * d * elt * 2 * 3
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9  # noqa: E731
     kernels = {
@@ -335,6 +339,8 @@ def main():
         "config": {"workload": wl.name, "batch": B, "hidden": H, "q_heads": Hq, "kv_heads": Hkv,
                    "head_dim": d, "context": T, "scorer": wl.scorer, "keep_quantile": q_keep,
                    "recent": wl.R, "page": 16, "visible_token_heads": visible,
+                   "low_precision_pool": ({"bits": wl.lp_bits, "token_heads": lp_visible}
+                                          if wl.int8_demote else None),
                    "total_token_heads": total_th},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -343,6 +349,18 @@ def main():
         "keep_scaling": keep_scaling,
     }
     print(json.dumps(line), flush=True)
+
+
+def attn_bytes(cache, wl, B, Hq, d) -> int:
+    """Algorithmic bytes of one decode attention over the cache as it stands: K and V of
+    every visible bf16/fp32 token-head, codes plus two fp32 scales of every token-head in
+    the low-precision pool, the queries read and the fp32 outputs written."""
+    import torch
+
+    elt = 2 if wl.kv_dtype == torch.bfloat16 else 4
+    lp = int(cache.kv.length8.sum()) if wl.int8_demote else 0
+    main = cache.visible_token_heads() - lp
+    return main * 2 * d * elt + lp * 2 * (d * wl.lp_bits // 8 + 4) + B * Hq * d * (elt + 4)
 
 
 def dms_loop(args, wl, dev):
@@ -535,7 +553,11 @@ def cpu_baseline(wl, hidden, kd, vd, q, h_new, k_new, v_new, sw, tau, T0, rows):
     vis = oracle.keep_mask(s, tau, wl.R)
     Ka = np.concatenate([Kd, kn[:, :, None]], axis=2)
     Va = np.concatenate([Vd, vn[:, :, None]], axis=2)
-    out = oracle.decode_attention(qq, Ka, Va, vis, oracle.sm_scale(wl.d))
+    if wl.int8_demote:  # every token stays visible; the evicted ones as low-precision codes
+        out = oracle.beacon_decode_attention(qq, Ka, Va, vis, oracle.sm_scale(wl.d), bits=wl.lp_bits)
+        vis = np.ones_like(vis)
+    else:
+        out = oracle.decode_attention(qq, Ka, Va, vis, oracle.sm_scale(wl.d))
     dt = time.perf_counter() - t0
     kept = int(vis.sum())
     assert np.isfinite(out).all()

@@ -52,7 +52,8 @@ class Workload:
     outlier_mult: float = 1.0
     prompt: int = 0  # DMS: prompt length
     steps: int = 0  # DMS: number of decode steps
-    int8_demote: bool = False
+    int8_demote: bool = False  # evicted tokens go to the low-precision pool
+    lp_bits: int = 8  # code width of that pool (8 or 4)
     index: int = 0
 
     @property
@@ -94,7 +95,10 @@ BEACON_MIXED = Workload("beacon_mixed", B=16, H=4096, Hq=32, Hkv=8, d=128, T=327
                         kv_dtype=torch.bfloat16, scorer="mlp", keep_quantiles=(0.90,),
                         int8_demote=True, index=4)
 
-ALL = (TINY, QWEN3_8B_LAYER, DMS_DELAYED, LONG_70B_LAYER, BEACON_MIXED)
+# The same inputs as beacon_mixed (same seeds) with an int4 pool for the demoted tokens.
+BEACON_INT4 = dataclasses.replace(BEACON_MIXED, name="beacon_int4", lp_bits=4)
+
+ALL = (TINY, QWEN3_8B_LAYER, DMS_DELAYED, LONG_70B_LAYER, BEACON_MIXED, BEACON_INT4)
 BY_NAME = {w.name: w for w in ALL}
 
 

@@ -7,11 +7,11 @@
 //
 // Work decomposition (split-K, evenly balanced):
 //   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages,
-//   then its ring pages, padded to an even count) and, when an int8 pool exists, a
-//   "region B" (its int8 pages, padded to even).  All regions are concatenated and
-//   the sequence is cut into NWAVES equal, even-length ranges; each wave walks its
-//   range 32 tokens (two pages) at a time and emits one partial (m, l, o) record per
-//   region it touches.  A second kernel (one wave per pair and query head) merges a
+//   then its ring pages, padded to an even count) and, when a low-precision pool
+//   exists, a "region B" (its int8 or int4 pages, padded to even).  The A regions are
+//   concatenated and cut into NWAVES equal, even-length ranges, and so are the B
+//   regions; each wave walks its A range, then its B range, 32 tokens (two pages) at a
+//   time, and emits one partial (m, l, o) record per region it touches.  A second kernel (one wave per pair and query head) merges a
 //   pair's records with a log-sum-exp combine in a fixed order, so the result is
 //   deterministic.  The kernel boundary makes the records visible: no atomics and no
 //   device-scope fences (each of which writes back an XCD's L2) in the hot kernel.
@@ -61,11 +61,17 @@ __device__ __forceinline__ int region_pages(const AttnArgs& a, int s) {
   return (n + 1) & ~1;
 }
 
+// The bf16/fp32 regions (A) and the low-precision regions (B) are split separately: a
+// wave takes per_a pages of the A sequence and per_b pages of the B sequence.  One
+// split over both would balance pages, but a bf16 page moves 2x (int8) to 4x (int4)
+// the bytes of a low-precision page, and the waves that drew bf16 pages set the time
+// (measured: the int4 pool ran no faster than the int8 one).
 struct Plan {
-  int* P;  // [nseg + 1]
-  int* C;  // [nseg + 1]
-  int total;
-  int per;
+  int* P;  // [nseg + 1] page prefix over the regions (A regions first)
+  int* C;  // [nseg + 1] record-slot prefix
+  int total;    // pages of all regions
+  int total_a;  // pages of the A regions (= P[num_pairs])
+  int per_a, per_b;
 };
 
 // Regions in the plan: the low-precision regions only exist with a low-precision pool.
@@ -82,13 +88,16 @@ __device__ Plan build_plan(const AttnArgs& a, int* lds) {
   for (int s = threadIdx.x; s <= nseg; s += blockDim.x) pl.P[s] = (s < nseg) ? region_pages(a, s) : 0;
   __syncthreads();
   pl.total = block_scan_excl(pl.P, nseg + 1, tmp);
-  int per = (pl.total + ATTN_NWAVES - 1) / ATTN_NWAVES;
-  per = max(2, (per + 1) & ~1);
-  pl.per = per;
+  const int np = a.kv.num_pairs;
+  pl.total_a = pl.P[np];
+  auto split = [](int pages) { return max(2, (((pages + ATTN_NWAVES - 1) / ATTN_NWAVES) + 1) & ~1); };
+  pl.per_a = split(pl.total_a);
+  pl.per_b = split(pl.total - pl.total_a);
   for (int s = threadIdx.x; s <= nseg; s += blockDim.x) {
     int c = 0;
     if (s < nseg) {
-      int p0 = pl.P[s], p1 = pl.P[s + 1];
+      const int base = s < np ? 0 : pl.total_a, per = s < np ? pl.per_a : pl.per_b;
+      const int p0 = pl.P[s] - base, p1 = pl.P[s + 1] - base;
       if (p1 > p0) c = (p1 - 1) / per - p0 / per + 1;
     }
     pl.C[s] = c;
@@ -367,7 +376,9 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
   // at some cache sizes that stride piles them onto the same HBM channels (measured:
   // 10% slower at one keep ratio); walking in opposite directions breaks the pattern.
   // The step order only changes the rounding order of this wave's partial softmax.
-  const bool rev = (((blockIdx.x * ATTN_WG_WAVES) + (threadIdx.x >> 6)) & 1) != 0;
+  // (readfirstlane: the wave index is uniform, and saying so keeps the range and step
+  // loops below scalar; a per-lane flag would make them exec-masked loops)
+  const bool rev = ((blockIdx.x * ATTN_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) & 1) != 0;
   const int nch = (v1 - v0 + 63) / 64;
   for (int ci = 0; ci < nch; ++ci) {
     // block-table chunk: pages [c0, c0 + 64) of this range
@@ -415,10 +426,16 @@ __device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, i
 // Low-precision region (BeaconKV demoted tokens, int8 or int4 codes): codes -> bf16
 // exactly, per-token scales.
 // -------------------------------------------------------------------------------
+// Two fp32 values whose low 16 bits are zero (small integers) -> packed bf16x2, in
+// one byte permute (bytes 2-3 of lo, then bytes 2-3 of hi).
+__device__ __forceinline__ uint32_t pack_hi16(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 __device__ __forceinline__ uint32_t i8pair_to_bf16x2(uint32_t word, int byte0) {
-  float f0 = (float)(int)(int8_t)((word >> (8 * byte0)) & 0xffu);
-  float f1 = (float)(int)(int8_t)((word >> (8 * (byte0 + 1))) & 0xffu);
-  return (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
+  const float f0 = (float)(int)(int8_t)((word >> (8 * byte0)) & 0xffu);
+  const float f1 = (float)(int)(int8_t)((word >> (8 * (byte0 + 1))) & 0xffu);
+  return pack_hi16(f0, f1);
 }
 
 // 8 int8 codes (two dwords) -> 8 bf16 (exact: |code| <= 127).
@@ -431,15 +448,21 @@ __device__ __forceinline__ u32x4 i8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
   return r;
 }
 
-// 8 int4 codes (one dword, element e in nibble e) -> 8 bf16 (exact: |code| <= 8).
+// 8 int4 codes (one dword, element e in nibble e, two's complement) -> 8 bf16 holding
+// I4_OFFSET + code, exactly.  Flipping each nibble's sign bit gives the offset-binary
+// code u = code + 8 in 0..15; bf16 0x4300 | u is 2^7 (1 + u / 128) = 128 + u, so a
+// byte permute that spreads the nibbles into the low mantissa bytes plus one OR with
+// the exponent decodes two elements.  The offset is taken out after the MFMAs: of the
+// scores as I4_OFFSET * sum_k q_k per head, of the outputs as I4_OFFSET * sum_t p_t.
+constexpr float I4_OFFSET = 136.0f;
 __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
+  const uint32_t u = w ^ 0x88888888u;
+  const uint32_t lo = u & 0x0f0f0f0fu;         // elements 0, 2, 4, 6 in bytes 0..3
+  const uint32_t hi = (u >> 4) & 0x0f0f0f0fu;  // elements 1, 3, 5, 7
   u32x4 r;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float f0 = (float)(static_cast<int>(w << (28 - 8 * q)) >> 28);
-    const float f1 = (float)(static_cast<int>(w << (24 - 8 * q)) >> 28);
-    r[q] = (__float_as_uint(f0) >> 16) | (__float_as_uint(f1) & 0xffff0000u);
-  }
+  for (int q = 0; q < 4; ++q)  // byte 0 <- lo byte q, byte 2 <- hi byte q, bytes 1 and 3 zero
+    r[q] = __builtin_amdgcn_perm(hi, lo, 0x0c000c00u | ((4u + q) << 16) | q) | 0x43004300u;
   return r;
 }
 
@@ -494,9 +517,10 @@ __device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS>& f
   f.vs[1] = *reinterpret_cast<const f32x4*>(vsc + 4);
 }
 
-template <int D, int BITS>
+template <int D, int BITS, int NSET>
 __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
                                 int slot) {
+  static_assert(NSET % 2 == 0, "steps are folded in pairs");
   const int lane = threadIdx.x & 63, j = lane >> 4;
   bf16x8 qf[D / 32];
   load_q<D>(a, pair, qf);
@@ -505,9 +529,23 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
   for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = neg_inf();
   st.l = 0.f;
+  // int4: I4_OFFSET * (sum of this lane's head's query) comes off every score; psum
+  // tracks sum_t p_t over this lane's tokens (rescaled like o) for the output offset
+  float qoff = 0.f, psum = 0.f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const u32x4 w = __builtin_bit_cast(u32x4, qf[kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qoff += bf16_to_f32(w[e] & 0xffffu) + bf16_to_f32(w[e] >> 16);
+    }
+    qoff += __shfl_xor(qoff, 16);
+    qoff += __shfl_xor(qoff, 32);
+    qoff *= I4_OFFSET;
+  }
   const int len = __builtin_amdgcn_readfirstlane(a.kv.length8[pair]);
   const int npm = cdiv(len, PAGE);  // v1 <= npm rounded up to even; the pad page is never loaded
-  const bool rev = (((blockIdx.x * ATTN_WG_WAVES) + (threadIdx.x >> 6)) & 1) != 0;  // as in region A
+  const bool rev = ((blockIdx.x * ATTN_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) & 1) != 0;  // as in region A
   const int nch = (v1 - v0 + 63) / 64;
   for (int ci = 0; ci < nch; ++ci) {
     const int c0 = v0 + 64 * (rev ? nch - 1 - ci : ci);
@@ -519,88 +557,140 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
       // the pad page of an odd page count re-uses the previous page (all slots masked)
       return __builtin_amdgcn_readlane(bt, min(vp, npm - 1) - c0);
     };
-    LpFrags<D, BITS> f;
+    // NSET steps of loads in flight, and steps folded in pairs (64 tokens) into one
+    // online-softmax update.  A step here moves half (int8) or a quarter (int4) of a
+    // bf16 step's bytes, so with one step in flight per wave the whole device would hold
+    // too few bytes in flight to cover the memory latency (measured: the int4 pool ran
+    // at the same step rate as int8, half the bandwidth).  A set is refilled with the
+    // step NSET ahead right after its last use (K after the QK MFMAs, V after the PV
+    // MFMAs).  Steps past the end of the range run on a repeat of the last pages with
+    // every token masked, and their refills repeat the last pages too, so every block
+    // issues the same loads and the wait counts stay exact.
     const int nst = (c1 - c0) / 2;
-    auto vat = [&](int i) { return c0 + 2 * (rev ? nst - 1 - i : i); };
-    int pgX = page(vat(0)), pgY = page(vat(0) + 1);
-    load_lp_k<D, BITS>(a, f, pgX, pgY, lane);
-    load_lp_v<D, BITS>(a, f, pgX, pgY, lane);
-    for (int i = 0; i < nst; ++i) {
-      const int v = vat(i);
-      const int vn = vat(i + 1 < nst ? i + 1 : i);
-      const int pgXn = page(vn), pgYn = page(vn + 1);
-      const int nvT = max(0, min(PAGE, len - (v + (j >> 1)) * PAGE));
-      const int s0 = 8 * (j & 1);
-      const uint32_t vb = (uint32_t)((1 << max(0, min(8, nvT - s0))) - 1);
-      const bool allv = __ballot(vb != 0xffu) == 0;
+    auto vat = [&](int i) {
+      i = min(i, nst - 1);
+      return c0 + 2 * (rev ? nst - 1 - i : i);
+    };
+    auto valid_bits = [&](int v, bool real) -> uint32_t {
+      const int nvT = real ? max(0, min(PAGE, len - (v + (j >> 1)) * PAGE)) : 0;
+      return (uint32_t)((1 << max(0, min(8, nvT - 8 * (j & 1)))) - 1);
+    };
+    auto qk = [&](const LpFrags<D, BITS>& f, float (&s)[8], float (&vsc)[8]) {
       f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         sA = mfma16x16x32(as_bf16x8(lp_to_bf16x8(f.kA[kk])), qf[kk], sA);
         sB = mfma16x16x32(as_bf16x8(lp_to_bf16x8(f.kB[kk])), qf[kk], sB);
       }
+      if constexpr (BITS == 4) {
+        sA -= qoff;
+        sB -= qoff;
+      }
       // per-token K scale folds into the logits; V scale into the probabilities
-      const f32x4 ks0 = f.ks[0], ks1 = f.ks[1];
-      const f32x4 vs0 = f.vs[0], vs1 = f.vs[1];
-      sA = sA * ks0;
-      sB = sB * ks1;
-      load_lp_k<D, BITS>(a, f, pgXn, pgYn, lane);
-      float s[8], vsc[8];
+      sA = sA * f.ks[0];
+      sB = sB * f.ks[1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         s[i] = sA[i] * a.scale_log2;
         s[i + 4] = sB[i] * a.scale_log2;
-        vsc[i] = vs0[i];
-        vsc[i + 4] = vs1[i];
+        vsc[i] = f.vs[0][i];
+        vsc[i + 4] = f.vs[1][i];
       }
-      if (!allv) {
+    };
+    auto mask = [&](float (&s)[8], float (&vsc)[8], uint32_t vb) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bool ok = (vb >> i) & 1u;
-          s[i] = ok ? s[i] : neg_inf();
-          vsc[i] = ok ? vsc[i] : 0.f;
-        }
+      for (int i = 0; i < 8; ++i) {
+        const bool ok = (vb >> i) & 1u;
+        s[i] = ok ? s[i] : neg_inf();
+        vsc[i] = ok ? vsc[i] : 0.f;
       }
-      float mx = s[0];
+    };
+    // sum_t p_t (scale_t code_t) = sum_t (p_t scale_t) code_t, weights split bf16 hi + lo
+    auto pv = [&](const LpFrags<D, BITS>& f, const float (&p)[8], const float (&vsc)[8]) {
+      u32x4 hi, lo;
 #pragma unroll
-      for (int i = 1; i < 8; ++i) mx = fmaxf(mx, s[i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(st.m, mx);
-      if (mnew != neg_inf()) {
-        const float alpha = exp2f(st.m - mnew);
-        float p[8], psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          p[i] = exp2f(s[i] - mnew);
-          psum += p[i];
-        }
-        st.l = st.l * alpha + psum;
-        st.m = mnew;
-        if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
-        }
-        // sum_t p_t (scale_t code_t) = sum_t (p_t scale_t) code_t
-        u32x4 hi, lo;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const float q0 = p[2 * w] * vsc[2 * w], q1 = p[2 * w + 1] * vsc[2 * w + 1];
-          const uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
-          hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          lo[w] = pack_bf16x2(q0 - bf16_to_f32(h0), q1 - bf16_to_f32(h1));
-        }
-        const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
-#pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          u32x4 vt = lp_to_bf16x8(f.v[t]);
-          if (!allv) vt = mask_tokens(vt, vb);
-          st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
-          st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
-        }
+      for (int w = 0; w < 4; ++w) {
+        const float q0 = p[2 * w] * vsc[2 * w], q1 = p[2 * w + 1] * vsc[2 * w + 1];
+        const uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
+        hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+        const uint16_t l0 = f32_to_bf16(q0 - bf16_to_f32(h0)), l1 = f32_to_bf16(q1 - bf16_to_f32(h1));
+        lo[w] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        if constexpr (BITS == 4)  // exactly the weights the MFMAs see
+          psum += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
       }
-      load_lp_v<D, BITS>(a, f, pgXn, pgYn, lane);
+      const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        // every code decodes to a finite value and the weight of an unused slot is
+        // exactly 0, so unlike the bf16 pool (whose unused slots may hold NaN bits) no
+        // element needs zeroing
+        const u32x4 vt = lp_to_bf16x8(f.v[t]);
+        st.o[t] = mfma16x16x32(as_bf16x8(vt), phi, st.o[t]);
+        st.o[t] = mfma16x16x32(as_bf16x8(vt), plo, st.o[t]);
+      }
+    };
+    // NSET register sets in a ring: set r holds step i + r of the block being worked on
+    // and is refilled with step i + r + NSET right after its last use.
+    LpFrags<D, BITS> f[NSET];
+#pragma unroll
+    for (int r = 0; r < NSET; ++r) {
+      load_lp_k<D, BITS>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
+      load_lp_v<D, BITS>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
     }
+    for (int i = 0; i < nst; i += NSET) {
+#pragma unroll
+      for (int r = 0; r < NSET; r += 2) {
+        const int va = vat(i + r), vb_ = vat(i + r + 1);
+        const int vna = vat(i + r + NSET), vnb = vat(i + r + 1 + NSET);
+        const uint32_t m0 = valid_bits(va, i + r < nst), m1 = valid_bits(vb_, i + r + 1 < nst);
+        const bool allv = __ballot((m0 & m1) != 0xffu) == 0;
+        float s0[8], s1[8], c0s[8], c1s[8];
+        qk(f[r], s0, c0s);
+        qk(f[r + 1], s1, c1s);
+        load_lp_k<D, BITS>(a, f[r], page(vna), page(vna + 1), lane);
+        load_lp_k<D, BITS>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
+        if (!allv) {
+          mask(s0, c0s, m0);
+          mask(s1, c1s, m1);
+        }
+        float mx = s0[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s0[e]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, s1[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(st.m, mx);
+        if (mnew != neg_inf()) {
+          const float alpha = exp2f(st.m - mnew);
+          float p0[8], p1[8], ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            p0[e] = exp2f(s0[e] - mnew);
+            p1[e] = exp2f(s1[e] - mnew);
+            ps += p0[e] + p1[e];
+          }
+          st.l = st.l * alpha + ps;
+          st.m = mnew;
+          if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+            for (int t = 0; t < D / 16; ++t) st.o[t] *= alpha;
+            if constexpr (BITS == 4) psum *= alpha;
+          }
+          pv(f[r], p0, c0s);
+          pv(f[r + 1], p1, c1s);
+        }
+        load_lp_v<D, BITS>(a, f[r], page(vna), page(vna + 1), lane);
+        load_lp_v<D, BITS>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
+      }
+    }
+  }
+  if constexpr (BITS == 4) {
+    psum += __shfl_xor(psum, 16);
+    psum += __shfl_xor(psum, 32);
+    const float off = I4_OFFSET * psum;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) st.o[t] -= off;
   }
   emit_partial<D>(a, pl, pair, slot, st);
 }
@@ -718,7 +808,8 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
 // The kernel
 // -------------------------------------------------------------------------------
 template <int D, bool F32>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_attn_kernel(AttnArgs a) {
+// One work-group per CU (ATTN_GRID = 256), so a wave may use a whole SIMD's registers.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_attn_kernel(AttnArgs a) {
   extern __shared__ int lds[];
   Plan pl = build_plan(a, lds);
   const int np = a.kv.num_pairs;
@@ -734,21 +825,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     for (int i = threadIdx.x; i <= 2 * np; i += blockDim.x) a.plan_c[i] = pl.C[min(i, nseg)];
 
   pl.total = __builtin_amdgcn_readfirstlane(pl.total);
-  pl.per = __builtin_amdgcn_readfirstlane(pl.per);
-  int start = gw * pl.per;
-  const int end = min(start + pl.per, pl.total);
-  if (start >= end) return;
-  int s = __builtin_amdgcn_readfirstlane(upper_segment(pl.P, nseg, start));
+  pl.total_a = __builtin_amdgcn_readfirstlane(pl.total_a);
+  pl.per_a = __builtin_amdgcn_readfirstlane(pl.per_a);
+  pl.per_b = __builtin_amdgcn_readfirstlane(pl.per_b);
   float* wlds = nullptr;
   int* wmask = lds + 2 * (nseg + 1) + 16 + wid * 64;
   if constexpr (F32) {
     wlds = reinterpret_cast<float*>(lds + 2 * (nseg + 1) + 16 + ATTN_WG_WAVES * 64) + wid * (16 * D + 16 * 32);
   }
+  // pass 0: this wave's share of the A sequence; pass 1: of the B sequence
+  for (int pass = 0; pass < 2; ++pass) {
+  const int base = pass ? pl.total_a : 0, per = pass ? pl.per_b : pl.per_a;
+  int start = base + gw * per;
+  const int end = min(start + per, pass ? pl.total : pl.total_a);
+  if (start >= end) continue;
+  int s = __builtin_amdgcn_readfirstlane(upper_segment(pl.P, nseg, start));
   while (start < end) {
     while (__builtin_amdgcn_readfirstlane(pl.P[s + 1]) <= start) ++s;
     const int ps = __builtin_amdgcn_readfirstlane(pl.P[s]);
     const int stop = min(end, __builtin_amdgcn_readfirstlane(pl.P[s + 1]));
-    const int slot = __builtin_amdgcn_readfirstlane(pl.C[s]) + (gw - ps / pl.per);
+    const int slot = __builtin_amdgcn_readfirstlane(pl.C[s]) + (gw - (ps - base) / per);
     const int v0 = start - ps, v1 = stop - ps;
     if (s < np) {
       if constexpr (F32) {
@@ -758,11 +854,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
     } else {
       if constexpr (!F32) {
-        if (a.kv.lp_bits == 4) run_region_b_lp<D, 4>(a, pl, s - np, v0, v1, slot);
-        else run_region_b_lp<D, 8>(a, pl, s - np, v0, v1, slot);
+#ifndef LP_SETS4
+#define LP_SETS4 4
+#endif
+#ifndef LP_SETS8
+#define LP_SETS8 2
+#endif
+        if (a.kv.lp_bits == 4) run_region_b_lp<D, 4, LP_SETS4>(a, pl, s - np, v0, v1, slot);
+        else run_region_b_lp<D, 8, LP_SETS8>(a, pl, s - np, v0, v1, slot);
       }
     }
     start = stop;
+  }
   }
 }
 
@@ -882,7 +985,7 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   const int Hkv = num_pairs / B;
   if (Hq % Hkv != 0) return 0;
   const int g = Hq / Hkv;
-  const size_t recs = (size_t)ATTN_NWAVES + 2 * (size_t)num_pairs;
+  const size_t recs = 2 * (size_t)ATTN_NWAVES + 2 * (size_t)num_pairs;  // both splits
   return attn_plan_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
 }
 

@@ -57,6 +57,7 @@ def oracle_scores(wl, sw, x_bits_rows, chunk=2048):
 
 
 def run_kvzap(K, wl, T, rows_check, tau=None, q_keep=None, demote=False, B=None):
+    bits = wl.lp_bits
     """Prefill T-1 tokens, one decode step; compare sampled batch rows with the oracle."""
     from sparse_decode_attention_kvzap_amd.pipeline import PrunedKVCache
     B = B or wl.B
@@ -71,7 +72,7 @@ def run_kvzap(K, wl, T, rows_check, tau=None, q_keep=None, demote=False, B=None)
         tau = float(oracle.threshold_quantile(s64, q_keep))
     tau = np.float32(tau)
     cache = PrunedKVCache(B, wl.Hkv, wl.Hq, wl.d, T, wl.kv_dtype, make_scorer(K, wl, sw), wl.R,
-                          float(tau), demote=demote, device=DEV, max_prompt=T0)
+                          float(tau), demote=demote, device=DEV, max_prompt=T0, lp_bits=bits)
     cache.prefill(x[:, :T0].contiguous(), kd[:, :, :T0].contiguous(), vd[:, :, :T0].contiguous())
     g_prefill_scores = cache.scores[rows_check].clone()
     out = cache.step(x[:, T0:].contiguous(), kd[:, :, T0].contiguous(), vd[:, :, T0].contiguous(),
@@ -97,7 +98,8 @@ def run_kvzap(K, wl, T, rows_check, tau=None, q_keep=None, demote=False, B=None)
     assert np.array_equal(vis_gpu[ok], keep[ok]), "visible set differs outside the band"
     vis_ref = np.where(band, vis_gpu, keep)
     if demote:
-        ref = oracle.beacon_decode_attention(q64, kd64, vd64, vis_ref, oracle.sm_scale(wl.d))
+        ref = oracle.beacon_decode_attention(q64, kd64, vd64, vis_ref, oracle.sm_scale(wl.d),
+                                             bits=bits)
         for ri, b in enumerate(rows_check):
             for h in range(wl.Hkv):
                 p = b * wl.Hkv + h
@@ -177,6 +179,21 @@ def test_beacon_full_size_sampled(K):
     row's 8 pairs; the oracle quantizes every demoted row itself."""
     wl = W.BEACON_MIXED
     r = run_kvzap(K, wl, wl.T, [11], q_keep=0.9, demote=True)
+    print(r)
+
+
+def test_beacon_int4_reduced_all_pairs(K):
+    wl = W.BEACON_INT4
+    r = run_kvzap(K, wl, 2500, [0, 1], q_keep=0.9, demote=True, B=2)
+    assert 0.1 < r["kept"] < 0.2
+
+
+@pytest.mark.slow
+def test_beacon_int4_full_size_sampled(K):
+    """The same shape and inputs with the demoted tokens in an int4 pool: one batch
+    row's 8 pairs against the oracle's int4 round trips."""
+    wl = W.BEACON_INT4
+    r = run_kvzap(K, wl, wl.T, [5], q_keep=0.9, demote=True)
     print(r)
 
 
