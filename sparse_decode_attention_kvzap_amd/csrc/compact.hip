@@ -5,16 +5,17 @@
 // into a compact, fixed-address KV buffer.  Here the index list is kvp_select's
 // ordered kept_idx, the preparation pass is compact_plan_kernel (page counts, page
 // bases by exclusive scan, lengths, capacity checks) and the copy pass is
-// compact_gather_kernel.  KVzap practical application: only kept entries (plus the
+// compact_copy_kernel.  KVzap practical application: only kept entries (plus the
 // recent window) remain.  BeaconKV body: in DEMOTE_INT8 mode the other entries are
-// kept at low precision instead (absmax int8 per (token, head), K and V separately).
+// kept at low precision instead (absmax int8 or int4 codes per (token, head), K and V
+// separately).
 //
 // Work units are destination pages of 16 slots.  Copy units (a pair's pool pages, then
-// its ring pages) go to compact_copy_kernel: each wave owns one contiguous run of
-// units, so it finds its first pair once and then walks pairs in order; a page is
-// copied by one wave (K rows straight through, V transposed through the wave's own LDS
-// tile), with no work-group barrier.  int8 units (DEMOTE_INT8) go to
-// compact_quant_kernel, one work-group per page.
+// its ring pages) go to compact_copy_kernel and low-precision pages to
+// compact_quant_kernel; in both, each wave owns one contiguous run of units, so it
+// finds its first pair once and then walks pairs in order, and a page is handled by
+// one wave (K rows straight through, V transposed through the wave's own LDS tile),
+// with no work-group barrier.
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -133,93 +134,6 @@ __device__ __forceinline__ float elem_to_f32<uint16_t>(uint16_t x) { return bf16
 template <>
 __device__ __forceinline__ float elem_to_f32<float>(float x) { return x; }
 
-// Quantize 16 source rows into a K page [16][d] and a V^T page [d][16] of BITS-bit
-// codes with one fp32 absmax scale per slot for K and for V.  int8: one code per
-// byte.  int4: two codes per byte, the even element in the low nibble (K: dims 2i and
-// 2i+1 of a token; V^T: tokens 2i and 2i+1 of a dim), so a K row takes d/2 bytes and
-// a V^T row 8.
-template <typename E, int BITS>
-__device__ void quant_page(const E* ksrc, const E* vsrc, int d, const int* src, int8_t* kdst,
-                           int8_t* vdst, float* ksc, float* vsc, int8_t* cbuf) {
-  constexpr float QMAX = BITS == 4 ? 7.0f : 127.0f;
-  const int tid = threadIdx.x;
-  constexpr int EPC = 16 / sizeof(E);
-  const int cpr = d / EPC;  // threads per row (power of two, <= 16)
-  for (int c = tid; c < PAGE * cpr; c += blockDim.x) {
-    const int row = c / cpr, col = (c % cpr) * EPC;
-    const int s = src[row];
-    float kf[EPC], vf[EPC];
-    if (s >= 0) {
-      u32x4 kx = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)s * d + col);
-      u32x4 vx = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)s * d + col);
-      const E* ke = reinterpret_cast<const E*>(&kx);
-      const E* ve = reinterpret_cast<const E*>(&vx);
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) {
-        kf[e] = elem_to_f32<E>(ke[e]);
-        vf[e] = elem_to_f32<E>(ve[e]);
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) kf[e] = vf[e] = 0.f;
-    }
-    float ka = 0.f, va = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      ka = fmaxf(ka, fabsf(kf[e]));
-      va = fmaxf(va, fabsf(vf[e]));
-    }
-    for (int o = 1; o < cpr; o <<= 1) {
-      ka = fmaxf(ka, __shfl_xor(ka, o));
-      va = fmaxf(va, __shfl_xor(va, o));
-    }
-    const float kscale = ka / QMAX, vscale = va / QMAX;
-    if constexpr (BITS == 4) {
-#pragma unroll
-      for (int e = 0; e < EPC; e += 2) {
-        const int c0 = quant_code(kf[e], kscale, QMAX), c1 = quant_code(kf[e + 1], kscale, QMAX);
-        kdst[(row * d + col + e) / 2] = static_cast<int8_t>((c0 & 0xf) | (c1 << 4));
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) kdst[row * d + col + e] = static_cast<int8_t>(quant_code(kf[e], kscale, QMAX));
-    }
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) cbuf[row * d + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale, QMAX));
-    if ((c % cpr) == 0) {
-      ksc[row] = kscale;
-      vsc[row] = vscale;
-    }
-  }
-  __syncthreads();
-  for (int dd = tid; dd < d; dd += blockDim.x) {
-    if constexpr (BITS == 4) {
-      uint32_t w[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          x |= (static_cast<uint32_t>(cbuf[(8 * q + e) * d + dd]) & 0xfu) << (4 * e);
-        w[q] = x;
-      }
-      *reinterpret_cast<u32x2*>(vdst + dd * (PAGE / 2)) = u32x2{w[0], w[1]};
-    } else {
-      uint32_t w[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t x = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          x |= (static_cast<uint32_t>(static_cast<uint8_t>(cbuf[(4 * q + e) * d + dd]))) << (8 * e);
-        w[q] = x;
-      }
-      *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
-    }
-  }
-  __syncthreads();
-}
-
 // Slot of ring page r, lane i: the ring holds positions [T - w, T), position t in slot
 // t mod w.  Returns the source row (t if t was kept, else -1) for lanes < PAGE.
 __device__ __forceinline__ int ring_src(const CompactArgs& a, const int* idx, int cnt, int nr, int r,
@@ -335,33 +249,122 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a
 
 // int8 pages: unit u is int8 page u of the pool; its pair is the last one whose page
 // base is <= u (pairs without int8 pages share the next pair's base).
-template <typename E, int BITS>
+// Low-precision pages, one wave per page over a contiguous range of pages (like the
+// copy kernel): the 16 source rows of K and of V are gathered as 16-byte chunks (a
+// row's chunks sit in consecutive lanes), each row's absmax is a shuffle reduction over
+// those lanes, K codes go straight to the token-major page, V codes through this wave's
+// LDS tile to the dim-major page.
+template <typename E, int D, int BITS>
 __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs a) {
-  __shared__ int src[PAGE];
-  __shared__ __attribute__((aligned(16))) int8_t cbuf[PAGE * 128];
+  constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;         // chunks per row (8 .. 32; divides 64)
+  constexpr int NPL = PAGE * CPR / 64; // chunks per lane
+  constexpr float QMAX = BITS == 4 ? 7.0f : 127.0f;
+  constexpr int CB = EPC * BITS / 8;   // code bytes per chunk (2 .. 8)
+  __shared__ int8_t vcodes[CPY_WAVES][PAGE * D];
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int8_t* vc = vcodes[wid];
   const int np = a.num_pairs;
-  const int d = a.d;
-  const int total8 = a.kv.page8_top[0];
-  for (int u = blockIdx.x; u < total8; u += gridDim.x) {
-    const int p = upper_segment(ws_p8base(a), np, u);
-    const int j8 = u - ws_p8base(a)[p];
+  const int* p8base = ws_p8base(a);
+  const int total = a.kv.page8_top[0];
+  const int nw = gridDim.x * CPY_WAVES;
+  const int per = cdiv(total, nw);
+  int u = (blockIdx.x * CPY_WAVES + wid) * per;
+  const int uend = min(total, u + per);
+  if (u >= uend) return;
+  int p = upper_segment(p8base, np, u);
+  int pb = p8base[p];
+  int pe = (p + 1 < np) ? p8base[p + 1] : total;
+  for (; u < uend; ++u) {
+    while (u >= pe) {  // next pair (a pair's pages are contiguous)
+      ++p;
+      pb = pe;
+      pe = (p + 1 < np) ? p8base[p + 1] : total;
+    }
+    const int j8 = u - pb;
     const int ne = ws_n8(a)[p];
-    if (j8 >= cdiv(ne, PAGE)) continue;  // uniform across the work-group
+    if (j8 >= cdiv(ne, PAGE)) continue;  // uniform across the wave
     const int cnt = a.kept_count[p];
     const int* idx = a.kept_idx + (int64_t)p * a.T;
-    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * d;
-    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * d;
-    if (threadIdx.x < PAGE) {
-      const int i = threadIdx.x;
-      const int s = (j8 * PAGE + i < ne) ? idx[cnt + j8 * PAGE + i] : -1;
-      src[i] = s;
-      a.kv.page8_pos[(int64_t)u * PAGE + i] = s;
+    const E* ksrc = reinterpret_cast<const E*>(a.k) + (int64_t)p * a.T * D;
+    const E* vsrc = reinterpret_cast<const E*>(a.v) + (int64_t)p * a.T * D;
+    int s = -1;  // lanes < PAGE: source row of slot `lane`
+    if (lane < PAGE) {
+      if (j8 * PAGE + lane < ne) s = idx[cnt + j8 * PAGE + lane];
+      a.kv.page8_pos[(int64_t)u * PAGE + lane] = s;
     }
-    if (threadIdx.x == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = u;
-    __syncthreads();
-    const int64_t page_bytes = (int64_t)PAGE * d * BITS / 8;
-    quant_page<E, BITS>(ksrc, vsrc, d, src, a.kv.k8_pages + u * page_bytes, a.kv.v8_pages + u * page_bytes,
-                        a.kv.k8_scale + (int64_t)u * PAGE, a.kv.v8_scale + (int64_t)u * PAGE, cbuf);
+    if (lane == 0) a.kv.block_table8[(int64_t)p * a.kv.max_pages8_per_pair + j8] = u;
+    u32x4 kx[NPL], vx[NPL];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i, row = c / CPR, col = (c % CPR) * EPC;
+      const int sr = __shfl(s, row);
+      kx[i] = u32x4{0u, 0u, 0u, 0u};
+      vx[i] = u32x4{0u, 0u, 0u, 0u};
+      if (sr >= 0) {
+        kx[i] = *reinterpret_cast<const u32x4*>(ksrc + (int64_t)sr * D + col);
+        vx[i] = *reinterpret_cast<const u32x4*>(vsrc + (int64_t)sr * D + col);
+      }
+    }
+    int8_t* kdst = a.kv.k8_pages + (int64_t)u * PAGE * D * BITS / 8;
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int c = lane + 64 * i, row = c / CPR, col = (c % CPR) * EPC;
+      const E* ke = reinterpret_cast<const E*>(&kx[i]);
+      const E* ve = reinterpret_cast<const E*>(&vx[i]);
+      float kf[EPC], vf[EPC], ka = 0.f, va = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        kf[e] = elem_to_f32<E>(ke[e]);
+        vf[e] = elem_to_f32<E>(ve[e]);
+        ka = fmaxf(ka, fabsf(kf[e]));
+        va = fmaxf(va, fabsf(vf[e]));
+      }
+#pragma unroll
+      for (int o = 1; o < CPR; o <<= 1) {  // the row's CPR chunks are CPR aligned lanes
+        ka = fmaxf(ka, __shfl_xor(ka, o));
+        va = fmaxf(va, __shfl_xor(va, o));
+      }
+      const float kscale = ka / QMAX, vscale = va / QMAX;
+      uint32_t w[2] = {0u, 0u};
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const uint32_t kc = static_cast<uint32_t>(quant_code(kf[e], kscale, QMAX));
+        if constexpr (BITS == 8) w[e / 4] |= (kc & 0xffu) << (8 * (e % 4));
+        else w[e / 8] |= (kc & 0xfu) << (4 * (e % 8));
+        vc[row * D + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale, QMAX));
+      }
+      int8_t* kd = kdst + (row * D + col) * BITS / 8;
+      if constexpr (CB == 8) *reinterpret_cast<u32x2*>(kd) = u32x2{w[0], w[1]};
+      else if constexpr (CB == 4) *reinterpret_cast<uint32_t*>(kd) = w[0];
+      else *reinterpret_cast<uint16_t*>(kd) = static_cast<uint16_t>(w[0]);
+      if ((c % CPR) == 0) {
+        a.kv.k8_scale[(int64_t)u * PAGE + row] = kscale;
+        a.kv.v8_scale[(int64_t)u * PAGE + row] = vscale;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    // V^T page: dim dd's 16 codes (int8: 16 bytes; int4: 8 bytes, token 2i in the low nibble)
+    int8_t* vdst = a.kv.v8_pages + (int64_t)u * PAGE * D * BITS / 8;
+#pragma unroll
+    for (int k = 0; k < D / 64; ++k) {
+      const int dd = lane + 64 * k;
+      uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int t = 0; t < PAGE; ++t) {
+        const uint32_t code = static_cast<uint32_t>(static_cast<int>(vc[t * D + dd]));
+        if constexpr (BITS == 8) w[t / 4] |= (code & 0xffu) << (8 * (t % 4));
+        else w[t / 8] |= (code & 0xfu) << (4 * (t % 8));
+      }
+      if constexpr (BITS == 8) *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
+      else *reinterpret_cast<u32x2*>(vdst + dd * (PAGE / 2)) = u32x2{w[0], w[1]};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
 }
 
@@ -409,14 +412,16 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
   KVP_LAUNCH_CHECK();
   if (demote) {
     const bool i4 = lp_bits_of(*kv) == 4;
-    if (bf && i4)
-      hipLaunchKernelGGL((compact_quant_kernel<uint16_t, 4>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
-    else if (bf)
-      hipLaunchKernelGGL((compact_quant_kernel<uint16_t, 8>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
-    else if (i4)
-      hipLaunchKernelGGL((compact_quant_kernel<float, 4>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
-    else
-      hipLaunchKernelGGL((compact_quant_kernel<float, 8>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
+    const dim3 g(CMP_GRID), b(CMP_THREADS);
+#define KVP_QUANT(E, DD, BB) hipLaunchKernelGGL((compact_quant_kernel<E, DD, BB>), g, b, 0, stream, a)
+    if (bf) {
+      if (d == 128) { if (i4) KVP_QUANT(uint16_t, 128, 4); else KVP_QUANT(uint16_t, 128, 8); }
+      else { if (i4) KVP_QUANT(uint16_t, 64, 4); else KVP_QUANT(uint16_t, 64, 8); }
+    } else {
+      if (d == 128) { if (i4) KVP_QUANT(float, 128, 4); else KVP_QUANT(float, 128, 8); }
+      else { if (i4) KVP_QUANT(float, 64, 4); else KVP_QUANT(float, 64, 8); }
+    }
+#undef KVP_QUANT
     KVP_LAUNCH_CHECK();
   }
   return KVP_OK;

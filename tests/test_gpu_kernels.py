@@ -196,19 +196,21 @@ def test_compact_exact(K, dtype, d, ring_w):
             assert np.array_equal(Sr, sb[p, rpos])
 
 
-@pytest.mark.parametrize("bits,d", [(8, 128), (4, 128), (4, 64)])
-def test_compact_demote_exact(K, bits, d):
+@pytest.mark.parametrize("bits,d,dtype", [(8, 128, torch.bfloat16), (4, 128, torch.bfloat16),
+                                          (4, 64, torch.bfloat16), (8, 64, torch.bfloat16),
+                                          (4, 128, torch.float32), (8, 64, torch.float32)])
+def test_compact_demote_exact(K, bits, d, dtype):
     B, Hkv, T = 2, 2, 500
     P = B * Hkv
-    k = seeded((B, Hkv, T, d), 41, torch.bfloat16)
-    v = seeded((B, Hkv, T, d), 42, torch.bfloat16, 3.0)
+    k = seeded((B, Hkv, T, d), 41, dtype)
+    v = seeded((B, Hkv, T, d), 42, dtype, 3.0)
     k[0, 0, 7] = 0  # all-zero row -> scale 0, codes 0
     s = seeded((B, Hkv, T), 43)
     keep = oracle.keep_mask(f64(s), 0.8, 128).reshape(P, T)
     idx, cnt = upload_selection(keep)
-    kv = K.PagedKV.allocate(P, d, P * 40, 40, torch.bfloat16, DEV, num_pages8=P * 40,
+    kv = K.PagedKV.allocate(P, d, P * 40, 40, dtype, DEV, num_pages8=P * 40,
                             max_pages8_per_pair=40, poison=True, lp_bits=bits)
-    ring = K.Ring.allocate(P, 128, d, torch.bfloat16, DEV, poison=True)
+    ring = K.Ring.allocate(P, 128, d, dtype, DEV, poison=True)
     K.kvp_compact(k, v, idx, cnt, kv, compact_ws(K, B, Hkv), ring=ring, scores=s,
                   mode=K.KVP_COMPACT_DEMOTE_INT8)
     assert K.kvp_check(kv) == 0
