@@ -273,10 +273,9 @@ __device__ __forceinline__ bool softmax_step(const AttnArgs& a, f32x4 sA, f32x4 
   u32x4 hi, lo;
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
-    uint16_t h0 = f32_to_bf16(p[2 * w]), h1 = f32_to_bf16(p[2 * w + 1]);
-    float r0 = p[2 * w] - bf16_to_f32(h0), r1 = p[2 * w + 1] - bf16_to_f32(h1);
-    hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    lo[w] = pack_bf16x2(r0, r1);
+    const u32x2 hl = split_bf16x2(p[2 * w], p[2 * w + 1]);
+    hi[w] = hl[0];
+    lo[w] = hl[1];
   }
   phi = as_bf16x8(hi);
   plo = as_bf16x8(lo);
@@ -610,13 +609,12 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
       u32x4 hi, lo;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float q0 = p[2 * w] * vsc[2 * w], q1 = p[2 * w + 1] * vsc[2 * w + 1];
-        const uint16_t h0 = f32_to_bf16(q0), h1 = f32_to_bf16(q1);
-        hi[w] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        const uint16_t l0 = f32_to_bf16(q0 - bf16_to_f32(h0)), l1 = f32_to_bf16(q1 - bf16_to_f32(h1));
-        lo[w] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        const u32x2 hl = split_bf16x2(p[2 * w] * vsc[2 * w], p[2 * w + 1] * vsc[2 * w + 1]);
+        hi[w] = hl[0];
+        lo[w] = hl[1];
         if constexpr (BITS == 4)  // exactly the weights the MFMAs see
-          psum += (bf16_to_f32(h0) + bf16_to_f32(l0)) + (bf16_to_f32(h1) + bf16_to_f32(l1));
+          psum += (__uint_as_float(hl[0] << 16) + __uint_as_float(hl[1] << 16)) +
+                  (__uint_as_float(hl[0] & 0xffff0000u) + __uint_as_float(hl[1] & 0xffff0000u));
       }
       const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
 #pragma unroll

@@ -364,9 +364,9 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
     }
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint16_t h0 = f32_to_bf16(wv[2 * q]), h1 = f32_to_bf16(wv[2 * q + 1]);
-      w2hi[kst][q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-      w2lo[kst][q] = pack_bf16x2(wv[2 * q] - bf16_to_f32(h0), wv[2 * q + 1] - bf16_to_f32(h1));
+      const u32x2 hl = split_bf16x2(wv[2 * q], wv[2 * q + 1]);
+      w2hi[kst][q] = hl[0];
+      w2lo[kst][q] = hl[1];
     }
   }
   float b1v[4][4];
@@ -392,9 +392,9 @@ __global__ __launch_bounds__(MLP_THREADS) __attribute__((amdgpu_waves_per_eu(2, 
       u32x4 uhi, ulo;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint16_t h0 = f32_to_bf16(u[2 * q]), h1 = f32_to_bf16(u[2 * q + 1]);
-        uhi[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-        ulo[q] = pack_bf16x2(u[2 * q] - bf16_to_f32(h0), u[2 * q + 1] - bf16_to_f32(h1));
+        const u32x2 hl = split_bf16x2(u[2 * q], u[2 * q + 1]);
+        uhi[q] = hl[0];
+        ulo[q] = hl[1];
       }
       sacc[nt] = mfma16x16x32(as_bf16x8(w2hi[kst]), as_bf16x8(uhi), sacc[nt]);
       sacc[nt] = mfma16x16x32(as_bf16x8(w2lo[kst]), as_bf16x8(uhi), sacc[nt]);
