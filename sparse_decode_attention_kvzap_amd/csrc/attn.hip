@@ -528,9 +528,12 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
   for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m = neg_inf();
   st.l = 0.f;
-  // int4: I4_OFFSET * (sum of this lane's head's query) comes off every score; psum
-  // tracks sum_t p_t over this lane's tokens (rescaled like o) for the output offset
-  float qoff = 0.f, psum = 0.f;
+  // int4: I4_OFFSET * (sum of this lane's head's query) comes off every score; psum is
+  // one more output tile, sum_t p_t per head, accumulated by MFMA from the same bf16
+  // weights as the outputs (a ones operand in place of V) and rescaled with them, so
+  // I4_OFFSET * psum is exactly the offset the decoded V values added
+  float qoff = 0.f;
+  f32x4 psum = {0.f, 0.f, 0.f, 0.f};
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
@@ -612,11 +615,13 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
         const u32x2 hl = split_bf16x2(p[2 * w] * vsc[2 * w], p[2 * w + 1] * vsc[2 * w + 1]);
         hi[w] = hl[0];
         lo[w] = hl[1];
-        if constexpr (BITS == 4)  // exactly the weights the MFMAs see
-          psum += (__uint_as_float(hl[0] << 16) + __uint_as_float(hl[1] << 16)) +
-                  (__uint_as_float(hl[0] & 0xffff0000u) + __uint_as_float(hl[1] & 0xffff0000u));
       }
       const bf16x8 phi = as_bf16x8(hi), plo = as_bf16x8(lo);
+      if constexpr (BITS == 4) {
+        const bf16x8 ones = as_bf16x8(u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u});
+        psum = mfma16x16x32(ones, phi, psum);
+        psum = mfma16x16x32(ones, plo, psum);
+      }
 #pragma unroll
       for (int t = 0; t < D / 16; ++t) {
         // every code decodes to a finite value and the weight of an unused slot is
@@ -684,9 +689,7 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
     }
   }
   if constexpr (BITS == 4) {
-    psum += __shfl_xor(psum, 16);
-    psum += __shfl_xor(psum, 32);
-    const float off = I4_OFFSET * psum;
+    const float off = I4_OFFSET * psum[0];  // every row of the tile holds the same sum
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) st.o[t] -= off;
   }
