@@ -856,7 +856,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else {
       if constexpr (!F32) {
 #ifndef LP_SETS4
-#define LP_SETS4 4
+#define LP_SETS4 2
 #endif
 #ifndef LP_SETS8
 #define LP_SETS8 2
