@@ -808,8 +808,10 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
 // -------------------------------------------------------------------------------
 // The kernel
 // -------------------------------------------------------------------------------
-template <int D, bool F32>
 // One work-group per CU (ATTN_GRID = 256), so a wave may use a whole SIMD's registers.
+// LP: the cache has a low-precision pool; the instantiation without one keeps the
+// code-pool path's register needs out of the bf16 loop's allocation.
+template <int D, bool F32, bool LP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_attn_kernel(AttnArgs a) {
   extern __shared__ int lds[];
   Plan pl = build_plan(a, lds);
@@ -854,7 +856,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         run_region_a_bf16<D>(a, pl, s, v0, v1, slot, wmask);
       }
     } else {
-      if constexpr (!F32) {
+      if constexpr (!F32 && LP) {
 #ifndef LP_SETS4
 #define LP_SETS4 2
 #endif
@@ -1013,11 +1015,17 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
   const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32);
   if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
   if (f32) {
-    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
-    else hipLaunchKernelGGL((decode_attn_kernel<128, true>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, true, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
   } else {
-    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
-    else hipLaunchKernelGGL((decode_attn_kernel<128, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    const dim3 g(ATTN_GRID), b(256);
+    if (kv->num_pages8 > 0) {
+      if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true>), g, b, lds, stream, a);
+      else hipLaunchKernelGGL((decode_attn_kernel<128, false, true>), g, b, lds, stream, a);
+    } else {
+      if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, false>), g, b, lds, stream, a);
+      else hipLaunchKernelGGL((decode_attn_kernel<128, false, false>), g, b, lds, stream, a);
+    }
   }
   KVP_LAUNCH_CHECK();
   const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
