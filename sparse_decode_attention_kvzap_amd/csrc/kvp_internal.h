@@ -23,13 +23,10 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN stays NaN): gfx950 converts in
-// hardware (v_cvt_pk_bf16_f32), two values per instruction.
+// Two fp32 -> packed bf16x2 (low half = a), round to nearest even (NaN stays NaN):
+// gfx950 converts in hardware (v_cvt_pk_bf16_f32), two values per instruction.
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
-
-// Two fp32 -> packed bf16x2 (low half = a), round to nearest even.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
