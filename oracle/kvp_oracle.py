@@ -230,6 +230,54 @@ def dms_visible(flags: np.ndarray, p: int, w: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------------
+# Prefill attention under eviction  [DMS, "Delayed Eviction"; KVzap, practical
+# application]
+# ----------------------------------------------------------------------------------
+
+
+def prefill_visible(keep: np.ndarray, W: int) -> np.ndarray:
+    """Which keys each prompt position sees while the prompt itself is processed.
+
+    Reading: every prompt position is a step of the sequence, so query position i sees
+    what a decode step at length i + 1 sees: a key j <= i that is kept, or that is one
+    of the last W positions (i - j < W).  KVzap: keep = (s >= tau), W = R (the recent
+    window); DMS: keep = not flagged, W = w (the eviction delay).
+    keep: [..., T] bool.  Returns [..., T (query), T (key)] bool.
+    """
+    keep = np.asarray(keep, dtype=bool)
+    T = keep.shape[-1]
+    i = np.arange(T)[:, None]
+    j = np.arange(T)[None, :]
+    return (j <= i) & (keep[..., None, :] | ((i - j) < W))
+
+
+def prefill_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, keep: np.ndarray, W: int,
+                      scale: float) -> np.ndarray:
+    """Masked causal attention of every prompt position (GQA, contiguous head groups).
+
+    q: [B,Hq,T,d]; K, V: [B,Hkv,T,d]; keep: [B,Hkv,T] bool.  Row i of query head jq is
+    softmax(scale * K q_i) V over the keys prefill_visible marks for position i; a row
+    with no visible key is 0.  Returns [B,Hq,T,d] float64.
+    """
+    B, Hq, T, d = q.shape
+    Hkv = K.shape[1]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, T, d), dtype=np.float64)
+    for b in range(B):
+        for h in range(Hkv):
+            vis = prefill_visible(keep[b, h], W)
+            for jq in range(h * g, (h + 1) * g):
+                logits = (q[b, jq] @ K[b, h].T) * np.float64(scale)
+                logits = np.where(vis, logits, -np.inf)
+                m = logits.max(axis=1, keepdims=True)
+                ok = np.isfinite(m[:, 0])
+                e = np.where(vis, np.exp(logits - np.where(ok[:, None], m, 0.0)), 0.0)
+                den = e.sum(axis=1, keepdims=True)
+                out[b, jq] = np.where(ok[:, None], (e @ V[b, h]) / np.where(ok[:, None], den, 1.0), 0.0)
+    return out
+
+
+# ----------------------------------------------------------------------------------
 # BeaconKV mixed precision  [BeaconKV, body and FAQ on how memory is saved]
 # ----------------------------------------------------------------------------------
 

@@ -369,6 +369,79 @@ def test_dms_keep_fraction_statistics():
     assert abs(n - mean) < 5 * sd
 
 
+# ------------------------------------------------------------------ prefill under eviction
+
+
+def _sdpa_prefill(q, K, V, mask, scale):
+    # torch fp64 SDPA with a [B,Hkv,T,T] boolean mask, KV heads expanded (library routine)
+    g = q.shape[1] // K.shape[1]
+    Kx = torch.from_numpy(K).repeat_interleave(g, dim=1)
+    Vx = torch.from_numpy(V).repeat_interleave(g, dim=1)
+    mx = torch.from_numpy(mask).repeat_interleave(g, dim=1)
+    return torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), Kx, Vx, attn_mask=mx, scale=float(scale)).numpy()
+
+
+def test_prefill_visible_rows_match_the_decode_rules():
+    rng = np.random.default_rng(30)
+    T = 300
+    s = rng.standard_normal((2, T)) - 0.8
+    tau, R = 0.1, 128
+    vis = oracle.prefill_visible(s >= tau, R)
+    flags = oracle.dms_evict_flags(s)
+    dvis = oracle.prefill_visible(~flags, 17)
+    for i in range(T):
+        # query position i sees what the decode step at length i + 1 sees
+        assert np.array_equal(vis[:, i, :i + 1], oracle.kvzap_visible_at_decode(s, tau, R, i))
+        assert not vis[:, i, i + 1:].any()
+        assert np.array_equal(dvis[:, i, :i + 1], oracle.dms_visible(flags, i, 17))
+        assert not dvis[:, i, i + 1:].any()
+    # brute force on a tiny case
+    keep = np.array([True, False, False, True, False, False])
+    W = 2
+    bf = np.zeros((6, 6), bool)
+    for i in range(6):
+        for j in range(6):
+            bf[i, j] = j <= i and (keep[j] or i - j < W)
+    assert np.array_equal(oracle.prefill_visible(keep, W), bf)
+
+
+def test_prefill_attention_equals_masked_sdpa_and_special_cases():
+    rng = np.random.default_rng(31)
+    B, Hq, Hkv, T, d, W = 2, 6, 2, 90, 8, 16
+    q = rng.standard_normal((B, Hq, T, d))
+    K = rng.standard_normal((B, Hkv, T, d)) * 2
+    V = rng.standard_normal((B, Hkv, T, d))
+    keep = rng.random((B, Hkv, T)) < 0.3
+    scale = oracle.sm_scale(d)
+    got = oracle.prefill_attention(q, K, V, keep, W, scale)
+    # a mask built by explicit loops, attention by the library routine
+    mask = np.zeros((B, Hkv, T, T), bool)
+    for b in range(B):
+        for h in range(Hkv):
+            for i in range(T):
+                for j in range(i + 1):
+                    mask[b, h, i, j] = keep[b, h, j] or i - j < W
+    assert np.allclose(got, _sdpa_prefill(q, K, V, mask, scale), atol=1e-12, rtol=0)
+    # keep-all is causal attention
+    allk = np.ones((B, Hkv, T), bool)
+    causal = np.broadcast_to(np.tril(np.ones((T, T), bool)), (B, Hkv, T, T)).copy()
+    assert np.allclose(oracle.prefill_attention(q, K, V, allk, W, scale),
+                       _sdpa_prefill(q, K, V, causal, scale), atol=1e-12, rtol=0)
+    # keep-none is a sliding window of W positions (current one included)
+    band = causal & (np.arange(T)[:, None] - np.arange(T)[None, :] < W)
+    assert np.allclose(oracle.prefill_attention(q, K, V, ~allk, W, scale),
+                       _sdpa_prefill(q, K, V, band, scale), atol=1e-12, rtol=0)
+    # row i equals one decode step at length i + 1 with its own query
+    for i in (0, 1, W - 1, W, 57, T - 1):
+        vis = oracle.prefill_visible(keep, W)[:, :, i, :i + 1]
+        ref = oracle.decode_attention(q[:, :, i], K[:, :, :i + 1], V[:, :, :i + 1], vis, scale)
+        assert np.allclose(got[:, :, i], ref, atol=1e-13, rtol=0)
+    # W = 0 and nothing kept: no visible key, a zero row
+    z = oracle.prefill_attention(q[:1, :3], K[:1, :1], V[:1, :1], ~allk[:1, :1], 0, scale)
+    assert np.array_equal(z, np.zeros_like(z))
+
+
 # ------------------------------------------------------------------ BeaconKV int8
 
 
