@@ -296,6 +296,30 @@ size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                       int32_t head_dim);
 
 /* ----------------------------------------------------------------------------
+ * kvp_prefill_attn - causal attention of every prompt position over the keys the
+ * cache still holds for it.
+ * Source: DMS "Delayed Eviction" (a flagged token stays readable for a window of
+ * steps, then leaves); KVzap key points (low-scoring entries removed, recent ones
+ * kept).  Position i of the prompt sees key j iff j <= i and (keep bit j is set or
+ * i - j < window): what the decode step at length i + 1 sees.  KVzap: the selection
+ * of kvp_select(tau, recent) with window = recent; DMS: kvp_select(0, w) with
+ * window = w.
+ *   q          [B][Hq][T][d] bf16; query head j reads KV head j / g, g = Hq / Hkv
+ *   k, v       [B][Hkv][T][d] bf16 (dtype must be KVP_BF16), finite
+ *   keep_bits  [B*Hkv][ceil(T/32)] u32, bit t%32 of word t/32 (tail bits ignored)
+ *   kept_idx   [B*Hkv][T] i32 whose first (number of set bits) entries are the kept
+ *              positions ascending -- as written by kvp_select for the same keep bits
+ *   out        [B][Hq][T][d] fp32: softmax(sm_scale * K q_i) V over the keys position
+ *              i sees; a row that sees no key (window 0, nothing kept before it) is 0
+ * g in {1, 2, 4, 8} and d in {64, 128} (else KVP_E_UNSUPPORTED); T >= 1, window >= 0.
+ * All buffers are caller-owned device memory; no workspace, no allocation.
+ * -------------------------------------------------------------------------- */
+kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t dtype,
+                            int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                            const uint32_t* keep_bits, const int32_t* kept_idx,
+                            int32_t window, float sm_scale, float* out, hipStream_t stream);
+
+/* ----------------------------------------------------------------------------
  * Helpers.
  * kvp_reset: empty the pools (lengths 0, page_top 0) and, if ring != NULL, the
  *            ring (pos -1).  Stream-ordered, no allocation.

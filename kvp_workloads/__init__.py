@@ -190,6 +190,11 @@ def queries(wl: Workload, device="cpu", stream="q") -> torch.Tensor:
     return normal((wl.B, wl.Hq, wl.d), wl.kv_dtype, wl.seed(stream), device)
 
 
+def prompt_queries(wl: Workload, T: int, device="cpu", stream="prompt_q") -> torch.Tensor:
+    """Queries of every prompt position [B, Hq, T, d] ~ N(0,1) in the KV dtype."""
+    return normal((wl.B, wl.Hq, T, wl.d), wl.kv_dtype, wl.seed(stream), device)
+
+
 def step_inputs(wl: Workload, step: int, device="cpu"):
     """Per-decode-step draws: new hidden [B,1,H], k/v [B,Hkv,d], q [B,Hq,d]."""
     tag = f"step{step}_"

@@ -96,6 +96,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
         "kvp_decode_attn_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+        "kvp_prefill_attn": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                       c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
+                                       c_float, c_void_p, c_void_p]),
         "kvp_reset": (c_int32, [P(KvpPagedKV), P(KvpRing), c_void_p]),
         "kvp_clear_error": (c_int32, [P(KvpPagedKV), c_void_p]),
         "kvp_check": (c_int32, [P(KvpPagedKV), c_void_p]),
@@ -304,6 +307,25 @@ def kvp_select(scores: torch.Tensor, T: int, tau, recent: int, keep_bits: torch.
     else:
         _ok(load().kvp_select(scores.data_ptr(), B, Hkv, T, ld_s, float(tau), recent, *args),
             "kvp_select")
+
+
+def kvp_prefill_attn(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, keep_bits: torch.Tensor,
+                     kept_idx: torch.Tensor, window: int, sm_scale: float, out: torch.Tensor,
+                     stream=None) -> torch.Tensor:
+    """q [B, Hq, T, d], k/v [B, Hkv, T, d] bf16; keep_bits [B*Hkv, ceil(T/32)] and
+    kept_idx [B*Hkv, T] (as written by kvp_select) -> out [B, Hq, T, d] fp32."""
+    _cuda(q, k, v, keep_bits, kept_idx, out)
+    B, Hq, T, d = q.shape
+    Hkv = k.shape[1]
+    assert tuple(k.shape) == (B, Hkv, T, d) and k.shape == v.shape and tuple(out.shape) == (B, Hq, T, d)
+    assert q.dtype == k.dtype == v.dtype and out.dtype == torch.float32
+    assert all(t.is_contiguous() for t in (q, k, v, keep_bits, kept_idx, out))
+    assert keep_bits.numel() >= B * Hkv * ((T + 31) // 32) and kept_idx.numel() >= B * Hkv * T
+    _ok(load().kvp_prefill_attn(q.data_ptr(), k.data_ptr(), v.data_ptr(), _dt(q), B, Hq, Hkv, T, d,
+                                keep_bits.data_ptr(), kept_idx.data_ptr(), int(window),
+                                float(sm_scale), out.data_ptr(), _stream(stream)),
+        "kvp_prefill_attn")
+    return out
 
 
 def kvp_threshold_workspace_size() -> int:

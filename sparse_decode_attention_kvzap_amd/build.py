@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkvp.so")
 
-SOURCES = ["kvp_api.hip", "score.hip", "select.hip", "threshold.hip", "compact.hip", "step.hip", "attn.hip"]
+SOURCES = ["kvp_api.hip", "score.hip", "select.hip", "threshold.hip", "compact.hip", "step.hip", "attn.hip", "prefill.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-I", INCLUDE, "-I", CSRC,

@@ -23,6 +23,9 @@ kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   hipStream_t stream);
+kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                                   int T, int d, const uint32_t* keep_bits, const int* kept_idx,
+                                   int window, float sm_scale, float* out, hipStream_t stream);
 kvp_status kvp_launch_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream);
 kvp_status kvp_launch_clear_error(const kvp_paged_kv* kv, hipStream_t stream);
 size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32);
@@ -209,6 +212,22 @@ extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, 
   if (!ws || ws_bytes < kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs, kv->head_dim))
     return KVP_E_WORKSPACE;
   return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream);
+}
+
+extern "C" kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t dtype,
+                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t T, int32_t d,
+                                       const uint32_t* keep_bits, const int32_t* kept_idx,
+                                       int32_t window, float sm_scale, float* out, hipStream_t stream) {
+  if (!q || !k || !v || !keep_bits || !kept_idx || !out) return KVP_E_ARG;
+  if (dtype != KVP_BF16) return is_kv_dtype(dtype) ? KVP_E_UNSUPPORTED : KVP_E_DTYPE;
+  if (B <= 0 || Hkv <= 0 || Hq <= 0 || T <= 0 || window < 0) return KVP_E_ARG;
+  if (Hq % Hkv != 0) return KVP_E_ARG;
+  const int g = Hq / Hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8) return KVP_E_UNSUPPORTED;
+  if (d != 64 && d != 128) return KVP_E_UNSUPPORTED;
+  if ((int64_t)B * Hkv > 65535 || T > kMaxTokens) return KVP_E_UNSUPPORTED;
+  return kvp_launch_prefill_attn(q, k, v, B, Hq, Hkv, T, d, keep_bits, kept_idx, window, sm_scale, out,
+                                 stream);
 }
 
 extern "C" kvp_status kvp_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream) {

@@ -1,0 +1,380 @@
+// Prefill attention under eviction (gfx950): every prompt position attends, causally,
+// to the keys the cache still holds for it.
+//
+// Method: DMS briefing, "Delayed Eviction" (a flagged token stays readable for a window
+// of steps, then leaves the cache); KVzap digest, key points (low-scoring entries are
+// removed, the most recent ones always kept).  Prompt position i sees key j iff
+// j <= i and (keep_j or i - j < W): what the decode step at length i + 1 sees.
+//
+// Work decomposition: one work-group (4 waves) per (pair (b, h_kv), block of
+// PB = 128 / g positions).  Its 128 query rows are the g query heads of the pair times
+// the PB positions; each wave owns 32 rows as two 16-row column tiles (one head, 16
+// consecutive positions each).  The keys a block needs are
+//   - the kept keys below lo64 = floor64(max(0, i0 - W + 1)): every row of the block
+//     sees all of them, so they carry no mask except the last tile's tail; they are
+//     gathered in ascending order through kept_idx, and
+//   - the band [lo64, min(T, i0 + PB)): dense, masked per row with the keep bits.
+// Both are walked in 64-key tiles staged through LDS: K row-major with its 16-byte
+// chunks swizzled per row, V transposed to [d][key] on the way in (register byte
+// permutes, then 8-byte LDS writes), so every MFMA operand is one 16-byte LDS read.
+// The next tile's K/V rows are loaded into registers while the current one is used;
+// the next-but-one tile's kept_idx entries are loaded a tile earlier still.
+//
+// Per 32-key chunk and column tile: S^T = K Q^T on 16x16x32 bf16 MFMA (exact
+// products, fp32 accumulation), with the K rows of the two 16-row MFMA tiles
+// interleaved so each lane holds the scores of 8 consecutive keys of one query row --
+// the B-operand layout of the P.V product that follows.  Online softmax in fp32 (log2
+// domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits).
+// Work-groups are numbered heavy-first (the last position blocks see the most keys),
+// and a pair's blocks share one XCD (pair = blockIdx % num_pairs, num_pairs % 8 == 0
+// in the common shapes) so its K/V rows are reused from that XCD's L2.
+#include "kvp_internal.h"
+
+namespace kvp {
+
+constexpr int PF_KT = 64;      // keys per LDS tile
+constexpr int PF_THREADS = 256;
+
+struct PrefillArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* out;
+  const uint32_t* keep_bits;
+  const int* kept_idx;
+  int Hq, Hkv, T, g, pb, nblk, window, words, num_pairs;
+  float scale_log2;  // sm_scale * log2(e)
+};
+
+// K tile: row r (key slot), 16-byte chunk c stored at chunk c ^ k_swz(r).  The 16 rows
+// one MFMA operand read touches (slots 8q + m and 8q + 4 + m, q, m < 4) map to 16
+// distinct chunk positions (D = 128) or to distinct (row parity, chunk) pairs (D = 64).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  if constexpr (D == 128) return (((r >> 3) & 3) << 2) | (r & 3);
+  else return (((r >> 3) & 3) << 1) | ((r >> 1) & 1);
+}
+// V^T tile: row d (64 keys = eight 16-byte units), unit u stored at u ^ v_swz(d).
+__device__ __forceinline__ int v_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+struct PfTile {
+  int prefix;  // 1: slots [base, base + 64) of the pair's kept list; 0: positions
+  int base;
+  int valid;   // valid slots in [0, 64]
+};
+
+__device__ __forceinline__ PfTile pf_tile(int tau, int ntp, int nk, int lo64, int hi) {
+  PfTile t;
+  if (tau < ntp) {
+    t.prefix = 1;
+    t.base = tau * PF_KT;
+    t.valid = min(PF_KT, nk - t.base);
+  } else {
+    t.prefix = 0;
+    t.base = lo64 + (tau - ntp) * PF_KT;
+    t.valid = min(PF_KT, hi - t.base);
+  }
+  return t;
+}
+
+// This thread's share of a tile: KG = D / 32 consecutive key slots, 16-byte chunk dc.
+template <int D>
+struct PfRegs {
+  static constexpr int KG = D / 32;
+  u32x4 k[KG];
+  u32x4 v[KG];
+};
+
+// Positions of this thread's slots in a tile (-1: empty slot).  Prefix tiles read
+// kept_idx (the pair's kept positions, ascending).
+template <int D>
+__device__ __forceinline__ void pf_positions(const PrefillArgs& a, const int* kidx, const PfTile& t,
+                                             int s0, int (&pos)[D / 32]) {
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r) {
+    const int slot = s0 + r;
+    if (slot < t.valid) pos[r] = t.prefix ? kidx[t.base + slot] : t.base + slot;
+    else pos[r] = -1;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pf_load(const uint16_t* kp, const uint16_t* vp, int dc,
+                                        const int (&pos)[D / 32], PfRegs<D>& R) {
+#pragma unroll
+  for (int r = 0; r < D / 32; ++r) {
+    if (pos[r] >= 0) {
+      const int64_t off = (int64_t)pos[r] * D + 8 * dc;
+      R.k[r] = *reinterpret_cast<const u32x4*>(kp + off);
+      R.v[r] = *reinterpret_cast<const u32x4*>(vp + off);
+    } else {
+      R.k[r] = u32x4{0u, 0u, 0u, 0u};
+      R.v[r] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// Registers -> LDS.  K rows keep their layout (swizzled chunk); V is transposed: for
+// each of the thread's 8 head-dim elements, its KG keys' values are packed with byte
+// permutes into one 8-byte (KG = 4) or 4-byte (KG = 2) LDS write.
+template <int D>
+__device__ __forceinline__ void pf_store(uint16_t* ks, uint16_t* vt, int dc, int s0, const PfRegs<D>& R) {
+  constexpr int KG = D / 32;
+#pragma unroll
+  for (int r = 0; r < KG; ++r) {
+    const int row = s0 + r;
+    *reinterpret_cast<u32x4*>(ks + row * D + 8 * (dc ^ k_swz<D>(row))) = R.k[r];
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * dc + e;
+    const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+    uint16_t* dst = vt + d * PF_KT + 8 * ((s0 >> 3) ^ v_swz(d)) + (s0 & 7);
+    if constexpr (KG == 4) {
+      u32x2 w;
+      w[0] = __builtin_amdgcn_perm(R.v[1][e >> 1], R.v[0][e >> 1], sel);
+      w[1] = __builtin_amdgcn_perm(R.v[3][e >> 1], R.v[2][e >> 1], sel);
+      *reinterpret_cast<u32x2*>(dst) = w;
+    } else {
+      *reinterpret_cast<uint32_t*>(dst) = __builtin_amdgcn_perm(R.v[1][e >> 1], R.v[0][e >> 1], sel);
+    }
+  }
+}
+
+__device__ __forceinline__ uint32_t low_bits(int n) {
+  n = max(0, min(8, n));
+  return (1u << n) - 1u;
+}
+
+template <int D>
+__global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_attn_kernel(
+    PrefillArgs a) {
+  constexpr int KG = D / 32;
+  constexpr int DC = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ks[PF_KT * D];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[D * PF_KT];
+  __shared__ int red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 15, G = lane >> 4;
+  const int pair = blockIdx.x % a.num_pairs;
+  const int blk = a.nblk - 1 - blockIdx.x / a.num_pairs;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  const int T = a.T;
+  const int i0 = blk * a.pb;
+  const int lo64 = max(0, i0 - a.window + 1) & ~(PF_KT - 1);
+  const int hi = min(T, i0 + a.pb);
+
+  // kept keys below lo64: popcount of the keep words [0, lo64 / 32)
+  const uint32_t* kb = a.keep_bits + (int64_t)pair * a.words;
+  int cnt = 0;
+  for (int w = tid; w < lo64 / 32; w += PF_THREADS) cnt += __builtin_popcount(kb[w]);
+  cnt = wave_sum_i(cnt);
+  if (lane == 0) red[wid] = cnt;
+  __syncthreads();
+  const int nk = __builtin_amdgcn_readfirstlane(red[0] + red[1] + red[2] + red[3]);
+  const int ntp = (nk + PF_KT - 1) / PF_KT;
+  const int ntiles = ntp + (hi - lo64 + PF_KT - 1) / PF_KT;
+
+  const int64_t kv_row0 = (int64_t)pair * T;
+  const uint16_t* kp = a.k + kv_row0 * D;
+  const uint16_t* vp = a.v + kv_row0 * D;
+  const int* kidx = a.kept_idx + kv_row0;
+  const int dc = tid % DC, s0 = KG * (tid / DC);
+
+  // this lane's two query rows (column tiles): head and position
+  int hq[2], qi[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int r0 = 32 * wid + 16 * c;
+    hq[c] = h * a.g + r0 / a.pb;
+    qi[c] = i0 + r0 % a.pb + n;
+  }
+  bf16x8 qf[2][D / 32];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint16_t* qrow = a.q + (((int64_t)b * a.Hq + hq[c]) * T + qi[c]) * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (qi[c] < T) x = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * kk + G));
+      qf[c][kk] = as_bf16x8(x);
+    }
+  }
+
+  f32x4 o[D / 16][2];
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) o[t][0] = o[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m[2] = {neg_inf(), neg_inf()}, l[2] = {0.f, 0.f};
+
+  // prologue: tile 0 in registers, tile 1's positions requested
+  PfRegs<D> R;
+  int pos[KG];
+  {
+    const PfTile t0 = pf_tile(0, ntp, nk, lo64, hi);
+    pf_positions<D>(a, kidx, t0, s0, pos);
+    pf_load<D>(kp, vp, dc, pos, R);
+    if (ntiles > 1) pf_positions<D>(a, kidx, pf_tile(1, ntp, nk, lo64, hi), s0, pos);
+  }
+
+  const int slotA = 8 * (n >> 2) + (n & 3);
+  for (int tau = 0; tau < ntiles; ++tau) {
+    const PfTile tl = pf_tile(tau, ntp, nk, lo64, hi);
+    __syncthreads();  // the previous tile's LDS reads are done
+    pf_store<D>(ks, vt, dc, s0, R);
+    __syncthreads();
+    if (tau + 1 < ntiles) {
+      pf_load<D>(kp, vp, dc, pos, R);
+      if (tau + 2 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 2, ntp, nk, lo64, hi), s0, pos);
+    }
+
+    uint32_t kw[2] = {0u, 0u};
+    if (!tl.prefix) {
+      const int w0 = tl.base >> 5;
+      kw[0] = kb[w0];
+      kw[1] = (w0 + 1 < a.words) ? kb[w0 + 1] : 0u;
+    }
+
+#pragma unroll
+    for (int ch = 0; ch < 2; ++ch) {
+      if (PF_KT / 2 * ch >= tl.valid) break;
+      // S^T for both column tiles
+      const int ra = PF_KT / 2 * ch + slotA, rb = ra + 4;
+      f32x4 sA[2], sB[2];
+      sA[0] = sA[1] = sB[0] = sB[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int cc = 4 * kk + G;
+        const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + ra * D + 8 * (cc ^ k_swz<D>(ra))));
+        const bf16x8 kb8 = as_bf16x8(*reinterpret_cast<const u32x4*>(ks + rb * D + 8 * (cc ^ k_swz<D>(rb))));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          sA[c] = mfma16x16x32(ka, qf[c][kk], sA[c]);
+          sB[c] = mfma16x16x32(kb8, qf[c][kk], sB[c]);
+        }
+      }
+
+      // visibility of this lane's 8 keys (slots 32 ch + 8 G + e) for each column tile
+      const int e0 = PF_KT / 2 * ch + 8 * G;
+      uint32_t vis[2];
+      bool full = false;
+      if (tl.prefix) {
+        vis[0] = vis[1] = low_bits(tl.valid - e0);
+        full = tl.valid == PF_KT;
+      } else {
+        const uint32_t keep8 = (kw[ch] >> (8 * G)) & 0xffu;
+        const int j0 = tl.base + e0;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const uint32_t causal = low_bits(qi[c] - j0 + 1);
+          const uint32_t win = 0xffu & ~low_bits(qi[c] - a.window + 1 - j0);
+          vis[c] = causal & (keep8 | win);
+        }
+      }
+
+      bf16x8 phi[2], plo[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        float s[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[e] = sA[c][e] * a.scale_log2;
+          s[e + 4] = sB[c][e] * a.scale_log2;
+        }
+        if (!full) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s[e] = ((vis[c] >> e) & 1u) ? s[e] : neg_inf();
+        }
+        float mx = s[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mnew = fmaxf(m[c], mx);
+        const float mref = (mnew == neg_inf()) ? 0.f : mnew;
+        const float alpha = exp2f(m[c] - mref);
+        float p[8], psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          p[e] = exp2f(s[e] - mref);
+          psum += p[e];
+        }
+        l[c] = l[c] * alpha + psum;
+        m[c] = mnew;
+        if (__ballot(alpha != 1.0f) != 0) {
+#pragma unroll
+          for (int t = 0; t < D / 16; ++t) o[t][c] *= alpha;
+        }
+        u32x4 ph, pl;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const u32x2 hl = split_bf16x2(p[2 * w], p[2 * w + 1]);
+          ph[w] = hl[0];
+          pl[w] = hl[1];
+        }
+        phi[c] = as_bf16x8(ph);
+        plo[c] = as_bf16x8(pl);
+      }
+
+      // O^T += V^T P^T
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) {
+        const int d = 16 * t + n;
+        const bf16x8 vf =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + d * PF_KT + 8 * ((4 * ch + G) ^ v_swz(d))));
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          o[t][c] = mfma16x16x32(vf, phi[c], o[t][c]);
+          o[t][c] = mfma16x16x32(vf, plo[c], o[t][c]);
+        }
+      }
+    }
+  }
+
+  // normalise and store: lane (n, G) holds d = 16 t + 4 G + (0..3) of its column's row
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float lt = l[c];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    if (qi[c] < T) {
+      float* orow = a.out + (((int64_t)b * a.Hq + hq[c]) * T + qi[c]) * D + 4 * G;
+#pragma unroll
+      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(orow + 16 * t) = o[t][c] * inv;
+    }
+  }
+}
+
+}  // namespace kvp
+
+using namespace kvp;
+
+kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
+                                   int T, int d, const uint32_t* keep_bits, const int* kept_idx,
+                                   int window, float sm_scale, float* out, hipStream_t stream) {
+  PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = out;
+  a.keep_bits = keep_bits;
+  a.kept_idx = kept_idx;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.T = T;
+  a.g = Hq / Hkv;
+  a.pb = 128 / a.g;
+  a.nblk = cdiv(T, a.pb);
+  a.window = window;
+  a.words = cdiv(T, 32);
+  a.num_pairs = B * Hkv;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  const int64_t grid = (int64_t)a.nblk * a.num_pairs;
+  if (grid > 0x7fffffff) return KVP_E_UNSUPPORTED;
+  if (d == 128) prefill_attn_kernel<128><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
+  else prefill_attn_kernel<64><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
+}

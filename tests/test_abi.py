@@ -191,6 +191,18 @@ def test_host_validation_without_device(L):
                                     L.KVP_BF16, fake, 1, None, fake, None) == E_ARG
     assert lib.kvp_step_delayed_dev(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
                                     L.KVP_BF16, fake, 1, fake, None, None) == E_ARG
+    # prefill attention: nulls, fp32 (not built), bad dtype, head ratio, head dim, window
+    pf = lib.kvp_prefill_attn
+    assert pf(None, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_ARG
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, None, 16, 0.1, fake, None) == E_ARG
+    assert pf(fake, fake, fake, L.KVP_F32, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
+    assert pf(fake, fake, fake, 9, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_DTYPE
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 6, 4, 64, 128, fake, fake, 16, 0.1, fake, None) == E_ARG
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 32, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 12, 4, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 96, fake, fake, 16, 0.1, fake, None) == E_UNSUP
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, -1, 0.1, fake, None) == E_ARG
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 0, 128, fake, fake, 16, 0.1, fake, None) == E_ARG
 
 
 def test_missing_library_fails_loudly(L, tmp_path):
