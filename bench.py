@@ -60,6 +60,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=16, help="batch rows in the CPU sample")
     ap.add_argument("--no-scaling", action="store_true",
                     help="skip the keep-ratio sweep (profiling runs of the headline workload)")
+    ap.add_argument("--no-prefill-attn", action="store_true",
+                    help="skip the prefill-attention-under-eviction measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
                          "kernel that scales the FETCH_SIZE / WRITE_SIZE counters)")
@@ -263,6 +265,14 @@ def main():
         f"attn {e['attn_isolated_ms']:.3f} ms (x{e['attn_ratio_vs_keep1']:.2f}), bytes x{e['bytes_ratio_vs_keep1']:.2f}"
         for e in keep_scaling))
 
+    prefill_attn = None
+    if not args.no_prefill_attn and wl.kv_dtype == torch.bfloat16 and not wl.int8_demote:
+        prefill_attn = measure_prefill_attn(K, W, wl, cache, kd, vd, T0, dev)
+        log(f"[bench] prefill attention under eviction (keep {1 - q_keep:.2f}, window {wl.R}): "
+            f"{prefill_attn['ms']:.2f} ms, {prefill_attn['tflops']:.0f} TFLOP/s useful "
+            f"({100 * prefill_attn['frac_of_bf16_peak']:.1f}% of the bf16 dense peak), "
+            f"visible keys {prefill_attn['visible_fraction']:.3f} of causal")
+
     # algorithmic work per call
     elt = 2 if wl.kv_dtype == torch.bfloat16 else 4
     ntok = B * T0
@@ -294,6 +304,7 @@ def main():
         "step_delayed": {"ms": per_call["step_delayed"], "gbs": gbs(step_bytes, per_call["step_delayed"])},
         "decode_attn": {"ms": per_call["decode_attn"], "gbs": gbs(kv_bytes_attn, per_call["decode_attn"]),
                         "token_heads_per_s": visible / (per_call["decode_attn"] * 1e-3)},
+        "prefill_attn": prefill_attn,
         "decode_attn_isolated": {"ms": attn_iso_ms, "gbs": gbs(kv_bytes_attn, attn_iso_ms),
                                  "frac_of_peak": gbs(kv_bytes_attn, attn_iso_ms) / PEAK_HBM_GBS,
                                  "token_heads_per_s": visible / (attn_iso_ms * 1e-3),
@@ -349,6 +360,41 @@ def main():
         "keep_scaling": keep_scaling,
     }
     print(json.dumps(line), flush=True)
+
+
+def measure_prefill_attn(K, W, wl, cache, kd, vd, T0, dev, reps=3) -> dict:
+    """kvp_prefill_attn over the prompt under the headline selection: every prompt
+    position attends to the kept keys before it plus the last `window` positions.
+    Useful work = 4 d flop per (query row, visible key) pair (QK^T and PV)."""
+    import torch
+    cache.select(T0)
+    qp = W.prompt_queries(wl, T0, dev)
+    out = torch.empty((wl.B, wl.Hq, T0, wl.d), dtype=torch.float32, device=dev)
+    R = cache.window
+    keep = (cache.scores[:, :, :T0] >= cache.tau_dev).reshape(cache.P, T0)
+    ck = torch.cumsum(keep.to(torch.int32), dim=1)
+    i = torch.arange(T0, device=dev)
+    before = torch.where(i >= R, ck[:, (i - R).clamp(min=0)], torch.zeros_like(ck))
+    vis = before.double().sum().item() + cache.P * float(torch.clamp(i + 1, max=R).double().sum())
+    pairs = vis * (wl.Hq // wl.Hkv)
+    flops = pairs * 4 * wl.d
+    causal = cache.P * (wl.Hq // wl.Hkv) * T0 * (T0 + 1) / 2
+    stream = torch.cuda.current_stream()
+    cache.prefill_attention(qp, kd, vd, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        cache.prefill_attention(qp, kd, vd, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del qp, out, keep, ck
+    torch.cuda.empty_cache()
+    tflops = flops / (ms * 1e-3) / 1e12
+    return {"ms": ms, "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+            "useful_flop": flops, "visible_pairs": pairs, "visible_fraction": pairs / causal,
+            "note": "kvp_prefill_attn (prefill_attn_kernel<128>), q/k/v bf16, out fp32; "
+                    "useful = 4 d flop per visible (row, key) pair"}
 
 
 def attn_bytes(cache, wl, B, Hq, d) -> int:

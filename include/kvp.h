@@ -311,7 +311,8 @@ size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
  *              positions ascending -- as written by kvp_select for the same keep bits
  *   out        [B][Hq][T][d] fp32: softmax(sm_scale * K q_i) V over the keys position
  *              i sees; a row that sees no key (window 0, nothing kept before it) is 0
- * g in {1, 2, 4, 8} and d in {64, 128} (else KVP_E_UNSUPPORTED); T >= 1, window >= 0.
+ * g in {1, 2, 4, 8} and d in {64, 128} (else KVP_E_UNSUPPORTED); T >= 1, window >= 0,
+ * sm_scale finite and > 0 (else KVP_E_ARG).
  * All buffers are caller-owned device memory; no workspace, no allocation.
  * -------------------------------------------------------------------------- */
 kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t dtype,

@@ -221,6 +221,7 @@ extern "C" kvp_status kvp_prefill_attn(const void* q, const void* k, const void*
   if (!q || !k || !v || !keep_bits || !kept_idx || !out) return KVP_E_ARG;
   if (dtype != KVP_BF16) return is_kv_dtype(dtype) ? KVP_E_UNSUPPORTED : KVP_E_DTYPE;
   if (B <= 0 || Hkv <= 0 || Hq <= 0 || T <= 0 || window < 0) return KVP_E_ARG;
+  if (!(sm_scale > 0.0f) || sm_scale == __builtin_huge_valf()) return KVP_E_ARG;
   if (Hq % Hkv != 0) return KVP_E_ARG;
   const int g = Hq / Hkv;
   if (g != 1 && g != 2 && g != 4 && g != 8) return KVP_E_UNSUPPORTED;

@@ -25,15 +25,16 @@
 // interleaved so each lane holds the scores of 8 consecutive keys of one query row --
 // the B-operand layout of the P.V product that follows.  Online softmax in fp32 (log2
 // domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits).
-// Work-groups are numbered heavy-first (the last position blocks see the most keys),
-// and a pair's blocks share one XCD (pair = blockIdx % num_pairs, num_pairs % 8 == 0
-// in the common shapes) so its K/V rows are reused from that XCD's L2.
+// Work-groups are numbered heavy-first (the last position blocks see the most keys);
+// a pair's blocks share one XCD, so its K/V rows are reused from that XCD's L2, and the
+// pairs of an XCD mix KV heads (the kept fraction differs between heads).
 #include "kvp_internal.h"
 
 namespace kvp {
 
 constexpr int PF_KT = 64;      // keys per LDS tile
 constexpr int PF_THREADS = 256;
+constexpr float PF_HEADROOM = 8.0f;  // log2 units a score may pass the reference by
 
 struct PrefillArgs {
   const uint16_t* q;
@@ -158,9 +159,16 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, G = lane >> 4;
-  const int pair = blockIdx.x % a.num_pairs;
+  // Work-group -> (pair, block): blocks heavy-first (the last positions see the most
+  // keys); slot = blockIdx % num_pairs fixes the pair, so a pair's blocks all run on
+  // one XCD (work-groups go round-robin over the 8 XCDs) and share its K/V rows in that
+  // XCD's L2.  Slots enumerate batch rows fastest: the kept fraction varies from head to
+  // head (one threshold for all), and an XCD must not inherit a single head's load.
+  const int slot = blockIdx.x % a.num_pairs;
+  const int B = a.num_pairs / a.Hkv;
+  const int b = slot % B, h = slot / B;
+  const int pair = b * a.Hkv + h;
   const int blk = a.nblk - 1 - blockIdx.x / a.num_pairs;
-  const int b = pair / a.Hkv, h = pair % a.Hkv;
   const int T = a.T;
   const int i0 = blk * a.pb;
   const int lo64 = max(0, i0 - a.window + 1) & ~(PF_KT - 1);
@@ -206,7 +214,14 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   f32x4 o[D / 16][2];
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) o[t][0] = o[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m[2] = {neg_inf(), neg_inf()}, l[2] = {0.f, 0.f};
+  // Softmax reference per column (uniform across the column's four lanes): mraw (raw
+  // score units, -inf until the column sees a key), mc = mraw * c (0 while mraw is
+  // -inf), mlim = mraw + headroom.  Probabilities are exp2(s c - mc); the reference
+  // moves only when a score passes mlim, so p <= 2^PF_HEADROOM and the common step
+  // needs no cross-lane maximum.
+  const float c = a.scale_log2, hr = PF_HEADROOM / c;
+  float mraw[2] = {neg_inf(), neg_inf()}, mc[2] = {0.f, 0.f}, mlim[2] = {neg_inf(), neg_inf()};
+  float l[2] = {0.f, 0.f};
 
   // prologue: tile 0 in registers, tile 1's positions requested
   PfRegs<D> R;
@@ -273,39 +288,46 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
         }
       }
 
-      bf16x8 phi[2], plo[2];
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        float s[8];
+      for (int cc = 0; cc < 2; ++cc) {
+        float sv[8];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[e] = sA[c][e] * a.scale_log2;
-          s[e + 4] = sB[c][e] * a.scale_log2;
+          sv[e] = sA[cc][e];
+          sv[e + 4] = sB[cc][e];
         }
         if (!full) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) s[e] = ((vis[c] >> e) & 1u) ? s[e] : neg_inf();
+          for (int e = 0; e < 8; ++e) sv[e] = ((vis[cc] >> e) & 1u) ? sv[e] : neg_inf();
         }
-        float mx = s[0];
+        float lm = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                         fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+        if (__ballot(lm > mlim[cc]) != 0) {
+          // some score passed its column's headroom: move the references to the column
+          // maxima and rescale what was accumulated against the old ones
+          lm = fmaxf(lm, __shfl_xor(lm, 16));
+          lm = fmaxf(lm, __shfl_xor(lm, 32));
+          const bool upd = lm > mraw[cc];
+          const float mcn = lm * c;
+          const float alpha = !upd ? 1.0f : (mraw[cc] == neg_inf() ? 0.0f : __builtin_amdgcn_exp2f(mc[cc] - mcn));
+          if (upd) {
+            mraw[cc] = lm;
+            mc[cc] = mcn;
+            mlim[cc] = lm + hr;
+          }
+          l[cc] *= alpha;
+          if (__ballot(alpha != 1.0f) != 0) {
 #pragma unroll
-        for (int e = 1; e < 8; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[c], mx);
-        const float mref = (mnew == neg_inf()) ? 0.f : mnew;
-        const float alpha = exp2f(m[c] - mref);
+            for (int t = 0; t < D / 16; ++t) o[t][cc] *= alpha;
+          }
+        }
         float p[8], psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          p[e] = exp2f(s[e] - mref);
+          p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], c, -mc[cc]));
           psum += p[e];
         }
-        l[c] = l[c] * alpha + psum;
-        m[c] = mnew;
-        if (__ballot(alpha != 1.0f) != 0) {
-#pragma unroll
-          for (int t = 0; t < D / 16; ++t) o[t][c] *= alpha;
-        }
+        l[cc] += psum;
         u32x4 ph, pl;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
@@ -313,20 +335,15 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
           ph[w] = hl[0];
           pl[w] = hl[1];
         }
-        phi[c] = as_bf16x8(ph);
-        plo[c] = as_bf16x8(pl);
-      }
-
-      // O^T += V^T P^T
+        const bf16x8 phi = as_bf16x8(ph), plo = as_bf16x8(pl);
+        // O^T += V^T P^T for this column tile
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) {
-        const int d = 16 * t + n;
-        const bf16x8 vf =
-            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + d * PF_KT + 8 * ((4 * ch + G) ^ v_swz(d))));
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          o[t][c] = mfma16x16x32(vf, phi[c], o[t][c]);
-          o[t][c] = mfma16x16x32(vf, plo[c], o[t][c]);
+        for (int t = 0; t < D / 16; ++t) {
+          const int d = 16 * t + n;
+          const bf16x8 vf =
+              as_bf16x8(*reinterpret_cast<const u32x4*>(vt + d * PF_KT + 8 * ((4 * ch + G) ^ v_swz(d))));
+          o[t][cc] = mfma16x16x32(vf, phi, o[t][cc]);
+          o[t][cc] = mfma16x16x32(vf, plo, o[t][cc]);
         }
       }
     }

@@ -82,6 +82,19 @@ class PrunedKVCache:
         L.kvp_select(self.scores, T, self.tau, self.window, self.keep_bits, self.kept_idx,
                      self.kept_count, self.ws_select, stream)
 
+    def prefill_attention(self, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+        """Attention of every prompt position under the current selection (call select(T)
+        first): position i sees key j iff j <= i and (j is kept or i - j < window).
+        q [B, Hq, T, d], k/v [B, Hkv, T, d] bf16 -> out [B, Hq, T, d] fp32."""
+        if self.demote:
+            raise ValueError("a demoting cache evicts nothing: its prompt attends densely")
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        # select(T) wrote keep_bits as [P][ceil(T/32)] and kept_idx as [P][T], packed
+        return L.kvp_prefill_attn(q, k, v, self.keep_bits, self.kept_idx, self.window, self.scale,
+                                  out, stream)
+
     def compact(self, k: torch.Tensor, v: torch.Tensor, stream=None):
         L.kvp_compact(k, v, self.kept_idx, self.kept_count, self.kv, self.ws_compact,
                       ring=self.ring, scores=self.scores,

@@ -203,6 +203,8 @@ def test_host_validation_without_device(L):
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 96, fake, fake, 16, 0.1, fake, None) == E_UNSUP
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, -1, 0.1, fake, None) == E_ARG
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 0, 128, fake, fake, 16, 0.1, fake, None) == E_ARG
+    for bad in (0.0, -0.1, float("inf"), float("nan")):
+        assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, 16, bad, fake, None) == E_ARG
 
 
 def test_missing_library_fails_loudly(L, tmp_path):
