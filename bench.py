@@ -392,6 +392,7 @@ def measure_prefill_attn(K, W, wl, cache, kd, vd, T0, dev, reps=3) -> dict:
     torch.cuda.empty_cache()
     tflops = flops / (ms * 1e-3) / 1e12
     return {"ms": ms, "tflops": tflops, "frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+            "traffic": pmc_traffic("prefill_attn"), "traffic_unit": "HBM bytes/launch",
             "useful_flop": flops, "visible_pairs": pairs, "visible_fraction": pairs / causal,
             "note": "kvp_prefill_attn (prefill_attn_kernel<128>), q/k/v bf16, out fp32; "
                     "useful = 4 d flop per visible (row, key) pair"}

@@ -28,8 +28,9 @@
 // the B-operand layout of the P.V product that follows.  Online softmax in fp32 (log2
 // domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits).
 // Work-groups are numbered heavy-first (the last position blocks see the most keys);
-// a pair's blocks share one XCD, so its K/V rows are reused from that XCD's L2, and the
-// pairs of an XCD mix KV heads (the kept fraction differs between heads).
+// the 32 blocks an XCD runs at a time are adjacent blocks of one pair, so the kept keys
+// they all read come from that XCD's L2, and the pairs of an XCD mix KV heads (the kept
+// fraction differs between heads).
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -38,6 +39,7 @@ constexpr int PF_KT = 64;      // keys per LDS tile
 constexpr int PF_THREADS = 512;
 constexpr int PF_WAVES = PF_THREADS / 64;
 constexpr int PF_ROWS = 32 * PF_WAVES;  // query rows per work-group
+constexpr int PF_GS = 32;               // work-groups per run: one per CU of an XCD
 // key slots of a tile each thread stages: 64 slots x D/8 chunks over the threads
 __host__ __device__ constexpr int pf_kg(int D) { return 64 * (D / 8) / PF_THREADS; }
 constexpr float PF_HEADROOM = 8.0f;  // log2 units a score may pass the reference by
@@ -50,6 +52,7 @@ struct PrefillArgs {
   const uint32_t* keep_bits;
   const int* kept_idx;
   int Hq, Hkv, T, g, pb, nblk, window, words, num_pairs;
+  int nx, per_x;  // XCD groups (8, or 1 when num_pairs % 8 != 0) and pairs per group
   float scale_log2;  // sm_scale * log2(e)
 };
 
@@ -167,16 +170,23 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 15, G = lane >> 4;
-  // Work-group -> (pair, block): blocks heavy-first (the last positions see the most
-  // keys); slot = blockIdx % num_pairs fixes the pair, so a pair's blocks all run on
-  // one XCD (work-groups go round-robin over the 8 XCDs) and share its K/V rows in that
-  // XCD's L2.  Slots enumerate batch rows fastest: the kept fraction varies from head to
-  // head (one threshold for all), and an XCD must not inherit a single head's load.
-  const int slot = blockIdx.x % a.num_pairs;
+  // Work-group -> (pair, block).  Work-groups are dispatched round-robin over the 8
+  // XCDs (blockIdx % 8); an XCD's work-groups are taken in runs of PF_GS (one per CU),
+  // each run = PF_GS adjacent position blocks of one pair, so the blocks that read the
+  // same kept keys at the same time sit on one XCD and share them through its L2.
+  // Runs go heavy-first (the last position blocks see the most keys) and cycle over the
+  // XCD's pairs.  Pair slots enumerate batch rows fastest: the kept fraction varies from
+  // head to head (one threshold for all), and an XCD must not inherit one head's load.
+  const int x = blockIdx.x % a.nx, k = blockIdx.x / a.nx;
+  const int grp = k / PF_GS, j = k % PF_GS;
+  const int pi = grp % a.per_x, bgi = grp / a.per_x;
+  const int blk_raw = bgi * PF_GS + j;
+  if (blk_raw >= a.nblk) return;  // padding of the last run (uniform per work-group)
+  const int slot = pi * a.nx + x;
   const int B = a.num_pairs / a.Hkv;
   const int b = slot % B, h = slot / B;
   const int pair = b * a.Hkv + h;
-  const int blk = a.nblk - 1 - blockIdx.x / a.num_pairs;
+  const int blk = a.nblk - 1 - blk_raw;
   const int T = a.T;
   const int i0 = blk * a.pb;
   const int lo64 = max(0, i0 - a.window + 1) & ~(PF_KT - 1);
@@ -405,7 +415,9 @@ kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, 
   a.words = cdiv(T, 32);
   a.num_pairs = B * Hkv;
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  const int64_t grid = (int64_t)a.nblk * a.num_pairs;
+  a.nx = (a.num_pairs % 8 == 0) ? 8 : 1;
+  a.per_x = a.num_pairs / a.nx;
+  const int64_t grid = (int64_t)a.nx * a.per_x * cdiv(a.nblk, PF_GS) * PF_GS;
   if (grid > 0x7fffffff) return KVP_E_UNSUPPORTED;
   if (d == 128) prefill_attn_kernel<128><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
   else prefill_attn_kernel<64><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
