@@ -17,8 +17,9 @@
 // Both are walked in 64-key tiles staged through LDS: K row-major with its 16-byte
 // chunks swizzled per row, V transposed to [d][key] on the way in (register byte
 // permutes, then 8-byte LDS writes), so every MFMA operand is one 16-byte LDS read.
-// Two register sets alternate: a tile's K/V rows are requested two tiles before they
-// are stored to LDS, and its kept_idx entries one tile before that.  One 8-wave
+// Two register sets and two LDS buffers alternate (one barrier per tile): a tile's K/V
+// rows are requested three tiles before their use and stored one tile before it; its
+// kept_idx entries are read a tile earlier than the rows.  One 8-wave
 // work-group per CU (two waves per SIMD): 256 rows share each staged tile, which halves
 // the gathered bytes per flop against 4-wave groups (measured 9% faster).
 //
@@ -163,9 +164,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     PrefillArgs a) {
   constexpr int KG = pf_kg(D);
   constexpr int DC = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t ks[PF_KT * D];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[D * PF_KT];
-  __shared__ int red[PF_WAVES];
+  // LDS: two buffers of (K tile, V^T tile), then the reduction slots
+  extern __shared__ __attribute__((aligned(16))) uint16_t pf_lds[];
+  uint16_t* const kbuf[2] = {pf_lds, pf_lds + 2 * PF_KT * D};
+  uint16_t* const vbuf[2] = {pf_lds + PF_KT * D, pf_lds + 3 * PF_KT * D};
+  int* const red = reinterpret_cast<int*>(pf_lds + 4 * PF_KT * D);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,8 +247,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   float mraw[2] = {neg_inf(), neg_inf()}, mc[2] = {0.f, 0.f}, mlim[2] = {neg_inf(), neg_inf()};
   float l[2] = {0.f, 0.f};
 
-  // prologue: tiles 0 and 1 in registers, tile 2's positions requested.  Two register
-  // sets alternate, so every tile's rows are requested two tiles before they are used.
+  // Pipeline: two register sets and two LDS buffers.  A tile's K/V rows are requested
+  // three tiles ahead of their use (into the register set of their parity), stored to
+  // LDS buffer tau % 2 one tile ahead, and the kept_idx entries are read one tile before
+  // the rows.  One barrier per tile: the buffer a step stores into was last read in the
+  // step before the previous barrier.
   PfRegs<D> R0, R1;
   int pos[KG];
   pf_positions<D>(a, kidx, pf_tile(0, ntp, nk, lo64, hi), s0, pos);
@@ -254,18 +260,27 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     pf_positions<D>(a, kidx, pf_tile(1, ntp, nk, lo64, hi), s0, pos);
     pf_load<D>(kp, vp, dc, pos, R1);
   }
-  if (ntiles > 2) pf_positions<D>(a, kidx, pf_tile(2, ntp, nk, lo64, hi), s0, pos);
+  pf_store<D>(kbuf[0], vbuf[0], dc, s0, R0);
+  if (ntiles > 2) {
+    pf_positions<D>(a, kidx, pf_tile(2, ntp, nk, lo64, hi), s0, pos);
+    pf_load<D>(kp, vp, dc, pos, R0);
+    if (ntiles > 3) pf_positions<D>(a, kidx, pf_tile(3, ntp, nk, lo64, hi), s0, pos);
+  }
+  __syncthreads();
 
   const int slotA = 8 * (n >> 2) + (n & 3);
-  auto step = [&](int tau, PfRegs<D>& R) {
+  // Rn holds tile tau + 1 (when there is one)
+  auto step = [&](int tau, PfRegs<D>& Rn) {
     const PfTile tl = pf_tile(tau, ntp, nk, lo64, hi);
-    __syncthreads();  // the previous tile's LDS reads are done
-    pf_store<D>(ks, vt, dc, s0, R);
-    __syncthreads();
-    if (tau + 2 < ntiles) {
-      pf_load<D>(kp, vp, dc, pos, R);
-      if (tau + 3 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 3, ntp, nk, lo64, hi), s0, pos);
+    if (tau + 1 < ntiles) {
+      pf_store<D>(kbuf[(tau + 1) & 1], vbuf[(tau + 1) & 1], dc, s0, Rn);
+      if (tau + 3 < ntiles) {
+        pf_load<D>(kp, vp, dc, pos, Rn);
+        if (tau + 4 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 4, ntp, nk, lo64, hi), s0, pos);
+      }
     }
+    const uint16_t* const ks = kbuf[tau & 1];
+    const uint16_t* const vt = vbuf[tau & 1];
 
     uint32_t kw[2] = {0u, 0u};
     if (!tl.prefix) {
@@ -370,10 +385,11 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
         }
       }
     }
+    __syncthreads();
   };
   for (int tau = 0; tau < ntiles; tau += 2) {
-    step(tau, R0);
-    if (tau + 1 < ntiles) step(tau + 1, R1);
+    step(tau, R1);
+    if (tau + 1 < ntiles) step(tau + 1, R0);
   }
 
   // normalise and store: lane (n, G) holds d = 16 t + 4 G + (0..3) of its column's row
@@ -419,8 +435,9 @@ kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, 
   a.per_x = a.num_pairs / a.nx;
   const int64_t grid = (int64_t)a.nx * a.per_x * cdiv(a.nblk, PF_GS) * PF_GS;
   if (grid > 0x7fffffff) return KVP_E_UNSUPPORTED;
-  if (d == 128) prefill_attn_kernel<128><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
-  else prefill_attn_kernel<64><<<(unsigned)grid, PF_THREADS, 0, stream>>>(a);
+  const size_t lds = 4 * (size_t)PF_KT * d * sizeof(uint16_t) + PF_WAVES * sizeof(int);
+  if (d == 128) prefill_attn_kernel<128><<<(unsigned)grid, PF_THREADS, lds, stream>>>(a);
+  else prefill_attn_kernel<64><<<(unsigned)grid, PF_THREADS, lds, stream>>>(a);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
 }
