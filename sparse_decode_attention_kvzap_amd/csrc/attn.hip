@@ -30,7 +30,13 @@ namespace kvp {
 
 constexpr int ATTN_WG_WAVES = 4;
 constexpr int ATTN_GRID = 256;  // one work-group (4 waves) per CU on a 256-CU part
-constexpr int ATTN_NWAVES = ATTN_GRID * ATTN_WG_WAVES;
+// int4 pools run two work-groups per CU (two waves per SIMD): a 32-token step of int4
+// codes moves a quarter of a bf16 step's bytes but costs more instructions (nibble
+// decode, the offset terms), and one wave per SIMD leaves its MFMA/VALU latencies
+// exposed (measured on the BeaconKV int4 cache: 194 -> 171 us).  Every other cache keeps
+// one wave per SIMD (the bf16 and int8 streams ran 1-4% slower with two).
+constexpr int ATTN_MAX_WPE = 2;
+constexpr int ATTN_MAX_NWAVES = ATTN_MAX_WPE * ATTN_GRID * ATTN_WG_WAVES;
 static_assert(ATTN_GRID % 8 == 0, "ranges are numbered per XCD (8 XCDs)");
 
 struct AttnArgs {
@@ -90,7 +96,8 @@ __device__ Plan build_plan(const AttnArgs& a, int* lds) {
   pl.total = block_scan_excl(pl.P, nseg + 1, tmp);
   const int np = a.kv.num_pairs;
   pl.total_a = pl.P[np];
-  auto split = [](int pages) { return max(2, (((pages + ATTN_NWAVES - 1) / ATTN_NWAVES) + 1) & ~1); };
+  const int nwaves = gridDim.x * ATTN_WG_WAVES;
+  auto split = [nwaves](int pages) { return max(2, (((pages + nwaves - 1) / nwaves) + 1) & ~1); };
   pl.per_a = split(pl.total_a);
   pl.per_b = split(pl.total - pl.total_a);
   for (int s = threadIdx.x; s <= nseg; s += blockDim.x) {
@@ -808,11 +815,12 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
 // -------------------------------------------------------------------------------
 // The kernel
 // -------------------------------------------------------------------------------
-// One work-group per CU (ATTN_GRID = 256), so a wave may use a whole SIMD's registers.
+// WPE work-groups per CU (ATTN_GRID * WPE of them): with WPE = 1 a wave may use a whole
+// SIMD's registers; with WPE = 2 (int4 pools) each wave fits in half of them.
 // LP: the cache has a low-precision pool; the instantiation without one keeps the
 // code-pool path's register needs out of the bf16 loop's allocation.
-template <int D, bool F32, bool LP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_attn_kernel(AttnArgs a) {
+template <int D, bool F32, bool LP, int WPE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_attn_kernel(AttnArgs a) {
   extern __shared__ int lds[];
   Plan pl = build_plan(a, lds);
   const int np = a.kv.num_pairs;
@@ -988,7 +996,7 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   const int Hkv = num_pairs / B;
   if (Hq % Hkv != 0) return 0;
   const int g = Hq / Hkv;
-  const size_t recs = 2 * (size_t)ATTN_NWAVES + 2 * (size_t)num_pairs;  // both splits
+  const size_t recs = 2 * (size_t)ATTN_MAX_NWAVES + 2 * (size_t)num_pairs;  // both splits
   return attn_plan_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
 }
 
@@ -1014,18 +1022,20 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
   const bool f32 = kv->dtype == KVP_F32;
   const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32);
   if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
+  const dim3 g1(ATTN_GRID), b(256);
   if (f32) {
-    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
-    else hipLaunchKernelGGL((decode_attn_kernel<128, true, false>), dim3(ATTN_GRID), dim3(256), lds, stream, a);
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false, 1>), g1, b, lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, true, false, 1>), g1, b, lds, stream, a);
+  } else if (kv->num_pages8 > 0 && kv->lp_bits == 4) {
+    const dim3 g2(ATTN_GRID * 2);
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 2>), g2, b, lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 2>), g2, b, lds, stream, a);
+  } else if (kv->num_pages8 > 0) {
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 1>), g1, b, lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 1>), g1, b, lds, stream, a);
   } else {
-    const dim3 g(ATTN_GRID), b(256);
-    if (kv->num_pages8 > 0) {
-      if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true>), g, b, lds, stream, a);
-      else hipLaunchKernelGGL((decode_attn_kernel<128, false, true>), g, b, lds, stream, a);
-    } else {
-      if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, false>), g, b, lds, stream, a);
-      else hipLaunchKernelGGL((decode_attn_kernel<128, false, false>), g, b, lds, stream, a);
-    }
+    if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, false, 1>), g1, b, lds, stream, a);
+    else hipLaunchKernelGGL((decode_attn_kernel<128, false, false, 1>), g1, b, lds, stream, a);
   }
   KVP_LAUNCH_CHECK();
   const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
