@@ -461,8 +461,7 @@ def dms_loop(args, wl, dev):
     visible, attn_ms = [], []
     for i in range(S):
         feed(i)
-        K.kvp_score(scorer, hb, cache.s_new, cache.ws_score)
-        K.kvp_step_delayed(cache.kv, cache.ring, kb, vb, cache.s_new, cache.tau_dev, cache.pos_dev, 1)
+        cache.advance(hb, kb, vb)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -557,8 +556,9 @@ def dms_loop(args, wl, dev):
                      "attn_ms_per_step": attn_total_ms / S,
                      "visible_token_heads_first": visible[0], "visible_token_heads_last": visible[-1],
                      "graph_output_equals_eager": same,
-                     "note": "each step: refill the 4 input buffers, score the new token, delayed "
-                             "step, attention; the graph holds the last three"},
+                     "note": "each step: refill the 4 input buffers, then score the new token + "
+                             "delayed step (one kernel, kvp_score_step_delayed, for the linear "
+                             "scorer) and attention (main + merge); the graph holds the last two"},
     }
     log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step, graph {graph_ms / S * 1e3:.1f} "
         f"us/step (replay only {replay_ms / S * 1e3:.1f}), attention {attn_total_ms / S * 1e3:.1f} "

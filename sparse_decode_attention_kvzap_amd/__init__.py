@@ -12,6 +12,7 @@ from ._lib import (  # noqa: F401
     kvp_decode_attn_workspace_size, kvp_prefill_attn, kvp_reset, kvp_score,
     kvp_score_workspace_size,
     kvp_select, kvp_select_workspace_size, kvp_status_str, kvp_step_delayed,
+    kvp_score_step_delayed,
     kvp_threshold, kvp_threshold_workspace_size, kvp_version,
     load, sm_scale, LIB_PATH,
 )

@@ -19,7 +19,9 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
                               void* ws, hipStream_t stream);
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream);
+                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream,
+                                   const kvp_scorer* sc = nullptr, const void* x_new = nullptr,
+                                   float* s_out = nullptr);
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   hipStream_t stream);
@@ -192,6 +194,28 @@ extern "C" kvp_status kvp_step_delayed_dev(const kvp_paged_kv* kv, const kvp_rin
                                            int32_t* pos, hipStream_t stream) {
   if (!tau || !pos) return KVP_E_ARG;
   return step_common(kv, ring, k_new, v_new, dtype, s_new, ld_s, 0.0f, tau, 0, pos, stream);
+}
+
+extern "C" kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* hidden_new,
+                                             int32_t hdtype, const kvp_paged_kv* kv,
+                                             const kvp_ring* ring, const void* k_new,
+                                             const void* v_new, int32_t dtype, float* s_new,
+                                             const float* tau, int32_t* pos, hipStream_t stream) {
+  kvp_status st = check_kv(kv);
+  if (st != KVP_OK) return st;
+  if (!ring) return KVP_E_ARG;
+  if ((st = check_ring(ring)) != KVP_OK) return st;
+  if (!sc || !hidden_new || !sc->w1 || !k_new || !v_new || !tau || !pos) return KVP_E_ARG;
+  if (sc->kind != KVP_SCORER_LINEAR) return KVP_E_UNSUPPORTED;
+  if (sc->n_kv_heads <= 0 || kv->num_pairs % sc->n_kv_heads != 0) return KVP_E_ARG;
+  if (!is_kv_dtype(hdtype) || hdtype != sc->wdtype) return KVP_E_DTYPE;
+  if (dtype != kv->dtype) return KVP_E_DTYPE;
+  // rows are read in 16-byte pieces
+  const int elt = hdtype == KVP_BF16 ? 2 : 4;
+  if (sc->hidden <= 0 || sc->hidden % (16 / elt) != 0) return KVP_E_UNSUPPORTED;
+  if (((uintptr_t)hidden_new | (uintptr_t)sc->w1) & 15) return KVP_E_ARG;
+  return kvp_launch_step_delayed(kv, ring, k_new, v_new, nullptr, 1, 0.0f, tau, 0, pos, stream,
+                                 sc, hidden_new, s_new);
 }
 
 extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,

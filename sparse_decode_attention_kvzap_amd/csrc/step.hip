@@ -25,6 +25,13 @@ struct StepArgs {
   const float* tau_dev;  // if set, tau is read from here
   int p;
   int* pos_dev;  // if set: [position, arrivals]; the position is read from here and advanced
+  // Fused linear scorer (s_new unused when x_new is set): the new token's score of pair
+  // (b, h) is x_new[b] . w[h] + bias[h], computed by the pair's wave.
+  const void* x_new;  // [B][H] hidden states of the new tokens
+  const void* w;      // [Hkv][H] scorer weights (nn.Linear layout), same dtype as x_new
+  const float* bias;  // [Hkv] or null
+  float* s_out;       // [B * Hkv] or null: the scores, as stored in the ring
+  int H, Hkv, x_bf16;
 };
 
 template <typename E>
@@ -33,6 +40,29 @@ template <>
 __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) { return bf16_to_f32(x); }
 template <>
 __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+
+// One lane's share of x . w over H elements (16-byte loads, fp32 fused multiply-adds in
+// a fixed order), summed across the wave.
+template <typename X>
+__device__ __forceinline__ float wave_dot(const X* __restrict__ x, const X* __restrict__ w, int H) {
+  constexpr int V = 16 / sizeof(X);
+  const int lane = threadIdx.x & 63;
+  float acc = 0.f;
+  for (int i = lane * V; i < H; i += 64 * V) {
+    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + i);
+    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (sizeof(X) == 2) {
+        acc = fmaf(bf16_to_f32(xv[e] & 0xffffu), bf16_to_f32(wv[e] & 0xffffu), acc);
+        acc = fmaf(bf16_to_f32(xv[e] >> 16), bf16_to_f32(wv[e] >> 16), acc);
+      } else {
+        acc = fmaf(__uint_as_float(xv[e]), __uint_as_float(wv[e]), acc);
+      }
+    }
+  }
+  return wave_sum(acc);
+}
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
@@ -46,6 +76,17 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   const int64_t roff = ((int64_t)pair * (w / PAGE) + rp) * PAGE * D;
   E* rk = reinterpret_cast<E*>(a.ring.k) + roff + rs * D;  // K row of the slot
   E* rv = reinterpret_cast<E*>(a.ring.v) + roff + rs;      // V column, stride PAGE
+  float s_new = 0.f;
+  if (a.x_new) {
+    const int b = pair / a.Hkv, h = pair % a.Hkv;
+    if (a.x_bf16)
+      s_new = wave_dot(reinterpret_cast<const uint16_t*>(a.x_new) + (int64_t)b * a.H,
+                       reinterpret_cast<const uint16_t*>(a.w) + (int64_t)h * a.H, a.H);
+    else
+      s_new = wave_dot(reinterpret_cast<const float*>(a.x_new) + (int64_t)b * a.H,
+                       reinterpret_cast<const float*>(a.w) + (int64_t)h * a.H, a.H);
+    if (a.bias) s_new += a.bias[h];
+  }
   const int old_pos = a.ring.pos[(int64_t)pair * w + slot];
   const float old_s = a.ring.score[(int64_t)pair * w + slot];
   constexpr int PER = (D + 63) / 64;
@@ -189,7 +230,9 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   }
   if (lane == 0) {
     a.ring.pos[(int64_t)pair * w + slot] = p;
-    a.ring.score[(int64_t)pair * w + slot] = a.s_new[(int64_t)pair * a.ld_s];
+    if (!a.x_new) s_new = a.s_new[(int64_t)pair * a.ld_s];
+    a.ring.score[(int64_t)pair * w + slot] = s_new;
+    if (a.s_out) a.s_out[pair] = s_new;
   }
   // Device-resident position: every pair's wave has read it (above) before it counts
   // itself here; the last of the num_pairs arrivals advances it and clears the count, so
@@ -208,8 +251,16 @@ using namespace kvp;
 
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
-                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream) {
+                                   const float* tau_dev, int p, int* pos_dev, hipStream_t stream,
+                                   const kvp_scorer* sc, const void* x_new, float* s_out) {
   StepArgs a;
+  a.x_new = x_new;
+  a.w = sc ? sc->w1 : nullptr;
+  a.bias = sc ? sc->b1 : nullptr;
+  a.s_out = s_out;
+  a.H = sc ? sc->hidden : 0;
+  a.Hkv = sc ? sc->n_kv_heads : 1;
+  a.x_bf16 = sc ? sc->wdtype == KVP_BF16 : 0;
   a.kv = *kv;
   a.ring = *ring;
   a.k_new = k_new;

@@ -120,18 +120,29 @@ class PrunedKVCache:
         self.pos_dev[0] = p
         self.pos_dev[1] = 0
 
-    def step(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
-             q: torch.Tensor, p: Optional[int] = None, stream=None) -> torch.Tensor:
-        """Append a position (p, or the device-held next position when p is None) and
-        attend with q over the cache that now holds it.  Every per-step value lives in
-        device memory, so this sequence can be captured in a HIP graph and replayed."""
+    def advance(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                p: Optional[int] = None, stream=None):
+        """Append a position (p, or the device-held next position when p is None): score
+        the new tokens, then the delayed step.  With a linear scorer both run in one kernel
+        (kvp_score_step_delayed); an MLP scorer runs kvp_score first."""
         if p is not None:
             self.set_position(p)
         if not isinstance(self.tau, torch.Tensor):
             self.tau_dev.fill_(self.tau)
-        L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
-        L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau_dev, self.pos_dev,
-                           1, stream)
+        if self.scorer.kind == L.KVP_SCORER_LINEAR:
+            L.kvp_score_step_delayed(self.scorer, hidden_new, self.kv, self.ring, k_new, v_new,
+                                     self.tau_dev, self.pos_dev, self.s_new, stream)
+        else:
+            L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
+            L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau_dev,
+                               self.pos_dev, 1, stream)
+
+    def step(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+             q: torch.Tensor, p: Optional[int] = None, stream=None) -> torch.Tensor:
+        """Append a position (see advance) and attend with q over the cache that now holds
+        it.  Every per-step value lives in device memory, so this sequence can be captured
+        in a HIP graph and replayed."""
+        self.advance(hidden_new, k_new, v_new, p, stream)
         return self.attend(q, stream)
 
     def attend(self, q: torch.Tensor, stream=None) -> torch.Tensor:

@@ -385,6 +385,79 @@ def test_step_delayed_state_machine(K, dtype, d, w, demote, bits):
                 assert vs[i] == sc and np.array_equal(Vc[i], c), (pr, t)
 
 
+def _same_cache(kvA, ringA, kvB, ringB):
+    """Two caches hold the same logical content: rings and per-pair counters bit for
+    bit, each pair's pool rows (positions, K, V; codes and scales of the low-precision
+    pool) in block-table order.  Physical page ids may differ: pages come from an atomic
+    bump allocator, so which pair gets which page depends on the waves' arrival order."""
+    for n, t in ringA.tensors.items():
+        iv = {1: torch.int8, 2: torch.int16, 4: torch.int32}[t.element_size()]
+        assert torch.equal(t.view(iv), ringB.tensors[n].view(iv)), "ring " + n
+    names = ["length", "page_top", "err"] + (["length8", "page8_top"] if kvA.c.num_pages8 else [])
+    for n in names:
+        assert torch.equal(kvA.tensors[n], kvB.tensors[n]), n
+    for pr in range(kvA.c.num_pairs):
+        for a, b in zip(read_pool(kvA, pr), read_pool(kvB, pr)):
+            assert np.array_equal(a, b), ("pool", pr)
+        if kvA.c.num_pages8:
+            for a, b in zip(read_pool8(kvA, pr), read_pool8(kvB, pr)):
+                assert np.array_equal(a, b), ("pool8", pr)
+
+
+@pytest.mark.parametrize("xdtype,H,kvdtype,d,w,bias,demote", [
+    (torch.bfloat16, 4096, torch.bfloat16, 128, 64, True, False),
+    (torch.float32, 256, torch.float32, 64, 32, False, False),
+    (torch.bfloat16, 1032, torch.bfloat16, 128, 32, True, True),  # H not a multiple of 512
+    (torch.float32, 100, torch.bfloat16, 64, 48, True, False),    # H not a multiple of 256
+])
+def test_score_step_delayed_fused(K, xdtype, H, kvdtype, d, w, bias, demote):
+    """kvp_score_step_delayed: the new tokens' linear scores match the oracle's, and the
+    cache it leaves holds, bit for bit, what kvp_step_delayed_dev leaves when fed those
+    scores -- two caches driven side by side for 80 steps (retentions, drops, demotions
+    and page allocations included)."""
+    B, Hkv, Hq, T0, steps = 3, 4, 8, 150, 80
+    P = B * Hkv
+    total = T0 + steps
+    Wt = seeded((Hkv, H), 101, xdtype, scale=1.0 / math.sqrt(H))
+    b = (seeded((Hkv,), 102) * 0.1 - 1.15) if bias else None
+    sc = K.Scorer(K.KVP_SCORER_LINEAR, Wt, b)
+    x_all = seeded((steps, B, 1, H), 103, xdtype)
+    k_all = seeded((B, Hkv, total, d), 104, kvdtype)
+    v_all = seeded((B, Hkv, total, d), 105, kvdtype)
+    s0 = seeded((B, Hkv, T0), 106) - 1.15
+    keep0 = oracle.dms_visible(oracle.dms_evict_flags(f64(s0).reshape(P, T0)), T0 - 1, w)
+    idx, cnt = upload_selection(keep0)
+    maxpp = total // 16 + 2
+    kw = dict(num_pages8=P * maxpp, max_pages8_per_pair=maxpp, lp_bits=8) if demote else {}
+    caches = []
+    for _ in range(2):
+        kv = K.PagedKV.allocate(P, d, P * maxpp, maxpp, kvdtype, DEV, poison=True, **kw)
+        ring = K.Ring.allocate(P, w, d, kvdtype, DEV, poison=True)
+        K.kvp_compact(k_all[:, :, :T0].contiguous(), v_all[:, :, :T0].contiguous(), idx, cnt, kv,
+                      compact_ws(K, B, Hkv), ring=ring, scores=s0.contiguous(),
+                      mode=K.KVP_COMPACT_DEMOTE_INT8 if demote else K.KVP_COMPACT_EVICT)
+        tau = torch.zeros(1, dtype=torch.float32, device=DEV)
+        pos = torch.tensor([T0, 0], dtype=torch.int32, device=DEV)
+        caches.append((kv, ring, tau, pos))
+    (kvA, ringA, tauA, posA), (kvB, ringB, tauB, posB) = caches
+    s_new = torch.full((P,), float("nan"), dtype=torch.float32, device=DEV)
+    Wf = f64(Wt)
+    bf = f64(b) if bias else None
+    for i in range(steps):
+        p = T0 + i
+        k_new = k_all[:, :, p].contiguous()
+        v_new = v_all[:, :, p].contiguous()
+        K.kvp_score_step_delayed(sc, x_all[i], kvA, ringA, k_new, v_new, tauA, posA, s_new)
+        K.kvp_step_delayed(kvB, ringB, k_new, v_new, s_new, tauB, posB)
+        ref = oracle.score_linear(f64(x_all[i]), Wf, bf).reshape(P)
+        err = np.abs(s_new.cpu().double().numpy() - ref).max()
+        assert err < 2.5e-5, (i, err)
+        if i % 8 == 0 or i == steps - 1:
+            _same_cache(kvA, ringA, kvB, ringB)
+    assert int(posA[0]) == total and int(posA[1]) == 0
+    assert K.kvp_check(kvA) == 0
+
+
 # ---------------------------------------------------------------------------- errors
 
 
