@@ -8,7 +8,8 @@ recent 128 kept):
     prefill compression:  kvp_score (MLP over 16 x 32767 hidden states)
                           -> kvp_threshold (tau = 75th percentile, on the device)
                           -> kvp_select -> kvp_compact (pool + 128-slot ring)
-    decode step:          kvp_score (new token) -> kvp_step_delayed -> kvp_decode_attn
+    decode step:          kvp_score_step_delayed (the new tokens scored inside the
+                          delayed step) -> kvp_decode_attn
 Inputs are resident in HBM before timing.  `value` is kept-KV decode-attention
 token-heads per second of whole step time; the per-call breakdown, the decode-only
 rate and an isolated (cache-flushed) decode-attention rate are reported beside it.
@@ -121,8 +122,7 @@ def main():
     tau = float(cache.tau_dev.item())
     log(f"[bench] tau = {tau:.6f} (quantile {q_keep}, computed on the device)")
 
-    calls = ["score_prefill", "threshold", "select", "compact", "score_new", "step_delayed",
-             "decode_attn"]
+    calls = ["score_prefill", "threshold", "select", "compact", "score_step", "decode_attn"]
     pos_start = torch.tensor([T0, 0], dtype=torch.int32, device=dev)
 
     def one_step(ev=None):
@@ -137,15 +137,13 @@ def main():
         cache.select(T0)
         mark(3)
         cache.compact(kd, vd)
-        mark(4)
-        K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
-        mark(5)
         cache.pos_dev.copy_(pos_start)  # the decode token's position, T0
-        K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, cache.tau_dev,
-                           cache.pos_dev, 1)
-        mark(6)
+        mark(4)
+        K.kvp_score_step_delayed(scorer, h_new, cache.kv, cache.ring, k_new, v_new, cache.tau_dev,
+                                 cache.pos_dev, cache.s_new, cache.ws_score)
+        mark(5)
         cache.attend(q)
-        mark(7)
+        mark(6)
 
     for i in range(args.warmup):
         one_step()
@@ -228,14 +226,15 @@ def main():
         for r in range(6):
             cache.select(T0)
             cache.compact(kd, vd)
-            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            cache.tau_dev.fill_(tau_k)
+            cache.pos_dev.copy_(pos_start)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             ev[0].record()
-            K.kvp_score(scorer, h_new, cache.s_new, cache.ws_score)
+            K.kvp_score_step_delayed(scorer, h_new, cache.kv, cache.ring, k_new, v_new,
+                                     cache.tau_dev, cache.pos_dev, cache.s_new, cache.ws_score)
             ev[1].record()
-            K.kvp_step_delayed(cache.kv, cache.ring, k_new, v_new, cache.s_new, tau_k, T0, 1)
-            ev[2].record()
             cache.attend(q)
-            ev[3].record()
+            ev[2].record()
             fsum.add_(flush.sum())
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
@@ -244,7 +243,7 @@ def main():
             e1.record()
             torch.cuda.synchronize()
             if r >= 1:
-                dec.append(ev[0].elapsed_time(ev[3]))
+                dec.append(ev[0].elapsed_time(ev[2]))
                 att.append(e0.elapsed_time(e1))
         vis_k = cache.visible_token_heads()
         keep_scaling.append({"keep": keep, "tau": tau_k if keep < 1.0 else None,
@@ -286,7 +285,6 @@ def main():
     if wl.int8_demote:  # demoted tokens: read in full, written as codes + one scale per row
         demoted = B * Hkv * T0 - kept_prefill
         compact_bytes += demoted * (2 * d * elt + 2 * (d * wl.lp_bits // 8 + 4) + 4)
-    step_bytes = B * Hkv * d * elt * 2 * 3
     gbs = lambda b, ms: b / (ms * 1e-3) / 1e9  # noqa: E731
     kernels = {
         "score_prefill": {"ms": per_call["score_prefill"],
@@ -300,8 +298,10 @@ def main():
         "select": {"ms": per_call["select"], "gbs": gbs(select_bytes, per_call["select"])},
         "compact": {"ms": per_call["compact"], "gbs": gbs(compact_bytes, per_call["compact"]),
                     "traffic": pmc_traffic("compact_copy")},
-        "score_new": {"ms": per_call["score_new"]},
-        "step_delayed": {"ms": per_call["step_delayed"], "gbs": gbs(step_bytes, per_call["step_delayed"])},
+        "score_step": {"ms": per_call["score_step"],
+                       "note": "kvp_score_step_delayed: the new tokens' scores computed inside the "
+                               "delayed step (linear: one kernel; MLP: split-K first layer, then "
+                               "the step with the MLP finish)"},
         "decode_attn": {"ms": per_call["decode_attn"], "gbs": gbs(kv_bytes_attn, per_call["decode_attn"]),
                         "token_heads_per_s": visible / (per_call["decode_attn"] * 1e-3)},
         "prefill_attn": prefill_attn,
@@ -311,7 +311,7 @@ def main():
                                  "traffic": pmc_traffic("decode_attn"),
                                  "note": "main + merge kernel, after a 1 GiB read flush"},
     }
-    decode_ms = per_call["score_new"] + per_call["step_delayed"] + per_call["decode_attn"]
+    decode_ms = per_call["score_step"] + per_call["decode_attn"]
     dominant = max(("score_prefill", "select", "compact", "decode_attn"), key=lambda c: per_call[c])
     if dominant == "score_prefill" and wl.scorer == "mlp":
         achieved = score_flops / (per_call[dominant] * 1e-3) / 1e12

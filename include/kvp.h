@@ -276,25 +276,33 @@ kvp_status kvp_step_delayed_dev(const kvp_paged_kv* kv, const kvp_ring* ring, co
                                 const void* v_new, int32_t dtype, const float* s_new,
                                 int64_t ld_s, const float* tau, int32_t* pos, hipStream_t stream);
 
-/* kvp_score_step_delayed - kvp_step_delayed_dev with the new token's score computed in
- * the same kernel by a linear scorer.  Sources: KVzap key points (a single linear layer
- * over the hidden states as the surrogate scorer); DMS "Delayed Eviction" (the step);
- * DeInfer methodology (b) (a fixed-address decode step replayed from a graph).
- *   sc          kind KVP_SCORER_LINEAR (else KVP_E_UNSUPPORTED); w1 [Hkv][H], b1 [Hkv]
- *               or NULL; n_kv_heads = Hkv with num_pairs = B * Hkv
- *   hidden_new  [B][H] hidden states of the new tokens, hdtype == sc->wdtype (bf16 or
- *               fp32); 16-byte aligned rows: H a multiple of 8 (bf16) or 4 (fp32), else
- *               KVP_E_UNSUPPORTED; misaligned hidden_new or w1 is KVP_E_ARG
+/* kvp_score_step_delayed - kvp_step_delayed_dev with the new tokens' scores computed by
+ * the scorer inside the step.  Sources: KVzap key points (a single linear layer or a
+ * two-layer MLP over the hidden states as the surrogate scorer); DMS "Delayed Eviction"
+ * (the step); DeInfer methodology (b) (a fixed-address decode step replayed from a graph).
+ *   sc          n_kv_heads = Hkv with num_pairs = B * Hkv (Hkv <= 16)
+ *               LINEAR: w1 [Hkv][H], b1 [Hkv] or NULL; one kernel.  hidden_new and w1
+ *                 16-byte aligned and H a multiple of 8 (bf16) or 4 (fp32), else
+ *                 KVP_E_ARG / KVP_E_UNSUPPORTED.  Score = x . w1[h] + b1[h] summed in
+ *                 fp32 (bf16 products are exact).
+ *               MLP: bf16, B <= 64, H a multiple of 256 and <= 8192, inner a multiple
+ *                 of 256 and <= 1024 (else KVP_E_UNSUPPORTED); two kernels: the split-K
+ *                 partial sums of the first layer (as kvp_score for small batches), then
+ *                 the step, whose wave per pair adds the slices, b1, GELU, W2 row h and
+ *                 b2.  ws >= kvp_score_workspace_size(sc, B, 1) bytes, 16-byte aligned,
+ *                 as are b1 and w2 (KVP_E_WORKSPACE / KVP_E_ARG).
+ *               Either score may differ from kvp_score's value for the same token in the
+ *               last bits (another summation order).
+ *   hidden_new  [B][H] hidden states of the new tokens, hdtype == sc->wdtype
  *   s_new       NULL, or [B * Hkv] fp32 output: the scores the ring stores for the new
  *               tokens, pair i = b * Hkv + h at s_new[i]
  *   tau, pos    device values exactly as in kvp_step_delayed_dev (both required)
- * The score is x . w[h] + b1[h] summed in fp32 (bf16 products are exact); it may differ
- * from kvp_score's value for the same token in the last bits (different summation
- * order).  Everything else is kvp_step_delayed_dev with s_new = that score. */
+ *   ws          MLP only (may be NULL for LINEAR)
+ * Everything else is kvp_step_delayed_dev with s_new = that score. */
 kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* hidden_new, int32_t hdtype,
                                   const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                   const void* v_new, int32_t dtype, float* s_new, const float* tau,
-                                  int32_t* pos, hipStream_t stream);
+                                  int32_t* pos, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
  * kvp_decode_attn - GQA decode attention over the kept entries only.

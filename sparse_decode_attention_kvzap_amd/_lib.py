@@ -94,7 +94,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                            c_void_p]),
         "kvp_score_step_delayed": (c_int32, [P(KvpScorer), c_void_p, c_int32, P(KvpPagedKV),
                                              P(KvpRing), c_void_p, c_void_p, c_int32, c_void_p,
-                                             c_void_p, c_void_p, c_void_p]),
+                                             c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
         "kvp_decode_attn": (c_int32, [c_void_p, c_int32, c_int32, c_int32, P(KvpPagedKV),
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
@@ -389,19 +389,23 @@ def kvp_step_delayed(kv: PagedKV, ring: Ring, k_new: torch.Tensor, v_new: torch.
 
 def kvp_score_step_delayed(scorer: Scorer, hidden_new: torch.Tensor, kv: PagedKV, ring: Ring,
                            k_new: torch.Tensor, v_new: torch.Tensor, tau: torch.Tensor,
-                           pos: torch.Tensor, s_new: Optional[torch.Tensor] = None, stream=None):
-    """Linear scorer + delayed step in one kernel: hidden_new [B, 1, H] (or [B, H]) in the
-    scorer's dtype, k_new / v_new [B, Hkv, d]; tau (fp32[1]) and pos (int32[2]) on the
+                           pos: torch.Tensor, s_new: Optional[torch.Tensor] = None,
+                           ws: Optional[torch.Tensor] = None, stream=None):
+    """Score the new tokens inside the delayed step: hidden_new [B, 1, H] (or [B, H]) in
+    the scorer's dtype, k_new / v_new [B, Hkv, d]; tau (fp32[1]) and pos (int32[2]) on the
     device as for kvp_step_delayed_dev; s_new (optional, fp32, B*Hkv elements) receives
-    the new tokens' scores."""
-    _cuda(hidden_new, k_new, v_new, tau, pos, s_new)
+    the new tokens' scores; ws: the MLP scorer's workspace (kvp_score_workspace_size for
+    B tokens), unused by a linear scorer."""
+    _cuda(hidden_new, k_new, v_new, tau, pos, s_new, ws)
     assert tau.dtype == torch.float32 and pos.dtype == torch.int32 and pos.numel() >= 2
     if s_new is not None:
         assert s_new.dtype == torch.float32 and s_new.numel() >= kv.c.num_pairs
     _ok(load().kvp_score_step_delayed(ctypes.byref(scorer.c), hidden_new.data_ptr(),
                                       _dt(hidden_new), _kvref(kv), _ringref(ring),
                                       k_new.data_ptr(), v_new.data_ptr(), _dt(k_new), _p(s_new),
-                                      tau.data_ptr(), pos.data_ptr(), _stream(stream)),
+                                      tau.data_ptr(), pos.data_ptr(), _p(ws),
+                                      0 if ws is None else ws.numel() * ws.element_size(),
+                                      _stream(stream)),
         "kvp_score_step_delayed")
 
 

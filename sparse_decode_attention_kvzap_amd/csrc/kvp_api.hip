@@ -21,7 +21,10 @@ kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
                                    const float* tau_dev, int p, int* pos_dev, hipStream_t stream,
                                    const kvp_scorer* sc = nullptr, const void* x_new = nullptr,
-                                   float* s_out = nullptr);
+                                   float* s_out = nullptr, const float* part = nullptr);
+bool kvp_score_small_mlp_ok(const kvp_scorer* sc, int ntok);
+kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hidden, int ntok,
+                                           float* part, hipStream_t stream);
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   hipStream_t stream);
@@ -200,22 +203,36 @@ extern "C" kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* h
                                              int32_t hdtype, const kvp_paged_kv* kv,
                                              const kvp_ring* ring, const void* k_new,
                                              const void* v_new, int32_t dtype, float* s_new,
-                                             const float* tau, int32_t* pos, hipStream_t stream) {
+                                             const float* tau, int32_t* pos, void* ws,
+                                             size_t ws_bytes, hipStream_t stream) {
   kvp_status st = check_kv(kv);
   if (st != KVP_OK) return st;
   if (!ring) return KVP_E_ARG;
   if ((st = check_ring(ring)) != KVP_OK) return st;
   if (!sc || !hidden_new || !sc->w1 || !k_new || !v_new || !tau || !pos) return KVP_E_ARG;
-  if (sc->kind != KVP_SCORER_LINEAR) return KVP_E_UNSUPPORTED;
-  if (sc->n_kv_heads <= 0 || kv->num_pairs % sc->n_kv_heads != 0) return KVP_E_ARG;
+  if (sc->n_kv_heads <= 0 || sc->n_kv_heads > 16 || kv->num_pairs % sc->n_kv_heads != 0)
+    return KVP_E_ARG;
   if (!is_kv_dtype(hdtype) || hdtype != sc->wdtype) return KVP_E_DTYPE;
   if (dtype != kv->dtype) return KVP_E_DTYPE;
-  // rows are read in 16-byte pieces
-  const int elt = hdtype == KVP_BF16 ? 2 : 4;
-  if (sc->hidden <= 0 || sc->hidden % (16 / elt) != 0) return KVP_E_UNSUPPORTED;
-  if (((uintptr_t)hidden_new | (uintptr_t)sc->w1) & 15) return KVP_E_ARG;
+  if (sc->kind == KVP_SCORER_LINEAR) {
+    // rows are read in 16-byte pieces
+    const int elt = hdtype == KVP_BF16 ? 2 : 4;
+    if (sc->hidden <= 0 || sc->hidden % (16 / elt) != 0) return KVP_E_UNSUPPORTED;
+    if (((uintptr_t)hidden_new | (uintptr_t)sc->w1) & 15) return KVP_E_ARG;
+    return kvp_launch_step_delayed(kv, ring, k_new, v_new, nullptr, 1, 0.0f, tau, 0, pos, stream,
+                                   sc, hidden_new, s_new);
+  }
+  if (sc->kind != KVP_SCORER_MLP) return KVP_E_ARG;
+  const int B = kv->num_pairs / sc->n_kv_heads;
+  if (!sc->w2) return KVP_E_ARG;
+  if (sc->hidden <= 0 || sc->inner <= 0 || !kvp_score_small_mlp_ok(sc, B)) return KVP_E_UNSUPPORTED;
+  // the finish reads b1, W2 rows and the partial sums in 16-byte pieces
+  if (((uintptr_t)ws | (uintptr_t)sc->b1 | (uintptr_t)sc->w2) & 15) return KVP_E_ARG;
+  if (!ws || ws_bytes < kvp_score_workspace_size(sc, B, 1)) return KVP_E_WORKSPACE;
+  float* part = reinterpret_cast<float*>(ws);
+  if ((st = kvp_launch_score_small_partials(sc, hidden_new, B, part, stream)) != KVP_OK) return st;
   return kvp_launch_step_delayed(kv, ring, k_new, v_new, nullptr, 1, 0.0f, tau, 0, pos, stream,
-                                 sc, hidden_new, s_new);
+                                 sc, hidden_new, s_new, part);
 }
 
 extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,

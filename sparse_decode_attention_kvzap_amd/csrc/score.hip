@@ -137,27 +137,6 @@ typedef __attribute__((address_space(1))) void glb_void_t;
 __device__ __forceinline__ int swz_slot(int row, int chunk) { return chunk ^ (row & 7); }
 __device__ __forceinline__ int swz(int row, int chunk) { return row * MLP_ROWB + 16 * swz_slot(row, chunk); }
 
-// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-// erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2), t = 1/(1 + p x),
-// x >= 0, |error| <= 1.5e-7; odd extension for x < 0.  Branch-free (the GELU runs on
-// every unit of every token), and its error moves a score by ~1e-6 at most here.
-__device__ __forceinline__ float erf_as7126(float x) {
-  const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
-  float poly = fmaf(t, 1.061405429f, -1.453152027f);
-  poly = fmaf(t, poly, 1.421413741f);
-  poly = fmaf(t, poly, -0.284496736f);
-  poly = fmaf(t, poly, 0.254829592f);
-  poly *= t;
-  const float e = __builtin_amdgcn_exp2f(-ax * ax * 1.4426950408889634f);
-  return copysignf(fmaf(-poly, e, 1.0f), x);
-}
-
-// Exact-form GELU: 0.5 a (1 + erf(a / sqrt 2)) (not the tanh approximation).
-__device__ __forceinline__ float gelu_erf(float a) {
-  return 0.5f * a * (1.0f + erf_as7126(a * 0.70710678118654752f));
-}
-
 struct MlpArgs {
   const uint16_t* X;   // [ntok][H]
   const uint16_t* W1;  // [inner][H]
@@ -587,6 +566,28 @@ extern "C" size_t kvp_score_workspace_size(const kvp_scorer* sc, int32_t B, int3
   }
   if (sc->kind != KVP_SCORER_MLP) return 0;
   return (size_t)(sc->inner / MLP_BM) * (size_t)ntok * 16 * sizeof(float);
+}
+
+// The split-K partial sums of a small batch's first layer, alone (the MLP decode step
+// finishes them inside the delayed-step kernel): part[ks][token][unit], ks < H / 256.
+bool kvp_score_small_mlp_ok(const kvp_scorer* sc, int ntok) {
+  return sc->kind == KVP_SCORER_MLP && small_path(sc, ntok) && sc->inner % 256 == 0;
+}
+
+kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hidden, int ntok,
+                                           float* part, hipStream_t stream) {
+  const int H = sc->hidden, ksplit = H / SMALL_KSLICE, rows = sc->inner, rtiles = cdiv(rows, 16);
+  const uint16_t* xh = reinterpret_cast<const uint16_t*>(hidden);
+  const uint16_t* w1 = reinterpret_cast<const uint16_t*>(sc->w1);
+  const dim3 g(cdiv(rtiles * ksplit, 4));
+  switch (cdiv(ntok, 16)) {
+    case 1: hipLaunchKernelGGL(score_small_gemm_kernel<1>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+    case 2: hipLaunchKernelGGL(score_small_gemm_kernel<2>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+    case 3: hipLaunchKernelGGL(score_small_gemm_kernel<3>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+    default: hipLaunchKernelGGL(score_small_gemm_kernel<4>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
+  }
+  KVP_LAUNCH_CHECK();
+  return KVP_OK;
 }
 
 kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int T, float* scores,

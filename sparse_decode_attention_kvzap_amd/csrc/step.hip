@@ -32,6 +32,14 @@ struct StepArgs {
   const float* bias;  // [Hkv] or null
   float* s_out;       // [B * Hkv] or null: the scores, as stored in the ring
   int H, Hkv, x_bf16;
+  // Fused MLP finish (s_new unused when part is set): part[ks][b][unit] holds the split-K
+  // partial sums of the first layer for the new token of sequence b (ks < ksplit); the
+  // pair's wave adds them, then b1, GELU, the row h of W2 and b2.
+  const float* part;
+  int ksplit, ntok, inner;
+  const float* b1;
+  const float* w2;  // [Hkv][inner]
+  const float* b2;  // [Hkv] or null
 };
 
 template <typename E>
@@ -64,6 +72,46 @@ __device__ __forceinline__ float wave_dot(const X* __restrict__ x, const X* __re
   return wave_sum(acc);
 }
 
+// MLP score of one new token by one wave: lane l owns units 256c + 4l .. 256c + 4l + 3
+// (NC = inner / 256); the K slices are summed in slice order, 16 slices' loads at a time.
+template <int NC>
+__device__ __forceinline__ float wave_mlp_finish(const StepArgs& a, int tok, int h) {
+  const int lane = threadIdx.x & 63;
+  f32x4 acc[NC], b1v[NC], w2v[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int u = 256 * c + 4 * lane;
+    acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    b1v[c] = a.b1 ? *reinterpret_cast<const f32x4*>(a.b1 + u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    w2v[c] = *reinterpret_cast<const f32x4*>(a.w2 + (int64_t)h * a.inner + u);
+  }
+  for (int ks0 = 0; ks0 < a.ksplit; ks0 += 16) {
+    f32x4 v[16][NC];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int ks = min(ks0 + k, a.ksplit - 1);  // in bounds; slices past the end add 0
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+        v[k][c] = *reinterpret_cast<const f32x4*>(a.part + ((int64_t)ks * a.ntok + tok) * a.inner +
+                                                  256 * c + 4 * lane);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (ks0 + k < a.ksplit) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] += v[k][c];
+      }
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s = fmaf(gelu_erf(acc[c][e] + b1v[c][e]), w2v[c][e], s);
+  s = wave_sum(s);
+  if (a.b2) s += a.b2[h];
+  return s;
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   const int lane = threadIdx.x & 63;
@@ -86,6 +134,14 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
       s_new = wave_dot(reinterpret_cast<const float*>(a.x_new) + (int64_t)b * a.H,
                        reinterpret_cast<const float*>(a.w) + (int64_t)h * a.H, a.H);
     if (a.bias) s_new += a.bias[h];
+  } else if (a.part) {
+    const int b = pair / a.Hkv, h = pair % a.Hkv;
+    switch (a.inner >> 8) {
+      case 1: s_new = wave_mlp_finish<1>(a, b, h); break;
+      case 2: s_new = wave_mlp_finish<2>(a, b, h); break;
+      case 3: s_new = wave_mlp_finish<3>(a, b, h); break;
+      default: s_new = wave_mlp_finish<4>(a, b, h); break;
+    }
   }
   const int old_pos = a.ring.pos[(int64_t)pair * w + slot];
   const float old_s = a.ring.score[(int64_t)pair * w + slot];
@@ -230,7 +286,7 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   }
   if (lane == 0) {
     a.ring.pos[(int64_t)pair * w + slot] = p;
-    if (!a.x_new) s_new = a.s_new[(int64_t)pair * a.ld_s];
+    if (!a.x_new && !a.part) s_new = a.s_new[(int64_t)pair * a.ld_s];
     a.ring.score[(int64_t)pair * w + slot] = s_new;
     if (a.s_out) a.s_out[pair] = s_new;
   }
@@ -252,15 +308,24 @@ using namespace kvp;
 kvp_status kvp_launch_step_delayed(const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                    const void* v_new, const float* s_new, int64_t ld_s, float tau,
                                    const float* tau_dev, int p, int* pos_dev, hipStream_t stream,
-                                   const kvp_scorer* sc, const void* x_new, float* s_out) {
+                                   const kvp_scorer* sc, const void* x_new, float* s_out,
+                                   const float* part) {
   StepArgs a;
-  a.x_new = x_new;
+  const bool mlp = sc && sc->kind == KVP_SCORER_MLP;
+  a.x_new = mlp ? nullptr : x_new;
   a.w = sc ? sc->w1 : nullptr;
   a.bias = sc ? sc->b1 : nullptr;
   a.s_out = s_out;
   a.H = sc ? sc->hidden : 0;
   a.Hkv = sc ? sc->n_kv_heads : 1;
   a.x_bf16 = sc ? sc->wdtype == KVP_BF16 : 0;
+  a.part = mlp ? part : nullptr;
+  a.ksplit = mlp ? sc->hidden / 256 : 0;
+  a.ntok = mlp ? kv->num_pairs / sc->n_kv_heads : 0;
+  a.inner = mlp ? sc->inner : 0;
+  a.b1 = mlp ? sc->b1 : nullptr;
+  a.w2 = mlp ? sc->w2 : nullptr;
+  a.b2 = mlp ? sc->b2 : nullptr;
   a.kv = *kv;
   a.ring = *ring;
   a.k_new = k_new;

@@ -66,6 +66,10 @@ class PrunedKVCache:
         self.ws_threshold = torch.empty(L.kvp_threshold_workspace_size() // 4 + 1,
                                         dtype=torch.int32, device=dev)
         self.T0 = 0
+        c = scorer.c
+        self._fused_score = (c.kind == L.KVP_SCORER_LINEAR and c.hidden % 8 == 0) or (
+            c.wdtype == L.KVP_BF16 and B <= 64 and c.hidden % 256 == 0 and c.hidden <= 8192
+            and c.inner % 256 == 0 and c.inner <= 1024)
 
     # -- prefill -----------------------------------------------------------------
     def score(self, hidden: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
@@ -123,15 +127,17 @@ class PrunedKVCache:
     def advance(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 p: Optional[int] = None, stream=None):
         """Append a position (p, or the device-held next position when p is None): score
-        the new tokens, then the delayed step.  With a linear scorer both run in one kernel
-        (kvp_score_step_delayed); an MLP scorer runs kvp_score first."""
+        the new tokens and run the delayed step.  The scoring runs inside the step
+        (kvp_score_step_delayed) for a linear scorer, and for an MLP scorer of the shapes
+        that call takes (bf16, B <= 64, H and the width multiples of 256); otherwise
+        kvp_score runs first."""
         if p is not None:
             self.set_position(p)
         if not isinstance(self.tau, torch.Tensor):
             self.tau_dev.fill_(self.tau)
-        if self.scorer.kind == L.KVP_SCORER_LINEAR:
+        if self._fused_score:
             L.kvp_score_step_delayed(self.scorer, hidden_new, self.kv, self.ring, k_new, v_new,
-                                     self.tau_dev, self.pos_dev, self.s_new, stream)
+                                     self.tau_dev, self.pos_dev, self.s_new, self.ws_score, stream)
         else:
             L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
             L.kvp_step_delayed(self.kv, self.ring, k_new, v_new, self.s_new, self.tau_dev,

@@ -191,23 +191,34 @@ def test_host_validation_without_device(L):
                                     L.KVP_BF16, fake, 1, None, fake, None) == E_ARG
     assert lib.kvp_step_delayed_dev(ctypes.byref(kv), ctypes.byref(ring), fake, fake,
                                     L.KVP_BF16, fake, 1, fake, None, None) == E_ARG
-    # fused linear score + step: linear scorers only, matching dtypes, 16-byte rows, a
-    # pair count divisible by Hkv, device tau and position
+    # fused score + step: matching dtypes, 16-byte rows, a pair count divisible by Hkv,
+    # device tau and position; MLP scorers of the small-batch shapes with a workspace
     sst = lib.kvp_score_step_delayed
     kr = (ctypes.byref(kv), ctypes.byref(ring), fake, fake)
     lin = L.KvpScorer(L.KVP_SCORER_LINEAR, 4096, 0, 2, L.KVP_BF16, 0, fake, 0, 0, 0)
     mlp = L.KvpScorer(L.KVP_SCORER_MLP, 4096, 512, 2, L.KVP_BF16, 0, fake, 0, fake, 0)
-    assert sst(ctypes.byref(mlp), fake, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, fake, None) == E_UNSUP
-    assert sst(ctypes.byref(lin), fake, L.KVP_F32, *kr, L.KVP_BF16, None, fake, fake, None) == E_DTYPE
-    assert sst(ctypes.byref(lin), fake, L.KVP_BF16, *kr, L.KVP_F32, None, fake, fake, None) == E_DTYPE
-    assert sst(ctypes.byref(lin), fake + 2, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, fake, None) == E_ARG
-    assert sst(ctypes.byref(lin), fake, L.KVP_BF16, *kr, L.KVP_BF16, None, None, fake, None) == E_ARG
-    assert sst(ctypes.byref(lin), fake, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, None, None) == E_ARG
-    assert sst(None, fake, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, fake, None) == E_ARG
+
+    def call(sc, x=fake, hdt=L.KVP_BF16, dt=L.KVP_BF16, tau=fake, pos=fake, ws=None, nws=0):
+        return sst(None if sc is None else ctypes.byref(sc), x, hdt, *kr, dt, None, tau, pos,
+                   ws, nws, None)
+    assert call(lin, hdt=L.KVP_F32) == E_DTYPE
+    assert call(lin, dt=L.KVP_F32) == E_DTYPE
+    assert call(lin, x=fake + 2) == E_ARG
+    assert call(lin, tau=None) == E_ARG
+    assert call(lin, pos=None) == E_ARG
+    assert call(None) == E_ARG
     lin.hidden = 4100  # rows of 8200 bytes are not read in 16-byte pieces
-    assert sst(ctypes.byref(lin), fake, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, fake, None) == E_UNSUP
+    assert call(lin) == E_UNSUP
     lin.hidden, lin.n_kv_heads = 4096, 3  # 4 pairs are not B x 3 heads
-    assert sst(ctypes.byref(lin), fake, L.KVP_BF16, *kr, L.KVP_BF16, None, fake, fake, None) == E_ARG
+    assert call(lin) == E_ARG
+    assert call(mlp) == E_WS  # no workspace for the first layer's partial sums
+    assert call(mlp, ws=fake + 4, nws=1 << 20) == E_ARG  # misaligned workspace
+    mlp.inner = 384  # the finish takes widths in multiples of 256
+    assert call(mlp, ws=fake, nws=1 << 20) == E_UNSUP
+    mlp.inner, mlp.hidden = 512, 4000  # the split-K slices are 256 wide
+    assert call(mlp, ws=fake, nws=1 << 20) == E_UNSUP
+    mlp.hidden, mlp.wdtype = 4096, L.KVP_F32
+    assert call(mlp, hdt=L.KVP_F32, ws=fake, nws=1 << 20) == E_UNSUP
     # prefill attention: nulls, fp32 (not built), bad dtype, head ratio, head dim, window
     pf = lib.kvp_prefill_attn
     assert pf(None, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_ARG

@@ -404,23 +404,36 @@ def _same_cache(kvA, ringA, kvB, ringB):
                 assert np.array_equal(a, b), ("pool8", pr)
 
 
-@pytest.mark.parametrize("xdtype,H,kvdtype,d,w,bias,demote", [
-    (torch.bfloat16, 4096, torch.bfloat16, 128, 64, True, False),
-    (torch.float32, 256, torch.float32, 64, 32, False, False),
-    (torch.bfloat16, 1032, torch.bfloat16, 128, 32, True, True),  # H not a multiple of 512
-    (torch.float32, 100, torch.bfloat16, 64, 48, True, False),    # H not a multiple of 256
+@pytest.mark.parametrize("kind,xdtype,H,inner,kvdtype,d,w,bias,demote", [
+    ("linear", torch.bfloat16, 4096, 0, torch.bfloat16, 128, 64, True, False),
+    ("linear", torch.float32, 256, 0, torch.float32, 64, 32, False, False),
+    ("linear", torch.bfloat16, 1032, 0, torch.bfloat16, 128, 32, True, True),  # H % 512 != 0
+    ("linear", torch.float32, 100, 0, torch.bfloat16, 64, 48, True, False),    # H % 256 != 0
+    ("mlp", torch.bfloat16, 4096, 512, torch.bfloat16, 128, 64, True, False),   # 16 K slices
+    ("mlp", torch.bfloat16, 8192, 512, torch.bfloat16, 128, 32, True, True),    # 32 K slices
+    ("mlp", torch.bfloat16, 768, 256, torch.bfloat16, 64, 32, False, False),    # 3 slices, width 256
+    ("mlp", torch.bfloat16, 512, 1024, torch.float32, 64, 48, True, False),     # width 1024
 ])
-def test_score_step_delayed_fused(K, xdtype, H, kvdtype, d, w, bias, demote):
-    """kvp_score_step_delayed: the new tokens' linear scores match the oracle's, and the
-    cache it leaves holds, bit for bit, what kvp_step_delayed_dev leaves when fed those
-    scores -- two caches driven side by side for 80 steps (retentions, drops, demotions
-    and page allocations included)."""
+def test_score_step_delayed_fused(K, kind, xdtype, H, inner, kvdtype, d, w, bias, demote):
+    """kvp_score_step_delayed: the new tokens' scores match the oracle's (and kvp_score's
+    own small-batch scores), and the cache it leaves holds, bit for bit, what
+    kvp_step_delayed_dev leaves when fed those scores -- two caches driven side by side
+    for 80 steps (retentions, drops, demotions and page allocations included)."""
     B, Hkv, Hq, T0, steps = 3, 4, 8, 150, 80
     P = B * Hkv
     total = T0 + steps
-    Wt = seeded((Hkv, H), 101, xdtype, scale=1.0 / math.sqrt(H))
-    b = (seeded((Hkv,), 102) * 0.1 - 1.15) if bias else None
-    sc = K.Scorer(K.KVP_SCORER_LINEAR, Wt, b)
+    if kind == "linear":
+        W1 = seeded((Hkv, H), 101, xdtype, scale=1.0 / math.sqrt(H))
+        b1 = (seeded((Hkv,), 102) * 0.1 - 1.15) if bias else None
+        sc = K.Scorer(K.KVP_SCORER_LINEAR, W1, b1)
+    else:
+        W1 = seeded((inner, H), 101, xdtype, scale=1.0 / math.sqrt(H))
+        b1 = seeded((inner,), 102, scale=0.5) if bias else None
+        W2 = seeded((Hkv, inner), 107, scale=1.0 / math.sqrt(inner))
+        b2 = (seeded((Hkv,), 108) * 0.1 - 0.3) if bias else None
+        sc = K.Scorer(K.KVP_SCORER_MLP, W1, b1, W2, b2)
+    ws = torch.empty(max(1, K.kvp_score_workspace_size(sc, B, 1) // 4), dtype=torch.float32,
+                     device=DEV)
     x_all = seeded((steps, B, 1, H), 103, xdtype)
     k_all = seeded((B, Hkv, total, d), 104, kvdtype)
     v_all = seeded((B, Hkv, total, d), 105, kvdtype)
@@ -441,19 +454,28 @@ def test_score_step_delayed_fused(K, xdtype, H, kvdtype, d, w, bias, demote):
         caches.append((kv, ring, tau, pos))
     (kvA, ringA, tauA, posA), (kvB, ringB, tauB, posB) = caches
     s_new = torch.full((P,), float("nan"), dtype=torch.float32, device=DEV)
-    Wf = f64(Wt)
-    bf = f64(b) if bias else None
+    s_sep = torch.full((B, Hkv, 1), float("nan"), dtype=torch.float32, device=DEV)
+    ws_sep = torch.empty_like(ws)
     for i in range(steps):
         p = T0 + i
         k_new = k_all[:, :, p].contiguous()
         v_new = v_all[:, :, p].contiguous()
-        K.kvp_score_step_delayed(sc, x_all[i], kvA, ringA, k_new, v_new, tauA, posA, s_new)
+        K.kvp_score_step_delayed(sc, x_all[i], kvA, ringA, k_new, v_new, tauA, posA, s_new, ws)
         K.kvp_step_delayed(kvB, ringB, k_new, v_new, s_new, tauB, posB)
-        ref = oracle.score_linear(f64(x_all[i]), Wf, bf).reshape(P)
-        err = np.abs(s_new.cpu().double().numpy() - ref).max()
+        if kind == "linear":
+            ref = oracle.score_linear(f64(x_all[i]), f64(W1), f64(b1) if bias else None)
+        else:
+            ref = oracle.score_mlp(f64(x_all[i]), f64(W1), f64(b1) if bias else None, f64(W2),
+                                   f64(b2) if bias else None)
+        got = s_new.cpu().double().numpy()
+        err = np.abs(got - ref.reshape(P)).max()
         assert err < 2.5e-5, (i, err)
-        if i % 8 == 0 or i == steps - 1:
+        if i % 8 == 0:
+            if not (kind == "linear" and xdtype == torch.bfloat16 and H % 32):  # kvp_score's shapes
+                K.kvp_score(sc, x_all[i], s_sep, ws_sep)
+                assert np.abs(got - s_sep.cpu().double().numpy().reshape(P)).max() < 1e-5
             _same_cache(kvA, ringA, kvB, ringB)
+    _same_cache(kvA, ringA, kvB, ringB)
     assert int(posA[0]) == total and int(posA[1]) == 0
     assert K.kvp_check(kvA) == 0
 
