@@ -50,22 +50,37 @@ template <>
 __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 
 // One lane's share of x . w over H elements (16-byte loads, fp32 fused multiply-adds in
-// a fixed order), summed across the wave.
+// a fixed order), summed across the wave.  Eight 16-byte pieces of x and of w per lane
+// are requested together (addresses clamped in bounds, pieces past the end zeroed), so
+// H = 4096 in bf16 costs one memory round trip.
 template <typename X>
 __device__ __forceinline__ float wave_dot(const X* __restrict__ x, const X* __restrict__ w, int H) {
   constexpr int V = 16 / sizeof(X);
+  constexpr int NB = 8;
   const int lane = threadIdx.x & 63;
   float acc = 0.f;
-  for (int i = lane * V; i < H; i += 64 * V) {
-    const u32x4 xv = *reinterpret_cast<const u32x4*>(x + i);
-    const u32x4 wv = *reinterpret_cast<const u32x4*>(w + i);
+  for (int i0 = lane * V; i0 < H; i0 += 64 * V * NB) {
+    u32x4 xv[NB], wv[NB];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (sizeof(X) == 2) {
-        acc = fmaf(bf16_to_f32(xv[e] & 0xffffu), bf16_to_f32(wv[e] & 0xffffu), acc);
-        acc = fmaf(bf16_to_f32(xv[e] >> 16), bf16_to_f32(wv[e] >> 16), acc);
-      } else {
-        acc = fmaf(__uint_as_float(xv[e]), __uint_as_float(wv[e]), acc);
+    for (int k = 0; k < NB; ++k) {
+      const int i = min(i0 + 64 * V * k, H - V);
+      xv[k] = *reinterpret_cast<const u32x4*>(x + i);
+      wv[k] = *reinterpret_cast<const u32x4*>(w + i);
+    }
+#pragma unroll
+    for (int k = 0; k < NB; ++k) {
+      if (i0 + 64 * V * k >= H) {  // a clamped repeat: contributes exactly 0
+        xv[k] = u32x4{0u, 0u, 0u, 0u};
+        wv[k] = u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if constexpr (sizeof(X) == 2) {
+          acc = fmaf(bf16_to_f32(xv[k][e] & 0xffffu), bf16_to_f32(wv[k][e] & 0xffffu), acc);
+          acc = fmaf(bf16_to_f32(xv[k][e] >> 16), bf16_to_f32(wv[k][e] >> 16), acc);
+        } else {
+          acc = fmaf(__uint_as_float(xv[k][e]), __uint_as_float(wv[k][e]), acc);
+        }
       }
     }
   }
@@ -124,6 +139,20 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
   const int64_t roff = ((int64_t)pair * (w / PAGE) + rp) * PAGE * D;
   E* rk = reinterpret_cast<E*>(a.ring.k) + roff + rs * D;  // K row of the slot
   E* rv = reinterpret_cast<E*>(a.ring.v) + roff + rs;      // V column, stride PAGE
+  const int old_pos = a.ring.pos[(int64_t)pair * w + slot];
+  const float old_s = a.ring.score[(int64_t)pair * w + slot];
+  constexpr int PER = (D + 63) / 64;
+  E ko[PER], vo[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int dd = lane + 64 * e;
+    if (dd < D) {
+      ko[e] = rk[dd];
+      vo[e] = rv[dd * PAGE];
+    }
+  }
+  // the new token's score (fused scorer): needed only at the end, requested after the
+  // ring loads so both latencies overlap
   float s_new = 0.f;
   if (a.x_new) {
     const int b = pair / a.Hkv, h = pair % a.Hkv;
@@ -141,18 +170,6 @@ __global__ __launch_bounds__(256) void step_delayed_kernel(StepArgs a) {
       case 2: s_new = wave_mlp_finish<2>(a, b, h); break;
       case 3: s_new = wave_mlp_finish<3>(a, b, h); break;
       default: s_new = wave_mlp_finish<4>(a, b, h); break;
-    }
-  }
-  const int old_pos = a.ring.pos[(int64_t)pair * w + slot];
-  const float old_s = a.ring.score[(int64_t)pair * w + slot];
-  constexpr int PER = (D + 63) / 64;
-  E ko[PER], vo[PER];
-#pragma unroll
-  for (int e = 0; e < PER; ++e) {
-    const int dd = lane + 64 * e;
-    if (dd < D) {
-      ko[e] = rk[dd];
-      vo[e] = rv[dd * PAGE];
     }
   }
   const float tau = a.tau_dev ? a.tau_dev[0] : a.tau;
