@@ -52,7 +52,7 @@ typedef enum kvp_status {
   KVP_E_WORKSPACE = 3,   /* workspace missing or smaller than *_workspace_size() */
   KVP_E_CAPACITY = 4,    /* a page pool or block table ran out (device-detected) */
   KVP_E_HIP = 5,         /* a HIP runtime call or kernel launch failed */
-  KVP_E_UNSUPPORTED = 6  /* valid request this build does not implement */
+  KVP_E_UNSUPPORTED = 6  /* valid request the library does not implement */
 } kvp_status;
 
 typedef enum kvp_dtype { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
