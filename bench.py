@@ -246,10 +246,35 @@ def main():
                 dec.append(ev[0].elapsed_time(ev[2]))
                 att.append(e0.elapsed_time(e1))
         vis_k = cache.visible_token_heads()
+        bytes_k = attn_bytes(cache, wl, B, Hq, d)
+        # steady state: decode steps back to back (positions T0, T0 + 1, ... appended on the
+        # device, as in a decode loop), timed after three untimed steps let the compaction's
+        # write-back drain
+        cache.select(T0)
+        cache.compact(kd, vd)
+        cache.tau_dev.fill_(tau_k)
+        cache.pos_dev.copy_(pos_start)
+
+        def dstep():
+            K.kvp_score_step_delayed(scorer, h_new, cache.kv, cache.ring, k_new, v_new,
+                                     cache.tau_dev, cache.pos_dev, cache.s_new, cache.ws_score)
+            cache.attend(q)
+        for _ in range(3):
+            dstep()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(8):
+            dstep()
+        e1.record()
+        torch.cuda.synchronize()
+        assert cache.check() == 0
         keep_scaling.append({"keep": keep, "tau": tau_k if keep < 1.0 else None,
                              "visible_token_heads": vis_k,
-                             "attn_bytes": attn_bytes(cache, wl, B, Hq, d),
+                             "attn_bytes": bytes_k,
                              "decode_step_ms": float(np.median(dec)),
+                             "decode_step_steady_ms": e0.elapsed_time(e1) / 8,
                              "attn_isolated_ms": float(np.median(att))})
     del flush
     cache.calibrate(q_keep, T0)
@@ -257,10 +282,12 @@ def main():
     for e in keep_scaling:
         e["bytes_ratio_vs_keep1"] = e["attn_bytes"] / base["attn_bytes"]
         e["decode_step_ratio_vs_keep1"] = e["decode_step_ms"] / base["decode_step_ms"]
+        e["decode_step_steady_ratio_vs_keep1"] = e["decode_step_steady_ms"] / base["decode_step_steady_ms"]
         e["attn_ratio_vs_keep1"] = e["attn_isolated_ms"] / base["attn_isolated_ms"]
         e["attn_gbs"] = e["attn_bytes"] / (e["attn_isolated_ms"] * 1e-3) / 1e9
     log("[bench] keep scaling: " + "; ".join(
         f"keep {e['keep']}: decode {e['decode_step_ms']:.3f} ms (x{e['decode_step_ratio_vs_keep1']:.2f}), "
+        f"steady {e['decode_step_steady_ms']:.3f} ms (x{e['decode_step_steady_ratio_vs_keep1']:.2f}), "
         f"attn {e['attn_isolated_ms']:.3f} ms (x{e['attn_ratio_vs_keep1']:.2f}), bytes x{e['bytes_ratio_vs_keep1']:.2f}"
         for e in keep_scaling))
 
