@@ -10,6 +10,12 @@
 // kept at low precision instead (absmax int8 or int4 codes per (token, head), K and V
 // separately).
 //
+// Pages are written with non-temporal stores: the pool (hundreds of MB) is not read again
+// until the next decode attention, and ordinary stores leave it as dirty lines in the
+// MALL whose write-back then competes with that attention's reads (measured on the
+// Qwen-3-8B-like layer: attention right after compaction 142 -> 113 us, compaction
+// 240 -> 255 us).
+//
 // Work units are destination pages of 16 slots.  Copy units (a pair's pool pages, then
 // its ring pages) go to compact_copy_kernel and low-precision pages to
 // compact_quant_kernel; in both, each wave owns one contiguous run of units, so it
@@ -226,7 +232,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a
 #pragma unroll
     for (int i = 0; i < NPL; ++i) {
       const int c = lane + 64 * i;
-      *reinterpret_cast<u32x4*>(kdst + c * EPC) = kx[i];
+      __builtin_nontemporal_store(kx[i], reinterpret_cast<u32x4*>(kdst + c * EPC));
       *reinterpret_cast<u32x4*>(vt + c * EPC) = vx[i];  // V rows [16][D] in LDS
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -239,7 +245,7 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a
       E tmp[EPC];
 #pragma unroll
       for (int e = 0; e < EPC; ++e) tmp[e] = vt[(t0 + e) * D + dd];
-      *reinterpret_cast<u32x4*>(vdst + dd * PAGE + t0) = *reinterpret_cast<const u32x4*>(tmp);
+      __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(tmp), reinterpret_cast<u32x4*>(vdst + dd * PAGE + t0));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
@@ -336,9 +342,9 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs 
         vc[row * D + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale, QMAX));
       }
       int8_t* kd = kdst + (row * D + col) * BITS / 8;
-      if constexpr (CB == 8) *reinterpret_cast<u32x2*>(kd) = u32x2{w[0], w[1]};
-      else if constexpr (CB == 4) *reinterpret_cast<uint32_t*>(kd) = w[0];
-      else *reinterpret_cast<uint16_t*>(kd) = static_cast<uint16_t>(w[0]);
+      if constexpr (CB == 8) __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(kd));
+      else if constexpr (CB == 4) __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(kd));
+      else __builtin_nontemporal_store(static_cast<uint16_t>(w[0]), reinterpret_cast<uint16_t*>(kd));
       if ((c % CPR) == 0) {
         a.kv.k8_scale[(int64_t)u * PAGE + row] = kscale;
         a.kv.v8_scale[(int64_t)u * PAGE + row] = vscale;
@@ -359,8 +365,8 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs 
         if constexpr (BITS == 8) w[t / 4] |= (code & 0xffu) << (8 * (t % 4));
         else w[t / 8] |= (code & 0xfu) << (4 * (t % 8));
       }
-      if constexpr (BITS == 8) *reinterpret_cast<u32x4*>(vdst + dd * PAGE) = u32x4{w[0], w[1], w[2], w[3]};
-      else *reinterpret_cast<u32x2*>(vdst + dd * (PAGE / 2)) = u32x2{w[0], w[1]};
+      if constexpr (BITS == 8) __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4*>(vdst + dd * PAGE));
+      else __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(vdst + dd * (PAGE / 2)));
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     __builtin_amdgcn_wave_barrier();
