@@ -256,6 +256,23 @@ def _sdpa_gqa(q, K, V, mask, scale):
     return o[:, :, 0, :].numpy()
 
 
+def test_softmax_scale_is_the_sdpa_default():
+    # the library routine's own default scale (1/sqrt(d), scale=None) against the fp32
+    # value the oracle hands to both paths: equal up to that value's rounding
+    rng = np.random.default_rng(71)
+    for d in (8, 64, 128):
+        B, Hq, Hkv, T = 1, 4, 2, 50
+        q = rng.standard_normal((B, Hq, d))
+        K = rng.standard_normal((B, Hkv, T, d))
+        V = rng.standard_normal((B, Hkv, T, d))
+        got = oracle.decode_attention(q, K, V, np.ones((B, Hkv, T), bool), oracle.sm_scale(d))
+        Kx = torch.from_numpy(K).repeat_interleave(Hq // Hkv, dim=1)
+        Vx = torch.from_numpy(V).repeat_interleave(Hq // Hkv, dim=1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(q)[:, :, None, :], Kx, Vx)[:, :, 0, :].numpy()
+        assert np.allclose(got, ref, atol=1e-6, rtol=0), d
+
+
 def test_dense_special_case_equals_sdpa():
     rng = np.random.default_rng(7)
     B, Hq, Hkv, T, d = 2, 8, 2, 300, 16
