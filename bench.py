@@ -209,6 +209,46 @@ def main():
             iso.append(e0.elapsed_time(e1))
     score_iso_ms = float(np.median(iso))
 
+    # The decode step alone, back to back on the compressed context (positions T0, T0 + 1,
+    # ... appended on the device): eagerly, and captured once as a HIP graph and replayed
+    # (every per-step value lives in device memory, so the replays need no host work).
+    def decode_only():
+        K.kvp_score_step_delayed(scorer, h_new, cache.kv, cache.ring, k_new, v_new,
+                                 cache.tau_dev, cache.pos_dev, cache.s_new, cache.ws_score)
+        cache.attend(q)
+
+    def time_steps(fn, n=8):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    cache.select(T0)
+    cache.compact(kd, vd)
+    cache.pos_dev.copy_(pos_start)
+    decode_eager_ms = time_steps(decode_only)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        decode_only()
+    torch.cuda.synchronize()
+    cache.select(T0)
+    cache.compact(kd, vd)
+    cache.pos_dev.copy_(pos_start)
+    decode_graph_ms = time_steps(graph.replay)
+    assert cache.check() == 0
+    del graph
+    log(f"[bench] decode step back to back: eager {decode_eager_ms * 1e3:.1f} us, "
+        f"graph replay {decode_graph_ms * 1e3:.1f} us")
+
     # End-to-end scaling with kept tokens: the decode step (score the new tokens ->
     # delayed step -> attention) right after compressing the same context at several
     # keep ratios (keep 1.0: tau = -inf keeps every token), and the attention alone after
@@ -382,7 +422,12 @@ def main():
                    "total_token_heads": total_th},
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "decode_step": {"ms": decode_ms, "token_heads_per_s": visible / (decode_ms * 1e-3)},
+        "decode_step": {"ms": decode_ms, "token_heads_per_s": visible / (decode_ms * 1e-3),
+                        "back_to_back_eager_ms": decode_eager_ms,
+                        "back_to_back_graph_ms": decode_graph_ms,
+                        "note": "ms: right after compaction, inside the step; back_to_back: the "
+                                "decode step repeated on the compressed context, eagerly and "
+                                "as one captured graph replayed"},
         "kernels": kernels,
         "keep_scaling": keep_scaling,
     }
