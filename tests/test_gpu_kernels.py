@@ -315,6 +315,41 @@ def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
         assert np.abs(ref8 - ref).max() > 10 * 2e-3
 
 
+@pytest.mark.parametrize("bits,B,Hq,Hkv,T,d,ring_w,case", [
+    (8, 2, 16, 2, 1500, 64, 128, "random"),   # int8 codes at d 64, g 8
+    (4, 1, 32, 2, 2000, 128, 128, "random"),  # int4, g 16 (the largest group)
+    (4, 8, 64, 8, 300, 128, 128, "random"),   # int4, 64 pairs of short contexts: many segments
+    (8, 2, 8, 2, 700, 128, 0, "random"),      # int8 without a ring
+    (4, 2, 8, 2, 900, 128, 128, "extremes"),  # one pair with no code region, one all codes
+    (8, 2, 8, 2, 900, 128, 0, "extremes"),    # ... and one pair with no full-precision token
+])
+def test_decode_attn_lowprec_edges(K, bits, B, Hq, Hkv, T, d, ring_w, case):
+    """Attention over a full-precision pool (+ ring) and an int8 / int4 pool in one
+    softmax, at the head-group, head-dim and pair-count limits and with regions of a
+    pair empty; reruns on a garbage-filled workspace are bit-identical."""
+    P = B * Hkv
+    g = torch.Generator().manual_seed(T + d + bits)
+    keep = (torch.rand((P, T), generator=g) < 0.15).numpy()
+    if case == "extremes":
+        keep[0, :] = True   # nothing demoted
+        keep[1, :] = False  # every token demoted (bar the ring, when there is one)
+    if ring_w:
+        keep[:, T - ring_w:] = True  # the ring's positions are never demoted
+    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, ring_w, seed=81,
+                                 demote=True, bits=bits)
+    q = seeded((B, Hq, d), 84, torch.bfloat16)
+    out = torch.full((B, Hq, d), float("nan"), device=DEV)
+    ws = K.decode_attn_workspace(B, Hq, kv)
+    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
+    ref = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
+                                         oracle.sm_scale(d), bits=bits)
+    check_attention(out, ref, torch.bfloat16)
+    out2 = torch.zeros_like(out)
+    ws.fill_(-1)
+    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out2, ws)
+    assert torch.equal(out, out2)
+
+
 # ---------------------------------------------------------------------------- delayed step
 
 
