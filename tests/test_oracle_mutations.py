@@ -165,6 +165,23 @@ def m_quant_truncate(x, qmax):
     return np.clip(np.trunc(xf / scale), -qmax, qmax).astype(np.int8), scale
 
 
+def m_beacon_v_left_exact(K, V, beacon, bits=8):
+    Kh, Vh, codes = orig["beacon_kv"](K, V, beacon, bits)
+    return Kh, np.array(V, dtype=np.float64, copy=True), codes
+
+
+def m_beacon_v_with_k_scale(K, V, beacon, bits=8):
+    Kh, Vh, (kc, ks, vc, vs) = orig["beacon_kv"](K, V, beacon, bits)
+    Vh = np.array(V, dtype=np.float64, copy=True)
+    dem = ~beacon
+    Vh[dem] = vc[dem].astype(np.float64) * ks[dem][:, None].astype(np.float64)
+    return Kh, Vh, (kc, ks, vc, vs)
+
+
+def m_beacon_mask_inverted(K, V, beacon, bits=8):
+    return orig["beacon_kv"](K, V, ~np.asarray(beacon, dtype=bool), bits)
+
+
 # (oracle function, mutant, pins that must catch it: (test function, kwargs))
 P = pins
 MUTANTS = [
@@ -205,6 +222,13 @@ MUTANTS = [
       (P.test_int4_on_grid_inputs_are_exact_and_round_half_even, {})]),
     ("quantize_absmax", m_quant_truncate,
      [(P.test_int8_roundtrip_bound_and_extremes, {}), (P.test_int8_codes_match_brute_force, {})]),
+    ("beacon_kv", m_beacon_v_left_exact,
+     [(P.test_beacon_round_trip_of_k_and_v_halves, {"bits": 8}),
+      (P.test_beacon_round_trip_of_k_and_v_halves, {"bits": 4})]),
+    ("beacon_kv", m_beacon_v_with_k_scale, [(P.test_beacon_round_trip_of_k_and_v_halves, {"bits": 8})]),
+    ("beacon_kv", m_beacon_mask_inverted,
+     [(P.test_beacon_round_trip_of_k_and_v_halves, {"bits": 8}),
+      (P.test_beacon_all_beacons_is_dense_and_demotion_changes_output, {})]),
 ]
 
 

@@ -578,3 +578,47 @@ def test_beacon_all_beacons_is_dense_and_demotion_changes_output():
     Kh, Vh, _ = oracle.beacon_kv(Kg.astype(np.float32).astype(np.float64),
                                  Vg.astype(np.float32).astype(np.float64), none)
     assert np.abs(Kh - Kg).max() < 1e-6
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_beacon_round_trip_of_k_and_v_halves(bits):
+    """BeaconKV briefing, body: beacon entries stay at full precision, every other
+    entry is stored at low precision.  Both halves of a demoted row, K and V, are
+    replaced by their own codes times their own absmax scale; beacon rows keep their
+    exact bits."""
+    rng = np.random.default_rng(40 + bits)
+    B, Hkv, T, d = 2, 2, 48, 16
+    qmax = 127 if bits == 8 else 7
+    K = (rng.standard_normal((B, Hkv, T, d)) * 2).astype(np.float32).astype(np.float64)
+    V = (rng.standard_normal((B, Hkv, T, d)) * 0.5).astype(np.float32).astype(np.float64)
+    beacon = rng.random((B, Hkv, T)) < 0.3
+    beacon[0, 0, :5] = True
+    beacon[1, 1, -5:] = False
+    Kh, Vh, (kc, ks, vc, vs) = oracle.beacon_kv(K, V, beacon, bits=bits)
+    # beacon rows: the exact input bits, no codes
+    assert np.array_equal(Kh[beacon], K[beacon]) and np.array_equal(Vh[beacon], V[beacon])
+    for X, Xh, c, s in ((K, Kh, kc, ks), (V, Vh, vc, vs)):
+        dem = ~beacon
+        # demoted rows: exactly code * scale of the row's own codes and scale
+        assert np.array_equal(Xh[dem], c[dem].astype(np.float64) * s[dem][:, None].astype(np.float64))
+        # the scale is the row's own absmax over qmax in fp32, and the absmax element maps to +-qmax
+        a = np.abs(X[dem]).max(axis=1).astype(np.float32)
+        assert np.array_equal(s[dem], (a / np.float32(qmax)).astype(np.float32))
+        assert np.all(np.abs(c[dem]).max(axis=1) == qmax)
+        # codes are the nearest grid points of x / scale (brute force over the grid)
+        rows = np.flatnonzero(dem.ravel())[:6]
+        Xr, cr, sr = X.reshape(-1, d), c.reshape(-1, d), s.ravel()
+        for r in rows:
+            y = Xr[r].astype(np.float32) / sr[r]
+            assert [int(v) for v in cr[r]] == [_nearest_code_brute(float(v), qmax) for v in y]
+        # a demoted row really moved, within half a grid step per element
+        err = np.abs(Xh[dem] - X[dem])
+        assert err.max() > 0
+        assert np.all(err <= s[dem][:, None].astype(np.float64) / 2 * (1 + 1e-6))
+    # the attention on a mixed mask differs from both the dense and the all-demoted one
+    q = rng.standard_normal((B, 4, d))
+    sc = oracle.sm_scale(d)
+    allv = np.ones((B, Hkv, T), bool)
+    mixed = oracle.beacon_decode_attention(q, K, V, beacon, sc, bits=bits)
+    assert np.allclose(mixed, oracle.decode_attention(q, Kh, Vh, allv, sc), rtol=0, atol=1e-15)
+    assert np.abs(mixed - oracle.decode_attention(q, K, V, allv, sc)).max() > 1e-6
