@@ -5,16 +5,25 @@
 // briefing (jiinsi.com), body -- beacon entries at full precision and the others at
 // low precision are read in one attention.
 //
-// Work decomposition (split-K, evenly balanced):
-//   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages,
-//   then its ring pages, padded to an even count) and, when a low-precision pool
-//   exists, a "region B" (its int8 or int4 pages, padded to even).  The A regions are
-//   concatenated and cut into NWAVES equal, even-length ranges, and so are the B
-//   regions; each wave walks its A range, then its B range, 32 tokens (two pages) at a
-//   time, and emits one partial (m, l, o) record per region it touches.  A second kernel (one wave per pair and query head) merges a
-//   pair's records with a log-sum-exp combine in a fixed order, so the result is
-//   deterministic.  The kernel boundary makes the records visible: no atomics and no
-//   device-scope fences (each of which writes back an XCD's L2) in the hot kernel.
+// One kernel per call, split-K with a deterministic in-kernel merge:
+//   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages, then
+//   its ring pages, padded to an even count) and, when a low-precision pool exists, a
+//   "region B" (its int8 or int4 pages, padded to even).  The A regions are concatenated
+//   into one page sequence and the B regions into another.  Each sequence is cut into
+//   units: one large static unit per wave (most of the pages), then small dynamic units
+//   that waves take from a ticket counter as they run out of work, so the waves of a
+//   faster XCD absorb the tail of a slower one.  Unit boundaries depend only on the page
+//   counts, never on timing, so every (unit, region) intersection -- a segment -- always
+//   covers the same pages.  A wave walks its segments 32 tokens (two pages) at a time and
+//   writes one partial (max, sum, output) record per segment; the wave that writes a
+//   pair's last record (per-pair arrival counter) merges the pair's records in page order
+//   and writes the output.  The result is therefore bit-identical from run to run.
+//   Records are published across XCDs without cache maintenance: they are stored with
+//   device-scope (sc1) stores, the writer waits for their completion before it bumps the
+//   arrival counter, and the merging wave reads them with device-scope loads.
+//   Record slot of the segment (region s, unit u) = base + s + u: along a sequence,
+//   consecutive segments advance s or u (or both), so the slot is unique, and a region's
+//   records occupy consecutive slots.
 //
 // Per 32-token step (bf16, head dim D, g query heads of one KV head):
 //   S^T[32 tok x 16 heads] = K . Q^T on 16x16x32 bf16 MFMA (exact products, fp32
@@ -24,6 +33,9 @@
 //   O^T[D x 16 heads] += V^T . P^T on MFMA, with P split into bf16 hi + lo parts so
 //   the probabilities keep ~16 significant bits (V is exact in bf16).
 //   V pages are stored dim-major ([d][16]) so V^T fragments are plain 16-byte loads.
+// The bf16 stream keeps one step of K/V loads in flight and, one segment ahead, the next
+// segment's query, length and block-table entries, so crossing from one pair to the
+// next costs no memory round trip.
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -37,7 +49,22 @@ constexpr int ATTN_GRID = 256;  // one work-group (4 waves) per CU on a 256-CU p
 // one wave per SIMD (the bf16 and int8 streams ran 1-4% slower with two).
 constexpr int ATTN_MAX_WPE = 2;
 constexpr int ATTN_MAX_NWAVES = ATTN_MAX_WPE * ATTN_GRID * ATTN_WG_WAVES;
-static_assert(ATTN_GRID % 8 == 0, "ranges are numbered per XCD (8 XCDs)");
+// Register sets of code-pool loads in flight per wave (two 32-token steps): more sets
+// (4 or 6) made the int4 stream 5-15% slower, fewer leave the loads exposed.
+constexpr int ATTN_LP_SETS = 2;
+static_assert(ATTN_GRID % 8 == 0, "units are numbered per XCD (8 XCDs)");
+
+// Workspace: control words, per-pair arrival counts, then the records.  The counts and
+// control words must be zero before the first call; every call leaves them zero.
+constexpr int CTL_TICKET_A = 0, CTL_TICKET_B = 1, CTL_DONE = 2;
+constexpr size_t ATTN_CTL_BYTES = 256;
+
+// Dynamic units: about 1/20 of a wave's fair share each (2..8 pages), covering up to 12%
+// of a sequence and at most two units per wave.
+constexpr int ATTN_DYN_DIV = 20;
+constexpr int ATTN_DYN_MAX_PAGES = 8;
+constexpr int ATTN_DYN_PCT = 12;
+constexpr int ATTN_DYN_PER_WAVE = 2;
 
 struct AttnArgs {
   const void* q;
@@ -47,71 +74,471 @@ struct AttnArgs {
   kvp_ring ring;
   int has_ring;
   float scale_log2;  // sm_scale * log2(e)
-  float* part;       // partial records
-  int* plan_c;       // [2 * num_pairs + 1] partial-slot prefix, written by work-group 0
-  int rec_floats;    // g * (D + 2)
+  int* ctl;          // control words (tickets, done count)
+  int* cnt;          // [num_pairs] record arrivals
+  int* link;         // [num_pairs] next pair of a wave's list of pairs to merge
+  float* part;       // records, rec_floats each
+  int part_bytes;    // size of the record area (buffer-resource range)
+  int rec_floats;    // g * (D + 2) rounded up to 4: o[g][D], then m[g], then l[g]
 };
 
 // -------------------------------------------------------------------------------
-// Plan: page prefix P[] over the 2*num_pairs regions and partial-slot prefix C[].
-// Every work-group recomputes it into LDS (num_pairs lengths, a few KB of L2 reads).
+// Plan: page prefix P[] over the regions, computed by wave 0 of every work-group into
+// LDS (one load per region, one wave scan, no barrier inside).
 // -------------------------------------------------------------------------------
-__device__ __forceinline__ int region_pages(const AttnArgs& a, int s) {
-  const int np = a.kv.num_pairs;
-  int n;
-  if (s < np) {
-    n = cdiv(a.kv.length[s], PAGE) + (a.has_ring ? a.ring.window / PAGE : 0);
-  } else {
-    n = (a.kv.num_pages8 > 0) ? cdiv(a.kv.length8[s - np], PAGE) : 0;
-  }
-  return (n + 1) & ~1;
-}
-
-// The bf16/fp32 regions (A) and the low-precision regions (B) are split separately: a
-// wave takes per_a pages of the A sequence and per_b pages of the B sequence.  One
-// split over both would balance pages, but a bf16 page moves 2x (int8) to 4x (int4)
-// the bytes of a low-precision page, and the waves that drew bf16 pages set the time
-// (measured: the int4 pool ran no faster than the int8 one).
-struct Plan {
-  int* P;  // [nseg + 1] page prefix over the regions (A regions first)
-  int* C;  // [nseg + 1] record-slot prefix
-  int total;    // pages of all regions
-  int total_a;  // pages of the A regions (= P[num_pairs])
-  int per_a, per_b;
-};
-
-// Regions in the plan: the low-precision regions only exist with a low-precision pool.
 __device__ __forceinline__ int plan_regions(const AttnArgs& a) {
   return (a.kv.num_pages8 > 0 ? 2 : 1) * a.kv.num_pairs;
 }
 
-__device__ Plan build_plan(const AttnArgs& a, int* lds) {
-  const int nseg = plan_regions(a);
-  Plan pl;
-  pl.P = lds;
-  pl.C = lds + nseg + 1;
-  int* tmp = pl.C + nseg + 1;
-  for (int s = threadIdx.x; s <= nseg; s += blockDim.x) pl.P[s] = (s < nseg) ? region_pages(a, s) : 0;
-  __syncthreads();
-  pl.total = block_scan_excl(pl.P, nseg + 1, tmp);
+__device__ __forceinline__ int region_pages_of(int len, int extra) { return (cdiv(len, PAGE) + extra + 1) & ~1; }
+
+// Wave 0: P[0] = 0, P[s + 1] = P[s] + pages of region s.  Each lane takes a run of
+// regions; lengths are requested eight at a time so the loads overlap.
+// The A regions' pool lengths go to Lens[] on the way.
+__device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Lens, int nseg) {
+  const int lane = threadIdx.x & 63;
   const int np = a.kv.num_pairs;
-  pl.total_a = pl.P[np];
-  const int nwaves = gridDim.x * ATTN_WG_WAVES;
-  auto split = [nwaves](int pages) { return max(2, (((pages + nwaves - 1) / nwaves) + 1) & ~1); };
-  pl.per_a = split(pl.total_a);
-  pl.per_b = split(pl.total - pl.total_a);
-  for (int s = threadIdx.x; s <= nseg; s += blockDim.x) {
-    int c = 0;
-    if (s < nseg) {
-      const int base = s < np ? 0 : pl.total_a, per = s < np ? pl.per_a : pl.per_b;
-      const int p0 = pl.P[s] - base, p1 = pl.P[s + 1] - base;
-      if (p1 > p0) c = (p1 - 1) / per - p0 / per + 1;
+  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
+  const int per = cdiv(nseg, 64);
+  const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
+  int sum = 0;
+  for (int b = s0; b < s1; b += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = b + i;
+      v[i] = 0;
+      if (s < s1) v[i] = (s < np) ? a.kv.length[s] : a.kv.length8[s - np];
     }
-    pl.C[s] = c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int s = b + i;
+      if (s < s1) {
+        if (s < np) Lens[s] = v[i];
+        const int n = region_pages_of(v[i], s < np ? nring : 0);
+        P[s + 1] = n;
+        sum += n;
+      }
+    }
   }
-  __syncthreads();
-  block_scan_excl(pl.C, nseg + 1, tmp);
-  return pl;
+  int run = wave_incl_scan(sum) - sum;
+  for (int b = s0; b < s1; b += 8) {
+    int v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = (b + i < s1) ? P[b + i + 1] : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (b + i < s1) {
+        run += v[i];
+        P[b + i + 1] = run;
+      }
+    }
+  }
+  if (lane == 0) P[0] = 0;
+}
+
+// Largest s in [lo, hi) with P[s] <= x (P nondecreasing, P[lo] <= x): one LDS read and
+// one ballot per level of 64.
+__device__ __forceinline__ int seg_search(const int* P, int lo, int hi, int x) {
+  const int lane = threadIdx.x & 63;
+  int n = hi - lo;
+  while (n > 64) {
+    const int stride = cdiv(n, 64);
+    const int s = lo + lane * stride;
+    const uint64_t m = __ballot(s < hi && P[s] <= x);
+    const int k = 63 - __builtin_clzll(m);
+    lo += k * stride;
+    hi = min(hi, lo + stride);
+    n = hi - lo;
+  }
+  const int s = lo + lane;
+  const uint64_t m = __ballot(s < hi && P[s] <= x);
+  return lo + (63 - __builtin_clzll(m));
+}
+
+// One page sequence (A: bf16/fp32 regions; B: low-precision regions) cut into units.
+struct SeqSplit {
+  int N;      // pages
+  int s0;     // static unit size (0: no static band)
+  int s1;     // dynamic unit size
+  int ud;     // dynamic units
+  int base;   // first record slot of the sequence
+  int r0;     // first region of the sequence in P
+  int pbase;  // P[r0]
+};
+
+__device__ __forceinline__ SeqSplit make_split(int N, int nw, int base, int r0, int pbase) {
+  SeqSplit q;
+  q.N = N;
+  q.base = base;
+  q.r0 = r0;
+  q.pbase = pbase;
+  q.s1 = 2;
+  q.ud = 0;
+  q.s0 = N > 0 ? ((cdiv(N, nw) + 1) & ~1) : 0;  // even; the last units may be short or empty
+  return q;
+}
+
+// Units of a sequence: u < nw static ([u s0, (u + 1) s0)), then dynamic.
+__device__ __forceinline__ int unit_of(const SeqSplit& q, int nw, int x) {
+  const int st = nw * q.s0;
+  return x < st ? x / max(1, q.s0) : nw + (x - st) / q.s1;
+}
+
+// Records (segments) of region s of the sequence, and the first one's unit.
+__device__ __forceinline__ int region_records(const SeqSplit& q, int nw, const int* P, int s, int& uf) {
+  const int p0 = P[s] - q.pbase, p1 = P[s + 1] - q.pbase;
+  if (p1 <= p0) {
+    uf = 0;
+    return 0;
+  }
+  uf = unit_of(q, nw, p0);
+  return unit_of(q, nw, p1 - 1) - uf + 1;
+}
+
+// -------------------------------------------------------------------------------
+// Units and segments
+// -------------------------------------------------------------------------------
+struct SegDesc {
+  int s;         // region index in P
+  int vlo, vhi;  // pages of the region covered by the segment
+  int u;         // unit
+  int rev;       // walk backwards
+  int ok;        // 0: no more work
+};
+
+// Walks a wave's units of one sequence: its static unit, then dynamic units by ticket.
+// The ticket of the next unit is requested when a unit starts, so its latency hides
+// behind that unit's pages.
+struct UnitIter {
+  SeqSplit sp;
+  int nw, gw, nreg;
+  int* ticket;
+  int started, have;
+  int u, X0, X1, rev;  // current unit, its pages in P coordinates
+  int r, r_end;        // next region to emit, last region (walk order)
+  int tk_v;            // lane 0: the requested ticket
+  int tk_pending;
+  int finished;        // a ticket past the end was drawn: no further requests
+};
+
+__device__ __forceinline__ void iter_init(UnitIter& it, const SeqSplit& sp, int nw, int gw, int nreg, int* ticket) {
+  it.sp = sp;
+  it.nw = nw;
+  it.gw = gw;
+  it.nreg = nreg;
+  it.ticket = ticket;
+  it.started = 0;
+  it.have = 0;
+  it.tk_v = 0;
+  it.tk_pending = 0;
+  it.finished = 0;
+}
+
+__device__ __forceinline__ int request_ticket(int* ticket) {
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(ticket, 1);
+  return v;
+}
+
+__device__ __forceinline__ bool iter_next_unit(UnitIter& it, const int* P) {
+  if (it.finished) return false;
+  int u = -1;
+  if (!it.started) {
+    it.started = 1;
+    if (it.sp.s0 > 0 && it.gw * it.sp.s0 < it.sp.N) u = it.gw;  // the last static units may be empty
+  }
+  if (u < 0) {
+    if (it.sp.ud == 0) {
+      it.finished = 1;
+      return false;
+    }
+    const int t = __builtin_amdgcn_readfirstlane(it.tk_pending ? it.tk_v : request_ticket(it.ticket));
+    it.tk_pending = 0;
+    if ((unsigned)t >= (unsigned)it.sp.ud) {
+      it.finished = 1;
+      return false;
+    }
+    u = it.nw + t;
+  }
+  if (it.sp.ud > 0) {
+    it.tk_v = request_ticket(it.ticket);
+    it.tk_pending = 1;
+  }
+  int x0, x1;
+  if (u < it.nw) {
+    x0 = u * it.sp.s0;
+    x1 = min(it.sp.N, x0 + it.sp.s0);
+    it.rev = u & 1;  // odd static units walk backwards: opposite directions keep the
+                     // 1024 streams from settling on the same HBM channels (measured: 10%
+                     // at one keep ratio); the order only changes rounding inside a record
+  } else {
+    x0 = it.nw * it.sp.s0 + (u - it.nw) * it.sp.s1;
+    x1 = min(it.sp.N, x0 + it.sp.s1);
+    it.rev = 0;
+  }
+  it.u = u;
+  it.X0 = it.sp.pbase + x0;
+  it.X1 = it.sp.pbase + x1;
+  const int rf = seg_search(P, it.sp.r0, it.sp.r0 + it.nreg, it.X0);
+  const int rl = seg_search(P, it.sp.r0, it.sp.r0 + it.nreg, it.X1 - 1);
+  it.r = it.rev ? rl : rf;
+  it.r_end = it.rev ? rf : rl;
+  it.have = 1;
+  return true;
+}
+
+__device__ __forceinline__ SegDesc iter_next_seg(UnitIter& it, const int* P) {
+  SegDesc d;
+  d.ok = 0;
+  for (;;) {
+    if (!it.have && !iter_next_unit(it, P)) return d;
+    while (it.have) {
+      const int r = it.r;
+      if (r == it.r_end) it.have = 0;
+      else it.r += it.rev ? -1 : 1;
+      const int p0 = __builtin_amdgcn_readfirstlane(P[r]), p1 = __builtin_amdgcn_readfirstlane(P[r + 1]);
+      if (p1 > p0) {
+        d.s = r;
+        d.vlo = max(it.X0, p0) - p0;
+        d.vhi = min(it.X1, p1) - p0;
+        d.u = it.u;
+        d.rev = it.rev;
+        d.ok = 1;
+        return d;
+      }
+    }
+  }
+}
+
+// -------------------------------------------------------------------------------
+// Records: publication, arrival, merge
+// -------------------------------------------------------------------------------
+struct Splits {
+  SeqSplit A, B;
+  int nw, lp;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const AttnArgs& a) {
+  return __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
+}
+constexpr int SC1 = 16;  // buffer cache policy: device scope (coherent across XCDs)
+
+__device__ __forceinline__ void rec_store4(__amdgpu_buffer_rsrc_t r, int off_f, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off_f * 4, 0, SC1);
+}
+__device__ __forceinline__ void rec_store1(__amdgpu_buffer_rsrc_t r, int off_f, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off_f * 4, 0, SC1);
+}
+__device__ __forceinline__ float rec_load1(__amdgpu_buffer_rsrc_t r, int off_f) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off_f * 4, 0, SC1));
+}
+
+// Records of a pair: A-sequence slots [slA, slA + nA), then B-sequence slots.
+struct PairRecs {
+  int slA, nA, slB, nB;
+};
+
+__device__ __forceinline__ PairRecs pair_records(const Splits& sp, const int* P, int np, int pair) {
+  PairRecs pr;
+  int uf = 0;
+  pr.nA = region_records(sp.A, sp.nw, P, pair, uf);
+  pr.slA = sp.A.base + pair + uf;
+  pr.nB = 0;
+  pr.slB = 0;
+  if (sp.lp) {
+    pr.nB = region_records(sp.B, sp.nw, P, np + pair, uf);
+    pr.slB = sp.B.base + pair + uf;
+  }
+  return pr;
+}
+
+__device__ __forceinline__ int slot_of(const Splits& sp, const SegDesc& d, int np) {
+  return d.s < np ? sp.A.base + d.s + d.u : sp.B.base + (d.s - np) + d.u;
+}
+
+__device__ __forceinline__ f32x4 rec_load4(__amdgpu_buffer_rsrc_t r, int off_f) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, SC1));
+}
+
+// Merge of a pair's records in slot order by one wave, 64 records per round (online
+// rescale between rounds).  Lane r holds record r's per-head max and sum; the outputs
+// o[g][D] are read as 16-byte pieces, lane l owning pieces c = l + 64 i (head 4 c / D),
+// RB records per batch with all their loads in flight; the first batch is requested
+// together with the maxima and sums.
+template <int D, int EC>  // EC: pieces per lane per record, ceil(g D / 256)
+__device__ __forceinline__ void merge_pair(const AttnArgs& a, const PairRecs& pr, int pair) {
+  constexpr int RB = EC >= 16 ? 1 : 16 / EC;
+  constexpr int PPH = D / 4;         // pieces per head
+  constexpr int LPH = 64 / PPH;      // heads covered by one row of 64 pieces
+  const int lane = threadIdx.x & 63, g = a.g, rf = a.rec_floats;
+  const int n = pr.nA + pr.nB;
+  const int npc = g * PPH;
+  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
+  auto slot = [&](int k) { return k < pr.nA ? pr.slA + k : pr.slB + (k - pr.nA); };
+  float M[16], den[16];
+#pragma unroll
+  for (int h = 0; h < 16; ++h) {
+    M[h] = neg_inf();
+    den[h] = 0.f;
+  }
+  f32x4 acc[EC];
+#pragma unroll
+  for (int i = 0; i < EC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < n; r0 += 64) {
+    const int nr = min(64, n - r0);
+    // maxima and sums of this round's records (lane = record), and the first batch
+    const int mb = slot(r0 + min(lane, nr - 1)) * rf + g * D;
+    float mv[16], lv[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      mv[h] = neg_inf();
+      lv[h] = 0.f;
+      if (h < g) {
+        mv[h] = rec_load1(rs, mb + h);
+        lv[h] = rec_load1(rs, mb + g + h);
+      }
+    }
+    f32x4 o[RB][EC];
+    auto issue = [&](int k0) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const int b = slot(r0 + min(k0 + r, nr - 1)) * rf;
+#pragma unroll
+        for (int i = 0; i < EC; ++i) {
+          const int c = lane + 64 * i;
+          o[r][i] = (c < npc) ? rec_load4(rs, b + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    };
+    issue(0);
+    float w[16], sc[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+      w[h] = 0.f;
+      sc[h] = 1.f;
+      if (h < g) {
+        const float mh = (lane < nr) ? mv[h] : neg_inf();
+        const float Mn = fmaxf(M[h], wave_max(mh));
+        sc[h] = (Mn == neg_inf()) ? 1.f : exp2f(M[h] - Mn);
+        w[h] = (mh == neg_inf()) ? 0.f : exp2f(mh - Mn);
+        den[h] = den[h] * sc[h] + wave_sum(w[h] * lv[h]);
+        M[h] = Mn;
+      }
+    }
+    // earlier rounds' sums move to the new maxima
+#pragma unroll
+    for (int i = 0; i < EC; ++i) {
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < LPH; ++q)
+        if (lane / PPH == q) s = sc[LPH * i + q < 16 ? LPH * i + q : 15];
+      acc[i] *= s;
+    }
+    for (int k0 = 0; k0 < nr; k0 += RB) {
+      if (k0 > 0) issue(k0);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        if (k0 + r < nr) {
+#pragma unroll
+          for (int i = 0; i < EC; ++i) {
+            float wl = 0.f;
+#pragma unroll
+            for (int q = 0; q < LPH; ++q) {
+              const int h = LPH * i + q < 16 ? LPH * i + q : 15;
+              const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[h]), k0 + r));
+              if (lane / PPH == q) wl = wh;
+            }
+            acc[i] += wl * o[r][i];
+          }
+        }
+      }
+    }
+  }
+  const int b = pair / a.Hkv, hk = pair % a.Hkv;
+  float* out = a.out + ((int64_t)b * a.Hq + (int64_t)hk * g) * D;
+#pragma unroll
+  for (int i = 0; i < EC; ++i) {
+    const int c = lane + 64 * i;
+    if (c < npc) {
+      float dn = 0.f;
+#pragma unroll
+      for (int q = 0; q < LPH; ++q)
+        if (lane / PPH == q) dn = den[LPH * i + q < 16 ? LPH * i + q : 15];
+      const float inv = dn > 0.f ? 1.0f / dn : 0.f;
+      *reinterpret_cast<f32x4*>(out + 4 * c) = acc[i] * inv;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void merge_dispatch(const AttnArgs& a, const PairRecs& pr, int pair) {
+  const int npc = a.g * D / 4;
+  if (npc <= 64) merge_pair<D, 1>(a, pr, pair);
+  else if (npc <= 128) merge_pair<D, 2>(a, pr, pair);
+  else if (npc <= 256) merge_pair<D, 4>(a, pr, pair);
+  else merge_pair<D, 8>(a, pr, pair);
+}
+
+// A published record waiting for its arrival (pend), an arrival whose count has not
+// been looked at yet (iss), and the pairs this wave has won and still has to merge: a
+// list threaded through the per-pair link array of the workspace (each pair is won by
+// exactly one wave per call), merged once the wave's stream is over so the merge's
+// registers never compete with the stream's.
+struct Arrivals {
+  int pend, pend_pair;
+  int iss, iss_pair, iss_old;
+  int won;  // first pair of the list, -1 when empty
+};
+
+__device__ __forceinline__ void arrivals_init(Arrivals& ar) {
+  ar.pend = 0;
+  ar.iss = 0;
+  ar.won = -1;
+}
+
+// The record stores must be complete (device scope) before the count moves: wait for
+// every outstanding vector memory operation, then bump the pair's count.
+__device__ __forceinline__ void arrival_issue(const AttnArgs& a, Arrivals& ar) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  int v = 0;
+  if ((threadIdx.x & 63) == 0) v = atomicAdd(a.cnt + ar.pend_pair, 1);
+  ar.iss = 1;
+  ar.iss_pair = ar.pend_pair;
+  ar.iss_old = v;
+  ar.pend = 0;
+}
+
+// The wave that brings a pair's count to its record total clears the count for the next
+// call and puts the pair on its list (merged later, see Arrivals).  A count beyond the
+// total can only come from a workspace that was not zeroed before its first use:
+// flagged in kv.err.
+template <int D>
+__device__ __forceinline__ void arrival_check(const AttnArgs& a, const Splits& sp, const int* P, Arrivals& ar) {
+  const int old = __builtin_amdgcn_readfirstlane(ar.iss_old);
+  ar.iss = 0;
+  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, ar.iss_pair);
+  const int n = pr.nA + pr.nB;
+  if (old == n - 1) {
+    if ((threadIdx.x & 63) == 0) {
+      __hip_atomic_store(a.cnt + ar.iss_pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      a.link[ar.iss_pair] = ar.won;
+    }
+    ar.won = ar.iss_pair;
+  } else if ((unsigned)old >= (unsigned)n) {
+    if ((threadIdx.x & 63) == 0) atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void merge_won(const AttnArgs& a, const Splits& sp, const int* P, Arrivals& ar) {
+  int pair = ar.won;
+  while (pair >= 0) {
+    const int next = __builtin_amdgcn_readfirstlane(a.link[pair]);
+    merge_dispatch<D>(a, pair_records(sp, P, a.kv.num_pairs, pair), pair);
+    pair = next;
+  }
+  ar.won = -1;
 }
 
 // -------------------------------------------------------------------------------
@@ -122,6 +549,7 @@ struct Bf16Frags {
   u32x4 kA[D / 32];  // K rows for score tile A (this lane's row, D/4 elements)
   u32x4 kB[D / 32];  // K rows for score tile B
   u32x4 v[D / 16];   // V^T fragments, one per 16-wide output tile
+  u32x4 rp0, rp1;    // ring pages: the positions of this lane's 8 tokens (-1 = empty)
 };
 
 struct PageRef {
@@ -131,29 +559,20 @@ struct PageRef {
   int nvalid;         // main: valid slots; ring: ring page index
 };
 
-// Segment context for region A: block-table entries of the pages this wave walks are
-// fetched once into a VGPR (lane i holds page base+i) and read back with readlane, so
-// no memory access sits between a step's loads and their use; the ring's slot
-// occupancy is summarised once into 16-bit masks in this wave's LDS area.
-struct SegA {
-  int pair, npm, len, nring;
-  int bt_base;   // virtual page index held by lane 0 of bt
-  int bt;        // this lane's block-table entry
-  const int* ringmask;  // LDS: 16-bit occupancy of each ring page
-};
-
+// Page v of region A of `pair` (walk position w, for the block-table chunk in bt).
 template <int D>
-__device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, const SegA& sg, int vp) {
+__device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, int v, int w, int bt, int npm,
+                                                 int len, int nring) {
   PageRef r;
-  if (vp < sg.npm) {
-    const int pg = __builtin_amdgcn_readlane(sg.bt, vp - sg.bt_base);
+  if (v < npm) {
+    const int pg = __builtin_amdgcn_readlane(bt, w & 63);
     r.k = reinterpret_cast<const uint16_t*>(a.kv.k_pages) + (int64_t)pg * PAGE * D;
     r.v = reinterpret_cast<const uint16_t*>(a.kv.v_pages) + (int64_t)pg * PAGE * D;
     r.kind = 0;
-    r.nvalid = min(PAGE, sg.len - vp * PAGE);
-  } else if (vp < sg.npm + sg.nring) {
-    const int rp = vp - sg.npm;
-    const int64_t off = ((int64_t)sg.pair * sg.nring + rp) * PAGE * D;
+    r.nvalid = min(PAGE, len - v * PAGE);
+  } else if (v < npm + nring) {
+    const int rp = v - npm;
+    const int64_t off = ((int64_t)pair * nring + rp) * PAGE * D;
     r.k = reinterpret_cast<const uint16_t*>(a.ring.k) + off;
     r.v = reinterpret_cast<const uint16_t*>(a.ring.v) + off;
     r.kind = 1;
@@ -167,28 +586,61 @@ __device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, const SegA& 
   return r;
 }
 
+// The two pages of step k of a segment (X the lower page): forward walks take pages
+// vlo + 2k, vlo + 2k + 1 (walk positions 2k, 2k + 1); backward walks vhi - 2 - 2k and
+// vhi - 1 - 2k (walk positions 2k + 1, 2k).  A lane of the block-table chunk register
+// holds the entry of walk position 64 c + lane.
+template <int D>
+__device__ __forceinline__ void step_pages(const AttnArgs& a, const SegDesc& d, int k, int bt, int npm, int len,
+                                           int nring, PageRef& X, PageRef& Y) {
+  const int vX = d.rev ? d.vhi - 2 - 2 * k : d.vlo + 2 * k;
+  const int wX = d.rev ? 2 * k + 1 : 2 * k, wY = d.rev ? 2 * k : 2 * k + 1;
+  X = region_a_page<D>(a, d.s, vX, wX, bt, npm, len, nring);
+  Y = region_a_page<D>(a, d.s, vX + 1, wY, bt, npm, len, nring);
+}
+
+// Block-table entries of walk positions [64 c, 64 c + 64) of segment d (lane i: position
+// 64 c + i); positions past the pool read a clamped entry that is never used.
+__device__ __forceinline__ int load_bt_chunk(const AttnArgs& a, const SegDesc& d, int c) {
+  const int lane = threadIdx.x & 63;
+  const int w = 64 * c + lane;
+  const int v = d.rev ? d.vhi - 1 - w : d.vlo + w;
+  const int vv = min(max(v, 0), a.kv.max_pages_per_pair - 1);
+  return a.kv.block_table[(int64_t)d.s * a.kv.max_pages_per_pair + vv];
+}
+
 // Validity bits of this lane's 8 tokens (8j .. 8j+7 of the 32-token step).
-__device__ __forceinline__ uint32_t lane_valid_bits(const SegA& sg, const PageRef& X,
+__device__ __forceinline__ uint32_t lane_valid_bits(const u32x4& rp0, const u32x4& rp1, const PageRef& X,
                                                     const PageRef& Y, int j) {
   const PageRef& P = (j < 2) ? X : Y;
-  const int s0 = 8 * (j & 1);
   if (P.kind == 0) {
-    int n = P.nvalid - s0;
-    n = max(0, min(8, n));
+    const int n = max(0, min(8, P.nvalid - 8 * (j & 1)));
     return (1u << n) - 1u;
   }
-  if (P.kind == 1) return (static_cast<uint32_t>(sg.ringmask[P.nvalid]) >> s0) & 0xffu;
+  if (P.kind == 1) {
+    uint32_t b = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b |= ((int)rp0[i] >= 0 ? 1u : 0u) << i;
+      b |= ((int)rp1[i] >= 0 ? 1u : 0u) << (i + 4);
+    }
+    return b;
+  }
   return 0u;
 }
 
+// K fragments of a step, and the ring positions of this lane's 8 tokens (for a lane
+// whose page is not a ring page the positions are read from its K page and ignored).
+// Every load is unconditional, so the wait counts in the step loop stay exact.
 template <int D>
-__device__ __forceinline__ void load_k(Bf16Frags<D>& f, const PageRef& X, const PageRef& Y, int lane) {
+__device__ __forceinline__ void load_k(const AttnArgs& a, Bf16Frags<D>& f, int pair, const PageRef& X,
+                                       const PageRef& Y, int lane) {
   const int m = lane & 15, j = lane >> 4;
   // Score tile A rows: token 8*(m/4) + m%4; tile B rows: token 8*(m/4) + 4 + m%4.
   const int tA = 8 * (m >> 2) + (m & 3);
   const int tB = tA + 4;
   const PageRef& PA = (tA < 16) ? X : Y;  // tA < 16 <=> tB < 16
-  const uint16_t* kbase = (PA.k != nullptr) ? PA.k : X.k;
+  const uint16_t* kbase = (PA.k != nullptr) ? PA.k : X.k;  // X is never a padding page
   const uint16_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
   const uint16_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
 #pragma unroll
@@ -196,6 +648,12 @@ __device__ __forceinline__ void load_k(Bf16Frags<D>& f, const PageRef& X, const 
     f.kA[kk] = *reinterpret_cast<const u32x4*>(rowA + 8 * kk);
     f.kB[kk] = *reinterpret_cast<const u32x4*>(rowB + 8 * kk);
   }
+  const PageRef& PT = (j < 2) ? X : Y;
+  const int* pp = (PT.kind == 1)
+                      ? a.ring.pos + (int64_t)pair * a.ring.window + PT.nvalid * PAGE + 8 * (j & 1)
+                      : reinterpret_cast<const int*>(X.k);
+  f.rp0 = *reinterpret_cast<const u32x4*>(pp);
+  f.rp1 = *reinterpret_cast<const u32x4*>(pp + 4);
 }
 
 template <int D>
@@ -214,6 +672,14 @@ struct SoftmaxState {
   float m;  // running max (log2 domain), this lane's head
   float l;  // running sum of p over this lane's tokens
 };
+
+template <int D>
+__device__ __forceinline__ void state_reset(SoftmaxState<D>& st) {
+#pragma unroll
+  for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = neg_inf();
+  st.l = 0.f;
+}
 
 // Zero the bf16 elements of a fragment whose token bit is clear (keeps 0*garbage out
 // of the MFMA when a slot of a partly filled page holds stale bits).
@@ -300,134 +766,168 @@ __device__ __forceinline__ void pv_step(const Bf16Frags<D>& f, SoftmaxState<D>& 
   }
 }
 
-// Store this wave's partial record for one region.
-template <int D>
-__device__ __forceinline__ void emit_partial(const AttnArgs& a, const Plan& pl, int pair, int slot,
-                                             SoftmaxState<D>& st) {
-  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
-  float l = st.l;
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
-  float* rec = a.part + (int64_t)slot * a.rec_floats;
-  if (n < a.g) {
-#pragma unroll
-    for (int t = 0; t < D / 16; ++t)
-      *reinterpret_cast<f32x4*>(rec + n * D + 16 * t + 4 * j) = st.o[t];
-    if (j == 0) {
-      rec[a.g * D + n] = st.m;
-      rec[a.g * D + a.g + n] = l;
-    }
-  }
-}
-
 template <int D>
 __device__ __forceinline__ void load_q(const AttnArgs& a, int pair, bf16x8 (&qf)[D / 32]) {
   const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
   const int b = pair / a.Hkv, h = pair % a.Hkv;
-  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.g + n) * D +
+  const uint16_t* q = reinterpret_cast<const uint16_t*>(a.q) + ((int64_t)b * a.Hq + h * a.g + min(n, a.g - 1)) * D +
                       (D / 4) * j;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (n < a.g) v = *reinterpret_cast<const u32x4*>(q + 8 * kk);
-    qf[kk] = as_bf16x8(v);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(q + 8 * kk);
+    qf[kk] = as_bf16x8(n < a.g ? v : u32x4{0u, 0u, 0u, 0u});
   }
 }
 
+// End of a segment of pair `pair` whose state is in the MFMA layout (lane: head n =
+// lane % 16, dims 16 t + 4 (lane / 16) + 0..3): a pair with a single record is finished
+// here; otherwise the record is published and its arrival left pending.
 template <int D>
-__device__ void run_region_a_bf16(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
-                                  int slot, int* wlds) {
-  const int lane = threadIdx.x & 63, j = lane >> 4;
-  bf16x8 qf[D / 32];
-  load_q<D>(a, pair, qf);
-  SoftmaxState<D> st;
+__device__ __forceinline__ void segment_done(const AttnArgs& a, const Splits& sp, const int* P, int pair, int slot,
+                             SoftmaxState<D>& st, Arrivals& ar) {
+  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+  float l = st.l;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, pair);
+  if (pr.nA + pr.nB == 1) {
+    const int b = pair / a.Hkv, h = pair % a.Hkv;
+    float* out = a.out + ((int64_t)b * a.Hq + h * a.g + n) * D;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    if (n < a.g) {
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = neg_inf();
-  st.l = 0.f;
-  SegA sg;
-  sg.pair = pair;
-  sg.nring = a.has_ring ? a.ring.window / PAGE : 0;
-  sg.ringmask = wlds;
-  // Issue the segment's independent loads together (length, first block-table chunk,
-  // ring occupancy) so their latencies overlap with the q load above.
-  const int len_raw = a.kv.length[pair];
-  const int bt_first = (v0 + lane < v1) ? a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair +
-                                                           min(v0 + lane, a.kv.max_pages_per_pair - 1)]
-                                        : 0;
-  int ring_m = 0;
-  const bool need_ring = sg.nring > 0 && lane < sg.nring;
-  if (need_ring) {
-    const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + lane * PAGE;
-#pragma unroll
-    for (int i = 0; i < PAGE; ++i) ring_m |= (pos[i] >= 0 ? 1 : 0) << i;
-  }
-  sg.len = __builtin_amdgcn_readfirstlane(len_raw);
-  sg.npm = cdiv(sg.len, PAGE);
-  if (sg.nring > 0) {
-    if (need_ring) wlds[lane] = ring_m;
-    for (int rp = lane + 64; rp < sg.nring; rp += 64) {
-      const int* pos = a.ring.pos + (int64_t)pair * a.ring.window + rp * PAGE;
-      int m = 0;
-#pragma unroll
-      for (int i = 0; i < PAGE; ++i) m |= (pos[i] >= 0 ? 1 : 0) << i;
-      wlds[rp] = m;
+      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(out + 16 * t + 4 * j) = st.o[t] * inv;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    return;
   }
-  // Odd waves walk their range from the end (chunks and steps in reverse).  With every
-  // wave walking forward, the 1024 streams keep a fixed distance from each other, and
-  // at some cache sizes that stride piles them onto the same HBM channels (measured:
-  // 10% slower at one keep ratio); walking in opposite directions breaks the pattern.
-  // The step order only changes the rounding order of this wave's partial softmax.
-  // (readfirstlane: the wave index is uniform, and saying so keeps the range and step
-  // loops below scalar; a per-lane flag would make them exec-masked loops)
-  const bool rev = ((blockIdx.x * ATTN_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) & 1) != 0;
-  const int nch = (v1 - v0 + 63) / 64;
-  for (int ci = 0; ci < nch; ++ci) {
-    // block-table chunk: pages [c0, c0 + 64) of this range
-    const int c0 = v0 + 64 * (rev ? nch - 1 - ci : ci);
-    const int c1 = min(v1, c0 + 64);
-    sg.bt_base = c0;
-    if (c0 == v0 && !rev) {
-      sg.bt = bt_first;  // entries past npm are never read (those pages are ring/pad)
-    } else {
-      sg.bt = 0;
-      if (c0 + lane < min(c1, sg.npm))
-        sg.bt = a.kv.block_table[(int64_t)pair * a.kv.max_pages_per_pair + c0 + lane];
-    }
-    // One register buffer: the next step's K is loaded as soon as this step's QK
-    // MFMAs have consumed K, and its V right after the PV MFMAs, so a full step of loads
-    // is in flight behind the math.  The last step re-loads its own pages (in range)
-    // instead of branching, which keeps the wait counts exact.
-    Bf16Frags<D> f;
-    const int nst = (c1 - c0) / 2;
-    auto vat = [&](int i) { return c0 + 2 * (rev ? nst - 1 - i : i); };
-    PageRef x = region_a_page<D>(a, sg, vat(0));
-    PageRef y = region_a_page<D>(a, sg, vat(0) + 1);
-    load_k<D>(f, x, y, lane);
-    load_v<D>(f, x, y, lane);
-    for (int i = 0; i < nst; ++i) {
-      const int vn = vat(i + 1 < nst ? i + 1 : i);
-      const PageRef xn = region_a_page<D>(a, sg, vn);
-      const PageRef yn = region_a_page<D>(a, sg, vn + 1);
-      const uint32_t vb = lane_valid_bits(sg, x, y, j);
-      const bool allv = __ballot(vb != 0xffu) == 0;
-      f32x4 sA, sB;
-      qk_step<D>(f, qf, sA, sB);
-      load_k<D>(f, xn, yn, lane);
-      bf16x8 phi, plo;
-      if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv);
-      load_v<D>(f, xn, yn, lane);
-      x = xn;
-      y = yn;
+  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
+  const int base = slot * a.rec_floats;
+  if (n < a.g) {
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) rec_store4(rs, base + n * D + 16 * t + 4 * j, st.o[t]);
+    if (j == 0) {
+      rec_store1(rs, base + a.g * D + n, st.m);
+      rec_store1(rs, base + a.g * D + a.g + n, l);
     }
   }
-  emit_partial<D>(a, pl, pair, slot, st);
+  ar.pend = 1;
+  ar.pend_pair = pair;
 }
 
+// -------------------------------------------------------------------------------
+// The bf16 stream over region-A segments.  One step of K/V loads is in flight behind
+// the math; the segment after the next one is looked up (block-table entries requested)
+// one iteration after a switch, so every segment's first pages are addressable by the
+// time the previous segment's last step issues their loads; the next pair's queries are
+// loaded together with its first K.  Record arrivals are issued right after the next
+// step's QK MFMAs, when only that step's V loads are outstanding, so waiting for the
+// record stores costs no stream stall.
+// -------------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& sp, const int* P, const int* Lens,
+                                              UnitIter& it, Arrivals& ar) {
+  const int lane = threadIdx.x & 63, j = lane >> 4;
+  const int np = a.kv.num_pairs;
+  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
+  SegDesc cur = iter_next_seg(it, P);
+  if (!cur.ok) return;
+  SegDesc nxt = iter_next_seg(it, P);
+  SegDesc nx2;
+  nx2.ok = 0;
+  int bt_cur0 = load_bt_chunk(a, cur, 0), bt_cur1 = 0;
+  int bt_nxt = nxt.ok ? load_bt_chunk(a, nxt, 0) : 0;
+  int bt_nx2 = 0;
+  bool fetch_nx2 = nxt.ok;
+  int len = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+  int npm = cdiv(len, PAGE);
+  int nst = (cur.vhi - cur.vlo) >> 1;
+  bool chunk_load = nst > 32;  // chunk 1 of the current segment still to request
+  int cc = 0;                  // block-table chunk of the current step
+  bf16x8 qf[D / 32], qn[D / 32];
+  load_q<D>(a, cur.s, qf);
+  PageRef x, y;
+  step_pages<D>(a, cur, 0, bt_cur0, npm, len, nring, x, y);
+  Bf16Frags<D> f;
+  load_k<D>(a, f, cur.s, x, y, lane);
+  load_v<D>(f, x, y, lane);
+  SoftmaxState<D> st;
+  state_reset(st);
+  int k = 0;
+  for (;;) {
+    const bool lastk = (k + 1 == nst);
+    const bool have_next = !lastk || nxt.ok;
+    // pages of the next step (when there is none, the current pages are loaded again,
+    // which keeps every step's loads identical); the next pair's queries
+    PageRef xn = x, yn = y;
+    int pair_n = cur.s;
+    if (!lastk) {
+      const int cw = (2 * (k + 1)) >> 6;
+      if (cw != cc) {
+        // entering chunk cw: its entries arrived long ago; request chunk cw + 1 into the
+        // register chunk cw - 1 used
+        cc = cw;
+        if (64 * (cc + 1) < 2 * nst) {
+          if (cc & 1) bt_cur0 = load_bt_chunk(a, cur, cc + 1);
+          else bt_cur1 = load_bt_chunk(a, cur, cc + 1);
+        }
+      }
+      step_pages<D>(a, cur, k + 1, (cc & 1) ? bt_cur1 : bt_cur0, npm, len, nring, xn, yn);
+    } else if (nxt.ok) {
+      const int lenn = __builtin_amdgcn_readfirstlane(Lens[nxt.s]);
+      step_pages<D>(a, nxt, 0, bt_nxt, cdiv(lenn, PAGE), lenn, nring, xn, yn);
+      pair_n = nxt.s;
+      load_q<D>(a, nxt.s, qn);
+    }
+    const uint32_t vb = lane_valid_bits(f.rp0, f.rp1, x, y, j);
+    const bool allv = __ballot(vb != 0xffu) == 0;
+    f32x4 sA, sB;
+    qk_step<D>(f, qf, sA, sB);
+    if (ar.pend) arrival_issue(a, ar);
+    load_k<D>(a, f, pair_n, xn, yn, lane);
+    bf16x8 phi, plo;
+    if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv);
+    load_v<D>(f, xn, yn, lane);
+    if (lastk) {
+      segment_done<D>(a, sp, P, cur.s, sp.A.base + cur.s + cur.u, st, ar);
+      state_reset(st);
+    }
+    if (ar.iss) arrival_check<D>(a, sp, P, ar);
+    // look-ahead requests (rare)
+    if (chunk_load) {
+      bt_cur1 = load_bt_chunk(a, cur, 1);
+      chunk_load = false;
+    }
+    if (fetch_nx2) {
+      nx2 = iter_next_seg(it, P);
+      if (nx2.ok) bt_nx2 = load_bt_chunk(a, nx2, 0);
+      fetch_nx2 = false;
+    }
+    if (!have_next) break;
+    x = xn;
+    y = yn;
+    if (lastk) {
+      cur = nxt;
+      nxt = nx2;
+      bt_cur0 = bt_nxt;
+      bt_nxt = bt_nx2;
+      len = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+      npm = cdiv(len, PAGE);
+      nst = (cur.vhi - cur.vlo) >> 1;
+      chunk_load = nst > 32;
+      cc = 0;
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) qf[kk] = qn[kk];
+      fetch_nx2 = nxt.ok;
+      nx2.ok = 0;
+      k = 0;
+    } else {
+      ++k;
+    }
+  }
+  if (ar.pend) arrival_issue(a, ar);
+  if (ar.iss) arrival_check<D>(a, sp, P, ar);
+  (void)np;
+}
 // -------------------------------------------------------------------------------
 // Low-precision region (BeaconKV demoted tokens, int8 or int4 codes): codes -> bf16
 // exactly, per-token scales.
@@ -524,17 +1024,12 @@ __device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS>& f
 }
 
 template <int D, int BITS, int NSET>
-__device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
-                                int slot) {
+__device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int v0, int v1, bool rev, SoftmaxState<D>& st) {
   static_assert(NSET % 2 == 0, "steps are folded in pairs");
   const int lane = threadIdx.x & 63, j = lane >> 4;
   bf16x8 qf[D / 32];
   load_q<D>(a, pair, qf);
-  SoftmaxState<D> st;
-#pragma unroll
-  for (int t = 0; t < D / 16; ++t) st.o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m = neg_inf();
-  st.l = 0.f;
+  state_reset(st);
   // int4: I4_OFFSET * (sum of this lane's head's query) comes off every score; psum is
   // one more output tile, sum_t p_t per head, accumulated by MFMA from the same bf16
   // weights as the outputs (a ones operand in place of V) and rescaled with them, so
@@ -554,7 +1049,6 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
   }
   const int len = __builtin_amdgcn_readfirstlane(a.kv.length8[pair]);
   const int npm = cdiv(len, PAGE);  // v1 <= npm rounded up to even; the pad page is never loaded
-  const bool rev = ((blockIdx.x * ATTN_WG_WAVES + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) & 1) != 0;  // as in region A
   const int nch = (v1 - v0 + 63) / 64;
   for (int ci = 0; ci < nch; ++ci) {
     const int c0 = v0 + 64 * (rev ? nch - 1 - ci : ci);
@@ -700,15 +1194,14 @@ __device__ void run_region_b_lp(const AttnArgs& a, const Plan& pl, int pair, int
 #pragma unroll
     for (int t = 0; t < D / 16; ++t) st.o[t] -= off;
   }
-  emit_partial<D>(a, pl, pair, slot, st);
 }
 
 // -------------------------------------------------------------------------------
 // fp32 region A (VALU; small head dims / tiny workloads)
 // -------------------------------------------------------------------------------
 template <int D>
-__device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
-                                 int slot, float* wlds) {
+__device__ __forceinline__ void run_region_a_f32(const AttnArgs& a, const Splits& sp, const int* P, int pair, int v0, int v1,
+                                 int slot, float* wlds, Arrivals& ar) {
   // wlds: this wave's LDS area: q [16][D] then p [16][32]
   const int lane = threadIdx.x & 63;
   const int g = a.g;
@@ -802,13 +1295,47 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  float* rec = a.part + (int64_t)slot * a.rec_floats;
-  for (int n = 0; n < g; ++n) {
-    for (int e = 0; e < D / 64; ++e) rec[n * D + lane + 64 * e] = o[n][e];
-    if (lane == 0) {
-      rec[g * D + n] = mrun[n];
-      rec[g * D + g + n] = lrun[n];
+  // end of the segment: finish a single-record pair here, else publish the record
+  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, pair);
+  if (pr.nA + pr.nB == 1) {
+    float* out = a.out + ((int64_t)b * a.Hq + h * g) * D;
+    for (int n = 0; n < g; ++n) {
+      const float inv = lrun[n] > 0.f ? 1.0f / lrun[n] : 0.f;
+      for (int e = 0; e < D / 64; ++e) out[n * D + lane + 64 * e] = o[n][e] * inv;
     }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
+  const int base = slot * a.rec_floats;
+  for (int n = 0; n < g; ++n) {
+    for (int e = 0; e < D / 64; ++e) rec_store1(rs, base + n * D + lane + 64 * e, o[n][e]);
+    if (lane == 0) {
+      rec_store1(rs, base + g * D + n, mrun[n]);
+      rec_store1(rs, base + g * D + g + n, lrun[n]);
+    }
+  }
+  ar.pend = 1;
+  ar.pend_pair = pair;
+}
+
+// Region-B (low-precision) and fp32 segments: one segment at a time (its query, length
+// and block table fetched at its start), arrivals issued at its end.
+template <int D, bool F32, int BITS>
+__device__ __forceinline__ void stream_segments(const AttnArgs& a, const Splits& sp, const int* P, UnitIter& it,
+                                                float* wlds, Arrivals& ar) {
+  const int np = a.kv.num_pairs;
+  for (;;) {
+    const SegDesc d = iter_next_seg(it, P);
+    if (!d.ok) break;
+    if constexpr (F32) {
+      run_region_a_f32<D>(a, sp, P, d.s, d.vlo, d.vhi, slot_of(sp, d, np), wlds, ar);
+    } else {
+      SoftmaxState<D> st;
+      run_region_b_lp<D, BITS, ATTN_LP_SETS>(a, d.s - np, d.vlo, d.vhi, d.rev != 0, st);
+      segment_done<D>(a, sp, P, d.s - np, slot_of(sp, d, np), st, ar);
+    }
+    if (ar.pend) arrival_issue(a, ar);
+    if (ar.iss) arrival_check<D>(a, sp, P, ar);
   }
 }
 
@@ -822,162 +1349,73 @@ __device__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, in
 template <int D, bool F32, bool LP, int WPE>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE))) void decode_attn_kernel(AttnArgs a) {
   extern __shared__ int lds[];
-  Plan pl = build_plan(a, lds);
   const int np = a.kv.num_pairs;
   const int nseg = plan_regions(a);
+  int* P = lds;
+  int* Lens = lds + nseg + 1;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Work-groups are dispatched round-robin over the 8 XCDs; numbering the ranges so that
-  // each XCD takes one contiguous eighth of the sequence evens out the XCDs' finish times
-  // (measured: 1-3 us off the call at the 361 MB and 543 MB shapes).
+  if (wid == 0) compute_plan(a, P, Lens, nseg);
+  __syncthreads();
+  const int nw = gridDim.x * ATTN_WG_WAVES;
+  // Work-groups are dispatched round-robin over the 8 XCDs; numbering the static units so
+  // that each XCD takes one contiguous eighth of the sequence evens out the XCDs' finish
+  // times (measured: 1-3 us at the 361 MB and 543 MB caches).
   const int gw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * ATTN_WG_WAVES + wid;
-
-  // the merge reads 2 * num_pairs + 1 entries; absent low-precision regions hold no records
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= 2 * np; i += blockDim.x) a.plan_c[i] = pl.C[min(i, nseg)];
-
-  pl.total = __builtin_amdgcn_readfirstlane(pl.total);
-  pl.total_a = __builtin_amdgcn_readfirstlane(pl.total_a);
-  pl.per_a = __builtin_amdgcn_readfirstlane(pl.per_a);
-  pl.per_b = __builtin_amdgcn_readfirstlane(pl.per_b);
+  Splits sp;
+  sp.nw = nw;
+  sp.lp = LP ? 1 : 0;
+  const int NA = __builtin_amdgcn_readfirstlane(P[np]);
+  sp.A = make_split(NA, nw, 0, 0, 0);
+  sp.B = make_split(LP ? __builtin_amdgcn_readfirstlane(P[nseg]) - NA : 0, nw, np + nw + sp.A.ud, np, NA);
+  // pairs with nothing visible: zeros
+  for (int p = gw; p < np; p += nw) {
+    const PairRecs pr = pair_records(sp, P, np, p);
+    if (pr.nA + pr.nB == 0) {
+      const int b = p / a.Hkv, hk = p % a.Hkv;
+      float* out = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g) * a.D;
+      for (int e = threadIdx.x & 63; e < a.g * a.D; e += 64) out[e] = 0.f;
+    }
+  }
+  Arrivals ar;
+  arrivals_init(ar);
   float* wlds = nullptr;
-  int* wmask = lds + 2 * (nseg + 1) + 16 + wid * 64;
+  if constexpr (F32) wlds = reinterpret_cast<float*>(lds + 2 * nseg + 2) + wid * (16 * D + 16 * 32);
+  UnitIter it;
+  iter_init(it, sp.A, nw, gw, np, a.ctl + CTL_TICKET_A);
   if constexpr (F32) {
-    wlds = reinterpret_cast<float*>(lds + 2 * (nseg + 1) + 16 + ATTN_WG_WAVES * 64) + wid * (16 * D + 16 * 32);
-  }
-  // pass 0: this wave's share of the A sequence; pass 1: of the B sequence
-  for (int pass = 0; pass < 2; ++pass) {
-  const int base = pass ? pl.total_a : 0, per = pass ? pl.per_b : pl.per_a;
-  int start = base + gw * per;
-  const int end = min(start + per, pass ? pl.total : pl.total_a);
-  if (start >= end) continue;
-  int s = __builtin_amdgcn_readfirstlane(upper_segment(pl.P, nseg, start));
-  while (start < end) {
-    while (__builtin_amdgcn_readfirstlane(pl.P[s + 1]) <= start) ++s;
-    const int ps = __builtin_amdgcn_readfirstlane(pl.P[s]);
-    const int stop = min(end, __builtin_amdgcn_readfirstlane(pl.P[s + 1]));
-    const int slot = __builtin_amdgcn_readfirstlane(pl.C[s]) + (gw - (ps - base) / per);
-    const int v0 = start - ps, v1 = stop - ps;
-    if (s < np) {
-      if constexpr (F32) {
-        run_region_a_f32<D>(a, pl, s, v0, v1, slot, wlds);
-      } else {
-        run_region_a_bf16<D>(a, pl, s, v0, v1, slot, wmask);
-      }
-    } else {
-      if constexpr (!F32 && LP) {
-#ifndef LP_SETS4
-#define LP_SETS4 2
-#endif
-#ifndef LP_SETS8
-#define LP_SETS8 2
-#endif
-        if (a.kv.lp_bits == 4) run_region_b_lp<D, 4, LP_SETS4>(a, pl, s - np, v0, v1, slot);
-        else run_region_b_lp<D, 8, LP_SETS8>(a, pl, s - np, v0, v1, slot);
-      }
+    stream_segments<D, true, 8>(a, sp, P, it, wlds, ar);
+  } else {
+    stream_a_bf16<D>(a, sp, P, Lens, it, ar);
+    if constexpr (LP) {
+      iter_init(it, sp.B, nw, gw, np, a.ctl + CTL_TICKET_B);
+      if (a.kv.lp_bits == 4) stream_segments<D, false, 4>(a, sp, P, it, nullptr, ar);
+      else stream_segments<D, false, 8>(a, sp, P, it, nullptr, ar);
     }
-    start = stop;
   }
+  merge_won<D>(a, sp, P, ar);
+  // The last wave out clears the tickets for the next call.  Every wave takes exactly one
+  // ticket past the end of each sequence it drew from, so the totals are known; other
+  // values mean the control words were not zero at the start.
+  int old = 0;
+  if ((threadIdx.x & 63) == 0) old = atomicAdd(a.ctl + CTL_DONE, 1);
+  old = __builtin_amdgcn_readfirstlane(old);
+  if (old == nw - 1 && (threadIdx.x & 63) == 0) {
+    const int ta = __hip_atomic_exchange(a.ctl + CTL_TICKET_A, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int tb = __hip_atomic_exchange(a.ctl + CTL_TICKET_B, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(a.ctl + CTL_DONE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int ea = sp.A.ud > 0 ? sp.A.ud + nw : 0;
+    const int eb = (LP && sp.B.ud > 0) ? sp.B.ud + nw : 0;
+    if (ta != ea || tb != eb) atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
+  } else if ((unsigned)old >= (unsigned)nw && (threadIdx.x & 63) == 0) {
+    atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
   }
 }
 
-// -------------------------------------------------------------------------------
-// Merge: one wave per (pair, query head).  Right after the plan entries arrive, the wave
-// requests the (m, l) of the pair's first 64 records (one per lane) and the outputs of the
-// first 16 in one batch, so a pair with up to 16 records costs two memory round trips.
-// The reference max M covers every record; the normaliser is sum_k 2^(m_k - M) l_k and
-// the output sum_k 2^(m_k - M) o_k / normaliser, accumulated in record order, so the
-// result is deterministic.  A pair with no visible token (no records) gets zeros.
-// -------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void decode_attn_combine_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int np = a.kv.num_pairs, g = a.g;
-  if (w >= np * g) return;
-  const int pair = w / g, n = w % g;
-  const int b = pair / a.Hkv, h = pair % a.Hkv;
-  const int r0 = a.plan_c[pair], na = a.plan_c[pair + 1] - r0;
-  const int s0 = a.plan_c[np + pair];
-  const int nrec = na + (a.plan_c[np + pair + 1] - s0);
-  float* out = a.out + ((int64_t)b * a.Hq + h * g + n) * D;
-  if (nrec == 0) {
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = 0.f;
-    return;
-  }
-  auto rec = [&](int k) {
-    const int slot = (k < na) ? r0 + k : s0 + (k - na);
-    return a.part + (int64_t)slot * a.rec_floats;
-  };
-  // first batch: lane k < 64 holds record k's (m, l); outputs of records 0..15
-  const float* rl = rec(min(lane, nrec - 1));
-  float m0 = rl[g * D + n], l0 = rl[g * D + g + n];
-  float ov0[16][D / 64];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float* o = rec(min(i, nrec - 1)) + n * D;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) ov0[i][e] = o[lane + 64 * e];
-  }
-  if (lane >= nrec) {
-    m0 = neg_inf();
-    l0 = 0.f;
-  }
-  float M = m0;
-  for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
-  M = wave_max(M);
-  float acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
-  float den = 0.f;
-  if (M != neg_inf()) {
-    for (int k0 = 0; k0 < nrec; k0 += 64) {
-      const int k = k0 + lane;
-      float wk = 0.f, lk = 0.f;
-      if (k0 == 0) {
-        wk = (m0 == neg_inf()) ? 0.f : exp2f(m0 - M);
-        lk = l0;
-      } else if (k < nrec) {
-        const float m = rec(k)[g * D + n];
-        wk = (m == neg_inf()) ? 0.f : exp2f(m - M);
-        lk = rec(k)[g * D + g + n];
-      }
-      den += wk * lk;
-      const int kn = min(64, nrec - k0);
-      // batches of 16 records: all loads issued before the accumulation
-      for (int kb = 0; kb < kn; kb += 16) {
-        float ov[16][D / 64];
-        if (k0 == 0 && kb == 0) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) ov[i][e] = ov0[i][e];
-        } else {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int kk = min(kb + i, kn - 1);
-            const float* o = rec(k0 + kk) + n * D;
-#pragma unroll
-            for (int e = 0; e < D / 64; ++e) ov[i][e] = o[lane + 64 * e];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float wb = (kb + i < kn) ? __shfl(wk, kb + i) : 0.f;
-#pragma unroll
-          for (int e = 0; e < D / 64; ++e) acc[e] += wb * ov[i][e];
-        }
-      }
-    }
-    den = wave_sum(den);
-  }
-  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] * inv;
-}
-
-size_t attn_lds_bytes(int num_pairs, int D, bool f32) {
-  size_t b = (size_t)(2 * (2 * num_pairs + 1) + 16 + ATTN_WG_WAVES * 64) * sizeof(int);
+// LDS: page prefix P[nseg + 1], the pool lengths [num_pairs] (padded to nseg + 1 ints),
+// and for fp32 caches one scratch area per wave.
+size_t attn_lds_bytes(int num_pairs, int D, bool f32, bool lp) {
+  const size_t nseg = (size_t)(lp ? 2 : 1) * num_pairs;
+  size_t b = 2 * (nseg + 1) * sizeof(int);
   if (f32) b += (size_t)ATTN_WG_WAVES * (16 * D + 16 * 32) * sizeof(float);
   return b;
 }
@@ -986,9 +1424,17 @@ size_t attn_lds_bytes(int num_pairs, int D, bool f32) {
 
 using namespace kvp;
 
-static size_t attn_plan_bytes(int num_pairs) {
-  return (((size_t)(2 * num_pairs + 1) * sizeof(int)) + 255) & ~(size_t)255;
+// Record slots of one sequence: regions + static units + dynamic units (at most 3 per
+// wave plus one, see make_split), for the largest launch (two waves per SIMD).
+static size_t attn_max_slots(int num_pairs) {
+  return 2 * ((size_t)num_pairs + 4 * (size_t)ATTN_MAX_NWAVES + 1);
 }
+
+static size_t attn_rec_floats(int g, int D) { return ((size_t)g * (D + 2) + 3) & ~(size_t)3; }
+
+static size_t attn_cnt_bytes(int num_pairs) { return (((size_t)num_pairs * sizeof(int)) + 255) & ~(size_t)255; }
+// Workspace: [control words][arrival counts][pair links][records]; only the first two
+// must start at zero.
 
 extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                                  int32_t head_dim) {
@@ -996,13 +1442,12 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   const int Hkv = num_pairs / B;
   if (Hq % Hkv != 0) return 0;
   const int g = Hq / Hkv;
-  const size_t recs = 2 * (size_t)ATTN_MAX_NWAVES + 2 * (size_t)num_pairs;  // both splits
-  return attn_plan_bytes(num_pairs) + recs * (size_t)g * (head_dim + 2) * sizeof(float);
+  return ATTN_CTL_BYTES + 2 * attn_cnt_bytes(num_pairs) + attn_max_slots(num_pairs) * attn_rec_floats(g, head_dim) * sizeof(float);
 }
 
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
-                                  hipStream_t stream) {
+                                  size_t ws_bytes, hipStream_t stream) {
   AttnArgs a;
   a.q = q;
   a.out = out;
@@ -1016,21 +1461,28 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
   if (ring) a.ring = *ring;
   else a.ring = kvp_ring{};
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  a.plan_c = reinterpret_cast<int*>(ws);
-  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_plan_bytes(kv->num_pairs));
-  a.rec_floats = a.g * (a.D + 2);
+  char* w = reinterpret_cast<char*>(ws);
+  a.ctl = reinterpret_cast<int*>(w);
+  a.cnt = reinterpret_cast<int*>(w + ATTN_CTL_BYTES);
+  a.link = reinterpret_cast<int*>(w + ATTN_CTL_BYTES + attn_cnt_bytes(kv->num_pairs));
+  a.part = reinterpret_cast<float*>(w + ATTN_CTL_BYTES + 2 * attn_cnt_bytes(kv->num_pairs));
+  const size_t part_bytes = ws_bytes - ATTN_CTL_BYTES - 2 * attn_cnt_bytes(kv->num_pairs);
+  if (part_bytes > 0x7fffffffu) return KVP_E_UNSUPPORTED;  // buffer offsets are 32-bit
+  a.part_bytes = (int)part_bytes;
+  a.rec_floats = (int)attn_rec_floats(a.g, a.D);
   const bool f32 = kv->dtype == KVP_F32;
-  const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32);
+  const bool lp = kv->num_pages8 > 0;
+  const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32, lp);
   if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
   const dim3 g1(ATTN_GRID), b(256);
   if (f32) {
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false, 1>), g1, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, true, false, 1>), g1, b, lds, stream, a);
-  } else if (kv->num_pages8 > 0 && kv->lp_bits == 4) {
+  } else if (lp && kv->lp_bits == 4) {
     const dim3 g2(ATTN_GRID * 2);
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 2>), g2, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 2>), g2, b, lds, stream, a);
-  } else if (kv->num_pages8 > 0) {
+  } else if (lp) {
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 1>), g1, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 1>), g1, b, lds, stream, a);
   } else {
@@ -1038,13 +1490,9 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, false, 1>), g1, b, lds, stream, a);
   }
   KVP_LAUNCH_CHECK();
-  const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
-  if (a.D == 64) hipLaunchKernelGGL((decode_attn_combine_kernel<64>), cgrid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((decode_attn_combine_kernel<128>), cgrid, dim3(256), 0, stream, a);
-  KVP_LAUNCH_CHECK();
   return KVP_OK;
 }
 
-size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32) {
-  return attn_lds_bytes(num_pairs, D, f32);
+size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32, bool lp) {
+  return attn_lds_bytes(num_pairs, D, f32, lp);
 }

@@ -27,13 +27,13 @@ kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hid
                                            float* part, hipStream_t stream);
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
-                                  hipStream_t stream);
+                                  size_t ws_bytes, hipStream_t stream);
 kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
                                    int T, int d, const uint32_t* keep_bits, const int* kept_idx,
                                    int window, float sm_scale, float* out, hipStream_t stream);
 kvp_status kvp_launch_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream);
 kvp_status kvp_launch_clear_error(const kvp_paged_kv* kv, hipStream_t stream);
-size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32);
+size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32, bool lp);
 
 namespace {
 
@@ -248,11 +248,13 @@ extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, 
   if (Hq / Hkv > 16) return KVP_E_UNSUPPORTED;
   if (qdtype != kv->dtype) return KVP_E_DTYPE;
   if (kv->num_pages8 > 0 && kv->dtype != KVP_BF16) return KVP_E_DTYPE;
-  if (kvp_attn_lds_bytes_host(kv->num_pairs, kv->head_dim, kv->dtype == KVP_F32) > 160 * 1024)
+  if (kvp_attn_lds_bytes_host(kv->num_pairs, kv->head_dim, kv->dtype == KVP_F32, kv->num_pages8 > 0) >
+      160 * 1024)
     return KVP_E_UNSUPPORTED;
   if (!ws || ws_bytes < kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs, kv->head_dim))
     return KVP_E_WORKSPACE;
-  return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream);
+  if (((uintptr_t)ws) & 255) return KVP_E_ARG;
+  return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, ws_bytes, stream);
 }
 
 extern "C" kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t dtype,
@@ -290,5 +292,6 @@ extern "C" kvp_status kvp_check(const kvp_paged_kv* kv, hipStream_t stream) {
   int host_err = 0;
   if (hipMemcpy(&host_err, kv->err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
     return KVP_E_HIP;
-  return host_err ? KVP_E_CAPACITY : KVP_OK;
+  if (host_err & (KVP_ERR_POOL_FULL | KVP_ERR_TABLE_FULL | KVP_ERR_POOL8_FULL)) return KVP_E_CAPACITY;
+  return host_err ? KVP_E_WORKSPACE : KVP_OK;
 }
