@@ -61,8 +61,6 @@ typedef enum kvp_dtype { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
 #define KVP_ERR_POOL_FULL 0x1   /* main page pool exhausted */
 #define KVP_ERR_TABLE_FULL 0x2  /* a pair needs more pages than max_pages_per_pair */
 #define KVP_ERR_POOL8_FULL 0x4  /* int8 pool or its block table exhausted */
-#define KVP_ERR_ATTN_WS 0x8     /* kvp_decode_attn found its workspace counters non-zero at
-                                   the start (workspace not zero-filled before first use) */
 
 /* ----------------------------------------------------------------------------
  * Surrogate scorer weights (KVzap, key points: surrogate model / structure).
@@ -315,19 +313,15 @@ kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* hidden_new, 
  *   out [B][Hq][d] fp32: softmax(sm_scale * K q) V over the pair's pool tokens, its
  *       non-empty ring slots and (if present) its int8 tokens, all in one softmax.
  *       A pair with no visible token yields zeros.
- *   ws  >= kvp_decode_attn_workspace_size(...) bytes, 256-byte aligned.  Its first
- *       256 + (4 * num_pairs rounded up to 256) bytes hold control words and per-pair
- *       arrival counts, the rest the partial (max, sum, output) records of the split
- *       (scratch).  The counter part must be ZERO before the first use of a workspace;
- *       every call leaves it zero again, so a workspace is reused without clearing
- *       (also from a captured graph).  Counters found non-zero set KVP_ERR_ATTN_WS in
- *       kv->err, reported by kvp_check() as KVP_E_WORKSPACE (the outputs of that call
- *       are then unspecified).  One workspace serves one call at a time.
- * Work split: one kernel.  The kept pages of all pairs are cut into a large static
- * share per wave plus small units handed out by a ticket counter at the end; the wave
- * that writes a pair's last partial record merges the pair's records in page order, so
- * the output does not depend on timing (bit-identical reruns).  Limits: num_pairs up to
- * 13000 with a low-precision pool, 20000 without (else KVP_E_UNSUPPORTED).
+ *   ws  >= kvp_decode_attn_workspace_size(...) bytes of scratch (any contents),
+ *       256-byte aligned; it holds the page prefix of the split and the partial
+ *       (max, sum, output) records between the two kernels.
+ * Work split: the kept pages of all pairs form one sequence (and the low-precision
+ * pages another), cut into one contiguous share per wave; each share is walked 32
+ * tokens at a time and leaves one partial record per pair it touches; a second kernel
+ * merges each pair's records in page order, so the output does not depend on timing
+ * (bit-identical reruns).  Limits: num_pairs up to 13000 with a low-precision pool,
+ * 20000 without (LDS plan; else KVP_E_UNSUPPORTED).
  * -------------------------------------------------------------------------- */
 kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
                            const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
@@ -365,8 +359,7 @@ kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t
  * kvp_reset: empty the pools (lengths 0, page_top 0) and, if ring != NULL, the
  *            ring (pos -1).  Stream-ordered, no allocation.
  * kvp_clear_error: zero kv->err.
- * kvp_check: synchronise `stream`, read kv->err; KVP_E_CAPACITY if a pool or table
- *            overflowed, KVP_E_WORKSPACE if only KVP_ERR_ATTN_WS is set.
+ * kvp_check: synchronise `stream`, read kv->err; KVP_E_CAPACITY if any bit is set.
  * -------------------------------------------------------------------------- */
 kvp_status kvp_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream);
 kvp_status kvp_clear_error(const kvp_paged_kv* kv, hipStream_t stream);

@@ -414,16 +414,9 @@ def kvp_decode_attn_workspace_size(B: int, Hq: int, num_pairs: int, head_dim: in
 
 
 def decode_attn_workspace(B: int, Hq: int, kv: PagedKV, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace of the size kvp_decode_attn needs (its counters must start
-    at zero; every call leaves them zero)."""
+    """A workspace of the size kvp_decode_attn needs (contents are scratch)."""
     n = kvp_decode_attn_workspace_size(B, Hq, kv.c.num_pairs, kv.c.head_dim)
-    return torch.zeros(max(n, 4) // 4 + 1, dtype=torch.int32, device=device)
-
-
-def decode_attn_counter_bytes(num_pairs: int) -> int:
-    """Bytes at the start of a decode-attention workspace that hold its counters (the
-    rest holds scratch records)."""
-    return 256 + -(-4 * num_pairs // 256) * 256
+    return torch.empty(max(n, 4) // 4 + 1, dtype=torch.int32, device=device)
 
 
 def kvp_decode_attn(q: torch.Tensor, kv: PagedKV, ring: Optional[Ring], sm_scale: float,

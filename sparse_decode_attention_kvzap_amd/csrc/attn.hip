@@ -5,25 +5,20 @@
 // briefing (jiinsi.com), body -- beacon entries at full precision and the others at
 // low precision are read in one attention.
 //
-// One kernel per call, split-K with a deterministic in-kernel merge:
-//   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages, then
-//   its ring pages, padded to an even count) and, when a low-precision pool exists, a
-//   "region B" (its int8 or int4 pages, padded to even).  The A regions are concatenated
-//   into one page sequence and the B regions into another.  Each sequence is cut into
-//   units: one large static unit per wave (most of the pages), then small dynamic units
-//   that waves take from a ticket counter as they run out of work, so the waves of a
-//   faster XCD absorb the tail of a slower one.  Unit boundaries depend only on the page
-//   counts, never on timing, so every (unit, region) intersection -- a segment -- always
-//   covers the same pages.  A wave walks its segments 32 tokens (two pages) at a time and
-//   writes one partial (max, sum, output) record per segment; the wave that writes a
-//   pair's last record (per-pair arrival counter) merges the pair's records in page order
-//   and writes the output.  The result is therefore bit-identical from run to run.
-//   Records are published across XCDs without cache maintenance: they are stored with
-//   device-scope (sc1) stores, the writer waits for their completion before it bumps the
-//   arrival counter, and the merging wave reads them with device-scope loads.
-//   Record slot of the segment (region s, unit u) = base + s + u: along a sequence,
-//   consecutive segments advance s or u (or both), so the slot is unique, and a region's
-//   records occupy consecutive slots.
+// Work decomposition (split-K, evenly balanced), two kernels:
+//   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages,
+//   then its ring pages, padded to an even count) and, when a low-precision pool exists,
+//   a "region B" (its int8 or int4 pages, padded to even).  The A regions are
+//   concatenated into one page sequence and the B regions into another; each sequence
+//   is cut into one contiguous unit per wave.  A wave walks its units 32 tokens (two
+//   pages) at a time and writes one partial (max, sum, output) record per segment (the
+//   part of a region inside a unit); a pair whose whole sequence lies in one segment is
+//   finished by that wave.  The merge kernel (one wave per pair and query head) combines
+//   a pair's records in page order with a log-sum-exp merge, so the result is
+//   deterministic; the kernel boundary makes the records visible (no atomics, no cache
+//   maintenance).  Record slot of segment (region s, unit u) = s + u: consecutive
+//   segments of a sequence advance s or u (or both), so slots are unique and a region's
+//   records are consecutive.
 //
 // Per 32-token step (bf16, head dim D, g query heads of one KV head):
 //   S^T[32 tok x 16 heads] = K . Q^T on 16x16x32 bf16 MFMA (exact products, fp32
@@ -33,9 +28,11 @@
 //   O^T[D x 16 heads] += V^T . P^T on MFMA, with P split into bf16 hi + lo parts so
 //   the probabilities keep ~16 significant bits (V is exact in bf16).
 //   V pages are stored dim-major ([d][16]) so V^T fragments are plain 16-byte loads.
-// The bf16 stream keeps one step of K/V loads in flight and, one segment ahead, the next
-// segment's query, length and block-table entries, so crossing from one pair to the
-// next costs no memory round trip.
+// The bf16 stream keeps one step of K/V loads in flight, issued unconditionally so the
+// compiler's wait counts stay exact (QK waits for K while V is still in flight), and
+// looks two segments ahead: the next segments' block-table entries are requested while
+// the current one streams and the next pair's queries with its first K, so crossing from
+// one pair to the next costs no memory round trip.
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -54,18 +51,6 @@ constexpr int ATTN_MAX_NWAVES = ATTN_MAX_WPE * ATTN_GRID * ATTN_WG_WAVES;
 constexpr int ATTN_LP_SETS = 2;
 static_assert(ATTN_GRID % 8 == 0, "units are numbered per XCD (8 XCDs)");
 
-// Workspace: control words, per-pair arrival counts, then the records.  The counts and
-// control words must be zero before the first call; every call leaves them zero.
-constexpr int CTL_TICKET_A = 0, CTL_TICKET_B = 1, CTL_DONE = 2;
-constexpr size_t ATTN_CTL_BYTES = 256;
-
-// Dynamic units: about 1/20 of a wave's fair share each (2..8 pages), covering up to 12%
-// of a sequence and at most two units per wave.
-constexpr int ATTN_DYN_DIV = 20;
-constexpr int ATTN_DYN_MAX_PAGES = 8;
-constexpr int ATTN_DYN_PCT = 12;
-constexpr int ATTN_DYN_PER_WAVE = 2;
-
 struct AttnArgs {
   const void* q;
   float* out;
@@ -74,17 +59,15 @@ struct AttnArgs {
   kvp_ring ring;
   int has_ring;
   float scale_log2;  // sm_scale * log2(e)
-  int* ctl;          // control words (tickets, done count)
-  int* cnt;          // [num_pairs] record arrivals
-  int* link;         // [num_pairs] next pair of a wave's list of pairs to merge
+  int* plan;         // page prefix P[0..nseg], written by work-group 0 for the merge kernel
+  int nw;            // waves of the streaming kernel
   float* part;       // records, rec_floats each
-  int part_bytes;    // size of the record area (buffer-resource range)
   int rec_floats;    // g * (D + 2) rounded up to 4: o[g][D], then m[g], then l[g]
 };
 
 // -------------------------------------------------------------------------------
 // Plan: page prefix P[] over the regions, computed by wave 0 of every work-group into
-// LDS (one load per region, one wave scan, no barrier inside).
+// LDS (one load per region, one wave scan).
 // -------------------------------------------------------------------------------
 __device__ __forceinline__ int plan_regions(const AttnArgs& a) {
   return (a.kv.num_pages8 > 0 ? 2 : 1) * a.kv.num_pairs;
@@ -156,389 +139,111 @@ __device__ __forceinline__ int seg_search(const int* P, int lo, int hi, int x) {
   return lo + (63 - __builtin_clzll(m));
 }
 
-// One page sequence (A: bf16/fp32 regions; B: low-precision regions) cut into units.
-struct SeqSplit {
-  int N;      // pages
-  int s0;     // static unit size (0: no static band)
-  int s1;     // dynamic unit size
-  int ud;     // dynamic units
-  int base;   // first record slot of the sequence
-  int r0;     // first region of the sequence in P
-  int pbase;  // P[r0]
+// Units and records.  Sequence A is regions [0, np) of P, sequence B regions [np, 2 np);
+// each is cut into nw units of s pages (the last ones short or empty).
+struct Plan {
+  const int* P;
+  int np, nw;
+  int sA, sB;  // unit sizes
+  int NA;      // pages of sequence A (= P[np])
+  int baseB;   // first record slot of sequence B
+  int lp;
 };
 
-__device__ __forceinline__ SeqSplit make_split(int N, int nw, int base, int r0, int pbase) {
-  SeqSplit q;
-  q.N = N;
-  q.base = base;
-  q.r0 = r0;
-  q.pbase = pbase;
-  q.s1 = 2;
-  q.ud = 0;
-  q.s0 = N > 0 ? ((cdiv(N, nw) + 1) & ~1) : 0;  // even; the last units may be short or empty
-  return q;
+__device__ __forceinline__ int unit_size(int N, int nw) { return N > 0 ? ((cdiv(N, nw) + 1) & ~1) : 0; }
+
+__device__ __forceinline__ Plan make_plan(const int* P, int np, int nw, bool lp) {
+  Plan pl;
+  pl.P = P;
+  pl.np = np;
+  pl.nw = nw;
+  pl.lp = lp ? 1 : 0;
+  pl.NA = P[np];
+  pl.sA = unit_size(pl.NA, nw);
+  pl.sB = lp ? unit_size(P[2 * np] - pl.NA, nw) : 0;
+  pl.baseB = np + nw;
+  return pl;
 }
 
-// Units of a sequence: u < nw static ([u s0, (u + 1) s0)), then dynamic.
-__device__ __forceinline__ int unit_of(const SeqSplit& q, int nw, int x) {
-  const int st = nw * q.s0;
-  return x < st ? x / max(1, q.s0) : nw + (x - st) / q.s1;
-}
-
-// Records (segments) of region s of the sequence, and the first one's unit.
-__device__ __forceinline__ int region_records(const SeqSplit& q, int nw, const int* P, int s, int& uf) {
-  const int p0 = P[s] - q.pbase, p1 = P[s + 1] - q.pbase;
+// Records of region s (first unit in uf): the units it intersects.
+__device__ __forceinline__ int region_records(const Plan& pl, int s, int& uf) {
+  const bool b = s >= pl.np;
+  const int base = b ? pl.NA : 0, us = b ? pl.sB : pl.sA;
+  const int p0 = pl.P[s] - base, p1 = pl.P[s + 1] - base;
   if (p1 <= p0) {
     uf = 0;
     return 0;
   }
-  uf = unit_of(q, nw, p0);
-  return unit_of(q, nw, p1 - 1) - uf + 1;
+  uf = p0 / us;
+  return (p1 - 1) / us - uf + 1;
 }
 
-// -------------------------------------------------------------------------------
-// Units and segments
-// -------------------------------------------------------------------------------
+__device__ __forceinline__ int pair_records(const Plan& pl, int pair) {
+  int uf;
+  int n = region_records(pl, pair, uf);
+  if (pl.lp) n += region_records(pl, pl.np + pair, uf);
+  return n;
+}
+
 struct SegDesc {
   int s;         // region index in P
   int vlo, vhi;  // pages of the region covered by the segment
   int u;         // unit
   int rev;       // walk backwards
-  int ok;        // 0: no more work
+  int ok;        // 1: a segment; 0: no more work; -1: not looked up yet
 };
 
-// Walks a wave's units of one sequence: its static unit, then dynamic units by ticket.
-// The ticket of the next unit is requested when a unit starts, so its latency hides
-// behind that unit's pages.
+__device__ __forceinline__ int slot_of(const Plan& pl, const SegDesc& d) {
+  return d.s < pl.np ? d.s + d.u : pl.baseB + (d.s - pl.np) + d.u;
+}
+
+// The segments of one wave's unit of a sequence, in walk order.  Odd units walk
+// backwards: with all 1024 streams walking forward at a fixed distance, one keep ratio
+// of the Qwen-3-8B-like cache ran 10% slower (HBM channel conflicts of the regular
+// stride); opposite directions remove that.  The order only changes rounding inside a
+// record.
 struct UnitIter {
-  SeqSplit sp;
-  int nw, gw, nreg;
-  int* ticket;
-  int started, have;
-  int u, X0, X1, rev;  // current unit, its pages in P coordinates
-  int r, r_end;        // next region to emit, last region (walk order)
-  int tk_v;            // lane 0: the requested ticket
-  int tk_pending;
-  int finished;        // a ticket past the end was drawn: no further requests
+  int X0, X1, rev;  // the unit's pages in P coordinates
+  int r, r_end;     // next region to emit, last region (walk order)
+  int have;
 };
 
-__device__ __forceinline__ void iter_init(UnitIter& it, const SeqSplit& sp, int nw, int gw, int nreg, int* ticket) {
-  it.sp = sp;
-  it.nw = nw;
-  it.gw = gw;
-  it.nreg = nreg;
-  it.ticket = ticket;
-  it.started = 0;
+__device__ __forceinline__ void iter_init(UnitIter& it, const Plan& pl, bool seqB, int u) {
+  const int base = seqB ? pl.NA : 0, us = seqB ? pl.sB : pl.sA;
+  const int N = seqB ? pl.P[2 * pl.np] - pl.NA : pl.NA;
+  const int r0 = seqB ? pl.np : 0;
   it.have = 0;
-  it.tk_v = 0;
-  it.tk_pending = 0;
-  it.finished = 0;
-}
-
-__device__ __forceinline__ int request_ticket(int* ticket) {
-  int v = 0;
-  if ((threadIdx.x & 63) == 0) v = atomicAdd(ticket, 1);
-  return v;
-}
-
-__device__ __forceinline__ bool iter_next_unit(UnitIter& it, const int* P) {
-  if (it.finished) return false;
-  int u = -1;
-  if (!it.started) {
-    it.started = 1;
-    if (it.sp.s0 > 0 && it.gw * it.sp.s0 < it.sp.N) u = it.gw;  // the last static units may be empty
-  }
-  if (u < 0) {
-    if (it.sp.ud == 0) {
-      it.finished = 1;
-      return false;
-    }
-    const int t = __builtin_amdgcn_readfirstlane(it.tk_pending ? it.tk_v : request_ticket(it.ticket));
-    it.tk_pending = 0;
-    if ((unsigned)t >= (unsigned)it.sp.ud) {
-      it.finished = 1;
-      return false;
-    }
-    u = it.nw + t;
-  }
-  if (it.sp.ud > 0) {
-    it.tk_v = request_ticket(it.ticket);
-    it.tk_pending = 1;
-  }
-  int x0, x1;
-  if (u < it.nw) {
-    x0 = u * it.sp.s0;
-    x1 = min(it.sp.N, x0 + it.sp.s0);
-    it.rev = u & 1;  // odd static units walk backwards: opposite directions keep the
-                     // 1024 streams from settling on the same HBM channels (measured: 10%
-                     // at one keep ratio); the order only changes rounding inside a record
-  } else {
-    x0 = it.nw * it.sp.s0 + (u - it.nw) * it.sp.s1;
-    x1 = min(it.sp.N, x0 + it.sp.s1);
-    it.rev = 0;
-  }
-  it.u = u;
-  it.X0 = it.sp.pbase + x0;
-  it.X1 = it.sp.pbase + x1;
-  const int rf = seg_search(P, it.sp.r0, it.sp.r0 + it.nreg, it.X0);
-  const int rl = seg_search(P, it.sp.r0, it.sp.r0 + it.nreg, it.X1 - 1);
+  const int x0 = u * us, x1 = min(N, x0 + us);
+  if (us == 0 || x1 <= x0) return;
+  it.X0 = base + x0;
+  it.X1 = base + x1;
+  it.rev = u & 1;
+  const int rf = seg_search(pl.P, r0, r0 + pl.np, it.X0);
+  const int rl = seg_search(pl.P, r0, r0 + pl.np, it.X1 - 1);
   it.r = it.rev ? rl : rf;
   it.r_end = it.rev ? rf : rl;
   it.have = 1;
-  return true;
 }
 
-__device__ __forceinline__ SegDesc iter_next_seg(UnitIter& it, const int* P) {
+__device__ __forceinline__ SegDesc iter_next_seg(UnitIter& it, const Plan& pl, int u) {
   SegDesc d;
   d.ok = 0;
-  for (;;) {
-    if (!it.have && !iter_next_unit(it, P)) return d;
-    while (it.have) {
-      const int r = it.r;
-      if (r == it.r_end) it.have = 0;
-      else it.r += it.rev ? -1 : 1;
-      const int p0 = __builtin_amdgcn_readfirstlane(P[r]), p1 = __builtin_amdgcn_readfirstlane(P[r + 1]);
-      if (p1 > p0) {
-        d.s = r;
-        d.vlo = max(it.X0, p0) - p0;
-        d.vhi = min(it.X1, p1) - p0;
-        d.u = it.u;
-        d.rev = it.rev;
-        d.ok = 1;
-        return d;
-      }
+  while (it.have) {
+    const int r = it.r;
+    if (r == it.r_end) it.have = 0;
+    else it.r += it.rev ? -1 : 1;
+    const int p0 = __builtin_amdgcn_readfirstlane(pl.P[r]), p1 = __builtin_amdgcn_readfirstlane(pl.P[r + 1]);
+    if (p1 > p0) {
+      d.s = r;
+      d.vlo = max(it.X0, p0) - p0;
+      d.vhi = min(it.X1, p1) - p0;
+      d.u = u;
+      d.rev = it.rev;
+      d.ok = 1;
+      return d;
     }
   }
-}
-
-// -------------------------------------------------------------------------------
-// Records: publication, arrival, merge
-// -------------------------------------------------------------------------------
-struct Splits {
-  SeqSplit A, B;
-  int nw, lp;
-};
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const AttnArgs& a) {
-  return __builtin_amdgcn_make_buffer_rsrc(a.part, (short)0, a.part_bytes, 0x00020000);
-}
-constexpr int SC1 = 16;  // buffer cache policy: device scope (coherent across XCDs)
-
-__device__ __forceinline__ void rec_store4(__amdgpu_buffer_rsrc_t r, int off_f, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off_f * 4, 0, SC1);
-}
-__device__ __forceinline__ void rec_store1(__amdgpu_buffer_rsrc_t r, int off_f, float v) {
-  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off_f * 4, 0, SC1);
-}
-__device__ __forceinline__ float rec_load1(__amdgpu_buffer_rsrc_t r, int off_f) {
-  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off_f * 4, 0, SC1));
-}
-
-// Records of a pair: A-sequence slots [slA, slA + nA), then B-sequence slots.
-struct PairRecs {
-  int slA, nA, slB, nB;
-};
-
-__device__ __forceinline__ PairRecs pair_records(const Splits& sp, const int* P, int np, int pair) {
-  PairRecs pr;
-  int uf = 0;
-  pr.nA = region_records(sp.A, sp.nw, P, pair, uf);
-  pr.slA = sp.A.base + pair + uf;
-  pr.nB = 0;
-  pr.slB = 0;
-  if (sp.lp) {
-    pr.nB = region_records(sp.B, sp.nw, P, np + pair, uf);
-    pr.slB = sp.B.base + pair + uf;
-  }
-  return pr;
-}
-
-__device__ __forceinline__ int slot_of(const Splits& sp, const SegDesc& d, int np) {
-  return d.s < np ? sp.A.base + d.s + d.u : sp.B.base + (d.s - np) + d.u;
-}
-
-__device__ __forceinline__ f32x4 rec_load4(__amdgpu_buffer_rsrc_t r, int off_f) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off_f * 4, 0, SC1));
-}
-
-// Merge of a pair's records in slot order by one wave, 64 records per round (online
-// rescale between rounds).  Lane r holds record r's per-head max and sum; the outputs
-// o[g][D] are read as 16-byte pieces, lane l owning pieces c = l + 64 i (head 4 c / D),
-// RB records per batch with all their loads in flight; the first batch is requested
-// together with the maxima and sums.
-template <int D, int EC>  // EC: pieces per lane per record, ceil(g D / 256)
-__device__ __forceinline__ void merge_pair(const AttnArgs& a, const PairRecs& pr, int pair) {
-  constexpr int RB = EC >= 16 ? 1 : 16 / EC;
-  constexpr int PPH = D / 4;         // pieces per head
-  constexpr int LPH = 64 / PPH;      // heads covered by one row of 64 pieces
-  const int lane = threadIdx.x & 63, g = a.g, rf = a.rec_floats;
-  const int n = pr.nA + pr.nB;
-  const int npc = g * PPH;
-  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
-  auto slot = [&](int k) { return k < pr.nA ? pr.slA + k : pr.slB + (k - pr.nA); };
-  float M[16], den[16];
-#pragma unroll
-  for (int h = 0; h < 16; ++h) {
-    M[h] = neg_inf();
-    den[h] = 0.f;
-  }
-  f32x4 acc[EC];
-#pragma unroll
-  for (int i = 0; i < EC; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < n; r0 += 64) {
-    const int nr = min(64, n - r0);
-    // maxima and sums of this round's records (lane = record), and the first batch
-    const int mb = slot(r0 + min(lane, nr - 1)) * rf + g * D;
-    float mv[16], lv[16];
-#pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      mv[h] = neg_inf();
-      lv[h] = 0.f;
-      if (h < g) {
-        mv[h] = rec_load1(rs, mb + h);
-        lv[h] = rec_load1(rs, mb + g + h);
-      }
-    }
-    f32x4 o[RB][EC];
-    auto issue = [&](int k0) {
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        const int b = slot(r0 + min(k0 + r, nr - 1)) * rf;
-#pragma unroll
-        for (int i = 0; i < EC; ++i) {
-          const int c = lane + 64 * i;
-          o[r][i] = (c < npc) ? rec_load4(rs, b + 4 * c) : f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-      }
-    };
-    issue(0);
-    float w[16], sc[16];
-#pragma unroll
-    for (int h = 0; h < 16; ++h) {
-      w[h] = 0.f;
-      sc[h] = 1.f;
-      if (h < g) {
-        const float mh = (lane < nr) ? mv[h] : neg_inf();
-        const float Mn = fmaxf(M[h], wave_max(mh));
-        sc[h] = (Mn == neg_inf()) ? 1.f : exp2f(M[h] - Mn);
-        w[h] = (mh == neg_inf()) ? 0.f : exp2f(mh - Mn);
-        den[h] = den[h] * sc[h] + wave_sum(w[h] * lv[h]);
-        M[h] = Mn;
-      }
-    }
-    // earlier rounds' sums move to the new maxima
-#pragma unroll
-    for (int i = 0; i < EC; ++i) {
-      float s = 0.f;
-#pragma unroll
-      for (int q = 0; q < LPH; ++q)
-        if (lane / PPH == q) s = sc[LPH * i + q < 16 ? LPH * i + q : 15];
-      acc[i] *= s;
-    }
-    for (int k0 = 0; k0 < nr; k0 += RB) {
-      if (k0 > 0) issue(k0);
-#pragma unroll
-      for (int r = 0; r < RB; ++r) {
-        if (k0 + r < nr) {
-#pragma unroll
-          for (int i = 0; i < EC; ++i) {
-            float wl = 0.f;
-#pragma unroll
-            for (int q = 0; q < LPH; ++q) {
-              const int h = LPH * i + q < 16 ? LPH * i + q : 15;
-              const float wh = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[h]), k0 + r));
-              if (lane / PPH == q) wl = wh;
-            }
-            acc[i] += wl * o[r][i];
-          }
-        }
-      }
-    }
-  }
-  const int b = pair / a.Hkv, hk = pair % a.Hkv;
-  float* out = a.out + ((int64_t)b * a.Hq + (int64_t)hk * g) * D;
-#pragma unroll
-  for (int i = 0; i < EC; ++i) {
-    const int c = lane + 64 * i;
-    if (c < npc) {
-      float dn = 0.f;
-#pragma unroll
-      for (int q = 0; q < LPH; ++q)
-        if (lane / PPH == q) dn = den[LPH * i + q < 16 ? LPH * i + q : 15];
-      const float inv = dn > 0.f ? 1.0f / dn : 0.f;
-      *reinterpret_cast<f32x4*>(out + 4 * c) = acc[i] * inv;
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void merge_dispatch(const AttnArgs& a, const PairRecs& pr, int pair) {
-  const int npc = a.g * D / 4;
-  if (npc <= 64) merge_pair<D, 1>(a, pr, pair);
-  else if (npc <= 128) merge_pair<D, 2>(a, pr, pair);
-  else if (npc <= 256) merge_pair<D, 4>(a, pr, pair);
-  else merge_pair<D, 8>(a, pr, pair);
-}
-
-// A published record waiting for its arrival (pend), an arrival whose count has not
-// been looked at yet (iss), and the pairs this wave has won and still has to merge: a
-// list threaded through the per-pair link array of the workspace (each pair is won by
-// exactly one wave per call), merged once the wave's stream is over so the merge's
-// registers never compete with the stream's.
-struct Arrivals {
-  int pend, pend_pair;
-  int iss, iss_pair, iss_old;
-  int won;  // first pair of the list, -1 when empty
-};
-
-__device__ __forceinline__ void arrivals_init(Arrivals& ar) {
-  ar.pend = 0;
-  ar.iss = 0;
-  ar.won = -1;
-}
-
-// The record stores must be complete (device scope) before the count moves: wait for
-// every outstanding vector memory operation, then bump the pair's count.
-__device__ __forceinline__ void arrival_issue(const AttnArgs& a, Arrivals& ar) {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  int v = 0;
-  if ((threadIdx.x & 63) == 0) v = atomicAdd(a.cnt + ar.pend_pair, 1);
-  ar.iss = 1;
-  ar.iss_pair = ar.pend_pair;
-  ar.iss_old = v;
-  ar.pend = 0;
-}
-
-// The wave that brings a pair's count to its record total clears the count for the next
-// call and puts the pair on its list (merged later, see Arrivals).  A count beyond the
-// total can only come from a workspace that was not zeroed before its first use:
-// flagged in kv.err.
-template <int D>
-__device__ __forceinline__ void arrival_check(const AttnArgs& a, const Splits& sp, const int* P, Arrivals& ar) {
-  const int old = __builtin_amdgcn_readfirstlane(ar.iss_old);
-  ar.iss = 0;
-  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, ar.iss_pair);
-  const int n = pr.nA + pr.nB;
-  if (old == n - 1) {
-    if ((threadIdx.x & 63) == 0) {
-      __hip_atomic_store(a.cnt + ar.iss_pair, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      a.link[ar.iss_pair] = ar.won;
-    }
-    ar.won = ar.iss_pair;
-  } else if ((unsigned)old >= (unsigned)n) {
-    if ((threadIdx.x & 63) == 0) atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void merge_won(const AttnArgs& a, const Splits& sp, const int* P, Arrivals& ar) {
-  int pair = ar.won;
-  while (pair >= 0) {
-    const int next = __builtin_amdgcn_readfirstlane(a.link[pair]);
-    merge_dispatch<D>(a, pair_records(sp, P, a.kv.num_pairs, pair), pair);
-    pair = next;
-  }
-  ar.won = -1;
+  return d;
 }
 
 // -------------------------------------------------------------------------------
@@ -779,65 +484,56 @@ __device__ __forceinline__ void load_q(const AttnArgs& a, int pair, bf16x8 (&qf)
   }
 }
 
-// End of a segment of pair `pair` whose state is in the MFMA layout (lane: head n =
-// lane % 16, dims 16 t + 4 (lane / 16) + 0..3): a pair with a single record is finished
-// here; otherwise the record is published and its arrival left pending.
+// End of a segment of `pair` whose state is in the MFMA layout (lane: head n = lane % 16,
+// dims 16 t + 4 (lane / 16) + 0..3): a pair with a single record is finished here,
+// otherwise the record is written for the merge kernel.
 template <int D>
-__device__ __forceinline__ void segment_done(const AttnArgs& a, const Splits& sp, const int* P, int pair, int slot,
-                             SoftmaxState<D>& st, Arrivals& ar) {
+__device__ __forceinline__ void segment_done(const AttnArgs& a, const Plan& pl, int pair, int slot,
+                                             SoftmaxState<D>& st) {
   const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
   float l = st.l;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, pair);
-  if (pr.nA + pr.nB == 1) {
+  if (n >= a.g) return;
+  if (pair_records(pl, pair) == 1) {
     const int b = pair / a.Hkv, h = pair % a.Hkv;
     float* out = a.out + ((int64_t)b * a.Hq + h * a.g + n) * D;
     const float inv = l > 0.f ? 1.0f / l : 0.f;
-    if (n < a.g) {
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(out + 16 * t + 4 * j) = st.o[t] * inv;
-    }
+    for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(out + 16 * t + 4 * j) = st.o[t] * inv;
     return;
   }
-  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
-  const int base = slot * a.rec_floats;
-  if (n < a.g) {
+  float* rec = a.part + (int64_t)slot * a.rec_floats;
 #pragma unroll
-    for (int t = 0; t < D / 16; ++t) rec_store4(rs, base + n * D + 16 * t + 4 * j, st.o[t]);
-    if (j == 0) {
-      rec_store1(rs, base + a.g * D + n, st.m);
-      rec_store1(rs, base + a.g * D + a.g + n, l);
-    }
+  for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(rec + n * D + 16 * t + 4 * j) = st.o[t];
+  if (j == 0) {
+    rec[a.g * D + n] = st.m;
+    rec[a.g * D + a.g + n] = l;
   }
-  ar.pend = 1;
-  ar.pend_pair = pair;
 }
 
 // -------------------------------------------------------------------------------
-// The bf16 stream over region-A segments.  One step of K/V loads is in flight behind
-// the math; the segment after the next one is looked up (block-table entries requested)
-// one iteration after a switch, so every segment's first pages are addressable by the
-// time the previous segment's last step issues their loads; the next pair's queries are
-// loaded together with its first K.  Record arrivals are issued right after the next
-// step's QK MFMAs, when only that step's V loads are outstanding, so waiting for the
-// record stores costs no stream stall.
+// The bf16 stream over one wave's unit of region-A pages.  One step of K/V loads is
+// in flight behind the math; the next two segments are looked up ahead (one lookup per
+// iteration, after the step's loads are issued), so every segment's first pages are
+// addressable by the time the previous segment's last step issues their loads; the
+// next pair's queries are loaded together with its first K.
 // -------------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& sp, const int* P, const int* Lens,
-                                              UnitIter& it, Arrivals& ar) {
+__device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl, const int* Lens, int u) {
   const int lane = threadIdx.x & 63, j = lane >> 4;
-  const int np = a.kv.num_pairs;
   const int nring = a.has_ring ? a.ring.window / PAGE : 0;
-  SegDesc cur = iter_next_seg(it, P);
+  UnitIter it;
+  iter_init(it, pl, false, u);
+  SegDesc cur = iter_next_seg(it, pl, u);
   if (!cur.ok) return;
-  SegDesc nxt = iter_next_seg(it, P);
-  SegDesc nx2;
-  nx2.ok = 0;
+  // Look-ahead queue: the next two segments, each valid (ok 1), past the end (ok 0) or not
+  // looked up yet (ok -1).
+  SegDesc nxt, nx2;
+  nxt.ok = -1;
+  nx2.ok = -1;
   int bt_cur0 = load_bt_chunk(a, cur, 0), bt_cur1 = 0;
-  int bt_nxt = nxt.ok ? load_bt_chunk(a, nxt, 0) : 0;
-  int bt_nx2 = 0;
-  bool fetch_nx2 = nxt.ok;
+  int bt_nxt = 0, bt_nx2 = 0;
   int len = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
   int npm = cdiv(len, PAGE);
   int nst = (cur.vhi - cur.vlo) >> 1;
@@ -855,7 +551,11 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& s
   int k = 0;
   for (;;) {
     const bool lastk = (k + 1 == nst);
-    const bool have_next = !lastk || nxt.ok;
+    if (lastk && nxt.ok < 0) {
+      nxt = iter_next_seg(it, pl, u);
+      if (nxt.ok) bt_nxt = load_bt_chunk(a, nxt, 0);
+    }
+    const bool have_next = !lastk || nxt.ok > 0;
     // pages of the next step (when there is none, the current pages are loaded again,
     // which keeps every step's loads identical); the next pair's queries
     PageRef xn = x, yn = y;
@@ -872,7 +572,7 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& s
         }
       }
       step_pages<D>(a, cur, k + 1, (cc & 1) ? bt_cur1 : bt_cur0, npm, len, nring, xn, yn);
-    } else if (nxt.ok) {
+    } else if (nxt.ok > 0) {
       const int lenn = __builtin_amdgcn_readfirstlane(Lens[nxt.s]);
       step_pages<D>(a, nxt, 0, bt_nxt, cdiv(lenn, PAGE), lenn, nring, xn, yn);
       pair_n = nxt.s;
@@ -882,25 +582,25 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& s
     const bool allv = __ballot(vb != 0xffu) == 0;
     f32x4 sA, sB;
     qk_step<D>(f, qf, sA, sB);
-    if (ar.pend) arrival_issue(a, ar);
     load_k<D>(a, f, pair_n, xn, yn, lane);
     bf16x8 phi, plo;
     if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv);
     load_v<D>(f, xn, yn, lane);
     if (lastk) {
-      segment_done<D>(a, sp, P, cur.s, sp.A.base + cur.s + cur.u, st, ar);
+      segment_done<D>(a, pl, cur.s, slot_of(pl, cur), st);
       state_reset(st);
     }
-    if (ar.iss) arrival_check<D>(a, sp, P, ar);
-    // look-ahead requests (rare)
+    // look-ahead requests (rare), at most one lookup per iteration
     if (chunk_load) {
       bt_cur1 = load_bt_chunk(a, cur, 1);
       chunk_load = false;
     }
-    if (fetch_nx2) {
-      nx2 = iter_next_seg(it, P);
+    if (nxt.ok < 0) {
+      nxt = iter_next_seg(it, pl, u);
+      if (nxt.ok) bt_nxt = load_bt_chunk(a, nxt, 0);
+    } else if (nxt.ok > 0 && nx2.ok < 0) {
+      nx2 = iter_next_seg(it, pl, u);
       if (nx2.ok) bt_nx2 = load_bt_chunk(a, nx2, 0);
-      fetch_nx2 = false;
     }
     if (!have_next) break;
     x = xn;
@@ -917,17 +617,14 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Splits& s
       cc = 0;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) qf[kk] = qn[kk];
-      fetch_nx2 = nxt.ok;
-      nx2.ok = 0;
+      nx2.ok = -1;
       k = 0;
     } else {
       ++k;
     }
   }
-  if (ar.pend) arrival_issue(a, ar);
-  if (ar.iss) arrival_check<D>(a, sp, P, ar);
-  (void)np;
 }
+
 // -------------------------------------------------------------------------------
 // Low-precision region (BeaconKV demoted tokens, int8 or int4 codes): codes -> bf16
 // exactly, per-token scales.
@@ -1200,8 +897,8 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
 // fp32 region A (VALU; small head dims / tiny workloads)
 // -------------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void run_region_a_f32(const AttnArgs& a, const Splits& sp, const int* P, int pair, int v0, int v1,
-                                 int slot, float* wlds, Arrivals& ar) {
+__device__ __forceinline__ void run_region_a_f32(const AttnArgs& a, const Plan& pl, int pair, int v0, int v1,
+                                                 int slot, float* wlds) {
   // wlds: this wave's LDS area: q [16][D] then p [16][32]
   const int lane = threadIdx.x & 63;
   const int g = a.g;
@@ -1295,52 +992,48 @@ __device__ __forceinline__ void run_region_a_f32(const AttnArgs& a, const Splits
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   }
-  // end of the segment: finish a single-record pair here, else publish the record
-  const PairRecs pr = pair_records(sp, P, a.kv.num_pairs, pair);
-  if (pr.nA + pr.nB == 1) {
-    float* out = a.out + ((int64_t)b * a.Hq + h * g) * D;
+  // end of the segment: a pair with a single record is finished here, else the record is
+  // written for the merge kernel
+  float* out = a.out + ((int64_t)b * a.Hq + h * g) * D;
+  if (pair_records(pl, pair) == 1) {
     for (int n = 0; n < g; ++n) {
       const float inv = lrun[n] > 0.f ? 1.0f / lrun[n] : 0.f;
       for (int e = 0; e < D / 64; ++e) out[n * D + lane + 64 * e] = o[n][e] * inv;
     }
     return;
   }
-  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(a);
-  const int base = slot * a.rec_floats;
+  float* rec = a.part + (int64_t)slot * a.rec_floats;
   for (int n = 0; n < g; ++n) {
-    for (int e = 0; e < D / 64; ++e) rec_store1(rs, base + n * D + lane + 64 * e, o[n][e]);
+    for (int e = 0; e < D / 64; ++e) rec[n * D + lane + 64 * e] = o[n][e];
     if (lane == 0) {
-      rec_store1(rs, base + g * D + n, mrun[n]);
-      rec_store1(rs, base + g * D + g + n, lrun[n]);
+      rec[g * D + n] = mrun[n];
+      rec[g * D + g + n] = lrun[n];
     }
   }
-  ar.pend = 1;
-  ar.pend_pair = pair;
 }
 
 // Region-B (low-precision) and fp32 segments: one segment at a time (its query, length
-// and block table fetched at its start), arrivals issued at its end.
+// and block table fetched at its start).
 template <int D, bool F32, int BITS>
-__device__ __forceinline__ void stream_segments(const AttnArgs& a, const Splits& sp, const int* P, UnitIter& it,
-                                                float* wlds, Arrivals& ar) {
-  const int np = a.kv.num_pairs;
+__device__ __forceinline__ void stream_segments(const AttnArgs& a, const Plan& pl, bool seqB, int u, float* wlds) {
+  UnitIter it;
+  iter_init(it, pl, seqB, u);
+  const int np = pl.np;
   for (;;) {
-    const SegDesc d = iter_next_seg(it, P);
+    const SegDesc d = iter_next_seg(it, pl, u);
     if (!d.ok) break;
     if constexpr (F32) {
-      run_region_a_f32<D>(a, sp, P, d.s, d.vlo, d.vhi, slot_of(sp, d, np), wlds, ar);
+      run_region_a_f32<D>(a, pl, d.s, d.vlo, d.vhi, slot_of(pl, d), wlds);
     } else {
       SoftmaxState<D> st;
       run_region_b_lp<D, BITS, ATTN_LP_SETS>(a, d.s - np, d.vlo, d.vhi, d.rev != 0, st);
-      segment_done<D>(a, sp, P, d.s - np, slot_of(sp, d, np), st, ar);
+      segment_done<D>(a, pl, d.s - np, slot_of(pl, d), st);
     }
-    if (ar.pend) arrival_issue(a, ar);
-    if (ar.iss) arrival_check<D>(a, sp, P, ar);
   }
 }
 
 // -------------------------------------------------------------------------------
-// The kernel
+// The streaming kernel
 // -------------------------------------------------------------------------------
 // WPE work-groups per CU (ATTN_GRID * WPE of them): with WPE = 1 a wave may use a whole
 // SIMD's registers; with WPE = 2 (int4 pools) each wave fits in half of them.
@@ -1356,59 +1049,127 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (wid == 0) compute_plan(a, P, Lens, nseg);
   __syncthreads();
-  const int nw = gridDim.x * ATTN_WG_WAVES;
-  // Work-groups are dispatched round-robin over the 8 XCDs; numbering the static units so
-  // that each XCD takes one contiguous eighth of the sequence evens out the XCDs' finish
-  // times (measured: 1-3 us at the 361 MB and 543 MB caches).
+  // the merge kernel reads the prefix from here
+  if (blockIdx.x == 0)
+    for (int s = threadIdx.x; s <= nseg; s += blockDim.x) a.plan[s] = P[s];
+  // Work-groups are dispatched round-robin over the 8 XCDs; numbering the units so that
+  // each XCD takes one contiguous eighth of a sequence evens out the XCDs' finish times
+  // (measured: 1-3 us at the 361 MB and 543 MB caches).
   const int gw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * ATTN_WG_WAVES + wid;
-  Splits sp;
-  sp.nw = nw;
-  sp.lp = LP ? 1 : 0;
-  const int NA = __builtin_amdgcn_readfirstlane(P[np]);
-  sp.A = make_split(NA, nw, 0, 0, 0);
-  sp.B = make_split(LP ? __builtin_amdgcn_readfirstlane(P[nseg]) - NA : 0, nw, np + nw + sp.A.ud, np, NA);
-  // pairs with nothing visible: zeros
-  for (int p = gw; p < np; p += nw) {
-    const PairRecs pr = pair_records(sp, P, np, p);
-    if (pr.nA + pr.nB == 0) {
-      const int b = p / a.Hkv, hk = p % a.Hkv;
-      float* out = a.out + ((int64_t)b * a.Hq + (int64_t)hk * a.g) * a.D;
-      for (int e = threadIdx.x & 63; e < a.g * a.D; e += 64) out[e] = 0.f;
-    }
-  }
-  Arrivals ar;
-  arrivals_init(ar);
+  const Plan pl = make_plan(P, np, gridDim.x * ATTN_WG_WAVES, LP);
   float* wlds = nullptr;
   if constexpr (F32) wlds = reinterpret_cast<float*>(lds + 2 * nseg + 2) + wid * (16 * D + 16 * 32);
-  UnitIter it;
-  iter_init(it, sp.A, nw, gw, np, a.ctl + CTL_TICKET_A);
   if constexpr (F32) {
-    stream_segments<D, true, 8>(a, sp, P, it, wlds, ar);
+    stream_segments<D, true, 8>(a, pl, false, gw, wlds);
   } else {
-    stream_a_bf16<D>(a, sp, P, Lens, it, ar);
+    stream_a_bf16<D>(a, pl, Lens, gw);
     if constexpr (LP) {
-      iter_init(it, sp.B, nw, gw, np, a.ctl + CTL_TICKET_B);
-      if (a.kv.lp_bits == 4) stream_segments<D, false, 4>(a, sp, P, it, nullptr, ar);
-      else stream_segments<D, false, 8>(a, sp, P, it, nullptr, ar);
+      if (a.kv.lp_bits == 4) stream_segments<D, false, 4>(a, pl, true, gw, nullptr);
+      else stream_segments<D, false, 8>(a, pl, true, gw, nullptr);
     }
   }
-  merge_won<D>(a, sp, P, ar);
-  // The last wave out clears the tickets for the next call.  Every wave takes exactly one
-  // ticket past the end of each sequence it drew from, so the totals are known; other
-  // values mean the control words were not zero at the start.
-  int old = 0;
-  if ((threadIdx.x & 63) == 0) old = atomicAdd(a.ctl + CTL_DONE, 1);
-  old = __builtin_amdgcn_readfirstlane(old);
-  if (old == nw - 1 && (threadIdx.x & 63) == 0) {
-    const int ta = __hip_atomic_exchange(a.ctl + CTL_TICKET_A, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int tb = __hip_atomic_exchange(a.ctl + CTL_TICKET_B, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(a.ctl + CTL_DONE, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int ea = sp.A.ud > 0 ? sp.A.ud + nw : 0;
-    const int eb = (LP && sp.B.ud > 0) ? sp.B.ud + nw : 0;
-    if (ta != ea || tb != eb) atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
-  } else if ((unsigned)old >= (unsigned)nw && (threadIdx.x & 63) == 0) {
-    atomicOr(a.kv.err, KVP_ERR_ATTN_WS);
+}
+
+// -------------------------------------------------------------------------------
+// Merge: one wave per (pair, query head).  The pair's records are the segments of its
+// A region then of its B region, consecutive slots each; the wave requests the (m, l)
+// of the first 64 records (one per lane) and the outputs of the first 16 in one batch,
+// so a pair with up to 16 records costs two memory round trips.  The reference max M
+// covers every record; the normaliser is sum_k 2^(m_k - M) l_k and the output
+// sum_k 2^(m_k - M) o_k / normaliser, accumulated in record order, so the result is
+// deterministic.  A pair with no visible token gets zeros; a pair with a single record
+// was finished by the streaming kernel.
+// -------------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void decode_attn_merge_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int np = a.kv.num_pairs, g = a.g;
+  if (w >= np * g) return;
+  const int pair = w / g, n = w % g;
+  const Plan pl = make_plan(a.plan, np, a.nw, a.kv.num_pages8 > 0);
+  int ufA = 0, ufB = 0;
+  const int na = region_records(pl, pair, ufA);
+  const int nb = pl.lp ? region_records(pl, np + pair, ufB) : 0;
+  const int nrec = na + nb;
+  const int b = pair / a.Hkv, h = pair % a.Hkv;
+  float* out = a.out + ((int64_t)b * a.Hq + h * g + n) * D;
+  if (nrec == 1) return;
+  if (nrec == 0) {
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = 0.f;
+    return;
   }
+  const int r0 = pair + ufA, s0 = pl.baseB + pair + ufB;
+  auto rec = [&](int k) {
+    const int slot = (k < na) ? r0 + k : s0 + (k - na);
+    return a.part + (int64_t)slot * a.rec_floats;
+  };
+  // first batch: lane k < 64 holds record k's (m, l); outputs of records 0..15
+  const float* rl = rec(min(lane, nrec - 1));
+  float m0 = rl[g * D + n], l0 = rl[g * D + g + n];
+  float ov0[16][D / 64];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const float* o = rec(min(i, nrec - 1)) + n * D;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) ov0[i][e] = o[lane + 64 * e];
+  }
+  if (lane >= nrec) {
+    m0 = neg_inf();
+    l0 = 0.f;
+  }
+  float M = m0;
+  for (int k = lane + 64; k < nrec; k += 64) M = fmaxf(M, rec(k)[g * D + n]);
+  M = wave_max(M);
+  float acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.f;
+  float den = 0.f;
+  if (M != neg_inf()) {
+    for (int k0 = 0; k0 < nrec; k0 += 64) {
+      const int k = k0 + lane;
+      float wk = 0.f, lk = 0.f;
+      if (k0 == 0) {
+        wk = (m0 == neg_inf()) ? 0.f : exp2f(m0 - M);
+        lk = l0;
+      } else if (k < nrec) {
+        const float m = rec(k)[g * D + n];
+        wk = (m == neg_inf()) ? 0.f : exp2f(m - M);
+        lk = rec(k)[g * D + g + n];
+      }
+      den += wk * lk;
+      const int kn = min(64, nrec - k0);
+      // batches of 16 records: all loads issued before the accumulation
+      for (int kb = 0; kb < kn; kb += 16) {
+        float ov[16][D / 64];
+        if (k0 == 0 && kb == 0) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) ov[i][e] = ov0[i][e];
+        } else {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int kk = min(kb + i, kn - 1);
+            const float* o = rec(k0 + kk) + n * D;
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) ov[i][e] = o[lane + 64 * e];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float wb = (kb + i < kn) ? __shfl(wk, kb + i) : 0.f;
+#pragma unroll
+          for (int e = 0; e < D / 64; ++e) acc[e] += wb * ov[i][e];
+        }
+      }
+    }
+    den = wave_sum(den);
+  }
+  const float inv = (den > 0.f) ? 1.0f / den : 0.f;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) out[lane + 64 * e] = acc[e] * inv;
 }
 
 // LDS: page prefix P[nseg + 1], the pool lengths [num_pairs] (padded to nseg + 1 ints),
@@ -1424,17 +1185,12 @@ size_t attn_lds_bytes(int num_pairs, int D, bool f32, bool lp) {
 
 using namespace kvp;
 
-// Record slots of one sequence: regions + static units + dynamic units (at most 3 per
-// wave plus one, see make_split), for the largest launch (two waves per SIMD).
-static size_t attn_max_slots(int num_pairs) {
-  return 2 * ((size_t)num_pairs + 4 * (size_t)ATTN_MAX_NWAVES + 1);
-}
-
+// Workspace: [plan: 2 num_pairs + 1 ints][records].  Record slots: per sequence, regions
+// + units (every segment is one (region, unit) pair and s + u is unique), for the
+// largest launch (two waves per SIMD).
+static size_t attn_plan_bytes(int num_pairs) { return (((size_t)(2 * num_pairs + 1) * sizeof(int)) + 255) & ~(size_t)255; }
 static size_t attn_rec_floats(int g, int D) { return ((size_t)g * (D + 2) + 3) & ~(size_t)3; }
-
-static size_t attn_cnt_bytes(int num_pairs) { return (((size_t)num_pairs * sizeof(int)) + 255) & ~(size_t)255; }
-// Workspace: [control words][arrival counts][pair links][records]; only the first two
-// must start at zero.
+static size_t attn_max_slots(int num_pairs) { return 2 * ((size_t)num_pairs + ATTN_MAX_NWAVES); }
 
 extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                                  int32_t head_dim) {
@@ -1442,12 +1198,13 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   const int Hkv = num_pairs / B;
   if (Hq % Hkv != 0) return 0;
   const int g = Hq / Hkv;
-  return ATTN_CTL_BYTES + 2 * attn_cnt_bytes(num_pairs) + attn_max_slots(num_pairs) * attn_rec_floats(g, head_dim) * sizeof(float);
+  return attn_plan_bytes(num_pairs) + attn_max_slots(num_pairs) * attn_rec_floats(g, head_dim) * sizeof(float);
 }
 
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream) {
+  (void)ws_bytes;
   AttnArgs a;
   a.q = q;
   a.out = out;
@@ -1461,25 +1218,20 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
   if (ring) a.ring = *ring;
   else a.ring = kvp_ring{};
   a.scale_log2 = sm_scale * 1.4426950408889634f;
-  char* w = reinterpret_cast<char*>(ws);
-  a.ctl = reinterpret_cast<int*>(w);
-  a.cnt = reinterpret_cast<int*>(w + ATTN_CTL_BYTES);
-  a.link = reinterpret_cast<int*>(w + ATTN_CTL_BYTES + attn_cnt_bytes(kv->num_pairs));
-  a.part = reinterpret_cast<float*>(w + ATTN_CTL_BYTES + 2 * attn_cnt_bytes(kv->num_pairs));
-  const size_t part_bytes = ws_bytes - ATTN_CTL_BYTES - 2 * attn_cnt_bytes(kv->num_pairs);
-  if (part_bytes > 0x7fffffffu) return KVP_E_UNSUPPORTED;  // buffer offsets are 32-bit
-  a.part_bytes = (int)part_bytes;
+  a.plan = reinterpret_cast<int*>(ws);
+  a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + attn_plan_bytes(kv->num_pairs));
   a.rec_floats = (int)attn_rec_floats(a.g, a.D);
   const bool f32 = kv->dtype == KVP_F32;
   const bool lp = kv->num_pages8 > 0;
   const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32, lp);
   if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
-  const dim3 g1(ATTN_GRID), b(256);
+  const dim3 g1(ATTN_GRID), g2(ATTN_GRID * 2), b(256);
+  a.nw = ATTN_GRID * ATTN_WG_WAVES;
   if (f32) {
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false, 1>), g1, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, true, false, 1>), g1, b, lds, stream, a);
   } else if (lp && kv->lp_bits == 4) {
-    const dim3 g2(ATTN_GRID * 2);
+    a.nw = 2 * ATTN_GRID * ATTN_WG_WAVES;
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 2>), g2, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 2>), g2, b, lds, stream, a);
   } else if (lp) {
@@ -1489,6 +1241,10 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, false, 1>), g1, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, false, 1>), g1, b, lds, stream, a);
   }
+  KVP_LAUNCH_CHECK();
+  const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
+  if (a.D == 64) hipLaunchKernelGGL((decode_attn_merge_kernel<64>), cgrid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((decode_attn_merge_kernel<128>), cgrid, dim3(256), 0, stream, a);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
 }

@@ -292,6 +292,5 @@ extern "C" kvp_status kvp_check(const kvp_paged_kv* kv, hipStream_t stream) {
   int host_err = 0;
   if (hipMemcpy(&host_err, kv->err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
     return KVP_E_HIP;
-  if (host_err & (KVP_ERR_POOL_FULL | KVP_ERR_TABLE_FULL | KVP_ERR_POOL8_FULL)) return KVP_E_CAPACITY;
-  return host_err ? KVP_E_WORKSPACE : KVP_OK;
+  return host_err ? KVP_E_CAPACITY : KVP_OK;
 }

@@ -271,44 +271,18 @@ def test_decode_attn(K, B, Hq, Hkv, T, d, dtype, ring_w, keepfrac):
     ref = oracle.decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
                                   oracle.sm_scale(d))
     check_attention(out, ref, dtype)
-    # deterministic: a rerun on the same workspace (counters left at zero by the first
-    # call, records garbage-filled) gives identical bits
+    # deterministic: a rerun (with a garbage-filled workspace) gives identical bits
     rerun_identical(K, q, kv, ring, d, out, ws)
 
 
 def rerun_identical(K, q, kv, ring, d, out, ws):
-    """The counter part of the workspace is zero after a call; a rerun with the record
-    part garbage-filled gives the same bits."""
-    nc = K.decode_attn_counter_bytes(kv.c.num_pairs) // 4
-    assert int(ws[:nc].abs().sum()) == 0, "counters not left at zero"
-    ws[nc:].fill_(-1)
+    """A rerun on a garbage-filled workspace gives the same bits (the split does not
+    depend on timing and every record is written before it is read)."""
+    ws.fill_(-1)
     out2 = torch.full_like(out, float("nan"))
     K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out2, ws)
     assert torch.equal(out, out2)
     assert K.kvp_check(kv) == 0
-
-
-def test_decode_attn_garbage_workspace_is_reported(K):
-    """Counters that were not zero before the first use are reported by kvp_check as
-    KVP_E_WORKSPACE; a zeroed workspace then gives the right result."""
-    B, Hq, Hkv, T, d = 2, 8, 2, 1500, 128
-    P = B * Hkv
-    keep = (torch.rand((P, T), generator=torch.Generator().manual_seed(5)) < 0.3).numpy()
-    keep[:, T - 128:] = True
-    k, v, kv, ring = build_cache(K, B, Hkv, T, d, torch.bfloat16, keep, 128, seed=91)
-    q = seeded((B, Hq, d), 94, torch.bfloat16)
-    out = torch.zeros((B, Hq, d), device=DEV)
-    ws = K.decode_attn_workspace(B, Hq, kv)
-    ws.fill_(-1)
-    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
-    assert K.kvp_check(kv) == 3  # KVP_E_WORKSPACE
-    K.kvp_clear_error(kv)
-    ws.zero_()
-    K.kvp_decode_attn(q, kv, ring, K.sm_scale(d), out, ws)
-    assert K.kvp_check(kv) == 0
-    ref = oracle.decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T), oracle.sm_scale(d))
-    check_attention(out, ref, torch.bfloat16)
-    rerun_identical(K, q, kv, ring, d, out, ws)
 
 
 def test_decode_attn_empty_pairs(K):
@@ -359,7 +333,7 @@ def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
 def test_decode_attn_lowprec_edges(K, bits, B, Hq, Hkv, T, d, ring_w, case):
     """Attention over a full-precision pool (+ ring) and an int8 / int4 pool in one
     softmax, at the head-group, head-dim and pair-count limits and with regions of a
-    pair empty; reruns on the same workspace (records garbage-filled) are bit-identical."""
+    pair empty; reruns on a garbage-filled workspace are bit-identical."""
     P = B * Hkv
     g = torch.Generator().manual_seed(T + d + bits)
     keep = (torch.rand((P, T), generator=g) < 0.15).numpy()
