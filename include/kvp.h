@@ -20,7 +20,8 @@
  * Conventions for every entry point:
  *   - All data pointers are DEVICE pointers owned by the caller (structs themselves
  *     live in host memory).  The library allocates nothing, keeps no hidden state
- *     between calls, and never synchronises, except kvp_check().
+ *     between calls (one exception: the fixed per-GPU scratch behind
+ *     kvp_decode_attn_noalloc), and never synchronises, except kvp_check().
  *   - Every call enqueues its kernels on `stream` and returns at once; outputs are
  *     valid once the stream reaches that point.  Calls on different streams must use
  *     disjoint buffers.
@@ -328,6 +329,29 @@ kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
                            float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                       int32_t head_dim);
+
+/* ----------------------------------------------------------------------------
+ * kvp_decode_attn_noalloc - kvp_decode_attn for callers that cannot allocate device
+ * memory at all (code under HIP graph capture, tight serving loops, hosts that forbid
+ * hipMalloc): no workspace argument; the library's own fixed device scratch of
+ * KVP_NOALLOC_SCRATCH_BYTES, one copy per GPU, reserved when the library's code is
+ * loaded on that GPU and held until the process ends, takes its place.  The call
+ * itself allocates nothing (no hipMalloc, no hipFree).
+ *   Arguments, layouts, output and errors as kvp_decode_attn, and the same kernels, so
+ *   the output is bit-identical to kvp_decode_attn's.  Additionally:
+ *   KVP_E_WORKSPACE  kvp_decode_attn_workspace_size(B, Hq, num_pairs, head_dim) exceeds
+ *                    KVP_NOALLOC_SCRATCH_BYTES (g = 4, d = 128 fits up to 14056 pairs,
+ *                    g = 8 up to 6012, g = 16 up to 1984)
+ *   KVP_E_ARG        `stream` belongs to another device than the current one
+ * The scratch is shared by every call on one GPU and keeps the last call's contents
+ * (nothing in it needs to start at zero): calls that overlap in time on one GPU, on
+ * different streams or from different threads, race and give undefined outputs.
+ * Serialise them (one stream, or events).
+ * -------------------------------------------------------------------------- */
+#define KVP_NOALLOC_SCRATCH_BYTES (64u << 20) /* 64 MiB per GPU */
+kvp_status kvp_decode_attn_noalloc(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
+                                   const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
+                                   float* out, hipStream_t stream);
 
 /* ----------------------------------------------------------------------------
  * kvp_prefill_attn - causal attention of every prompt position over the keys the

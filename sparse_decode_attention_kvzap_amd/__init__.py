@@ -9,7 +9,8 @@ from ._lib import (  # noqa: F401
     KVP_SCORER_LINEAR, KVP_SCORER_MLP, ERR_POOL8_FULL, ERR_POOL_FULL, ERR_TABLE_FULL,
     KvpError, PagedKV, Ring, Scorer, decode_attn_workspace, kvp_check, kvp_clear_error,
     kvp_compact, kvp_compact_workspace_size, kvp_decode_attn,
-    kvp_decode_attn_workspace_size, kvp_prefill_attn, kvp_reset, kvp_score,
+    kvp_decode_attn_workspace_size, kvp_decode_attn_noalloc, KVP_NOALLOC_SCRATCH_BYTES,
+    kvp_prefill_attn, kvp_reset, kvp_score,
     kvp_score_workspace_size,
     kvp_select, kvp_select_workspace_size, kvp_status_str, kvp_step_delayed,
     kvp_score_step_delayed,

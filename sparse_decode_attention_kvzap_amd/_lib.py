@@ -99,6 +99,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
         "kvp_decode_attn_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+        "kvp_decode_attn_noalloc": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
+                                              P(KvpPagedKV), P(KvpRing), c_float, c_void_p,
+                                              c_void_p]),
         "kvp_prefill_attn": (c_int32, [c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                        c_int32, c_int32, c_int32, c_void_p, c_void_p, c_int32,
                                        c_float, c_void_p, c_void_p]),
@@ -429,6 +432,20 @@ def kvp_decode_attn(q: torch.Tensor, kv: PagedKV, ring: Optional[Ring], sm_scale
                                ws.numel() * ws.element_size(), _stream(stream)),
         "kvp_decode_attn")
     return out
+
+
+def kvp_decode_attn_noalloc(q: torch.Tensor, kv: PagedKV, ring: Optional[Ring], sm_scale: float,
+                            out: torch.Tensor, stream=None) -> torch.Tensor:
+    """kvp_decode_attn on the library's fixed per-GPU scratch (no workspace argument)."""
+    _cuda(q, out)
+    B, Hq, _ = q.shape
+    _ok(load().kvp_decode_attn_noalloc(q.data_ptr(), _dt(q), B, Hq, _kvref(kv), _ringref(ring),
+                                       float(sm_scale), out.data_ptr(), _stream(stream)),
+        "kvp_decode_attn_noalloc")
+    return out
+
+
+KVP_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def kvp_reset(kv: PagedKV, ring: Optional[Ring] = None, stream=None):

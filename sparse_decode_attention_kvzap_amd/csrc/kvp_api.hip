@@ -3,6 +3,8 @@
 // allocates or synchronises (except kvp_check), and no exception escapes.
 #include <string.h>
 
+#include <mutex>
+
 #include "kvp_internal.h"
 
 // launchers (defined next to their kernels)
@@ -235,9 +237,11 @@ extern "C" kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* h
                                  sc, hidden_new, s_new, part);
 }
 
-extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
-                                      const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
-                                      float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+
+// Shape and dtype rules shared by both decode-attention entry points.
+kvp_status check_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
+                             const kvp_paged_kv* kv, const kvp_ring* ring, const float* out) {
   kvp_status st = check_kv(kv);
   if (st != KVP_OK) return st;
   if ((st = check_ring(ring)) != KVP_OK) return st;
@@ -251,10 +255,67 @@ extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, 
   if (kvp_attn_lds_bytes_host(kv->num_pairs, kv->head_dim, kv->dtype == KVP_F32, kv->num_pages8 > 0) >
       160 * 1024)
     return KVP_E_UNSUPPORTED;
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
+                                      const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
+                                      float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const kvp_status st = check_decode_attn(q, qdtype, B, Hq, kv, ring, out);
+  if (st != KVP_OK) return st;
   if (!ws || ws_bytes < kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs, kv->head_dim))
     return KVP_E_WORKSPACE;
   if (((uintptr_t)ws) & 255) return KVP_E_ARG;
   return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, ws_bytes, stream);
+}
+
+// Decode-attention scratch for callers that cannot allocate: a fixed array in device
+// memory, one copy per GPU the library runs on, held until the process ends.  Host
+// code never passes `scratch` itself to a kernel (on the host it is only a stand-in
+// for the symbol); it uses the device address looked up once per device below.
+static __device__ __align__(256) unsigned char scratch[KVP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices];  // device address of `scratch`, per device id
+
+// Device address of `scratch` on `dev`, which must be the current device.  The first
+// call on a device looks it up; later calls return the cached address.
+kvp_status scratch_address(int dev, void** ptr) {
+  if (dev < 0 || dev >= kMaxScratchDevices) return KVP_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVP_E_HIP;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return KVP_OK;
+}
+
+}  // namespace
+
+extern "C" kvp_status kvp_decode_attn_noalloc(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
+                                              const kvp_paged_kv* kv, const kvp_ring* ring,
+                                              float sm_scale, float* out, hipStream_t stream) {
+  const kvp_status st = check_decode_attn(q, qdtype, B, Hq, kv, ring, out);
+  if (st != KVP_OK) return st;
+  const size_t need = kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs, kv->head_dim);
+  if (need == 0 || need > (size_t)KVP_NOALLOC_SCRATCH_BYTES) return KVP_E_WORKSPACE;
+  int cur = -1, sdev = -1;
+  if (hipGetDevice(&cur) != hipSuccess || hipStreamGetDevice(stream, &sdev) != hipSuccess)
+    return KVP_E_HIP;
+  if (sdev != cur) return KVP_E_ARG;
+  void* ws = nullptr;
+  const kvp_status sa = scratch_address(cur, &ws);
+  if (sa != KVP_OK) return sa;
+  // Nothing in the scratch has to start at zero: the first kernel writes the page
+  // prefix and every record before the merge kernel reads them.
+  return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, need, stream);
 }
 
 extern "C" kvp_status kvp_prefill_attn(const void* q, const void* k, const void* v, int32_t dtype,
