@@ -18,6 +18,7 @@ all arithmetic runs in the HIP kernels.
 """
 from __future__ import annotations
 
+import contextlib
 from typing import Optional
 
 import torch
@@ -114,15 +115,27 @@ class PrunedKVCache:
         self.T0 = T
 
     # -- decode ------------------------------------------------------------------
-    def set_tau(self, tau: float):
+    @staticmethod
+    def _on(stream):
+        """Run torch's own writes (fills) on `stream` too, so they stay in order with the
+        library calls made on it.  A raw handle is wrapped; None is torch's current stream."""
+        if stream is None:
+            return contextlib.nullcontext()
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        return torch.cuda.stream(stream)
+
+    def set_tau(self, tau: float, stream=None):
         """A fixed threshold (also mirrored to the device copy the decode step reads)."""
         self.tau = float(tau)
-        self.tau_dev.fill_(self.tau)
+        with self._on(stream):
+            self.tau_dev.fill_(self.tau)
 
-    def set_position(self, p: int):
+    def set_position(self, p: int, stream=None):
         """The absolute position the next decode step appends (kept on the device)."""
-        self.pos_dev[0] = p
-        self.pos_dev[1] = 0
+        with self._on(stream):
+            self.pos_dev[0] = p
+            self.pos_dev[1] = 0
 
     def advance(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
                 p: Optional[int] = None, stream=None):
@@ -132,9 +145,10 @@ class PrunedKVCache:
         that call takes (bf16, B <= 64, H and the width multiples of 256); otherwise
         kvp_score runs first."""
         if p is not None:
-            self.set_position(p)
+            self.set_position(p, stream)
         if not isinstance(self.tau, torch.Tensor):
-            self.tau_dev.fill_(self.tau)
+            with self._on(stream):
+                self.tau_dev.fill_(self.tau)
         if self._fused_score:
             L.kvp_score_step_delayed(self.scorer, hidden_new, self.kv, self.ring, k_new, v_new,
                                      self.tau_dev, self.pos_dev, self.s_new, self.ws_score, stream)
