@@ -13,11 +13,14 @@ on the device, step after step.
 
     value        kept token-heads attended per second of decode-step time: the token-heads
                  each timed step's attention reads, summed over the K timed steps, over
-                 their total time (HIP events on the launch stream, K steps back to back)
+                 their total time (one HIP event pair on the launch stream around the K
+                 steps, queued back to back)
     ms_per_step  that time / K
     roofline     decode attention (its stream kernel + merge kernel): algorithmic bytes per
-                 call / mean call duration, timed with HIP events around every attention
-                 call inside the timed steps, on the stream it is launched on
+                 call / mean call duration, from K calls back to back on the cache the timed
+                 steps left, one HIP event pair around them on the launch stream (an event
+                 recorded between two kernels idles the GPU for microseconds, so no event
+                 sits inside a timed loop)
 
 Records of the same run, each on its own seeded synthetic inputs:
     prefill         the compression calls of the headline workload, one by one
@@ -129,6 +132,11 @@ class Context:
     def advance(self, stream):
         self.cache.advance(self.h_new, self.k_new, self.v_new, stream=stream)
 
+    def step(self, stream):
+        """One decode step: kvp_decode_step (the delayed step folded into the attention)
+        for a bf16 cache without a low-precision pool, else the separate calls."""
+        self.cache.step(self.h_new, self.k_new, self.v_new, self.q, stream=stream)
+
     def attend(self, stream):
         self.cache.attend(self.q, stream)
 
@@ -153,9 +161,12 @@ class Context:
 # ------------------------------------------------------------------------------ decode
 
 def decode_run(ctx, q_keep, steps, warmup, stream, graph=False):
-    """Compress, then `warmup` + `steps` decode steps back to back; events around every
-    attention call of the timed steps.  The token-heads each step's attention reads come
-    from an identical untimed pass (same inputs, same device state sequence)."""
+    """Compress, then `warmup` + `steps` decode steps back to back, timed by one pair of
+    events around the `steps` (an event recorded between kernels costs the GPU several
+    microseconds of idle time, so none sits inside the timed steps).  The token-heads each
+    step's attention reads come from an identical untimed pass (same inputs, same device
+    state sequence).  The decode attention alone is then timed the same way: `steps` calls
+    back to back on the cache the steps left."""
     import numpy as np
     import torch
 
@@ -168,42 +179,61 @@ def decode_run(ctx, q_keep, steps, warmup, stream, graph=False):
         split.append(ctx.read_split())
     tau = float(ctx.cache.tau_dev.item())
 
-    ctx.compress(q_keep, stream)
-    for _ in range(warmup):
-        ctx.advance(stream)
+    def timed_steps(fused):
+        ctx.compress(q_keep, stream)
+        for _ in range(warmup):
+            if fused:
+                ctx.step(stream)
+            else:
+                ctx.advance(stream)
+                ctx.attend(stream)
+        start, end = new_event(), new_event()
+        stream.synchronize()
+        start.record(stream)
+        for _ in range(steps):
+            if fused:
+                ctx.step(stream)
+            else:
+                ctx.advance(stream)
+                ctx.attend(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        assert ctx.cache.check(stream) == 0, "pool overflow"
+        return start.elapsed_time(end)
+
+    # the same steps as separate calls (delayed step, then attention), then as the fused
+    # call, which the headline times
+    separate_ms = timed_steps(False)
+    total_ms = timed_steps(True)
+    # the attention alone, back to back on the cache as the last step left it
+    last = ctx.read_split()
+    for _ in range(2):
         ctx.attend(stream)
-    a0 = [new_event() for _ in range(steps)]
-    a1 = [new_event() for _ in range(steps)]
-    start, end = new_event(), new_event()
-    stream.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        ctx.advance(stream)
-        a0[i].record(stream)
+    e0, e1 = new_event(), new_event()
+    e0.record(stream)
+    for _ in range(steps):
         ctx.attend(stream)
-        a1[i].record(stream)
-    end.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    assert ctx.cache.check(stream) == 0, "pool overflow"
-    total_ms = start.elapsed_time(end)
-    attn = [a0[i].elapsed_time(a1[i]) for i in range(steps)]
+    attn_ms = e0.elapsed_time(e1) / steps
+    nbytes = ctx.attn_bytes(*last)
     timed = split[warmup:]
     th = [m + lp for m, lp in timed]
-    nbytes = [ctx.attn_bytes(m, lp) for m, lp in timed]
-    attn_ms = float(np.mean(attn))
-    mean_bytes = float(np.mean(nbytes))
     r = {
         "keep_quantile": q_keep, "tau": tau,
         "token_heads_per_step": float(np.mean(th)),
         "low_precision_token_heads_per_step": float(np.mean([lp for _, lp in timed])),
         "total_token_heads": ctx.wl.B * ctx.wl.Hkv * ctx.wl.T,
         "ms_per_step": total_ms / steps,
+        "separate_calls_ms_per_step": separate_ms / steps,
+        "fused_step": bool(ctx.cache.fused_step),
         "token_heads_per_s": float(np.sum(th)) / (total_ms * 1e-3),
-        "attn": {"ms": attn_ms, "ms_min": float(np.min(attn)), "ms_max": float(np.max(attn)),
-                 "launches": steps, "bytes_per_call": mean_bytes,
-                 "gbs": gbs(mean_bytes, attn_ms),
-                 "frac_of_peak": gbs(mean_bytes, attn_ms) / PEAK_HBM_GBS,
-                 "token_heads_per_s": float(np.mean(th)) / (attn_ms * 1e-3)},
+        "attn": {"ms": attn_ms, "launches": steps, "bytes_per_call": nbytes,
+                 "token_heads": sum(last), "gbs": gbs(nbytes, attn_ms),
+                 "frac_of_peak": gbs(nbytes, attn_ms) / PEAK_HBM_GBS,
+                 "token_heads_per_s": sum(last) / (attn_ms * 1e-3),
+                 "timing": "calls back to back on the cache after the timed steps, one "
+                           "event pair around them"},
     }
     if graph:
         # the same decode step captured once and replayed: every per-step value lives in
@@ -212,8 +242,7 @@ def decode_run(ctx, q_keep, steps, warmup, stream, graph=False):
         side.wait_stream(stream)
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=side):
-            ctx.advance(side)
-            ctx.attend(side)
+            ctx.step(side)
         torch.cuda.synchronize()
         ctx.compress(q_keep, stream)
         with torch.cuda.stream(stream):
@@ -490,34 +519,38 @@ def dms_loop(dev, stream):
             vb.copy_(V_all[i])
             qb.copy_(Q_all[i])
 
-    # 1. token-heads each step's attention reads, and per-call attention time
+    # 1. token-heads each step's attention reads (untimed)
     prefill()
-    visible, attn_ms = [], []
+    visible = []
     for i in range(S):
         feed(i)
         cache.advance(hb, kb, vb, stream=stream)
-        e0, e1 = new_event(), new_event()
-        e0.record(stream)
-        cache.attend(qb, stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        attn_ms.append(e0.elapsed_time(e1))
         visible.append(cache.visible_token_heads())
     assert cache.check(stream) == 0
-    out_eager = cache.out.clone()
 
-    # 2. eager loop, timed
-    prefill()
-    torch.cuda.synchronize()
-    e0, e1 = new_event(), new_event()
-    e0.record(stream)
-    for i in range(S):
-        feed(i)
-        cache.step(hb, kb, vb, qb, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    eager_ms = e0.elapsed_time(e1)
-    assert torch.equal(cache.out, out_eager)
+    def timed_loop(fused):
+        prefill()
+        torch.cuda.synchronize()
+        e0, e1 = new_event(), new_event()
+        e0.record(stream)
+        for i in range(S):
+            feed(i)
+            if fused:
+                cache.step(hb, kb, vb, qb, stream=stream)
+            else:
+                cache.advance(hb, kb, vb, stream=stream)
+                cache.attend(qb, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    # 2. eager loops, timed: the separate calls (delayed step, then attention), and the
+    #    fused decode step
+    separate_ms = timed_loop(False)
+    out_separate = cache.out.clone()
+    eager_ms = timed_loop(True)
+    out_fused = cache.out.clone()
+    fused_vs_separate = float((out_fused - out_separate).abs().max())
 
     # 3. the same loop with the step captured once and replayed
     prefill()
@@ -541,28 +574,43 @@ def dms_loop(dev, stream):
     torch.cuda.synchronize()
     graph_ms = e0.elapsed_time(e1)
     assert cache.check(stream) == 0
-    same = bool(torch.equal(cache.out, out_eager))
+    same = bool(torch.equal(cache.out, out_fused))
     del graph
-
+    # the decode attention alone, back to back on the cache the loop left (the last step's
+    # token-heads)
+    for _ in range(2):
+        cache.attend(qb, stream)
+    e0, e1 = new_event(), new_event()
+    e0.record(stream)
+    for _ in range(20):
+        cache.attend(qb, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    attn_ms = e0.elapsed_time(e1) / 20
+    last_bytes = visible[-1] * (2 * d * elt + 4 / 16) + B * Hq * d * (elt + 4)
+    achieved = gbs(last_bytes, attn_ms)
     th = float(np.sum(visible))
-    nbytes = th * 2 * d * elt + th / 16 * 4 + S * B * Hq * d * (elt + 4)
-    attn_total = float(np.sum(attn_ms))
-    achieved = gbs(nbytes, attn_total)
     r = {"workload": wl.name, "batch": B, "prompt": P0, "decode_steps": S, "delay_window": wl.w,
          "tau": wl.fixed_tau, "dtype": dtype_name(wl.kv_dtype),
-         "eager_ms_per_step": eager_ms / S, "graph_ms_per_step": graph_ms / S,
+         "eager_ms_per_step": eager_ms / S, "separate_calls_ms_per_step": separate_ms / S,
+         "graph_ms_per_step": graph_ms / S,
+         "token_heads_per_s_eager": th / (eager_ms * 1e-3),
          "token_heads_per_s_graph": th / (graph_ms * 1e-3),
-         "attn": {"ms_per_step": attn_total / S, "bytes_per_step": nbytes / S, "gbs": achieved,
-                  "frac_of_peak": achieved / PEAK_HBM_GBS,
-                  "token_heads_per_s": th / (attn_total * 1e-3)},
-         "token_heads_first_step": visible[0], "token_heads_last_step": visible[-1],
+         "fused_vs_separate_max_abs": fused_vs_separate,
          "graph_output_equals_eager": same,
-         "note": "each step: refill the 4 input buffers, then kvp_score_step_delayed (linear "
-                 "scorer inside the delayed step, one kernel) and kvp_decode_attn (stream + "
-                 "merge kernels); the graph holds the last two"}
-    log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step, graph {graph_ms / S * 1e3:.1f} "
-        f"us/step, attention {attn_total / S * 1e3:.1f} us/step at {achieved:.0f} GB/s; "
-        f"token-heads {visible[0]} -> {visible[-1]}")
+         "attn": {"ms": attn_ms, "bytes_per_call": last_bytes, "token_heads": visible[-1],
+                  "gbs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS,
+                  "token_heads_per_s": visible[-1] / (attn_ms * 1e-3),
+                  "timing": "kvp_decode_attn back to back on the cache after the last step"},
+         "token_heads_first_step": visible[0], "token_heads_last_step": visible[-1],
+         "note": "each step: refill the 4 input buffers, then kvp_decode_step (the linear "
+                 "scorer and the delayed step folded into the attention's stream and merge "
+                 "kernels); separate_calls = kvp_score_step_delayed then kvp_decode_attn; the "
+                 "graph holds the decode step"}
+    log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step (separate calls "
+        f"{separate_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step; attention "
+        f"{attn_ms * 1e3:.1f} us at {achieved:.0f} GB/s on the last cache; token-heads "
+        f"{visible[0]} -> {visible[-1]}; fused vs separate max diff {fused_vs_separate:.2e}")
     return r
 
 

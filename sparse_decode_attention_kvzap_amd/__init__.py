@@ -10,6 +10,7 @@ from ._lib import (  # noqa: F401
     KvpError, PagedKV, Ring, Scorer, decode_attn_workspace, kvp_check, kvp_clear_error,
     kvp_compact, kvp_compact_workspace_size, kvp_decode_attn,
     kvp_decode_attn_workspace_size, kvp_decode_attn_noalloc, KVP_NOALLOC_SCRATCH_BYTES,
+    kvp_decode_step, kvp_decode_step_workspace_size, decode_step_workspace,
     kvp_prefill_attn, kvp_reset, kvp_score,
     kvp_score_workspace_size,
     kvp_select, kvp_select_workspace_size, kvp_status_str, kvp_step_delayed,

@@ -99,6 +99,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                       P(KvpRing), c_float, c_void_p, c_void_p, c_size_t,
                                       c_void_p]),
         "kvp_decode_attn_workspace_size": (c_size_t, [c_int32, c_int32, c_int32, c_int32]),
+        "kvp_decode_step": (c_int32, [P(KvpScorer), c_void_p, c_int32, P(KvpPagedKV), P(KvpRing),
+                                      c_void_p, c_void_p, c_void_p, c_int64, c_void_p, c_void_p,
+                                      c_void_p, c_void_p, c_int32, c_int32, c_int32, c_float,
+                                      c_void_p, c_void_p, c_size_t, c_void_p]),
+        "kvp_decode_step_workspace_size": (c_size_t, [P(KvpScorer), c_int32, c_int32, c_int32,
+                                                     c_int32]),
         "kvp_decode_attn_noalloc": (c_int32, [c_void_p, c_int32, c_int32, c_int32,
                                               P(KvpPagedKV), P(KvpRing), c_float, c_void_p,
                                               c_void_p]),
@@ -446,6 +452,40 @@ def kvp_decode_attn_noalloc(q: torch.Tensor, kv: PagedKV, ring: Optional[Ring], 
 
 
 KVP_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def kvp_decode_step_workspace_size(scorer: Optional["Scorer"], B: int, Hq: int, num_pairs: int,
+                                   head_dim: int) -> int:
+    return load().kvp_decode_step_workspace_size(None if scorer is None else ctypes.byref(scorer.c),
+                                                 B, Hq, num_pairs, head_dim)
+
+
+def decode_step_workspace(scorer: Optional["Scorer"], B: int, Hq: int, kv: PagedKV,
+                          device="cuda") -> torch.Tensor:
+    """A workspace of the size kvp_decode_step needs (contents are scratch)."""
+    n = kvp_decode_step_workspace_size(scorer, B, Hq, kv.c.num_pairs, kv.c.head_dim)
+    return torch.empty(max(n, 4) // 4 + 1, dtype=torch.int32, device=device)
+
+
+def kvp_decode_step(scorer: Optional["Scorer"], hidden_new: Optional[torch.Tensor], kv: PagedKV,
+                    ring: Ring, k_new: torch.Tensor, v_new: torch.Tensor, tau: torch.Tensor,
+                    pos: torch.Tensor, q: torch.Tensor, sm_scale: float, out: torch.Tensor,
+                    ws: torch.Tensor, s_in: Optional[torch.Tensor] = None, ld_s: int = 1,
+                    s_out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One fused decode step: the delayed step (new tokens scored by `scorer` from
+    hidden_new, or read from s_in[pair * ld_s] when scorer is None) and the attention of
+    q [B, Hq, d] over the cache it leaves -> out [B, Hq, d] fp32."""
+    _cuda(hidden_new, k_new, v_new, tau, pos, q, out, ws, s_in, s_out)
+    assert tau.dtype == torch.float32 and pos.dtype == torch.int32 and pos.numel() >= 2
+    B, Hq, _ = q.shape
+    _ok(load().kvp_decode_step(None if scorer is None else ctypes.byref(scorer.c),
+                               _p(hidden_new), 0 if hidden_new is None else _dt(hidden_new),
+                               _kvref(kv), _ringref(ring), k_new.data_ptr(), v_new.data_ptr(),
+                               _p(s_in), ld_s, _p(s_out), tau.data_ptr(), pos.data_ptr(),
+                               q.data_ptr(), _dt(q), B, Hq, float(sm_scale), out.data_ptr(),
+                               ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream)),
+        "kvp_decode_step")
+    return out
 
 
 def kvp_reset(kv: PagedKV, ring: Optional[Ring] = None, stream=None):

@@ -33,7 +33,7 @@
 // looks two segments ahead: the next segments' block-table entries are requested while
 // the current one streams and the next pair's queries with its first K, so crossing from
 // one pair to the next costs no memory round trip.
-#include "kvp_internal.h"
+#include "step_core.h"
 
 namespace kvp {
 
@@ -63,6 +63,12 @@ struct AttnArgs {
   int nw;            // waves of the streaming kernel
   float* part;       // records, rec_floats each
   int rec_floats;    // g * (D + 2) rounded up to 4: o[g][D], then m[g], then l[g]
+  // Fused decode step (fstep = 1, bf16 pool with a ring, no low-precision pool): the
+  // attention reads the cache as the delayed step st would leave it -- the token leaving
+  // ring slot p mod window counts iff it is retained, the new token (st.k_new, st.v_new)
+  // is one more virtual page of its pair -- and the merge kernel then applies the step.
+  int fstep;
+  StepArgs st;
 };
 
 // -------------------------------------------------------------------------------
@@ -77,27 +83,39 @@ __device__ __forceinline__ int region_pages_of(int len, int extra) { return (cdi
 
 // Wave 0: P[0] = 0, P[s + 1] = P[s] + pages of region s.  Each lane takes a run of
 // regions; lengths are requested eight at a time so the loads overlap.
-// The A regions' pool lengths go to Lens[] on the way.
-__device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Lens, int nseg) {
+// The A regions' pool lengths go to Lens[] on the way; with a fused step, bit 31 of
+// Lens[s] says whether the token leaving pair s's ring slot `slot` is retained (its
+// position >= 0 and score >= tau), and each A region has one more page (the new token).
+constexpr int LEN_MASK = 0x7fffffff;
+__device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Lens, int nseg, int slot,
+                                             float tau) {
   const int lane = threadIdx.x & 63;
   const int np = a.kv.num_pairs;
-  const int nring = a.has_ring ? a.ring.window / PAGE : 0;
+  const int nring = a.has_ring ? a.ring.window / PAGE + a.fstep : 0;
   const int per = cdiv(nseg, 64);
   const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
   int sum = 0;
   for (int b = s0; b < s1; b += 8) {
     int v[8];
+    int rpos[8];
+    float rsc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = b + i;
       v[i] = 0;
+      rpos[i] = -1;
+      rsc[i] = 0.f;
       if (s < s1) v[i] = (s < np) ? a.kv.length[s] : a.kv.length8[s - np];
+      if (a.fstep && s < s1) {
+        rpos[i] = a.ring.pos[(int64_t)s * a.ring.window + slot];
+        rsc[i] = a.ring.score[(int64_t)s * a.ring.window + slot];
+      }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int s = b + i;
       if (s < s1) {
-        if (s < np) Lens[s] = v[i];
+        if (s < np) Lens[s] = v[i] | ((rpos[i] >= 0 && rsc[i] >= tau) ? (int)0x80000000u : 0);
         const int n = region_pages_of(v[i], s < np ? nring : 0);
         P[s + 1] = n;
         sum += n;
@@ -260,15 +278,25 @@ struct Bf16Frags {
 struct PageRef {
   const uint16_t* k;  // K page base
   const uint16_t* v;  // V^T page base
-  int kind;           // 0 main, 1 ring, 2 padding
+  int kind;           // 0 main, 1 ring, 2 padding, 3 the new token of a fused step
   int nvalid;         // main: valid slots; ring: ring page index
+  int rowmask;        // K row r of the page is row (r & rowmask): 15, or 0 for kind 3
+  uint32_t drop;      // ring: slots hidden although occupied (the leaving token, not retained)
+};
+
+// Fused step: the ring slot being turned over (page fs.rp, slot fs.rs; fs.rp = -1 when
+// there is no fused step) and whether the leaving token of the current pair is retained.
+struct FStep {
+  int rp, rs;
 };
 
 // Page v of region A of `pair` (walk position w, for the block-table chunk in bt).
 template <int D>
 __device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, int v, int w, int bt, int npm,
-                                                 int len, int nring) {
+                                                 int len, int nring, FStep fs, bool app) {
   PageRef r;
+  r.rowmask = 15;
+  r.drop = 0u;
   if (v < npm) {
     const int pg = __builtin_amdgcn_readlane(bt, w & 63);
     r.k = reinterpret_cast<const uint16_t*>(a.kv.k_pages) + (int64_t)pg * PAGE * D;
@@ -282,9 +310,26 @@ __device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, in
     r.v = reinterpret_cast<const uint16_t*>(a.ring.v) + off;
     r.kind = 1;
     r.nvalid = rp;
+    if (rp == fs.rp && !app) r.drop = 1u << fs.rs;
+  } else if (fs.rp >= 0 && v == npm + nring) {
+    // the new token: K row and V values of the pair in k_new / v_new (every K row of
+    // the page reads row 0; only token 0 is valid)
+    r.k = reinterpret_cast<const uint16_t*>(a.st.k_new) + (int64_t)pair * D;
+    r.v = reinterpret_cast<const uint16_t*>(a.st.v_new) + (int64_t)pair * D;
+    r.kind = 3;
+    r.nvalid = 1;
+    r.rowmask = 0;
   } else {
+    // padding: its (ignored) loads read page X, which is always a full page -- except
+    // with a fused step, where X may be the one-row new-token page; then they read the
+    // pair's first ring page instead
     r.k = nullptr;
     r.v = nullptr;
+    if (fs.rp >= 0) {
+      const int64_t off = (int64_t)pair * nring * PAGE * D;
+      r.k = reinterpret_cast<const uint16_t*>(a.ring.k) + off;
+      r.v = reinterpret_cast<const uint16_t*>(a.ring.v) + off;
+    }
     r.kind = 2;
     r.nvalid = 0;
   }
@@ -297,11 +342,11 @@ __device__ __forceinline__ PageRef region_a_page(const AttnArgs& a, int pair, in
 // holds the entry of walk position 64 c + lane.
 template <int D>
 __device__ __forceinline__ void step_pages(const AttnArgs& a, const SegDesc& d, int k, int bt, int npm, int len,
-                                           int nring, PageRef& X, PageRef& Y) {
+                                           int nring, FStep fs, bool app, PageRef& X, PageRef& Y) {
   const int vX = d.rev ? d.vhi - 2 - 2 * k : d.vlo + 2 * k;
   const int wX = d.rev ? 2 * k + 1 : 2 * k, wY = d.rev ? 2 * k : 2 * k + 1;
-  X = region_a_page<D>(a, d.s, vX, wX, bt, npm, len, nring);
-  Y = region_a_page<D>(a, d.s, vX + 1, wY, bt, npm, len, nring);
+  X = region_a_page<D>(a, d.s, vX, wX, bt, npm, len, nring, fs, app);
+  Y = region_a_page<D>(a, d.s, vX + 1, wY, bt, npm, len, nring, fs, app);
 }
 
 // Block-table entries of walk positions [64 c, 64 c + 64) of segment d (lane i: position
@@ -329,8 +374,9 @@ __device__ __forceinline__ uint32_t lane_valid_bits(const u32x4& rp0, const u32x
       b |= ((int)rp0[i] >= 0 ? 1u : 0u) << i;
       b |= ((int)rp1[i] >= 0 ? 1u : 0u) << (i + 4);
     }
-    return b;
+    return b & ~(P.drop >> (8 * (j & 1)));
   }
+  if (P.kind == 3) return (j & 1) == 0 ? 1u : 0u;
   return 0u;
 }
 
@@ -346,8 +392,8 @@ __device__ __forceinline__ void load_k(const AttnArgs& a, Bf16Frags<D>& f, int p
   const int tB = tA + 4;
   const PageRef& PA = (tA < 16) ? X : Y;  // tA < 16 <=> tB < 16
   const uint16_t* kbase = (PA.k != nullptr) ? PA.k : X.k;  // X is never a padding page
-  const uint16_t* rowA = kbase + (tA & 15) * D + (D / 4) * j;
-  const uint16_t* rowB = kbase + (tB & 15) * D + (D / 4) * j;
+  const uint16_t* rowA = kbase + (tA & PA.rowmask) * D + (D / 4) * j;
+  const uint16_t* rowB = kbase + (tB & PA.rowmask) * D + (D / 4) * j;
 #pragma unroll
   for (int kk = 0; kk < D / 32; ++kk) {
     f.kA[kk] = *reinterpret_cast<const u32x4*>(rowA + 8 * kk);
@@ -366,9 +412,13 @@ __device__ __forceinline__ void load_v(Bf16Frags<D>& f, const PageRef& X, const 
   const int m = lane & 15, j = lane >> 4;
   const PageRef& PV = (j < 2) ? X : Y;
   const uint16_t* vbase = (PV.v != nullptr) ? PV.v : X.v;
-  const uint16_t* vcol = vbase + m * PAGE + 8 * (j & 1);
+  // a new-token page holds V as one row [D]: the aligned 8 values containing dim 16 t + m
+  // are loaded, and pv_step takes element m % 8 (unconditional loads either way)
+  const bool v3 = PV.kind == 3;
+  const uint16_t* vcol = vbase + (v3 ? (m & 8) : m * PAGE + 8 * (j & 1));
+  const int vstride = v3 ? 16 : 16 * PAGE;
 #pragma unroll
-  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const u32x4*>(vcol + t * 16 * PAGE);
+  for (int t = 0; t < D / 16; ++t) f.v[t] = *reinterpret_cast<const u32x4*>(vcol + t * vstride);
 }
 
 template <int D>
@@ -460,9 +510,29 @@ __device__ __forceinline__ bool softmax_step(const AttnArgs& a, f32x4 sA, f32x4 
   return true;
 }
 
+// Element k of eight packed bf16 values, as element 0 of an otherwise zero fragment.
+__device__ __forceinline__ u32x4 bf16_elem_to_front(const u32x4& x, int k) {
+  const int wi = k >> 1;
+  const uint32_t w = wi == 0 ? x[0] : wi == 1 ? x[1] : wi == 2 ? x[2] : x[3];
+  return u32x4{(k & 1) ? (w >> 16) : (w & 0xffffu), 0u, 0u, 0u};
+}
+
+// any3: some lane's V page is a new-token page (x3 for that lane).
 template <int D>
 __device__ __forceinline__ void pv_step(const Bf16Frags<D>& f, SoftmaxState<D>& st, bf16x8 phi,
-                                        bf16x8 plo, uint32_t vbits, bool all_valid) {
+                                        bf16x8 plo, uint32_t vbits, bool all_valid, bool any3 = false,
+                                        bool x3 = false) {
+  if (any3) {
+    const int m7 = threadIdx.x & 7;
+#pragma unroll
+    for (int t = 0; t < D / 16; ++t) {
+      const u32x4 raw = x3 ? bf16_elem_to_front(f.v[t], m7) : f.v[t];
+      const bf16x8 vt = as_bf16x8(mask_tokens(raw, vbits));
+      st.o[t] = mfma16x16x32(vt, phi, st.o[t]);
+      st.o[t] = mfma16x16x32(vt, plo, st.o[t]);
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < D / 16; ++t) {
     const bf16x8 vt = as_bf16x8(all_valid ? f.v[t] : mask_tokens(f.v[t], vbits));
@@ -520,7 +590,8 @@ __device__ __forceinline__ void segment_done(const AttnArgs& a, const Plan& pl, 
 // next pair's queries are loaded together with its first K.
 // -------------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl, const int* Lens, int u) {
+__device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl, const int* Lens, int u,
+                                              FStep fs) {
   const int lane = threadIdx.x & 63, j = lane >> 4;
   const int nring = a.has_ring ? a.ring.window / PAGE : 0;
   UnitIter it;
@@ -534,7 +605,9 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl,
   nx2.ok = -1;
   int bt_cur0 = load_bt_chunk(a, cur, 0), bt_cur1 = 0;
   int bt_nxt = 0, bt_nx2 = 0;
-  int len = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+  int lw = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+  int len = lw & LEN_MASK;
+  bool app = lw < 0;
   int npm = cdiv(len, PAGE);
   int nst = (cur.vhi - cur.vlo) >> 1;
   bool chunk_load = nst > 32;  // chunk 1 of the current segment still to request
@@ -542,7 +615,7 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl,
   bf16x8 qf[D / 32], qn[D / 32];
   load_q<D>(a, cur.s, qf);
   PageRef x, y;
-  step_pages<D>(a, cur, 0, bt_cur0, npm, len, nring, x, y);
+  step_pages<D>(a, cur, 0, bt_cur0, npm, len, nring, fs, app, x, y);
   Bf16Frags<D> f;
   load_k<D>(a, f, cur.s, x, y, lane);
   load_v<D>(f, x, y, lane);
@@ -571,20 +644,23 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl,
           else bt_cur1 = load_bt_chunk(a, cur, cc + 1);
         }
       }
-      step_pages<D>(a, cur, k + 1, (cc & 1) ? bt_cur1 : bt_cur0, npm, len, nring, xn, yn);
+      step_pages<D>(a, cur, k + 1, (cc & 1) ? bt_cur1 : bt_cur0, npm, len, nring, fs, app, xn, yn);
     } else if (nxt.ok > 0) {
-      const int lenn = __builtin_amdgcn_readfirstlane(Lens[nxt.s]);
-      step_pages<D>(a, nxt, 0, bt_nxt, cdiv(lenn, PAGE), lenn, nring, xn, yn);
+      const int lwn = __builtin_amdgcn_readfirstlane(Lens[nxt.s]);
+      const int lenn = lwn & LEN_MASK;
+      step_pages<D>(a, nxt, 0, bt_nxt, cdiv(lenn, PAGE), lenn, nring, fs, lwn < 0, xn, yn);
       pair_n = nxt.s;
       load_q<D>(a, nxt.s, qn);
     }
     const uint32_t vb = lane_valid_bits(f.rp0, f.rp1, x, y, j);
     const bool allv = __ballot(vb != 0xffu) == 0;
+    const bool x3 = ((j < 2) ? x.kind : y.kind) == 3;
+    const bool any3 = __ballot(x3) != 0;
     f32x4 sA, sB;
     qk_step<D>(f, qf, sA, sB);
     load_k<D>(a, f, pair_n, xn, yn, lane);
     bf16x8 phi, plo;
-    if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv);
+    if (softmax_step<D>(a, sA, sB, st, vb, allv, phi, plo)) pv_step<D>(f, st, phi, plo, vb, allv, any3, x3);
     load_v<D>(f, xn, yn, lane);
     if (lastk) {
       segment_done<D>(a, pl, cur.s, slot_of(pl, cur), st);
@@ -610,7 +686,9 @@ __device__ __forceinline__ void stream_a_bf16(const AttnArgs& a, const Plan& pl,
       nxt = nx2;
       bt_cur0 = bt_nxt;
       bt_nxt = bt_nx2;
-      len = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+      lw = __builtin_amdgcn_readfirstlane(Lens[cur.s]);
+      len = lw & LEN_MASK;
+      app = lw < 0;
       npm = cdiv(len, PAGE);
       nst = (cur.vhi - cur.vlo) >> 1;
       chunk_load = nst > 32;
@@ -1047,11 +1125,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   int* P = lds;
   int* Lens = lds + nseg + 1;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (wid == 0) compute_plan(a, P, Lens, nseg);
+  // fused step: the position being appended and the ring slot it turns over
+  FStep fs{-1, 0};
+  int p = 0;
+  float tau = 0.f;
+  if (a.fstep) {
+    p = a.st.pos_dev[0];
+    tau = a.st.tau_dev[0];
+    const int slot = ((p % a.ring.window) + a.ring.window) % a.ring.window;
+    fs.rp = slot / PAGE;
+    fs.rs = slot % PAGE;
+  }
+  if (wid == 0) compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
   __syncthreads();
-  // the merge kernel reads the prefix from here
-  if (blockIdx.x == 0)
+  // the merge kernel reads the prefix (and the position) from here
+  if (blockIdx.x == 0) {
     for (int s = threadIdx.x; s <= nseg; s += blockDim.x) a.plan[s] = P[s];
+    if (threadIdx.x == 0) a.plan[nseg + 1] = p;
+  }
   // Work-groups are dispatched round-robin over the 8 XCDs; numbering the units so that
   // each XCD takes one contiguous eighth of a sequence evens out the XCDs' finish times
   // (measured: 1-3 us at the 361 MB and 543 MB caches).
@@ -1062,7 +1153,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   if constexpr (F32) {
     stream_segments<D, true, 8>(a, pl, false, gw, wlds);
   } else {
-    stream_a_bf16<D>(a, pl, Lens, gw);
+    stream_a_bf16<D>(a, pl, Lens, gw, fs);
     if constexpr (LP) {
       if (a.kv.lp_bits == 4) stream_segments<D, false, 4>(a, pl, true, gw, nullptr);
       else stream_segments<D, false, 8>(a, pl, true, gw, nullptr);
@@ -1085,6 +1176,16 @@ __global__ __launch_bounds__(256) void decode_attn_merge_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int np = a.kv.num_pairs, g = a.g;
+  if (a.fstep && w >= np * g && w < np * (g + 1)) {
+    // fused step: waves np g .. np (g + 1) - 1 apply the delayed step of one pair each,
+    // now that every read of the ring slots is done; their memory round trips overlap
+    // the merge waves'
+    const int pair = w - np * g;
+    const int p = a.plan[np + 1];
+    step_pair<uint16_t, D>(a.st, pair, p);
+    if (pair == 0 && lane == 0) a.st.pos_dev[0] = p + 1;
+    return;
+  }
   if (w >= np * g) return;
   const int pair = w / g, n = w % g;
   const Plan pl = make_plan(a.plan, np, a.nw, a.kv.num_pages8 > 0);
@@ -1201,11 +1302,12 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
   return attn_plan_bytes(num_pairs) + attn_max_slots(num_pairs) * attn_rec_floats(g, head_dim) * sizeof(float);
 }
 
-kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
-                                  const kvp_ring* ring, float sm_scale, float* out, void* ws,
-                                  size_t ws_bytes, hipStream_t stream) {
-  (void)ws_bytes;
+static kvp_status launch_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv, const kvp_ring* ring,
+                              float sm_scale, float* out, void* ws, hipStream_t stream,
+                              const StepArgs* fused) {
   AttnArgs a;
+  a.fstep = fused != nullptr;
+  if (fused) a.st = *fused;
   a.q = q;
   a.out = out;
   a.B = B;
@@ -1242,11 +1344,31 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, false, 1>), g1, b, lds, stream, a);
   }
   KVP_LAUNCH_CHECK();
-  const dim3 cgrid(cdiv(kv->num_pairs * a.g, 4));
+  const dim3 cgrid(cdiv(kv->num_pairs * (a.g + a.fstep), 4));
   if (a.D == 64) hipLaunchKernelGGL((decode_attn_merge_kernel<64>), cgrid, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL((decode_attn_merge_kernel<128>), cgrid, dim3(256), 0, stream, a);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
+}
+
+kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
+                                  const kvp_ring* ring, float sm_scale, float* out, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+  (void)ws_bytes;
+  return launch_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream, nullptr);
+}
+
+// The fused decode step: the delayed step's arguments (scores from s_in, or from the
+// scorer: x_new for a linear one, the split-K partial sums in part for an MLP) and the
+// attention, in the stream kernel plus the merge kernel.
+kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, const float* part,
+                                  const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                  const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
+                                  const float* tau, int* pos, const void* q, int B, int Hq,
+                                  float sm_scale, float* out, void* ws, hipStream_t stream) {
+  const StepArgs st = make_step_args(kv, ring, k_new, v_new, s_in, ld_s, 0.0f, tau, 0, pos, sc, x_new,
+                                     s_out, part);
+  return launch_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream, &st);
 }
 
 size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32, bool lp) {

@@ -30,6 +30,11 @@ kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hid
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
+kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, const float* part,
+                                  const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                  const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
+                                  const float* tau, int* pos, const void* q, int B, int Hq,
+                                  float sm_scale, float* out, void* ws, hipStream_t stream);
 kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, int B, int Hq, int Hkv,
                                    int T, int d, const uint32_t* keep_bits, const int* kept_idx,
                                    int window, float sm_scale, float* out, hipStream_t stream);
@@ -269,6 +274,64 @@ extern "C" kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, 
     return KVP_E_WORKSPACE;
   if (((uintptr_t)ws) & 255) return KVP_E_ARG;
   return kvp_launch_decode_attn(q, B, Hq, kv, ring, sm_scale, out, ws, ws_bytes, stream);
+}
+
+static size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+extern "C" size_t kvp_decode_step_workspace_size(const kvp_scorer* sc, int32_t B, int32_t Hq,
+                                                 int32_t num_pairs, int32_t head_dim) {
+  const size_t attn = kvp_decode_attn_workspace_size(B, Hq, num_pairs, head_dim);
+  if (attn == 0) return 0;
+  const bool mlp = sc && sc->kind == KVP_SCORER_MLP;
+  return align256(attn) + (mlp ? kvp_score_workspace_size(sc, B, 1) : 0);
+}
+
+extern "C" kvp_status kvp_decode_step(const kvp_scorer* sc, const void* hidden_new, int32_t hdtype,
+                                      const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                                      const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
+                                      const float* tau, int32_t* pos, const void* q, int32_t qdtype,
+                                      int32_t B, int32_t Hq, float sm_scale, float* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream) {
+  kvp_status st = check_decode_attn(q, qdtype, B, Hq, kv, ring, out);
+  if (st != KVP_OK) return st;
+  if (!ring) return KVP_E_ARG;
+  if (kv->dtype != KVP_BF16 || kv->num_pages8 > 0) return KVP_E_UNSUPPORTED;
+  if (!k_new || !v_new || !tau || !pos) return KVP_E_ARG;
+  // the new token's K row and V values are read in 16-byte pieces
+  if (((uintptr_t)k_new | (uintptr_t)v_new) & 15) return KVP_E_ARG;
+  const int Hkv = kv->num_pairs / B;
+  const float* part = nullptr;
+  if (!sc) {
+    if (!s_in || ld_s < 1) return KVP_E_ARG;
+  } else {
+    if (!hidden_new || !sc->w1) return KVP_E_ARG;
+    if (sc->n_kv_heads != Hkv) return KVP_E_ARG;
+    if (!is_kv_dtype(hdtype) || hdtype != sc->wdtype) return KVP_E_DTYPE;
+    if (sc->kind == KVP_SCORER_LINEAR) {
+      const int elt = hdtype == KVP_BF16 ? 2 : 4;
+      if (sc->hidden <= 0 || sc->hidden % (16 / elt) != 0) return KVP_E_UNSUPPORTED;
+      if (((uintptr_t)hidden_new | (uintptr_t)sc->w1) & 15) return KVP_E_ARG;
+    } else if (sc->kind == KVP_SCORER_MLP) {
+      if (!sc->w2) return KVP_E_ARG;
+      if (sc->hidden <= 0 || sc->inner <= 0 || !kvp_score_small_mlp_ok(sc, B)) return KVP_E_UNSUPPORTED;
+      if (((uintptr_t)sc->b1 | (uintptr_t)sc->w2) & 15) return KVP_E_ARG;
+    } else {
+      return KVP_E_ARG;
+    }
+  }
+  if (!ws || ws_bytes < kvp_decode_step_workspace_size(sc, B, Hq, kv->num_pairs, kv->head_dim))
+    return KVP_E_WORKSPACE;
+  if (((uintptr_t)ws) & 255) return KVP_E_ARG;
+  if (sc && sc->kind == KVP_SCORER_MLP) {
+    float* pws = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
+                                          align256(kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs,
+                                                                                  kv->head_dim)));
+    if ((st = kvp_launch_score_small_partials(sc, hidden_new, B, pws, stream)) != KVP_OK) return st;
+    part = pws;
+  }
+  return kvp_launch_decode_step(sc, sc ? hidden_new : nullptr, part, kv, ring, k_new, v_new,
+                                sc ? nullptr : s_in, ld_s, s_out, tau, pos, q, B, Hq, sm_scale, out, ws,
+                                stream);
 }
 
 // Decode-attention scratch for callers that cannot allocate: a fixed array in device

@@ -71,6 +71,11 @@ class PrunedKVCache:
         self._fused_score = (c.kind == L.KVP_SCORER_LINEAR and c.hidden % 8 == 0) or (
             c.wdtype == L.KVP_BF16 and B <= 64 and c.hidden % 256 == 0 and c.hidden <= 8192
             and c.inner % 256 == 0 and c.inner <= 1024)
+        # one fused call per decode step (kvp_decode_step) for a bf16 cache without a
+        # low-precision pool; otherwise step() makes the separate calls
+        self.fused_step = dtype == torch.bfloat16 and not demote
+        self.ws_step = (L.decode_step_workspace(scorer if self._fused_score else None, B, Hq,
+                                                self.kv, dev) if self.fused_step else None)
 
     # -- prefill -----------------------------------------------------------------
     def score(self, hidden: torch.Tensor, out: Optional[torch.Tensor] = None, stream=None):
@@ -160,10 +165,28 @@ class PrunedKVCache:
     def step(self, hidden_new: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
              q: torch.Tensor, p: Optional[int] = None, stream=None) -> torch.Tensor:
         """Append a position (see advance) and attend with q over the cache that now holds
-        it.  Every per-step value lives in device memory, so this sequence can be captured
-        in a HIP graph and replayed."""
-        self.advance(hidden_new, k_new, v_new, p, stream)
-        return self.attend(q, stream)
+        it: one kvp_decode_step call (plus kvp_score first when the scorer's shape is not
+        one the step scores itself) for a bf16 cache without a low-precision pool, else
+        advance() then attend().  Every per-step value lives in device memory, so this
+        sequence can be captured in a HIP graph and replayed."""
+        if not self.fused_step:
+            self.advance(hidden_new, k_new, v_new, p, stream)
+            return self.attend(q, stream)
+        if p is not None:
+            self.set_position(p, stream)
+        if not isinstance(self.tau, torch.Tensor):
+            with self._on(stream):
+                self.tau_dev.fill_(self.tau)
+        if self._fused_score:
+            L.kvp_decode_step(self.scorer, hidden_new, self.kv, self.ring, k_new, v_new,
+                              self.tau_dev, self.pos_dev, q, self.scale, self.out, self.ws_step,
+                              s_out=self.s_new, stream=stream)
+        else:
+            L.kvp_score(self.scorer, hidden_new, self.s_new, self.ws_score, stream)
+            L.kvp_decode_step(None, None, self.kv, self.ring, k_new, v_new, self.tau_dev,
+                              self.pos_dev, q, self.scale, self.out, self.ws_step, s_in=self.s_new,
+                              stream=stream)
+        return self.out
 
     def attend(self, q: torch.Tensor, stream=None) -> torch.Tensor:
         L.kvp_decode_attn(q, self.kv, self.ring, self.scale, self.out, self.ws_attn, stream)
