@@ -331,7 +331,42 @@ size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
                                       int32_t head_dim);
 
 /* ----------------------------------------------------------------------------
- * kvp_decode_attn_noalloc - kvp_decode_attn for callers that cannot allocate device
+ * kvp_decode_step - one whole decode step in one call: the delayed step (with the new
+ * tokens scored by the surrogate scorer, or scores given) followed by the decode
+ * attention over the cache it leaves.  Sources: DMS "Delayed Eviction" (the step);
+ * KVzap key points (surrogate scorer; attention over the kept entries only); DeInfer
+ * methodology (b) (a fixed-address decode step replayed from a graph).
+ * Equivalent to kvp_score_step_delayed (sc != NULL) or kvp_step_delayed_dev (sc == NULL,
+ * scores s_in[pair * ld_s]) followed by kvp_decode_attn with the same q: the cache, the
+ * device position, the stored scores and s_out are bit-identical to that sequence's; out
+ * agrees to fp32 rounding (the tokens are summed in another grouping).  The work runs in
+ * the attention's two kernels (plus the MLP scorer's split-K first layer before them):
+ * the streaming kernel reads the cache as the step will leave it (the token leaving its
+ * ring slot counts iff it is retained; the new token is read from k_new/v_new) without
+ * writing it, and the merge kernel applies the step.
+ *   sc, hidden_new, hdtype  as kvp_score_step_delayed (sc->n_kv_heads = num_pairs / B), or
+ *                sc == NULL: hidden_new unused, scores from s_in (ld_s >= 1)
+ *   k_new, v_new [B*Hkv][d] bf16, 16-byte aligned; s_out NULL or [B*Hkv] fp32 (scorer)
+ *   tau, pos     device values as in kvp_step_delayed_dev (tau[0]; pos[0] the position
+ *                appended, advanced by 1; pos[1] must be 0 and is left 0)
+ *   q, qdtype, B, Hq, sm_scale, out  as kvp_decode_attn
+ *   ws           >= kvp_decode_step_workspace_size(sc, B, Hq, num_pairs, head_dim) bytes,
+ *                256-byte aligned, scratch (any contents)
+ * Takes bf16 caches with a ring and no low-precision pool (else KVP_E_UNSUPPORTED: make
+ * the separate calls).  If the pool or a block table overflows (kv->err, kvp_check), this
+ * step's output may include the retained token the pool could not take.
+ * -------------------------------------------------------------------------- */
+kvp_status kvp_decode_step(const kvp_scorer* sc, const void* hidden_new, int32_t hdtype,
+                           const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
+                           const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
+                           const float* tau, int32_t* pos, const void* q, int32_t qdtype,
+                           int32_t B, int32_t Hq, float sm_scale, float* out, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+size_t kvp_decode_step_workspace_size(const kvp_scorer* sc, int32_t B, int32_t Hq,
+                                      int32_t num_pairs, int32_t head_dim);
+
+/* ----------------------------------------------------------------------------
+ * kvp_decode_attn_noalloc -kvp_decode_attn for callers that cannot allocate device
  * memory at all (code under HIP graph capture, tight serving loops, hosts that forbid
  * hipMalloc): no workspace argument; the library's own fixed device scratch of
  * KVP_NOALLOC_SCRATCH_BYTES, one copy per GPU, reserved when the library's code is
