@@ -260,6 +260,41 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_copy_kernel(CompactArgs a
 // row's chunks sit in consecutive lanes), each row's absmax is a shuffle reduction over
 // those lanes, K codes go straight to the token-major page, V codes through this wave's
 // LDS tile to the dim-major page.
+// Codes of N values of one row for the row scale s, bit for bit clamp(rint(fl(x / s)),
+// -qmax, qmax) with fl the correctly rounded fp32 quotient, at a fraction of N divisions'
+// cost.  inv is an approximate 1 / s (0 when s = 0, whose row is all zeros).  y = x * inv
+// is within 127 (2^-22 + 2^-24) < 2^-14.7 of x / s and fl(x / s) within 2^-18 of x / s,
+// so unless y lies within 2^-12 of a half-integer both round to the same integer; those
+// values (rare: a branch per value, taken when any lane needs it) are divided exactly.  The code is the
+// low byte of the bits of y + 1.5 2^23 (that addition rounds to the nearest integer,
+// ties to even, and keeps it in the low mantissa bits).  No clamp is needed: with
+// s = fl(max |x| / qmax), |x / s| <= qmax (1 + 2^-23) and |y| < qmax + 1/2.
+template <int N>
+__device__ __forceinline__ void quant_codes_fast(const float (&x)[N], float s, float inv,
+                                                 uint32_t (&bits)[N]) {
+  constexpr float M = 12582912.0f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) {
+    const float y = x[e] * inv;
+    float t = y + M;
+    if (fabsf(y - (t - M)) > 0.5f - 0x1p-12f) t = rintf(x[e] / s) + M;
+    bits[e] = __float_as_uint(t);
+  }
+}
+
+// max over each aligned group of G lanes (G = 8, 16 or 32), every lane of the group
+// receiving it: DPP quad swaps and row mirrors, and one cross-row exchange for G = 32.
+template <int G>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xf, 0xf, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+  if constexpr (G >= 16)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+  if constexpr (G >= 32) v = fmaxf(v, __shfl_xor(v, 16));
+  return v;
+}
+
 template <typename E, int D, int BITS>
 __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs a) {
   constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
@@ -327,19 +362,21 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs 
         ka = fmaxf(ka, fabsf(kf[e]));
         va = fmaxf(va, fabsf(vf[e]));
       }
-#pragma unroll
-      for (int o = 1; o < CPR; o <<= 1) {  // the row's CPR chunks are CPR aligned lanes
-        ka = fmaxf(ka, __shfl_xor(ka, o));
-        va = fmaxf(va, __shfl_xor(va, o));
-      }
+      // the row's CPR chunks are CPR aligned lanes
+      ka = group_max<CPR>(ka);
+      va = group_max<CPR>(va);
       const float kscale = ka / QMAX, vscale = va / QMAX;
+      const float kinv = kscale > 0.f ? __builtin_amdgcn_rcpf(kscale) : 0.f;
+      const float vinv = vscale > 0.f ? __builtin_amdgcn_rcpf(vscale) : 0.f;
+      uint32_t kb[EPC], vb[EPC];
+      quant_codes_fast<EPC>(kf, kscale, kinv, kb);
+      quant_codes_fast<EPC>(vf, vscale, vinv, vb);
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
-        const uint32_t kc = static_cast<uint32_t>(quant_code(kf[e], kscale, QMAX));
-        if constexpr (BITS == 8) w[e / 4] |= (kc & 0xffu) << (8 * (e % 4));
-        else w[e / 8] |= (kc & 0xfu) << (4 * (e % 8));
-        vc[row * D + col + e] = static_cast<int8_t>(quant_code(vf[e], vscale, QMAX));
+        if constexpr (BITS == 8) w[e / 4] |= (kb[e] & 0xffu) << (8 * (e % 4));
+        else w[e / 8] |= (kb[e] & 0xfu) << (4 * (e % 8));
+        vc[row * D + col + e] = static_cast<int8_t>(vb[e]);
       }
       int8_t* kd = kdst + (row * D + col) * BITS / 8;
       if constexpr (CB == 8) __builtin_nontemporal_store(u32x2{w[0], w[1]}, reinterpret_cast<u32x2*>(kd));

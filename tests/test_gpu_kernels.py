@@ -205,8 +205,23 @@ def test_compact_demote_exact(K, bits, d, dtype):
     k = seeded((B, Hkv, T, d), 41, dtype)
     v = seeded((B, Hkv, T, d), 42, dtype, 3.0)
     k[0, 0, 7] = 0  # all-zero row -> scale 0, codes 0
+    qmax = oracle.LP_QMAX[bits]
+    # rows whose quotients x / scale sit on or next to half-integers, where the rounding
+    # decision is taken by an exact division: ties (scale exactly 1: row max = qmax, the
+    # rest k + 1/2) and, with an inexact scale, x = fp(scale (k + 1/2)) and its neighbours
+    ties = np.concatenate([[qmax], (np.arange(d - 1) % (2 * qmax)) - qmax + 0.5]).astype(np.float32)
+    sc = np.float32(np.float32(100.0) / np.float32(qmax))
+    near = np.float32(sc) * ((np.arange(d - 1) % (2 * qmax)) - qmax + 0.5).astype(np.float32)
+    near = near.astype(np.float32)
+    near[1::3] = np.nextafter(near[1::3], np.float32(np.inf))
+    near[2::3] = np.nextafter(near[2::3], np.float32(-np.inf))
+    near = np.concatenate([[np.float32(100.0)], near]).astype(np.float32)
+    for t, row in ((3, ties), (11, near)):
+        k[0, 0, t] = torch.from_numpy(row).to(dtype)
+        v[0, 0, t] = torch.from_numpy(-row).to(dtype)
     s = seeded((B, Hkv, T), 43)
     keep = oracle.keep_mask(f64(s), 0.8, 128).reshape(P, T)
+    keep[0, [3, 7, 11]] = False  # the crafted rows are demoted
     idx, cnt = upload_selection(keep)
     kv = K.PagedKV.allocate(P, d, P * 40, 40, dtype, DEV, num_pages8=P * 40,
                             max_pages8_per_pair=40, poison=True, lp_bits=bits)
@@ -216,7 +231,6 @@ def test_compact_demote_exact(K, bits, d, dtype):
     assert K.kvp_check(kv) == 0
     kf = f64(k).reshape(P, T, d)
     vf = f64(v).reshape(P, T, d)
-    qmax = oracle.LP_QMAX[bits]
     for p in range(P):
         ev = np.flatnonzero(~keep[p])
         pos, Kc, Vc, ks, vs = read_pool8(kv, p)

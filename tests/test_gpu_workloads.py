@@ -156,11 +156,14 @@ def test_long_70b_layer_reduced(K, q_keep):
 
 
 @pytest.mark.slow
-def test_long_70b_layer_full_size_sampled(K):
-    """B=4, H=8192, 64/8 heads, T=131072, outliers x8, keep 0.5: batch row 2 in full."""
+@pytest.mark.parametrize("q_keep,row", [(0.5, 2), (0.75, 1)])
+def test_long_70b_layer_full_size_sampled(K, q_keep, row):
+    """B=4, H=8192, 64/8 heads, T=131072, outliers x8, keep 0.5 and 0.25: one batch row
+    (8 pairs, 64 query heads) in full, tau from that row's oracle scores."""
     wl = W.LONG_70B_LAYER
-    r = run_kvzap(K, wl, wl.T, [2], q_keep=0.5)
-    assert 0.47 < r["kept"] < 0.53
+    print(f"long_70b_layer full size q_keep={q_keep} row={row}", flush=True)
+    r = run_kvzap(K, wl, wl.T, [row], q_keep=q_keep)
+    assert abs(r["kept"] - (1 - q_keep)) < 0.03
     print(r)
 
 
