@@ -323,30 +323,100 @@ def dequantize_int8(codes: np.ndarray, scale: np.float32) -> np.ndarray:
     return codes.astype(np.float64) * np.float64(scale)
 
 
-def beacon_kv(K: np.ndarray, V: np.ndarray, beacon: np.ndarray, bits: int = 8):
+# A third reading of "low precision": 8-bit floating-point codes in the OCP FP8 E4M3
+# format (1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; the
+# all-ones exponent and mantissa pattern is NaN, so the largest finite magnitude is
+# 1.75 * 2^8 = 448; exponent field 0 holds the subnormals m * 2^-9).  One fp32 absmax
+# scale per row maps the row's largest magnitude onto 448.  The encoder rounds to the
+# nearest code, ties to the even mantissa; a magnitude at or above 448 saturates to 448
+# (reading: the scaling keeps every value at most 448 (1 + 2^-23), which rounds to 448
+# anyway, so saturation only guards the definition).
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Values (float64) of E4M3 byte codes; NaN for the two NaN codes."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int64))
+    sub = m * 2.0 ** -9
+    val = sign * np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, val)
+
+
+def fp8_e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """E4M3 byte codes of float32 values: round to nearest, ties to even; magnitudes at
+    or above 448 saturate to 448.  (Not defined for NaN inputs.)"""
+    xf = np.asarray(x, dtype=np.float32)
+    a = np.abs(xf).astype(np.float64)  # exact
+    sign = np.where(np.signbit(xf), 0x80, 0).astype(np.int64)
+    out = np.zeros(xf.shape, dtype=np.int64)
+    # subnormal range (below the smallest normal 2^-6): the code is the nearest
+    # multiple m of 2^-9 (m = 8 is the smallest normal, code 0x08, by the same bits)
+    sub = a < 2.0 ** -6
+    out[sub] = np.rint(a[sub] * 2.0 ** 9).astype(np.int64)
+    # normal range: a = 2^k (1 + f), the mantissa f rounded to 3 bits; a carry out of
+    # the mantissa moves to the next exponent through the integer addition
+    nrm = ~sub
+    mant, ex = np.frexp(a[nrm])  # a = mant 2^ex, mant in [0.5, 1)
+    k = ex - 1
+    frac8 = np.rint((mant * 2.0 - 1.0) * 8.0).astype(np.int64)  # 0..8
+    out[nrm] = ((k + 7) << 3) + frac8
+    out = np.minimum(out, 0x7E)  # saturate at 448 (0x7F would be NaN)
+    out = np.where(a >= FP8_E4M3_MAX, 0x7E, out)
+    return (sign | out).astype(np.uint8)
+
+
+def quantize_absmax_fp8(x: np.ndarray) -> Tuple[np.ndarray, np.float32]:
+    """E4M3 codes with one fp32 absmax scale per row: scale = fp32(a / 448) with
+    a = max |x|, code = E4M3 rounding of the fp32 quotient x / scale (correctly rounded,
+    as for the integer codes).  A zero row has scale 0 and zero codes."""
+    xf = np.asarray(x, dtype=np.float32)
+    a = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0)
+    scale = np.float32(a / np.float32(FP8_E4M3_MAX))
+    if scale == 0:
+        return np.zeros(xf.shape, dtype=np.uint8), np.float32(0.0)
+    return fp8_e4m3_encode(xf / scale), scale
+
+
+def dequantize_fp8(codes: np.ndarray, scale: np.float32) -> np.ndarray:
+    """x_hat = value(code) * scale (exact in float64)."""
+    return fp8_e4m3_decode(codes) * np.float64(scale)
+
+
+def lp_round_trip(x: np.ndarray, bits):
+    """(codes, scale, x_hat) of one row in the low-precision format `bits`: 8 or 4
+    (integer codes) or "fp8" (E4M3 codes)."""
+    if bits == "fp8":
+        c, s = quantize_absmax_fp8(x)
+        return c, s, dequantize_fp8(c, s)
+    c, s = quantize_absmax(x, LP_QMAX[bits])
+    return c, s, dequantize_int8(c, s)
+
+
+def beacon_kv(K: np.ndarray, V: np.ndarray, beacon: np.ndarray, bits=8):
     """Beacon entries keep their exact values; every other (token, head) row of K and
-    of V (separately) is replaced by its round trip through `bits`-bit codes (8 or 4).
+    of V (separately) is replaced by its round trip through the low-precision format
+    `bits`: 8 or 4 (integer codes) or "fp8" (E4M3 codes).
 
     K, V: [B,Hkv,T,d] float64 holding bf16 values; beacon: [B,Hkv,T] bool.
     Returns K_hat, V_hat float64, plus the codes and scales of the demoted rows.
     """
-    qmax = LP_QMAX[bits]
     Kh = np.array(K, dtype=np.float64, copy=True)
     Vh = np.array(V, dtype=np.float64, copy=True)
     B, Hkv, T, d = K.shape
-    kc = np.zeros((B, Hkv, T, d), dtype=np.int8)
-    vc = np.zeros((B, Hkv, T, d), dtype=np.int8)
+    cdt = np.uint8 if bits == "fp8" else np.int8
+    kc = np.zeros((B, Hkv, T, d), dtype=cdt)
+    vc = np.zeros((B, Hkv, T, d), dtype=cdt)
     ks = np.zeros((B, Hkv, T), dtype=np.float32)
     vs = np.zeros((B, Hkv, T), dtype=np.float32)
     for b in range(B):
         for h in range(Hkv):
             for t in np.flatnonzero(~beacon[b, h]):
-                c, s = quantize_absmax(K[b, h, t], qmax)
-                kc[b, h, t], ks[b, h, t] = c, s
-                Kh[b, h, t] = dequantize_int8(c, s)
-                c, s = quantize_absmax(V[b, h, t], qmax)
-                vc[b, h, t], vs[b, h, t] = c, s
-                Vh[b, h, t] = dequantize_int8(c, s)
+                kc[b, h, t], ks[b, h, t], Kh[b, h, t] = lp_round_trip(K[b, h, t], bits)
+                vc[b, h, t], vs[b, h, t], Vh[b, h, t] = lp_round_trip(V[b, h, t], bits)
     return Kh, Vh, (kc, ks, vc, vs)
 
 
@@ -379,9 +449,9 @@ def kvzap_visible_at_decode(s: np.ndarray, tau: float, R: int, p: int) -> np.nda
     return keep_mask(s[..., :p + 1], tau, R)
 
 
-def beacon_decode_attention(q, K, V, beacon, scale, bits: int = 8):
+def beacon_decode_attention(q, K, V, beacon, scale, bits=8):
     """One softmax over all T tokens: exact values for beacon rows, round trips through
-    `bits`-bit codes for the others."""
+    the low-precision format `bits` (8, 4 or "fp8") for the others."""
     Kh, Vh, _ = beacon_kv(K, V, beacon, bits)
     allvis = np.ones(beacon.shape, dtype=bool)
     return decode_attention(q, Kh, Vh, allvis, scale)

@@ -182,6 +182,36 @@ def m_beacon_mask_inverted(K, V, beacon, bits=8):
     return orig["beacon_kv"](K, V, ~np.asarray(beacon, dtype=bool), bits)
 
 
+def m_fp8_truncate(x):
+    xf = np.asarray(x, dtype=np.float32)
+    a = np.abs(xf).astype(np.float64)
+    sign = np.where(np.signbit(xf), 0x80, 0).astype(np.int64)
+    out = np.zeros(xf.shape, dtype=np.int64)
+    sub = a < 2.0 ** -6
+    out[sub] = np.floor(a[sub] * 2.0 ** 9).astype(np.int64)
+    mant, ex = np.frexp(a[~sub])
+    out[~sub] = ((ex - 1 + 7) << 3) + np.floor((mant * 2.0 - 1.0) * 8.0).astype(np.int64)
+    out = np.where(a >= 448.0, 0x7E, np.minimum(out, 0x7E))
+    return (sign | out).astype(np.uint8)
+
+
+def m_fp8_subnormal_as_normal(codes):
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e, m = (c >> 3) & 0xF, (c & 0x7).astype(np.float64)
+    val = sign * np.ldexp(1.0 + m / 8.0, (np.maximum(e, 1) - 7).astype(np.int64))
+    return np.where((c & 0x7F) == 0x7F, np.nan, np.where((c & 0x7F) == 0, 0.0, val))
+
+
+def m_fp8_scale_127(x):
+    xf = np.asarray(x, dtype=np.float32)
+    a = np.float32(np.max(np.abs(xf))) if xf.size else np.float32(0)
+    scale = np.float32(a / np.float32(127.0))
+    if scale == 0:
+        return np.zeros(xf.shape, dtype=np.uint8), np.float32(0.0)
+    return ko.fp8_e4m3_encode(xf / scale), scale
+
+
 # (oracle function, mutant, pins that must catch it: (test function, kwargs))
 P = pins
 MUTANTS = [
@@ -229,6 +259,14 @@ MUTANTS = [
     ("beacon_kv", m_beacon_mask_inverted,
      [(P.test_beacon_round_trip_of_k_and_v_halves, {"bits": 8}),
       (P.test_beacon_all_beacons_is_dense_and_demotion_changes_output, {})]),
+    ("beacon_kv", m_beacon_v_left_exact, [(P.test_beacon_fp8_round_trip_of_k_and_v_halves, {})]),
+    ("fp8_e4m3_encode", m_fp8_truncate,
+     [(P.test_fp8_encode_rounds_to_nearest_even, {}), (P.test_fp8_encode_round_trips_every_code, {})]),
+    ("fp8_e4m3_decode", m_fp8_subnormal_as_normal,
+     [(P.test_fp8_decode_every_code_matches_library, {}), (P.test_fp8_encode_round_trips_every_code, {})]),
+    ("quantize_absmax_fp8", m_fp8_scale_127,
+     [(P.test_fp8_absmax_quantization_bound_and_extremes, {}),
+      (P.test_beacon_fp8_round_trip_of_k_and_v_halves, {})]),
 ]
 
 

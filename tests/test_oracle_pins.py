@@ -622,3 +622,132 @@ def test_beacon_round_trip_of_k_and_v_halves(bits):
     mixed = oracle.beacon_decode_attention(q, K, V, beacon, sc, bits=bits)
     assert np.allclose(mixed, oracle.decode_attention(q, Kh, Vh, allv, sc), rtol=0, atol=1e-15)
     assert np.abs(mixed - oracle.decode_attention(q, K, V, allv, sc)).max() > 1e-6
+
+
+# ---------------------------------------------------------------- fp8 E4M3 pool
+# BeaconKV briefing, body: non-beacon entries are kept at low precision.  Reading (one
+# of three formats): OCP FP8 E4M3 codes with one fp32 absmax scale per row.
+
+
+def _torch_fp8_codes(x):
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _nearest_fp8_brute(y: float) -> int:
+    """Brute force over every finite code: the nearest value, ties to the even code."""
+    vals = oracle.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+    a = abs(y)
+    if a >= 448.0:
+        k = 0x7E
+    else:
+        dist = np.abs(vals - a)
+        best = np.flatnonzero(dist == dist.min())
+        k = int(best[0]) if len(best) == 1 else int(best[best % 2 == 0][0])
+    return k | (0x80 if np.signbit(np.float32(y)) else 0)
+
+
+def test_fp8_decode_every_code_matches_library():
+    """The 256 E4M3 codes decode to the values of torch.float8_e4m3fn (an independent
+    implementation of the OCP format): 0x7F and 0xFF are NaN, 0x7E is 448, 0x08 the
+    smallest normal 2^-6, 0x01 the smallest subnormal 2^-9; positive codes ascend."""
+    import torch
+    c = np.arange(256, dtype=np.uint8)
+    d = oracle.fp8_e4m3_decode(c)
+    t = torch.from_numpy(c).view(torch.float8_e4m3fn).float().double().numpy()
+    assert np.array_equal(np.isnan(d), np.isnan(t))
+    assert np.array_equal(d[~np.isnan(d)], t[~np.isnan(t)])
+    assert np.flatnonzero(np.isnan(d)).tolist() == [0x7F, 0xFF]
+    assert d[0x7E] == 448.0 and d[0x08] == 2.0 ** -6 and d[0x01] == 2.0 ** -9
+    assert d[0x80] == 0.0 and np.signbit(d[0x80]) and d[0xFE] == -448.0
+    assert np.all(np.diff(d[:0x7F]) > 0)
+
+
+def test_fp8_encode_round_trips_every_code():
+    c = np.arange(256, dtype=np.uint8)
+    d = oracle.fp8_e4m3_decode(c)
+    ok = ~np.isnan(d)
+    assert np.array_equal(oracle.fp8_e4m3_encode(d[ok].astype(np.float32)), c[ok])
+
+
+def test_fp8_encode_rounds_to_nearest_even():
+    """Midpoints between neighbouring codes go to the even code; one fp32 ulp either side
+    of a midpoint goes to the nearer code; over random values in the finite range (and
+    in the subnormal range) the codes equal torch's float32 -> float8_e4m3fn cast and a
+    brute-force nearest-code search."""
+    c = np.arange(0x7F, dtype=np.uint8)
+    v = oracle.fp8_e4m3_decode(c)
+    mid = ((v[:-1] + v[1:]) / 2).astype(np.float32)  # exact in fp32
+    assert np.array_equal(oracle.fp8_e4m3_encode(mid), np.where(c[:-1] % 2 == 0, c[:-1], c[1:]))
+    up = np.nextafter(mid, np.float32(np.inf))
+    dn = np.nextafter(mid, np.float32(0))
+    assert np.array_equal(oracle.fp8_e4m3_encode(up), c[1:])
+    assert np.array_equal(oracle.fp8_e4m3_encode(dn), c[:-1])
+    rng = np.random.default_rng(7)
+    xs = np.concatenate([mid, up, dn, rng.uniform(-447.9, 447.9, 20000).astype(np.float32),
+                         rng.uniform(-2.0 ** -6, 2.0 ** -6, 5000).astype(np.float32)])
+    xs = np.concatenate([xs, -xs]).astype(np.float32)
+    assert np.array_equal(oracle.fp8_e4m3_encode(xs), _torch_fp8_codes(xs))
+    for y in xs[::997]:
+        assert int(oracle.fp8_e4m3_encode(np.array([y]))[0]) == _nearest_fp8_brute(float(y))
+
+
+def test_fp8_saturation_reading():
+    """Reading: magnitudes at or above 448 saturate to +-448 (the library cast turns
+    those past the last midpoint into NaN); the absmax scaling never produces them."""
+    x = np.array([448.0, np.nextafter(np.float32(448.0), np.float32(1e9)), 463.9, 464.0, 500.0,
+                  1e30, -500.0, -1e30], dtype=np.float32)
+    assert oracle.fp8_e4m3_encode(x).tolist() == [0x7E] * 6 + [0xFE] * 2
+
+
+def test_fp8_absmax_quantization_bound_and_extremes():
+    """scale = fp32(max |x| / 448); the largest element maps to +-448; every element is
+    within half a code step of its value (2^-4 relative above 2^-6 scale, 2^-10 scale
+    below); a zero row has scale 0 and zero codes."""
+    rng = np.random.default_rng(17)
+    for mag in (1e-3, 0.7, 3.0, 250.0, 3e4):
+        x = (rng.standard_normal(128) * mag).astype(np.float32)
+        x[5] = np.float32(0.0)
+        c, s = oracle.quantize_absmax_fp8(x)
+        a = np.float32(np.abs(x).max())
+        assert s == np.float32(a / np.float32(448.0))
+        assert int(c[np.argmax(np.abs(x))]) & 0x7F == 0x7E
+        assert int(c[5]) & 0x7F == 0
+        xh = oracle.dequantize_fp8(c, s)
+        xd = x.astype(np.float64)
+        tol = np.maximum(2.0 ** -4 * np.abs(xd), 2.0 ** -10 * float(s)) * (1 + 1e-6)
+        assert np.all(np.abs(xh - xd) <= tol)
+        assert np.array_equal(c, oracle.fp8_e4m3_encode(x / s))
+    c, s = oracle.quantize_absmax_fp8(np.zeros(16, np.float32))
+    assert s == 0 and not c.any()
+
+
+def test_beacon_fp8_round_trip_of_k_and_v_halves():
+    """BeaconKV with fp8 codes: beacon rows exact; a demoted K or V row is exactly the
+    values of its own codes times its own scale, the codes are the brute-force nearest
+    codes of x / scale, and the mixed-mask attention differs from the dense one."""
+    rng = np.random.default_rng(44)
+    B, Hkv, T, d = 2, 2, 40, 16
+    K = (rng.standard_normal((B, Hkv, T, d)) * 2).astype(np.float32).astype(np.float64)
+    V = (rng.standard_normal((B, Hkv, T, d)) * 0.5).astype(np.float32).astype(np.float64)
+    beacon = rng.random((B, Hkv, T)) < 0.3
+    Kh, Vh, (kc, ks, vc, vs) = oracle.beacon_kv(K, V, beacon, bits="fp8")
+    assert np.array_equal(Kh[beacon], K[beacon]) and np.array_equal(Vh[beacon], V[beacon])
+    dem = ~beacon
+    for X, Xh, c, s in ((K, Kh, kc, ks), (V, Vh, vc, vs)):
+        vals = oracle.fp8_e4m3_decode(c[dem])
+        assert np.array_equal(Xh[dem], vals * s[dem][:, None].astype(np.float64))
+        a = np.abs(X[dem]).max(axis=1).astype(np.float32)
+        assert np.array_equal(s[dem], (a / np.float32(448.0)).astype(np.float32))
+        Xr, cr, sr = X.reshape(-1, d), c.reshape(-1, d), s.ravel()
+        for r in np.flatnonzero(dem.ravel())[:5]:
+            y = Xr[r].astype(np.float32) / sr[r]
+            assert [int(v) for v in cr[r]] == [_nearest_fp8_brute(float(v)) for v in y]
+        assert np.abs(Xh[dem] - X[dem]).max() > 0
+    q = rng.standard_normal((B, 4, d))
+    sc = oracle.sm_scale(d)
+    allv = np.ones((B, Hkv, T), bool)
+    mixed = oracle.beacon_decode_attention(q, K, V, beacon, sc, bits="fp8")
+    assert np.allclose(mixed, oracle.decode_attention(q, Kh, Vh, allv, sc), rtol=0, atol=1e-15)
+    assert np.abs(mixed - oracle.decode_attention(q, K, V, allv, sc)).max() > 1e-6
