@@ -28,6 +28,7 @@ Records of the same run, each on its own seeded synthetic inputs:
     dms_delayed     8192-token prompt + 1024 delayed-eviction decode steps, eager and graph
     long_70b_layer  decode steps at keep 0.5 / 0.25 (and 1.0) on the 70B-like layer
     beacon_mixed    decode steps over the bf16 + int8 pools, and the demoting compaction
+    beacon_fp8      the same with the demoted tokens as fp8 E4M3 codes
     copy_ceiling    a plain 1 GiB device copy and a 1 GiB read (torch kernels)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME[,NAME...]] [--no-cpu]
@@ -47,7 +48,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "kept-KV decode attention tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
 RECORDS = ("headline", "prefill", "keep_scaling", "dms_delayed", "long_70b_layer",
-           "beacon_mixed", "copy_ceiling")
+           "beacon_mixed", "beacon_fp8", "copy_ceiling")
 
 
 def log(msg):
@@ -82,6 +83,11 @@ def new_event():
 
 def gbs(nbytes, ms):
     return nbytes / (ms * 1e-3) / 1e9
+
+
+def code_bytes(lp_bits) -> float:
+    """Bytes per low-precision code: int4 two per byte, int8 and fp8 one."""
+    return 0.5 if lp_bits == 4 else 1.0
 
 
 # ------------------------------------------------------------------------------ inputs
@@ -154,7 +160,7 @@ class Context:
         entry per 16 tokens, the queries read and the fp32 outputs written."""
         wl = self.wl
         elt = 2 if dtype_name(wl.kv_dtype) == "bf16" else 4
-        return (main * 2 * wl.d * elt + lp * 2 * (wl.d * wl.lp_bits // 8 + 4)
+        return (main * 2 * wl.d * elt + lp * 2 * (wl.d * code_bytes(wl.lp_bits) + 4)
                 + (main + lp) / 16 * 4 + wl.B * wl.Hq * wl.d * (elt + 4))
 
 
@@ -324,7 +330,7 @@ def record_prefill(ctx, stream, reps=5):
     compact_bytes = kept * 2 * d * elt * 2 + kept * 4
     if wl.int8_demote:  # demoted tokens: read in full, written as codes + one scale per row
         demoted = B * Hkv * T0 - kept
-        compact_bytes += demoted * (2 * d * elt + 2 * (d * wl.lp_bits // 8 + 4) + 4)
+        compact_bytes += demoted * (2 * d * elt + 2 * (d * code_bytes(wl.lp_bits) + 4) + 4)
     tflops = flops / (ms["score"] * 1e-3) / 1e12
     out = {
         "workload": wl.name, "kept_token_heads": kept,
@@ -426,13 +432,13 @@ def record_long(dev, stream, steps, warmup):
     return out
 
 
-def record_beacon(dev, stream, steps, warmup):
-    """Beacon-style mixed precision: decode steps over the bf16 and int8 pools, and the
-    demoting compaction."""
+def record_beacon(dev, stream, steps, warmup, name="beacon_mixed"):
+    """Beacon-style mixed precision: decode steps over the bf16 and low-precision pools
+    (int8 codes; fp8 E4M3 codes for beacon_fp8), and the demoting compaction."""
     import torch
 
     import kvp_workloads as W
-    wl = W.BY_NAME["beacon_mixed"]
+    wl = W.BY_NAME[name]
     ctx = Context(wl, dev, extra=warmup + steps + 16)
     r = decode_run(ctx, wl.keep_quantiles[0], steps, warmup, stream)
     r["attn_flushed_ms"] = flushed_attn_ms(ctx, stream)
@@ -777,8 +783,10 @@ def main():
     if "long_70b_layer" in only:
         records["long_70b_layer"] = record_long(dev, stream, args.steps, args.warmup)
         torch.cuda.empty_cache()
-    if "beacon_mixed" in only:
-        records["beacon_mixed"] = record_beacon(dev, stream, args.steps, args.warmup)
+    for name in ("beacon_mixed", "beacon_fp8"):
+        if name in only:
+            records[name] = record_beacon(dev, stream, args.steps, args.warmup, name)
+            torch.cuda.empty_cache()
     if "copy_ceiling" in only:
         records["copy_ceiling"] = record_copy_ceiling(dev, stream)
         log(f"[bench] copy ceiling: copy {records['copy_ceiling']['copy_gbs']:.0f} GB/s, read "

@@ -63,6 +63,12 @@ typedef enum kvp_dtype { KVP_F32 = 0, KVP_BF16 = 1 } kvp_dtype;
 #define KVP_ERR_TABLE_FULL 0x2  /* a pair needs more pages than max_pages_per_pair */
 #define KVP_ERR_POOL8_FULL 0x4  /* int8 pool or its block table exhausted */
 
+/* kvp_paged_kv.lp_bits: code format of the low-precision pool. */
+#define KVP_LP_INT8 8          /* int8 codes (0 means the same) */
+#define KVP_LP_INT4 4          /* int4 codes, two per byte */
+#define KVP_LP_FP8_E4M3 0x108  /* OCP FP8 E4M3 codes, one per byte (8-bit code width in the
+                                  low byte, bit 8 marks floating-point codes) */
+
 /* ----------------------------------------------------------------------------
  * Surrogate scorer weights (KVzap, key points: surrogate model / structure).
  * nn.Linear layout [out][in].
@@ -100,13 +106,14 @@ typedef struct kvp_scorer {
  * block_table[pair][j] is the physical page of the pair's j-th page; the pair holds
  * length[pair] tokens in its pages, in ascending position order.  page_top[0] is a
  * bump allocator over the pool.  The optional low-precision pool (BeaconKV
- * demotion; all fields NULL/0 when absent) has the same layout with symmetric
- * integer codes plus one fp32 absmax scale per slot for K and for V: lp_bits = 8
- * holds int8 codes (-127..127, scale = absmax/127), lp_bits = 4 int4 codes (-7..7,
- * scale = absmax/7) two per byte, the even element in the low nibble (K rows: dims
- * 2i, 2i+1; V^T rows: tokens 2i, 2i+1), so its pages are half the size.  Source:
- * BeaconKV briefing (jiinsi.com), body and FAQ: non-beacon entries are kept at low
- * precision; the format is not given there.
+ * demotion; all fields NULL/0 when absent) has the same layout with codes plus one
+ * fp32 absmax scale per slot for K and for V: lp_bits = KVP_LP_INT8 holds int8 codes
+ * (-127..127, scale = absmax/127), KVP_LP_INT4 int4 codes (-7..7, scale = absmax/7)
+ * two per byte, the even element in the low nibble (K rows: dims 2i, 2i+1; V^T rows:
+ * tokens 2i, 2i+1), so its pages are half the size, and KVP_LP_FP8_E4M3 OCP FP8 E4M3
+ * codes one per byte (scale = absmax/448; code = E4M3 rounding, to nearest even, of
+ * the fp32 quotient value/scale).  Source: BeaconKV briefing (jiinsi.com), body and
+ * FAQ: non-beacon entries are kept at low precision; the format is not given there.
  * Physical page ids and the unused slots of partly filled pages are unspecified.
  * -------------------------------------------------------------------------- */
 typedef struct kvp_paged_kv {
@@ -117,7 +124,8 @@ typedef struct kvp_paged_kv {
   int32_t max_pages_per_pair; /* row stride of block_table */
   int32_t num_pages8;         /* low-precision pool capacity (0 = no such pool) */
   int32_t max_pages8_per_pair;
-  int32_t lp_bits;            /* code width of that pool: 8 (0 also means 8) or 4 */
+  int32_t lp_bits;            /* code format of that pool: KVP_LP_INT8 (or 0), KVP_LP_INT4,
+                                 KVP_LP_FP8_E4M3 */
   void* k_pages;
   void* v_pages;
   int32_t* page_pos;
@@ -125,8 +133,8 @@ typedef struct kvp_paged_kv {
   int32_t* length;      /* [num_pairs] */
   int32_t* page_top;    /* [1] */
   int32_t* err;         /* [1] KVP_ERR_* bits */
-  int8_t* k8_pages;     /* [num_pages8][16][d * lp_bits / 8] */
-  int8_t* v8_pages;     /* [num_pages8][d][16 * lp_bits / 8] */
+  int8_t* k8_pages;     /* [num_pages8][16][d] code bytes ([16][d/2] for int4) */
+  int8_t* v8_pages;     /* [num_pages8][d][16] code bytes ([d][8] for int4) */
   float* k8_scale;      /* [num_pages8][16] */
   float* v8_scale;      /* [num_pages8][16] */
   int32_t* page8_pos;   /* [num_pages8][16] */

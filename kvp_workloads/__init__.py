@@ -53,7 +53,7 @@ class Workload:
     prompt: int = 0  # DMS: prompt length
     steps: int = 0  # DMS: number of decode steps
     int8_demote: bool = False  # evicted tokens go to the low-precision pool
-    lp_bits: int = 8  # code width of that pool (8 or 4)
+    lp_bits: object = 8  # code format of that pool: 8, 4 (integer codes) or "fp8" (E4M3)
     index: int = 0
 
     @property
@@ -97,8 +97,10 @@ BEACON_MIXED = Workload("beacon_mixed", B=16, H=4096, Hq=32, Hkv=8, d=128, T=327
 
 # The same inputs as beacon_mixed (same seeds) with an int4 pool for the demoted tokens.
 BEACON_INT4 = dataclasses.replace(BEACON_MIXED, name="beacon_int4", lp_bits=4)
+# ... and with an fp8 E4M3 pool.
+BEACON_FP8 = dataclasses.replace(BEACON_MIXED, name="beacon_fp8", lp_bits="fp8")
 
-ALL = (TINY, QWEN3_8B_LAYER, DMS_DELAYED, LONG_70B_LAYER, BEACON_MIXED, BEACON_INT4)
+ALL = (TINY, QWEN3_8B_LAYER, DMS_DELAYED, LONG_70B_LAYER, BEACON_MIXED, BEACON_INT4, BEACON_FP8)
 BY_NAME = {w.name: w for w in ALL}
 
 

@@ -7,6 +7,7 @@ include/kvp.h); this package is its thin ctypes binding plus the in-tree build.
 from ._lib import (  # noqa: F401
     KVP_BF16, KVP_COMPACT_DEMOTE_INT8, KVP_COMPACT_EVICT, KVP_F32, KVP_PAGE,
     KVP_SCORER_LINEAR, KVP_SCORER_MLP, ERR_POOL8_FULL, ERR_POOL_FULL, ERR_TABLE_FULL,
+    KVP_LP_INT8, KVP_LP_INT4, KVP_LP_FP8_E4M3,
     KvpError, PagedKV, Ring, Scorer, decode_attn_workspace, kvp_check, kvp_clear_error,
     kvp_compact, kvp_compact_workspace_size, kvp_decode_attn,
     kvp_decode_attn_workspace_size, kvp_decode_attn_noalloc, KVP_NOALLOC_SCRATCH_BYTES,

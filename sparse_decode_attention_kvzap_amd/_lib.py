@@ -26,6 +26,7 @@ KVP_COMPACT_EVICT, KVP_COMPACT_DEMOTE_INT8 = 0, 1
 STATUS = {0: "KVP_OK", 1: "KVP_E_ARG", 2: "KVP_E_DTYPE", 3: "KVP_E_WORKSPACE",
           4: "KVP_E_CAPACITY", 5: "KVP_E_HIP", 6: "KVP_E_UNSUPPORTED"}
 ERR_POOL_FULL, ERR_TABLE_FULL, ERR_POOL8_FULL = 1, 2, 4
+KVP_LP_INT8, KVP_LP_INT4, KVP_LP_FP8_E4M3 = 8, 4, 0x108
 
 
 class KvpError(RuntimeError):
@@ -189,11 +190,12 @@ class PagedKV:
     def allocate(num_pairs: int, head_dim: int, num_pages: int, max_pages_per_pair: int,
                  dtype=torch.bfloat16, device="cuda", num_pages8: int = 0,
                  max_pages8_per_pair: int = 0, poison: bool = False,
-                 lp_bits: int = 8) -> "PagedKV":
-        """lp_bits: code width of the low-precision pool (8: int8 codes; 4: int4 codes,
-        two per byte, so its K pages are [16][d/2] bytes and its V^T pages [d][8])."""
-        if lp_bits not in (4, 8):
-            raise ValueError("lp_bits must be 8 or 4")
+                 lp_bits=8) -> "PagedKV":
+        """lp_bits: code format of the low-precision pool: 8 (int8 codes), 4 (int4 codes,
+        two per byte, so its K pages are [16][d/2] bytes and its V^T pages [d][8]) or
+        "fp8" (E4M3 codes, one per byte)."""
+        if lp_bits not in (4, 8, "fp8"):
+            raise ValueError("lp_bits must be 8, 4 or 'fp8'")
         dev = torch.device(device)
         t = {}
         fill = float("nan") if poison else 0.0
@@ -205,7 +207,7 @@ class PagedKV:
         t["page_top"] = torch.zeros(1, dtype=torch.int32, device=dev)
         t["err"] = torch.zeros(1, dtype=torch.int32, device=dev)
         if num_pages8 > 0:
-            per = 8 // lp_bits  # codes per byte
+            per = 2 if lp_bits == 4 else 1  # codes per byte
             t["k8_pages"] = torch.full((num_pages8, KVP_PAGE, head_dim // per), 0x55, dtype=torch.int8, device=dev)
             t["v8_pages"] = torch.full((num_pages8, head_dim, KVP_PAGE // per), 0x55, dtype=torch.int8, device=dev)
             t["k8_scale"] = torch.full((num_pages8, KVP_PAGE), fill, dtype=torch.float32, device=dev)
@@ -219,7 +221,7 @@ class PagedKV:
         c.num_pairs, c.head_dim, c.num_pages = num_pairs, head_dim, num_pages
         c.max_pages_per_pair = max_pages_per_pair
         c.num_pages8, c.max_pages8_per_pair = num_pages8, max_pages8_per_pair
-        c.lp_bits = lp_bits
+        c.lp_bits = KVP_LP_FP8_E4M3 if lp_bits == "fp8" else lp_bits
         for name, ten in t.items():
             setattr(c, name, ten.data_ptr())
         return PagedKV(c, t)

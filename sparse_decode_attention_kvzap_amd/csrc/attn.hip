@@ -747,15 +747,66 @@ __device__ __forceinline__ u32x4 i4x8_to_bf16x8(uint32_t w) {
   return r;
 }
 
-// 8 codes of a fragment: two dwords of int8 codes or one dword of int4 codes.
-template <int BITS> struct LpWord { typedef u32x2 T; };
-template <> struct LpWord<4> { typedef uint32_t T; };
+// 8 E4M3 codes (two dwords, element e in byte e) -> 8 bf16, exactly.  A normal code
+// (exponent field e >= 1) is 2^(e - 7) (1 + m / 8), whose bf16 pattern is the code's 7
+// low bits shifted left by 4 plus (127 - 7) << 7, the sign moved to bit 15: two per
+// dword after a byte permute.  Exponent field 0 (zero, and the subnormals m 2^-9) is
+// rare after absmax scaling; a fragment holding one in any lane decodes element by
+// element.  The NaN codes decode as 480 (finite), like the other codes of unused slots,
+// whose weights are exactly zero.
+struct F8x8 {
+  u32x2 w;
+};
+__device__ __forceinline__ uint32_t f8_code_to_bf16(uint32_t c) {
+  const uint32_t c7 = c & 0x7fu;
+  uint32_t v;
+  if (c7 >= 8u) {
+    v = (c7 << 4) + 0x3C00u;
+  } else if (c7 == 0u) {
+    v = 0u;
+  } else {  // m 2^-9 = 2^(e - 9) (m / 2^e) with e = floor(log2 m)
+    const uint32_t e = 31u - __builtin_clz(c7);
+    v = ((118u + e) << 7) | ((c7 << (7u - e)) & 0x7fu);
+  }
+  return v | ((c & 0x80u) << 8);
+}
+__device__ __forceinline__ u32x4 f8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  const uint32_t small = (~((w0 & 0x7f7f7f7fu) + 0x78787878u) | ~((w1 & 0x7f7f7f7fu) + 0x78787878u)) &
+                         0x80808080u;  // bit 7 of a byte: that code's 7 low bits are < 8
+  u32x4 r;
+  if (__builtin_expect(__ballot(small != 0u) != 0, 0)) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w = q < 2 ? w0 : w1, sh = 16u * (q & 1);
+      r[q] = f8_code_to_bf16((w >> sh) & 0xffu) | (f8_code_to_bf16((w >> (sh + 8)) & 0xffu) << 16);
+    }
+    return r;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t w = i ? w1 : w0;
+    const uint32_t c7 = w & 0x7f7f7f7fu, sg = w & 0x80808080u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // codes 2h, 2h + 1 of the dword -> bits 0..15, 16..31
+      const uint32_t sel = h ? 0x0c030c02u : 0x0c010c00u;
+      r[2 * i + h] = ((__builtin_amdgcn_perm(0u, c7, sel) << 4) + 0x3C003C00u) |
+                     (__builtin_amdgcn_perm(0u, sg, sel) << 8);
+    }
+  }
+  return r;
+}
+
+// 8 codes of a fragment: two dwords of int8 or fp8 codes, or one dword of int4 codes.
+template <int BITS, bool F8 = false> struct LpWord { typedef u32x2 T; };
+template <> struct LpWord<4, false> { typedef uint32_t T; };
+template <> struct LpWord<8, true> { typedef F8x8 T; };
 __device__ __forceinline__ u32x4 lp_to_bf16x8(u32x2 w) { return i8x8_to_bf16x8(w[0], w[1]); }
 __device__ __forceinline__ u32x4 lp_to_bf16x8(uint32_t w) { return i4x8_to_bf16x8(w); }
+__device__ __forceinline__ u32x4 lp_to_bf16x8(F8x8 x) { return f8x8_to_bf16x8(x.w[0], x.w[1]); }
 
-template <int D, int BITS>
+template <int D, int BITS, bool F8 = false>
 struct LpFrags {
-  typedef typename LpWord<BITS>::T W;
+  typedef typename LpWord<BITS, F8>::T W;
   W kA[D / 32];  // 8 K codes per MFMA K-step, score tile A row
   W kB[D / 32];
   W v[D / 16];   // 8 V^T codes per output tile
@@ -765,9 +816,9 @@ struct LpFrags {
 
 // Byte offsets scale with the code width: a K row is D * BITS / 8 bytes, a V^T row
 // 16 * BITS / 8.
-template <int D, int BITS>
-__device__ __forceinline__ void load_lp_k(const AttnArgs& a, LpFrags<D, BITS>& f, int pgX, int pgY, int lane) {
-  typedef typename LpWord<BITS>::T W;
+template <int D, int BITS, bool F8>
+__device__ __forceinline__ void load_lp_k(const AttnArgs& a, LpFrags<D, BITS, F8>& f, int pgX, int pgY, int lane) {
+  typedef typename LpWord<BITS, F8>::T W;
   const int m = lane & 15, j = lane >> 4;
   const int tA = 8 * (m >> 2) + (m & 3), tB = tA + 4;
   const int pgK = (tA < 16) ? pgX : pgY;
@@ -785,9 +836,9 @@ __device__ __forceinline__ void load_lp_k(const AttnArgs& a, LpFrags<D, BITS>& f
   f.ks[1] = *reinterpret_cast<const f32x4*>(ksc + 4);
 }
 
-template <int D, int BITS>
-__device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS>& f, int pgX, int pgY, int lane) {
-  typedef typename LpWord<BITS>::T W;
+template <int D, int BITS, bool F8>
+__device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS, F8>& f, int pgX, int pgY, int lane) {
+  typedef typename LpWord<BITS, F8>::T W;
   const int m = lane & 15, j = lane >> 4;
   const int pgT = (j < 2) ? pgX : pgY;
   const int8_t* vcol = a.kv.v8_pages + ((int64_t)pgT * PAGE * D + m * PAGE + 8 * (j & 1)) * BITS / 8;
@@ -798,7 +849,7 @@ __device__ __forceinline__ void load_lp_v(const AttnArgs& a, LpFrags<D, BITS>& f
   f.vs[1] = *reinterpret_cast<const f32x4*>(vsc + 4);
 }
 
-template <int D, int BITS, int NSET>
+template <int D, int BITS, int NSET, bool F8 = false>
 __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int v0, int v1, bool rev, SoftmaxState<D>& st) {
   static_assert(NSET % 2 == 0, "steps are folded in pairs");
   const int lane = threadIdx.x & 63, j = lane >> 4;
@@ -853,7 +904,7 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
       const int nvT = real ? max(0, min(PAGE, len - (v + (j >> 1)) * PAGE)) : 0;
       return (uint32_t)((1 << max(0, min(8, nvT - 8 * (j & 1)))) - 1);
     };
-    auto qk = [&](const LpFrags<D, BITS>& f, float (&s)[8], float (&vsc)[8]) {
+    auto qk = [&](const LpFrags<D, BITS, F8>& f, float (&s)[8], float (&vsc)[8]) {
       f32x4 sA = {0.f, 0.f, 0.f, 0.f}, sB = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
@@ -884,7 +935,7 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
       }
     };
     // sum_t p_t (scale_t code_t) = sum_t (p_t scale_t) code_t, weights split bf16 hi + lo
-    auto pv = [&](const LpFrags<D, BITS>& f, const float (&p)[8], const float (&vsc)[8]) {
+    auto pv = [&](const LpFrags<D, BITS, F8>& f, const float (&p)[8], const float (&vsc)[8]) {
       u32x4 hi, lo;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -910,11 +961,11 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
     };
     // NSET register sets in a ring: set r holds step i + r of the block being worked on
     // and is refilled with step i + r + NSET right after its last use.
-    LpFrags<D, BITS> f[NSET];
+    LpFrags<D, BITS, F8> f[NSET];
 #pragma unroll
     for (int r = 0; r < NSET; ++r) {
-      load_lp_k<D, BITS>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
-      load_lp_v<D, BITS>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
+      load_lp_k<D, BITS, F8>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
+      load_lp_v<D, BITS, F8>(a, f[r], page(vat(r)), page(vat(r) + 1), lane);
     }
     for (int i = 0; i < nst; i += NSET) {
 #pragma unroll
@@ -926,8 +977,8 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
         float s0[8], s1[8], c0s[8], c1s[8];
         qk(f[r], s0, c0s);
         qk(f[r + 1], s1, c1s);
-        load_lp_k<D, BITS>(a, f[r], page(vna), page(vna + 1), lane);
-        load_lp_k<D, BITS>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
+        load_lp_k<D, BITS, F8>(a, f[r], page(vna), page(vna + 1), lane);
+        load_lp_k<D, BITS, F8>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
         if (!allv) {
           mask(s0, c0s, m0);
           mask(s1, c1s, m1);
@@ -959,8 +1010,8 @@ __device__ __forceinline__ void run_region_b_lp(const AttnArgs& a, int pair, int
           pv(f[r], p0, c0s);
           pv(f[r + 1], p1, c1s);
         }
-        load_lp_v<D, BITS>(a, f[r], page(vna), page(vna + 1), lane);
-        load_lp_v<D, BITS>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
+        load_lp_v<D, BITS, F8>(a, f[r], page(vna), page(vna + 1), lane);
+        load_lp_v<D, BITS, F8>(a, f[r + 1], page(vnb), page(vnb + 1), lane);
       }
     }
   }
@@ -1092,7 +1143,7 @@ __device__ __forceinline__ void run_region_a_f32(const AttnArgs& a, const Plan& 
 
 // Region-B (low-precision) and fp32 segments: one segment at a time (its query, length
 // and block table fetched at its start).
-template <int D, bool F32, int BITS>
+template <int D, bool F32, int BITS, bool F8 = false>
 __device__ __forceinline__ void stream_segments(const AttnArgs& a, const Plan& pl, bool seqB, int u, float* wlds) {
   UnitIter it;
   iter_init(it, pl, seqB, u);
@@ -1104,7 +1155,7 @@ __device__ __forceinline__ void stream_segments(const AttnArgs& a, const Plan& p
       run_region_a_f32<D>(a, pl, d.s, d.vlo, d.vhi, slot_of(pl, d), wlds);
     } else {
       SoftmaxState<D> st;
-      run_region_b_lp<D, BITS, ATTN_LP_SETS>(a, d.s - np, d.vlo, d.vhi, d.rev != 0, st);
+      run_region_b_lp<D, BITS, ATTN_LP_SETS, F8>(a, d.s - np, d.vlo, d.vhi, d.rev != 0, st);
       segment_done<D>(a, pl, d.s - np, slot_of(pl, d), st);
     }
   }
@@ -1155,7 +1206,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   } else {
     stream_a_bf16<D>(a, pl, Lens, gw, fs);
     if constexpr (LP) {
-      if (a.kv.lp_bits == 4) stream_segments<D, false, 4>(a, pl, true, gw, nullptr);
+      if (a.kv.lp_bits == KVP_LP_INT4) stream_segments<D, false, 4>(a, pl, true, gw, nullptr);
+      else if (a.kv.lp_bits == KVP_LP_FP8_E4M3) stream_segments<D, false, 8, true>(a, pl, true, gw, nullptr);
       else stream_segments<D, false, 8>(a, pl, true, gw, nullptr);
     }
   }

@@ -295,12 +295,15 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
-template <typename E, int D, int BITS>
+// F8: E4M3 codes (BITS = 8): scale = absmax / 448, each code the E4M3 rounding of the
+// correctly rounded quotient (an IEEE division per element; this format is not tuned).
+template <typename E, int D, int BITS, bool F8 = false>
 __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs a) {
+  static_assert(!F8 || BITS == 8, "fp8 codes are one byte");
   constexpr int EPC = 16 / sizeof(E);  // elements per 16-byte chunk
   constexpr int CPR = D / EPC;         // chunks per row (8 .. 32; divides 64)
   constexpr int NPL = PAGE * CPR / 64; // chunks per lane
-  constexpr float QMAX = BITS == 4 ? 7.0f : 127.0f;
+  constexpr float QMAX = F8 ? 448.0f : (BITS == 4 ? 7.0f : 127.0f);
   constexpr int CB = EPC * BITS / 8;   // code bytes per chunk (2 .. 8)
   __shared__ int8_t vcodes[CPY_WAVES][PAGE * D];
   const int lane = threadIdx.x & 63;
@@ -369,8 +372,16 @@ __global__ __launch_bounds__(CMP_THREADS) void compact_quant_kernel(CompactArgs 
       const float kinv = kscale > 0.f ? __builtin_amdgcn_rcpf(kscale) : 0.f;
       const float vinv = vscale > 0.f ? __builtin_amdgcn_rcpf(vscale) : 0.f;
       uint32_t kb[EPC], vb[EPC];
-      quant_codes_fast<EPC>(kf, kscale, kinv, kb);
-      quant_codes_fast<EPC>(vf, vscale, vinv, vb);
+      if constexpr (F8) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+          kb[e] = fp8_quant_code(kf[e], kscale);
+          vb[e] = fp8_quant_code(vf[e], vscale);
+        }
+      } else {
+        quant_codes_fast<EPC>(kf, kscale, kinv, kb);
+        quant_codes_fast<EPC>(vf, vscale, vinv, vb);
+      }
       uint32_t w[2] = {0u, 0u};
 #pragma unroll
       for (int e = 0; e < EPC; ++e) {
@@ -454,15 +465,20 @@ kvp_status kvp_launch_compact(const void* k, const void* v, int num_pairs, int T
     hipLaunchKernelGGL((compact_copy_kernel<float, 64>), dim3(CMP_GRID), dim3(CMP_THREADS), 0, stream, a);
   KVP_LAUNCH_CHECK();
   if (demote) {
-    const bool i4 = lp_bits_of(*kv) == 4;
+    const bool i4 = lp_bits_of(*kv) == 4, f8 = lp_is_fp8(*kv);
     const dim3 g(CMP_GRID), b(CMP_THREADS);
-#define KVP_QUANT(E, DD, BB) hipLaunchKernelGGL((compact_quant_kernel<E, DD, BB>), g, b, 0, stream, a)
+#define KVP_QUANT(E, DD)                                                                           \
+  do {                                                                                             \
+    if (i4) hipLaunchKernelGGL((compact_quant_kernel<E, DD, 4>), g, b, 0, stream, a);              \
+    else if (f8) hipLaunchKernelGGL((compact_quant_kernel<E, DD, 8, true>), g, b, 0, stream, a);   \
+    else hipLaunchKernelGGL((compact_quant_kernel<E, DD, 8>), g, b, 0, stream, a);                 \
+  } while (0)
     if (bf) {
-      if (d == 128) { if (i4) KVP_QUANT(uint16_t, 128, 4); else KVP_QUANT(uint16_t, 128, 8); }
-      else { if (i4) KVP_QUANT(uint16_t, 64, 4); else KVP_QUANT(uint16_t, 64, 8); }
+      if (d == 128) KVP_QUANT(uint16_t, 128);
+      else KVP_QUANT(uint16_t, 64);
     } else {
-      if (d == 128) { if (i4) KVP_QUANT(float, 128, 4); else KVP_QUANT(float, 128, 8); }
-      else { if (i4) KVP_QUANT(float, 64, 4); else KVP_QUANT(float, 64, 8); }
+      if (d == 128) KVP_QUANT(float, 128);
+      else KVP_QUANT(float, 64);
     }
 #undef KVP_QUANT
     KVP_LAUNCH_CHECK();

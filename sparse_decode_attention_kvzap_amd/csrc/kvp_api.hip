@@ -60,7 +60,9 @@ kvp_status check_kv(const kvp_paged_kv* kv) {
   if (kv->num_pages8 < 0) return KVP_E_ARG;
   if (kv->num_pages8 > 0) {
     if (kv->max_pages8_per_pair <= 0) return KVP_E_ARG;
-    if (kv->lp_bits != 0 && kv->lp_bits != 8 && kv->lp_bits != 4) return KVP_E_ARG;
+    if (kv->lp_bits != 0 && kv->lp_bits != KVP_LP_INT8 && kv->lp_bits != KVP_LP_INT4 &&
+        kv->lp_bits != KVP_LP_FP8_E4M3)
+      return KVP_E_ARG;
     if (!kv->k8_pages || !kv->v8_pages || !kv->k8_scale || !kv->v8_scale || !kv->page8_pos ||
         !kv->block_table8 || !kv->length8 || !kv->page8_top)
       return KVP_E_ARG;

@@ -173,8 +173,37 @@ __device__ __forceinline__ int quant_code(float x, float scale, float qmax = 127
   return static_cast<int>(y);
 }
 
-// Low-precision pool code width (kvp_paged_kv::lp_bits; 0 means 8).
+// Low-precision pool code width (kvp_paged_kv::lp_bits; 0 means 8; the fp8 format has
+// 8-bit codes, so it shares the int8 pool's layout).
 __host__ __device__ inline int lp_bits_of(const kvp_paged_kv& kv) { return kv.lp_bits == 4 ? 4 : 8; }
+__host__ __device__ inline bool lp_is_fp8(const kvp_paged_kv& kv) { return kv.lp_bits == KVP_LP_FP8_E4M3; }
+
+// OCP FP8 E4M3 code of an fp32 value (1 sign, 4 exponent bits with bias 7, 3 mantissa
+// bits; largest finite magnitude 448; exponent field 0 holds the subnormals m 2^-9):
+// round to nearest, ties to even; magnitudes at or above 448 saturate to 448.
+__device__ __forceinline__ uint32_t fp8_e4m3_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fabsf(y);
+  uint32_t c;
+  if (!(a < 448.0f)) {
+    c = 0x7Eu;
+  } else if (a < 0x1p-6f) {
+    c = static_cast<uint32_t>(rintf(a * 512.0f));  // 0..8 (8: the smallest normal)
+  } else {
+    const uint32_t ua = __float_as_uint(a);
+    const uint32_t m = ua & 0x7fffffu, rem = m & 0xfffffu;
+    uint32_t k = (((ua >> 23) - 120u) << 3) | (m >> 20);  // biased exponent 127 -> 7
+    k += (rem > 0x80000u || (rem == 0x80000u && (k & 1u))) ? 1u : 0u;
+    c = k < 0x7Eu ? k : 0x7Eu;
+  }
+  return sign | c;
+}
+
+// fp8 code of x for a row scale s = fp32(max |x| / 448): the code of the correctly
+// rounded fp32 quotient; a zero scale (an all-zero row) gives code 0.
+__device__ __forceinline__ uint32_t fp8_quant_code(float x, float scale) {
+  return scale == 0.0f ? 0u : fp8_e4m3_code(x / scale);
+}
 
 }  // namespace kvp
 

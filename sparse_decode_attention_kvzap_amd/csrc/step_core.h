@@ -236,7 +236,8 @@ __device__ __forceinline__ void step_pair(const StepArgs& a, int pair, int p) {
         }
       }
     } else if (a.kv.num_pages8 > 0) {
-      // demote to the int8 pool (BeaconKV): absmax per row, K and V separately
+      // demote to the low-precision pool (BeaconKV): absmax per row, K and V separately;
+      // int8, int4 or fp8 E4M3 codes
       float kf[PER], vf[PER];
       float ka = 0.f, va = 0.f;
 #pragma unroll
@@ -249,8 +250,8 @@ __device__ __forceinline__ void step_pair(const StepArgs& a, int pair, int p) {
       }
       ka = wave_max(ka);
       va = wave_max(va);
-      const bool i4 = lp_bits_of(a.kv) == 4;
-      const float qmax = i4 ? 7.0f : 127.0f;
+      const bool i4 = lp_bits_of(a.kv) == 4, f8 = lp_is_fp8(a.kv);
+      const float qmax = f8 ? 448.0f : (i4 ? 7.0f : 127.0f);
       const float ks = ka / qmax, vs = va / qmax;
       const int j = j8, sl = sl8;
       int pg = -1;
@@ -297,8 +298,8 @@ __device__ __forceinline__ void step_pair(const StepArgs& a, int pair, int p) {
         for (int e = 0; e < PER; ++e) {
           const int dd = lane + 64 * e;
           if (dd < D) {
-            kp[dd] = static_cast<int8_t>(quant_code(kf[e], ks));
-            vp[dd * PAGE] = static_cast<int8_t>(quant_code(vf[e], vs));
+            kp[dd] = static_cast<int8_t>(f8 ? fp8_quant_code(kf[e], ks) : quant_code(kf[e], ks));
+            vp[dd * PAGE] = static_cast<int8_t>(f8 ? fp8_quant_code(vf[e], vs) : quant_code(vf[e], vs));
           }
         }
       }

@@ -11,7 +11,7 @@ KVzap (max5.ai digest, practical application): score every entry, drop low score
 always keep the most recent tokens.  DMS (euno.news, Delayed Eviction): with tau = 0
 and window w the same machinery keeps a flagged token for w steps.  BeaconKV
 (jiinsi.com, body): with demote=True evicted entries go to a low-precision pool
-instead (int8 codes, or int4 with lp_bits=4).
+instead (int8 codes, int4 with lp_bits=4, or fp8 E4M3 with lp_bits="fp8").
 
 This class only allocates device buffers (torch) and calls libkvp in stream order;
 all arithmetic runs in the HIP kernels.
@@ -29,7 +29,7 @@ from . import _lib as L
 class PrunedKVCache:
     def __init__(self, B: int, Hkv: int, Hq: int, d: int, T_max: int, dtype: torch.dtype,
                  scorer: L.Scorer, window: int, tau: float, demote: bool = False,
-                 device="cuda", max_prompt: Optional[int] = None, lp_bits: int = 8):
+                 device="cuda", max_prompt: Optional[int] = None, lp_bits=8):
         self.B, self.Hkv, self.Hq, self.d = B, Hkv, Hq, d
         self.P = B * Hkv
         self.T_max = T_max

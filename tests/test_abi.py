@@ -159,8 +159,9 @@ def test_host_validation_without_device(L):
     for name in ("k8_pages", "v8_pages", "k8_scale", "v8_scale", "page8_pos", "block_table8",
                  "length8", "page8_top"):
         setattr(kv, name, fake)
-    kv.lp_bits = 3
-    assert lib.kvp_reset(ctypes.byref(kv), None, None) == E_ARG
+    for bad in (3, 0x18, 0x208):  # not int8, int4 or fp8 E4M3
+        kv.lp_bits = bad
+        assert lib.kvp_reset(ctypes.byref(kv), None, None) == E_ARG
     kv.lp_bits = 4
     kv.num_pages8, kv.max_pages8_per_pair = 0, 0
     # compact: demotion without an int8 pool, wrong pair count

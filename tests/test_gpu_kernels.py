@@ -196,22 +196,43 @@ def test_compact_exact(K, dtype, d, ring_w):
             assert np.array_equal(Sr, sb[p, rpos])
 
 
+def lp_quant(bits, x):
+    """The oracle's codes and scale of one row in the pool's format (8, 4 or "fp8")."""
+    if bits == "fp8":
+        return oracle.quantize_absmax_fp8(x)
+    return oracle.quantize_absmax(x, oracle.LP_QMAX[bits])
+
+
+def lp_codes_equal(bits, gpu_codes, ref_codes):
+    if bits == "fp8":  # E4M3 bytes: compare the bit patterns
+        return np.array_equal(np.asarray(gpu_codes).view(np.uint8), np.asarray(ref_codes, np.uint8))
+    return np.array_equal(gpu_codes, ref_codes)
+
+
 @pytest.mark.parametrize("bits,d,dtype", [(8, 128, torch.bfloat16), (4, 128, torch.bfloat16),
                                           (4, 64, torch.bfloat16), (8, 64, torch.bfloat16),
-                                          (4, 128, torch.float32), (8, 64, torch.float32)])
+                                          (4, 128, torch.float32), (8, 64, torch.float32),
+                                          ("fp8", 128, torch.bfloat16), ("fp8", 64, torch.bfloat16),
+                                          ("fp8", 128, torch.float32)])
 def test_compact_demote_exact(K, bits, d, dtype):
     B, Hkv, T = 2, 2, 500
     P = B * Hkv
     k = seeded((B, Hkv, T, d), 41, dtype)
     v = seeded((B, Hkv, T, d), 42, dtype, 3.0)
     k[0, 0, 7] = 0  # all-zero row -> scale 0, codes 0
-    qmax = oracle.LP_QMAX[bits]
-    # rows whose quotients x / scale sit on or next to half-integers, where the rounding
-    # decision is taken by an exact division: ties (scale exactly 1: row max = qmax, the
-    # rest k + 1/2) and, with an inexact scale, x = fp(scale (k + 1/2)) and its neighbours
-    ties = np.concatenate([[qmax], (np.arange(d - 1) % (2 * qmax)) - qmax + 0.5]).astype(np.float32)
+    qmax = 448 if bits == "fp8" else oracle.LP_QMAX[bits]
+    # rows whose quotients x / scale sit on or next to rounding boundaries: ties (scale
+    # exactly 1: row max = qmax, the rest halfway between neighbouring codes) and, with
+    # an inexact scale, x = fp(scale * halfway point) and its neighbours
+    if bits == "fp8":
+        cv = oracle.fp8_e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+        mids = (cv[:-1] + cv[1:]) / 2
+        half = np.resize(mids[::-1], d - 1) * np.where(np.arange(d - 1) % 2, -1.0, 1.0)
+    else:
+        half = (np.arange(d - 1) % (2 * qmax)) - qmax + 0.5
+    ties = np.concatenate([[qmax], half]).astype(np.float32)
     sc = np.float32(np.float32(100.0) / np.float32(qmax))
-    near = np.float32(sc) * ((np.arange(d - 1) % (2 * qmax)) - qmax + 0.5).astype(np.float32)
+    near = np.float32(sc) * half.astype(np.float32)
     near = near.astype(np.float32)
     near[1::3] = np.nextafter(near[1::3], np.float32(np.inf))
     near[2::3] = np.nextafter(near[2::3], np.float32(-np.inf))
@@ -236,10 +257,10 @@ def test_compact_demote_exact(K, bits, d, dtype):
         pos, Kc, Vc, ks, vs = read_pool8(kv, p)
         assert np.array_equal(pos, ev)
         for i, t in enumerate(ev):
-            c, sc = oracle.quantize_absmax(kf[p, t], qmax)
-            assert ks[i] == sc and np.array_equal(Kc[i], c), (p, t)
-            c, sc = oracle.quantize_absmax(vf[p, t], qmax)
-            assert vs[i] == sc and np.array_equal(Vc[i], c), (p, t)
+            c, sc = lp_quant(bits, kf[p, t])
+            assert ks[i] == sc and lp_codes_equal(bits, Kc[i], c), (p, t)
+            c, sc = lp_quant(bits, vf[p, t])
+            assert vs[i] == sc and lp_codes_equal(bits, Vc[i], c), (p, t)
         # every position is held exactly once across bf16 pool, ring and int8 pool
         allpos = visible_positions(kv, ring, p)
         assert np.array_equal(allpos, np.arange(T))
@@ -315,7 +336,8 @@ def test_decode_attn_empty_pairs(K):
     assert (out[0, :4] == 0).all() and (out[1, :4] == 0).all()
 
 
-@pytest.mark.parametrize("bits,d,Hq,T", [(8, 128, 8, 900), (4, 128, 8, 900), (4, 64, 16, 777)])
+@pytest.mark.parametrize("bits,d,Hq,T", [(8, 128, 8, 900), (4, 128, 8, 900), (4, 64, 16, 777),
+                                         ("fp8", 128, 8, 900), ("fp8", 64, 16, 777)])
 def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
     B, Hkv = 2, 2
     P = B * Hkv
@@ -330,10 +352,10 @@ def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
     ref = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
                                          oracle.sm_scale(d), bits=bits)
     check_attention(out, ref, torch.bfloat16)
-    if bits == 4:  # the coarser pool really is read: int8 codes would give another result
+    if bits in (4, "fp8"):  # that pool really is read: int8 codes would give another result
         ref8 = oracle.beacon_decode_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T),
                                               oracle.sm_scale(d), bits=8)
-        assert np.abs(ref8 - ref).max() > 10 * 2e-3
+        assert np.abs(ref8 - ref).max() > (10 if bits == 4 else 1) * 2e-3
 
 
 @pytest.mark.parametrize("bits,B,Hq,Hkv,T,d,ring_w,case", [
@@ -343,13 +365,15 @@ def test_decode_attn_lowprec_pool(K, bits, d, Hq, T):
     (8, 2, 8, 2, 700, 128, 0, "random"),      # int8 without a ring
     (4, 2, 8, 2, 900, 128, 128, "extremes"),  # one pair with no code region, one all codes
     (8, 2, 8, 2, 900, 128, 0, "extremes"),    # ... and one pair with no full-precision token
+    ("fp8", 2, 16, 2, 1500, 64, 128, "random"),   # fp8 E4M3 codes at d 64, g 8
+    ("fp8", 2, 8, 2, 900, 128, 0, "extremes"),    # fp8 pool with its edge pairs
 ])
 def test_decode_attn_lowprec_edges(K, bits, B, Hq, Hkv, T, d, ring_w, case):
     """Attention over a full-precision pool (+ ring) and an int8 / int4 pool in one
     softmax, at the head-group, head-dim and pair-count limits and with regions of a
     pair empty; reruns on a garbage-filled workspace are bit-identical."""
     P = B * Hkv
-    g = torch.Generator().manual_seed(T + d + bits)
+    g = torch.Generator().manual_seed(T + d + (9 if bits == "fp8" else bits))
     keep = (torch.rand((P, T), generator=g) < 0.15).numpy()
     if case == "extremes":
         keep[0, :] = True   # nothing demoted
@@ -375,7 +399,8 @@ def test_decode_attn_lowprec_edges(K, bits, B, Hq, Hkv, T, d, ring_w, case):
                                                    (torch.float32, 64, 32, False, 8),
                                                    (torch.bfloat16, 128, 32, True, 8),
                                                    (torch.bfloat16, 128, 32, True, 4),
-                                                   (torch.bfloat16, 64, 48, True, 4)])
+                                                   (torch.bfloat16, 64, 48, True, 4),
+                                                   (torch.bfloat16, 128, 32, True, "fp8")])
 def test_step_delayed_state_machine(K, dtype, d, w, demote, bits):
     """DMS: flagged tokens stay w steps; the visible set is re-derived from scratch by
     the oracle at every step and compared with the ring + pool content."""
@@ -426,16 +451,15 @@ def test_step_delayed_state_machine(K, dtype, d, w, demote, bits):
             check_attention(out, ref, dtype)
     assert K.kvp_check(kv) == 0
     if demote:  # every demoted row (by compaction or by a step) holds the oracle's codes
-        qmax = oracle.LP_QMAX[bits]
         kr, vr = kf.reshape(P, total, d), vf.reshape(P, total, d)
         for pr in range(P):
             pos, Kc, Vc, ks, vs = read_pool8(kv, pr)
             assert len(pos) > w // 2
             for i, t in enumerate(pos):
-                c, sc = oracle.quantize_absmax(kr[pr, t], qmax)
-                assert ks[i] == sc and np.array_equal(Kc[i], c), (pr, t)
-                c, sc = oracle.quantize_absmax(vr[pr, t], qmax)
-                assert vs[i] == sc and np.array_equal(Vc[i], c), (pr, t)
+                c, sc = lp_quant(bits, kr[pr, t])
+                assert ks[i] == sc and lp_codes_equal(bits, Kc[i], c), (pr, t)
+                c, sc = lp_quant(bits, vr[pr, t])
+                assert vs[i] == sc and lp_codes_equal(bits, Vc[i], c), (pr, t)
 
 
 def _same_cache(kvA, ringA, kvB, ringB):

@@ -200,6 +200,21 @@ def test_beacon_int4_full_size_sampled(K):
     print(r)
 
 
+def test_beacon_fp8_reduced_all_pairs(K):
+    wl = W.BEACON_FP8
+    r = run_kvzap(K, wl, 2500, [0, 1], q_keep=0.9, demote=True, B=2)
+    assert 0.1 < r["kept"] < 0.2
+
+
+@pytest.mark.slow
+def test_beacon_fp8_full_size_sampled(K):
+    """The beacon shape and inputs with the demoted tokens as fp8 E4M3 codes: one batch
+    row's 8 pairs against the oracle's E4M3 round trips."""
+    wl = W.BEACON_FP8
+    r = run_kvzap(K, wl, wl.T, [3], q_keep=0.9, demote=True)
+    print(r)
+
+
 # ------------------------------------------------------------------ DMS delayed eviction
 
 
