@@ -3,9 +3,11 @@
 The timed step is the DECODE step of the Qwen-3-8B-like single layer (B=16, H=4096,
 32 Q / 8 KV heads, d=128, bf16 KV in 16-token pages, MLP scorer 4096->512->8) on a
 context of 32767 prompt positions compressed to ~25% (tau at the 75th percentile of
-the prompt's scores, computed on the device; the most recent 128 positions kept):
-    kvp_score_step_delayed  the new tokens scored by the MLP inside the delayed step
-    kvp_decode_attn         GQA attention over the kept entries only
+the prompt's scores, computed on the device; the most recent 128 positions kept): one
+kvp_decode_step call, which scores the 16 new tokens with the MLP (its split-K first layer,
+then the rest inside the step), applies the delayed step and runs GQA attention over the
+kept entries only.  The same steps as separate calls (kvp_score_step_delayed, then
+kvp_decode_attn) are timed beside it.
 The prompt is compressed once before timing (kvp_score -> kvp_threshold -> kvp_select ->
 kvp_compact); those calls are timed one by one in the "prefill" record.  Every input is
 resident in HBM before the timed region; the decode positions T-1, T, ... are appended
@@ -28,6 +30,7 @@ Records of the same run, each on its own seeded synthetic inputs:
     dms_delayed     8192-token prompt + 1024 delayed-eviction decode steps, eager and graph
     long_70b_layer  decode steps at keep 0.5 / 0.25 (and 1.0) on the 70B-like layer
     beacon_mixed    decode steps over the bf16 + int8 pools, and the demoting compaction
+    beacon_int4     the same with the demoted tokens as int4 codes
     beacon_fp8      the same with the demoted tokens as fp8 E4M3 codes
     copy_ceiling    a plain 1 GiB device copy and a 1 GiB read (torch kernels)
 
@@ -48,7 +51,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 METRIC = "kept-KV decode attention tokens/s + achieved HBM GB/s (% of peak), 1 GPU"
 RECORDS = ("headline", "prefill", "keep_scaling", "dms_delayed", "long_70b_layer",
-           "beacon_mixed", "beacon_fp8", "copy_ceiling")
+           "beacon_mixed", "beacon_int4", "beacon_fp8", "copy_ceiling")
 
 
 def log(msg):
@@ -57,16 +60,18 @@ def log(msg):
 
 def pmc_traffic(key):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE runs
-    (scaled by the plain-copy calibration), or None once the kernel's source differs
-    from the one that was profiled."""
+    (scaled by the plain-copy calibration), or None once any source file of the kernel
+    differs from the one that was profiled."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "pmc_traffic.json")
     try:
         rec = json.load(open(path))[key]
-        src = open(os.path.join(ROOT, rec["source"]), "rb").read()
+        h = hashlib.sha256()
+        for f in rec["sources"]:  # every source file the kernel is built from
+            h.update(open(os.path.join(ROOT, f), "rb").read())
     except (OSError, KeyError, ValueError):
         return None
-    if hashlib.sha256(src).hexdigest()[:16] != rec["source_sha256_16"]:
+    if h.hexdigest()[:16] != rec["source_sha256_16"]:
         return None
     return rec["hbm_bytes_per_launch"]
 
@@ -332,6 +337,7 @@ def record_prefill(ctx, stream, reps=5):
         demoted = B * Hkv * T0 - kept
         compact_bytes += demoted * (2 * d * elt + 2 * (d * code_bytes(wl.lp_bits) + 4) + 4)
     tflops = flops / (ms["score"] * 1e-3) / 1e12
+    tk = ("compact_quant" if wl.lp_bits == 8 else None) if wl.int8_demote else "compact_copy"
     out = {
         "workload": wl.name, "kept_token_heads": kept,
         "score": {"ms": ms["score"], "kind": wl.scorer, "flop": flops, "tflops": tflops,
@@ -343,7 +349,8 @@ def record_prefill(ctx, stream, reps=5):
         "compact": {"ms": ms["compact"], "bytes": compact_bytes,
                     "gbs": gbs(compact_bytes, ms["compact"]),
                     "frac_of_peak": gbs(compact_bytes, ms["compact"]) / PEAK_HBM_GBS,
-                    "traffic": pmc_traffic("compact_quant" if wl.int8_demote else "compact_copy")},
+                    # counters were taken for the copy kernel, and for the int8 quantizing kernel
+                    "traffic": pmc_traffic(tk) if tk else None, "traffic_kernel": tk},
     }
     if not wl.int8_demote and dtype_name(wl.kv_dtype) == "bf16":
         out["prefill_attn"] = measure_prefill_attn(ctx, stream)
@@ -434,7 +441,8 @@ def record_long(dev, stream, steps, warmup):
 
 def record_beacon(dev, stream, steps, warmup, name="beacon_mixed"):
     """Beacon-style mixed precision: decode steps over the bf16 and low-precision pools
-    (int8 codes; fp8 E4M3 codes for beacon_fp8), and the demoting compaction."""
+    (int8 codes; int4 for beacon_int4, fp8 E4M3 for beacon_fp8), and the demoting
+    compaction."""
     import torch
 
     import kvp_workloads as W
@@ -482,7 +490,9 @@ def record_copy_ceiling(dev, stream):
     torch.cuda.empty_cache()
     return {"copy_gbs": copy_gbs, "read_gbs": read_gbs,
             "copy_frac_of_peak": copy_gbs / PEAK_HBM_GBS, "read_frac_of_peak": read_gbs / PEAK_HBM_GBS,
-            "note": "torch copy_ of 1 GiB (2 GiB moved) and torch sum over 1 GiB, medians of 6"}
+            "note": "torch copy_ of 1 GiB (2 GiB moved) and torch sum over 1 GiB, medians of 6; "
+                    "the sum is torch's reduction kernel, which does not reach the read "
+                    "bandwidth, so only the copy serves as a ceiling"}
 
 
 def dms_loop(dev, stream):
@@ -726,7 +736,8 @@ def main():
                 f"scorer={wl.scorer} keep quantile {wl.keep_quantiles[0]}")
             r = decode_run(ctx, wl.keep_quantiles[0], args.steps, args.warmup, stream, graph=True)
             a = r["attn"]
-            log(f"[bench] decode step {r['ms_per_step'] * 1e3:.1f} us (graph replay "
+            log(f"[bench] decode step {r['ms_per_step'] * 1e3:.1f} us (separate calls "
+                f"{r['separate_calls_ms_per_step'] * 1e3:.1f} us, graph replay "
                 f"{r['graph_ms_per_step'] * 1e3:.1f} us); attention {a['ms'] * 1e3:.1f} us = "
                 f"{a['gbs']:.0f} GB/s ({100 * a['frac_of_peak']:.1f}% of peak); "
                 f"{r['token_heads_per_step']:.0f} token-heads per step")
@@ -752,7 +763,8 @@ def main():
                            "recent": wl.R, "page": 16,
                            "token_heads_per_step": r["token_heads_per_step"],
                            "total_token_heads": r["total_token_heads"],
-                           "step": "kvp_score_step_delayed + kvp_decode_attn"},
+                           "step": "kvp_decode_step (MLP split-K first layer, then scoring finish, "
+                                   "delayed step and attention in the attention's two kernels)"},
                 "roofline": {"kernel": "kvp_decode_attn (decode_attn_kernel + decode_attn_merge_kernel)",
                              "bound": "hbm", "achieved": a["gbs"], "peak": PEAK_HBM_GBS,
                              "unit": "GB/s", "frac": a["frac_of_peak"],
@@ -763,6 +775,7 @@ def main():
                              "launches_timed": a["launches"]},
                 "cpu_baseline": cpu,
                 "decode_step": {"ms": r["ms_per_step"], "graph_replay_ms": r["graph_ms_per_step"],
+                                "separate_calls_ms": r["separate_calls_ms_per_step"],
                                 "steps_per_s": 1e3 / r["ms_per_step"],
                                 "sequence_steps_per_s": wl.B * 1e3 / r["ms_per_step"]},
                 "decode_attn": a,
@@ -783,7 +796,7 @@ def main():
     if "long_70b_layer" in only:
         records["long_70b_layer"] = record_long(dev, stream, args.steps, args.warmup)
         torch.cuda.empty_cache()
-    for name in ("beacon_mixed", "beacon_fp8"):
+    for name in ("beacon_mixed", "beacon_int4", "beacon_fp8"):
         if name in only:
             records[name] = record_beacon(dev, stream, args.steps, args.warmup, name)
             torch.cuda.empty_cache()
@@ -798,7 +811,6 @@ def main():
     cc = records.get("copy_ceiling")
     if cc:
         line["roofline"]["frac_of_measured_copy"] = line["roofline"]["achieved"] / cc["copy_gbs"]
-        line["roofline"]["frac_of_measured_read"] = line["roofline"]["achieved"] / cc["read_gbs"]
     line["records"] = records
     print(json.dumps(line), flush=True)
 
