@@ -30,8 +30,12 @@
 // domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits).
 // Work-groups are numbered heavy-first (the last position blocks see the most keys);
 // the 32 blocks an XCD runs at a time are adjacent blocks of one pair, so the kept keys
-// they all read come from that XCD's L2, and the pairs of an XCD mix KV heads (the kept
-// fraction differs between heads).
+// they all read come from that XCD's L2; an XCD finishes a pair before the next, and
+// consecutive runs walk the kept keys in opposite directions, so a run starts on what
+// the previous run left in L2.  Query rows (read once) are loaded and outputs (written
+// once) stored non-temporally, so they do not evict the shared keys; outputs are staged
+// through LDS first so that every store covers whole lines.  The pairs of an XCD mix KV
+// heads (the kept fraction differs between heads).
 #include "kvp_internal.h"
 
 namespace kvp {
@@ -74,11 +78,13 @@ struct PfTile {
   int valid;   // valid slots in [0, 64]
 };
 
-__device__ __forceinline__ PfTile pf_tile(int tau, int ntp, int nk, int lo64, int hi) {
+// Tile tau of a work-group's sequence: the ntp prefix tiles (walked from the last one
+// down when rev is set), then the band tiles in ascending order.
+__device__ __forceinline__ PfTile pf_tile(int tau, int ntp, int nk, int lo64, int hi, int rev) {
   PfTile t;
   if (tau < ntp) {
     t.prefix = 1;
-    t.base = tau * PF_KT;
+    t.base = (rev ? ntp - 1 - tau : tau) * PF_KT;
     t.valid = min(PF_KT, nk - t.base);
   } else {
     t.prefix = 0;
@@ -176,13 +182,17 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   // Work-group -> (pair, block).  Work-groups are dispatched round-robin over the 8
   // XCDs (blockIdx % 8); an XCD's work-groups are taken in runs of PF_GS (one per CU),
   // each run = PF_GS adjacent position blocks of one pair, so the blocks that read the
-  // same kept keys at the same time sit on one XCD and share them through its L2.
-  // Runs go heavy-first (the last position blocks see the most keys) and cycle over the
-  // XCD's pairs.  Pair slots enumerate batch rows fastest: the kept fraction varies from
-  // head to head (one threshold for all), and an XCD must not inherit one head's load.
+  // same kept keys at the same time sit on one XCD and share them through its L2.  An
+  // XCD runs all runs of one pair, heavy-first (the last position blocks see the most
+  // keys), before the next pair, and consecutive runs walk the kept prefix in opposite
+  // directions: a run starts on the keys the previous run read last, which its L2 still
+  // holds.  Pair slots enumerate batch rows fastest: the kept fraction varies from head
+  // to head (one threshold for all), and an XCD must not inherit one head's load.
   const int x = blockIdx.x % a.nx, k = blockIdx.x / a.nx;
   const int grp = k / PF_GS, j = k % PF_GS;
-  const int pi = grp % a.per_x, bgi = grp / a.per_x;
+  const int runs = (a.nblk + PF_GS - 1) / PF_GS;
+  const int pi = grp / runs, bgi = grp % runs;
+  const int rev = bgi & 1;
   const int blk_raw = bgi * PF_GS + j;
   if (blk_raw >= a.nblk) return;  // padding of the last run (uniform per work-group)
   const int slot = pi * a.nx + x;
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (qi[c] < T) x = *reinterpret_cast<const u32x4*>(qrow + 8 * (4 * kk + G));
+      if (qi[c] < T) x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(qrow + 8 * (4 * kk + G)));
       qf[c][kk] = as_bf16x8(x);
     }
   }
@@ -254,29 +264,29 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   // step before the previous barrier.
   PfRegs<D> R0, R1;
   int pos[KG];
-  pf_positions<D>(a, kidx, pf_tile(0, ntp, nk, lo64, hi), s0, pos);
+  pf_positions<D>(a, kidx, pf_tile(0, ntp, nk, lo64, hi, rev), s0, pos);
   pf_load<D>(kp, vp, dc, pos, R0);
   if (ntiles > 1) {
-    pf_positions<D>(a, kidx, pf_tile(1, ntp, nk, lo64, hi), s0, pos);
+    pf_positions<D>(a, kidx, pf_tile(1, ntp, nk, lo64, hi, rev), s0, pos);
     pf_load<D>(kp, vp, dc, pos, R1);
   }
   pf_store<D>(kbuf[0], vbuf[0], dc, s0, R0);
   if (ntiles > 2) {
-    pf_positions<D>(a, kidx, pf_tile(2, ntp, nk, lo64, hi), s0, pos);
+    pf_positions<D>(a, kidx, pf_tile(2, ntp, nk, lo64, hi, rev), s0, pos);
     pf_load<D>(kp, vp, dc, pos, R0);
-    if (ntiles > 3) pf_positions<D>(a, kidx, pf_tile(3, ntp, nk, lo64, hi), s0, pos);
+    if (ntiles > 3) pf_positions<D>(a, kidx, pf_tile(3, ntp, nk, lo64, hi, rev), s0, pos);
   }
   __syncthreads();
 
   const int slotA = 8 * (n >> 2) + (n & 3);
   // Rn holds tile tau + 1 (when there is one)
   auto step = [&](int tau, PfRegs<D>& Rn) {
-    const PfTile tl = pf_tile(tau, ntp, nk, lo64, hi);
+    const PfTile tl = pf_tile(tau, ntp, nk, lo64, hi, rev);
     if (tau + 1 < ntiles) {
       pf_store<D>(kbuf[(tau + 1) & 1], vbuf[(tau + 1) & 1], dc, s0, Rn);
       if (tau + 3 < ntiles) {
         pf_load<D>(kp, vp, dc, pos, Rn);
-        if (tau + 4 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 4, ntp, nk, lo64, hi), s0, pos);
+        if (tau + 4 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 4, ntp, nk, lo64, hi, rev), s0, pos);
       }
     }
     const uint16_t* const ks = kbuf[tau & 1];
@@ -392,18 +402,35 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
     if (tau + 1 < ntiles) step(tau + 1, R0);
   }
 
-  // normalise and store: lane (n, G) holds d = 16 t + 4 G + (0..3) of its column's row
+  // Normalise and store.  Lane (n, G) holds d = 16 t + 4 G + (0..3) of row n of its
+  // column tile; the tile's 16 rows are consecutive positions of one head, i.e. one
+  // contiguous 16 x D block of the output.  Each wave passes the block through its own
+  // LDS rows (padded by 16 bytes against bank conflicts) and writes it as whole lines
+  // with non-temporal stores, which keeps the outputs out of L2 (where the kept keys are
+  // shared) without the partial-line writes of storing the MFMA layout directly.
+  constexpr int OSTR = D * 4 + 16;  // bytes per staged row
+  char* const ost = reinterpret_cast<char*>(pf_lds) + wid * 16 * OSTR;
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
     float lt = l[c];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (qi[c] < T) {
-      float* orow = a.out + (((int64_t)b * a.Hq + hq[c]) * T + qi[c]) * D + 4 * G;
 #pragma unroll
-      for (int t = 0; t < D / 16; ++t) *reinterpret_cast<f32x4*>(orow + 16 * t) = o[t][c] * inv;
+    for (int t = 0; t < D / 16; ++t)
+      *reinterpret_cast<f32x4*>(ost + n * OSTR + (16 * t + 4 * G) * 4) = o[t][c] * inv;
+    __syncthreads();
+    const int r0 = 32 * wid + 16 * c;
+    const int qrow0 = i0 + r0 % a.pb;  // position of row 0 of the block
+    float* const oblk = a.out + (((int64_t)b * a.Hq + hq[c]) * T + qrow0) * D;
+#pragma unroll
+    for (int i = 0; i < 16 * D * 4 / 1024; ++i) {
+      const int k = lane + 64 * i;  // 16-byte chunk of the block
+      const int row = k / (D / 4), col = k % (D / 4);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ost + row * OSTR + col * 16);
+      if (qrow0 + row < T) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(oblk + 4 * k));
     }
+    __syncthreads();
   }
 }
 
@@ -435,7 +462,10 @@ kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, 
   a.per_x = a.num_pairs / a.nx;
   const int64_t grid = (int64_t)a.nx * a.per_x * cdiv(a.nblk, PF_GS) * PF_GS;
   if (grid > 0x7fffffff) return KVP_E_UNSUPPORTED;
-  const size_t lds = 4 * (size_t)PF_KT * d * sizeof(uint16_t) + PF_WAVES * sizeof(int);
+  // tile buffers + reduction slots; at the end each wave stages 16 output rows there
+  const size_t lds_tiles = 4 * (size_t)PF_KT * d * sizeof(uint16_t) + PF_WAVES * sizeof(int);
+  const size_t lds_out = (size_t)PF_WAVES * 16 * (d * 4 + 16);
+  const size_t lds = lds_tiles > lds_out ? lds_tiles : lds_out;
   if (d == 128) prefill_attn_kernel<128><<<(unsigned)grid, PF_THREADS, lds, stream>>>(a);
   else prefill_attn_kernel<64><<<(unsigned)grid, PF_THREADS, lds, stream>>>(a);
   KVP_LAUNCH_CHECK();
