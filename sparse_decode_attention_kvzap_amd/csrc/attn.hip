@@ -39,11 +39,11 @@ namespace kvp {
 
 constexpr int ATTN_WG_WAVES = 4;
 constexpr int ATTN_GRID = 256;  // one work-group (4 waves) per CU on a 256-CU part
-// int4 pools run two work-groups per CU (two waves per SIMD): a 32-token step of int4
-// codes moves a quarter of a bf16 step's bytes but costs more instructions (nibble
-// decode, the offset terms), and one wave per SIMD leaves its MFMA/VALU latencies
-// exposed (measured on the BeaconKV int4 cache: 194 -> 171 us).  Every other cache keeps
-// one wave per SIMD (the bf16 and int8 streams ran 1-4% slower with two).
+// int4 and fp8 pools run two work-groups per CU (two waves per SIMD): a 32-token step of
+// their codes costs more instructions than the bytes it moves (nibble decode and offset
+// terms; the E4M3 -> bf16 rebuild), and one wave per SIMD leaves its MFMA/VALU latencies
+// exposed (measured on the BeaconKV cache: int4 194 -> 171 us, fp8 297 -> 255 us).  Every
+// other cache keeps one wave per SIMD (the bf16 and int8 streams ran 1-4% slower with two).
 constexpr int ATTN_MAX_WPE = 2;
 constexpr int ATTN_MAX_NWAVES = ATTN_MAX_WPE * ATTN_GRID * ATTN_WG_WAVES;
 // Register sets of code-pool loads in flight per wave (two 32-token steps): more sets
@@ -1384,7 +1384,7 @@ static kvp_status launch_attn(const void* q, int B, int Hq, const kvp_paged_kv* 
   if (f32) {
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, true, false, 1>), g1, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, true, false, 1>), g1, b, lds, stream, a);
-  } else if (lp && kv->lp_bits == 4) {
+  } else if (lp && (kv->lp_bits == KVP_LP_INT4 || kv->lp_bits == KVP_LP_FP8_E4M3)) {
     a.nw = 2 * ATTN_GRID * ATTN_WG_WAVES;
     if (a.D == 64) hipLaunchKernelGGL((decode_attn_kernel<64, false, true, 2>), g2, b, lds, stream, a);
     else hipLaunchKernelGGL((decode_attn_kernel<128, false, true, 2>), g2, b, lds, stream, a);

@@ -6,8 +6,8 @@ Shapes cover every supported head ratio (g = 1, 2, 4, 8), both head dims, ragged
 (tails of the 64-key tiles and of the 128 / g position blocks), W = 0 (rows that see
 nothing), W > T (plain causal attention), nothing or everything kept, keep bits set
 past T, outlier keys (peaked softmax), the selection written by kvp_select for the
-KVzap and DMS rules, and the full qwen3-8B-like layer shape on sampled rows.
-Tolerance: max-abs 2e-3 (bf16 K/V).
+KVzap and DMS rules, V values beyond fp16's range, and the full qwen3-8B-like layer
+shape on sampled rows.  Tolerance: max-abs 2e-3 (bf16 K/V).
 """
 import numpy as np
 import pytest
@@ -96,10 +96,37 @@ def test_prefill_attn(K, B, Hq, Hkv, T, d, window, keepfrac, outl):
     out = run(K, q, k, v, bits, idx, window)
     ref = oracle.prefill_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T), window,
                                    oracle.sm_scale(d))
-    check_attention(out, ref, torch.bfloat16)
+    err = check_attention(out, ref, torch.bfloat16)
+    print(f"prefill B{B} Hq{Hq} Hkv{Hkv} T{T} d{d} W{window}: max-abs error {err:.2e}")
     # deterministic
     out2 = run(K, q, k, v, bits, idx, window)
     assert torch.equal(out, out2)
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_prefill_attn_large_values(K, d):
+    """A pair whose V holds magnitudes at and beyond 2^16 (past the fp16 range, so a
+    product in fp16 would overflow): its outputs stay finite and within 2e-3 + 2^-14
+    max|v| of the oracle (the error of P's ~16 significant bits scales with |v|); the
+    other pair keeps the plain 2e-3 bar."""
+    B, Hq, Hkv, T, window = 1, 8, 2, 900, 128
+    rng = np.random.default_rng(31 + d)
+    keep = rng.random((B * Hkv, T)) < 0.3
+    q, k, v = inputs(B, Hq, Hkv, T, d, 4242 + d)
+    big = torch.tensor([70000.0, -131072.0, 65536.0, 3.0e5], dtype=torch.bfloat16, device=DEV)
+    pos = torch.tensor([5, 300, 301, 811], device=DEV)
+    v[0, 1, pos, 7] = big
+    bits, idx = pack_bits(keep), kept_list(keep)
+    out = run(K, q, k, v, bits, idx, window)
+    assert torch.isfinite(out).all()
+    ref = oracle.prefill_attention(f64(q), f64(k), f64(v), keep.reshape(B, Hkv, T), window,
+                                   oracle.sm_scale(d))
+    g = Hq // Hkv
+    err = np.abs(out.double().cpu().numpy() - ref)
+    assert err[:, :g].max() <= 2e-3, err[:, :g].max()
+    vmax = float(v[0, 1].abs().max())
+    assert vmax >= 65536
+    assert err[:, g:].max() <= 2e-3 + 2.0 ** -14 * vmax, err[:, g:].max()
 
 
 @pytest.mark.parametrize("rule", ["kvzap", "dms"])
