@@ -33,6 +33,7 @@
 // looks two segments ahead: the next segments' block-table entries are requested while
 // the current one streams and the next pair's queries with its first K, so crossing from
 // one pair to the next costs no memory round trip.
+#include "small_gemm.h"
 #include "step_core.h"
 
 namespace kvp {
@@ -69,6 +70,11 @@ struct AttnArgs {
   // is one more virtual page of its pair -- and the merge kernel then applies the step.
   int fstep;
   StepArgs st;
+  // Fused decode step with the MLP scorer (fgemm = 1): the split-K slices of the new
+  // tokens' first layer, taken by waves 1..3 of every work-group while wave 0 builds the
+  // plan; the merge kernel's step waves add them up (st.part = gm.part).
+  int fgemm;
+  SmallGemm gm;
 };
 
 // -------------------------------------------------------------------------------
@@ -1187,7 +1193,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     fs.rp = slot / PAGE;
     fs.rs = slot % PAGE;
   }
-  if (wid == 0) compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
+  if (wid == 0) {
+    compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
+  } else if constexpr (!F32 && !LP) {
+    if (a.fgemm)
+      small_gemm_slices(a.gm, blockIdx.x * (ATTN_WG_WAVES - 1) + wid - 1, gridDim.x * (ATTN_WG_WAVES - 1));
+  }
   __syncthreads();
   // the merge kernel reads the prefix (and the position) from here
   if (blockIdx.x == 0) {
@@ -1356,10 +1367,12 @@ extern "C" size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t 
 
 static kvp_status launch_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv, const kvp_ring* ring,
                               float sm_scale, float* out, void* ws, hipStream_t stream,
-                              const StepArgs* fused) {
+                              const StepArgs* fused, const SmallGemm* gm = nullptr) {
   AttnArgs a;
   a.fstep = fused != nullptr;
   if (fused) a.st = *fused;
+  a.fgemm = gm != nullptr;
+  if (gm) a.gm = *gm;
   a.q = q;
   a.out = out;
   a.B = B;
@@ -1413,13 +1426,17 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
 // The fused decode step: the delayed step's arguments (scores from s_in, or from the
 // scorer: x_new for a linear one, the split-K partial sums in part for an MLP) and the
 // attention, in the stream kernel plus the merge kernel.
-kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, const float* part,
+kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, float* part,
                                   const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                   const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
                                   const float* tau, int* pos, const void* q, int B, int Hq,
                                   float sm_scale, float* out, void* ws, hipStream_t stream) {
   const StepArgs st = make_step_args(kv, ring, k_new, v_new, s_in, ld_s, 0.0f, tau, 0, pos, sc, x_new,
                                      s_out, part);
+  if (sc && sc->kind == KVP_SCORER_MLP) {
+    const SmallGemm gm = small_gemm_of(sc, x_new, st.ntok, sc->inner, part);
+    return launch_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream, &st, &gm);
+  }
   return launch_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream, &st);
 }
 

@@ -30,7 +30,7 @@ kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hid
 kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_kv* kv,
                                   const kvp_ring* ring, float sm_scale, float* out, void* ws,
                                   size_t ws_bytes, hipStream_t stream);
-kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, const float* part,
+kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, float* part,
                                   const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                   const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
                                   const float* tau, int* pos, const void* q, int B, int Hq,
@@ -302,7 +302,7 @@ extern "C" kvp_status kvp_decode_step(const kvp_scorer* sc, const void* hidden_n
   // the new token's K row and V values are read in 16-byte pieces
   if (((uintptr_t)k_new | (uintptr_t)v_new) & 15) return KVP_E_ARG;
   const int Hkv = kv->num_pairs / B;
-  const float* part = nullptr;
+  float* part = nullptr;
   if (!sc) {
     if (!s_in || ld_s < 1) return KVP_E_ARG;
   } else {
@@ -328,8 +328,7 @@ extern "C" kvp_status kvp_decode_step(const kvp_scorer* sc, const void* hidden_n
     float* pws = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) +
                                           align256(kvp_decode_attn_workspace_size(B, Hq, kv->num_pairs,
                                                                                   kv->head_dim)));
-    if ((st = kvp_launch_score_small_partials(sc, hidden_new, B, pws, stream)) != KVP_OK) return st;
-    part = pws;
+    part = pws;  // written by the attention's stream kernel, summed by its merge kernel
   }
   return kvp_launch_decode_step(sc, sc ? hidden_new : nullptr, part, kv, ring, k_new, v_new,
                                 sc ? nullptr : s_in, ld_s, s_out, tau, pos, q, B, Hq, sm_scale, out, ws,

@@ -20,6 +20,7 @@
 //                      term.  Each 256-unit slice writes a partial score; a small finish
 //                      kernel adds the slices in a fixed order plus b2.
 #include "kvp_internal.h"
+#include "small_gemm.h"
 
 namespace kvp {
 
@@ -428,62 +429,13 @@ __global__ __launch_bounds__(256) void score_mlp_finish_kernel(const float* __re
 }
 
 // ------------------------------------------------------------------ small batches
-// Decode steps score only a handful of tokens (one per sequence).  The big-tile GEMM
-// would leave all but a few CUs idle and walk the whole K loop serially, so small
-// batches split K instead: wave (r, ks) contracts rows [16r, 16r+16) of W (zero past
-// `rows`) with every token over K slice ks (256 wide) on MFMA, straight from global
-// memory, into part[ks][token][row]; a per-token epilogue adds the slices in a fixed
-// order and finishes the scorer.
-constexpr int SMALL_MAX_TOK = 64;
-constexpr int SMALL_KSLICE = 256;
-
-// NTT = number of 16-token tiles.  Loads are unconditional (token rows clamped, rows of
-// W past `rows` read row 0 and are zeroed) so the compiler issues all of a wave's loads
-// before its MFMAs instead of waiting on each behind a branch.
+// Decode steps score only a handful of tokens (one per sequence): the first layer is
+// split over K (small_gemm.h), one slice per wave.
 template <int NTT>
-__global__ __launch_bounds__(256) void score_small_gemm_kernel(
-    const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, int rows, int ntok, int H,
-    int rtiles, int ksplit, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, n = lane & 15, j = lane >> 4;
+__global__ __launch_bounds__(256) void score_small_gemm_kernel(SmallGemm g) {
   const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (w >= rtiles * ksplit) return;
-  const int rt = w % rtiles, ks = w / rtiles;
-  const int row = rt * 16 + n;
-  const bool rv = row < rows;
-  const uint16_t* wr = W + (int64_t)(rv ? row : 0) * H + ks * SMALL_KSLICE + 8 * j;
-  const uint16_t* xr[NTT];
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int tok = min(tt * 16 + n, ntok - 1);
-    xr[tt] = X + (int64_t)tok * H + ks * SMALL_KSLICE + 8 * j;
-  }
-  constexpr int NK = SMALL_KSLICE / 32;
-  u32x4 wv[NK], xv[NK][NTT];
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    wv[kk] = *reinterpret_cast<const u32x4*>(wr + 32 * kk);
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) xv[kk][tt] = *reinterpret_cast<const u32x4*>(xr[tt] + 32 * kk);
-  }
-  f32x4 acc[NTT];
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) acc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kk = 0; kk < NK; ++kk) {
-    const u32x4 wk = rv ? wv[kk] : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int tt = 0; tt < NTT; ++tt) acc[tt] = mfma16x16x32(as_bf16x8(wk), as_bf16x8(xv[kk][tt]), acc[tt]);
-  }
-  // acc[tt][i] = C[row 16rt + 4j + i][token 16tt + n]
-  const int rpad = rtiles * 16;
-#pragma unroll
-  for (int tt = 0; tt < NTT; ++tt) {
-    const int tok = tt * 16 + n;
-    if (tok < ntok) {
-      float* dst = part + ((int64_t)ks * ntok + tok) * rpad + rt * 16 + 4 * j;
-      *reinterpret_cast<f32x4*>(dst) = acc[tt];
-    }
-  }
+  if (w >= g.rtiles * g.ksplit) return;
+  small_gemm_slice<NTT>(g, w);
 }
 
 // K slices are summed in a fixed order; loads of absent slices (ks >= ksplit) read the
@@ -574,18 +526,32 @@ bool kvp_score_small_mlp_ok(const kvp_scorer* sc, int ntok) {
   return sc->kind == KVP_SCORER_MLP && small_path(sc, ntok) && sc->inner % 256 == 0;
 }
 
+SmallGemm kvp::small_gemm_of(const kvp_scorer* sc, const void* hidden, int ntok, int rows, float* part) {
+  SmallGemm g;
+  g.x = reinterpret_cast<const uint16_t*>(hidden);
+  g.w = reinterpret_cast<const uint16_t*>(sc->w1);
+  g.part = part;
+  g.rows = rows;
+  g.ntok = ntok;
+  g.H = sc->hidden;
+  g.rtiles = cdiv(rows, 16);
+  g.ksplit = sc->hidden / SMALL_KSLICE;
+  return g;
+}
+
+static void launch_small_gemm(const SmallGemm& g, hipStream_t stream) {
+  const dim3 grid(cdiv(g.rtiles * g.ksplit, 4)), b(256);
+  switch (cdiv(g.ntok, 16)) {
+    case 1: hipLaunchKernelGGL(score_small_gemm_kernel<1>, grid, b, 0, stream, g); break;
+    case 2: hipLaunchKernelGGL(score_small_gemm_kernel<2>, grid, b, 0, stream, g); break;
+    case 3: hipLaunchKernelGGL(score_small_gemm_kernel<3>, grid, b, 0, stream, g); break;
+    default: hipLaunchKernelGGL(score_small_gemm_kernel<4>, grid, b, 0, stream, g); break;
+  }
+}
+
 kvp_status kvp_launch_score_small_partials(const kvp_scorer* sc, const void* hidden, int ntok,
                                            float* part, hipStream_t stream) {
-  const int H = sc->hidden, ksplit = H / SMALL_KSLICE, rows = sc->inner, rtiles = cdiv(rows, 16);
-  const uint16_t* xh = reinterpret_cast<const uint16_t*>(hidden);
-  const uint16_t* w1 = reinterpret_cast<const uint16_t*>(sc->w1);
-  const dim3 g(cdiv(rtiles * ksplit, 4));
-  switch (cdiv(ntok, 16)) {
-    case 1: hipLaunchKernelGGL(score_small_gemm_kernel<1>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-    case 2: hipLaunchKernelGGL(score_small_gemm_kernel<2>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-    case 3: hipLaunchKernelGGL(score_small_gemm_kernel<3>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-    default: hipLaunchKernelGGL(score_small_gemm_kernel<4>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-  }
+  launch_small_gemm(small_gemm_of(sc, hidden, ntok, sc->inner, part), stream);
   KVP_LAUNCH_CHECK();
   return KVP_OK;
 }
@@ -597,18 +563,8 @@ kvp_status kvp_launch_score(const kvp_scorer* sc, const void* hidden, int B, int
   if (small_path(sc, ntok)) {
     const int ksplit = H / SMALL_KSLICE;
     const bool mlp = sc->kind == KVP_SCORER_MLP;
-    const int rows = mlp ? sc->inner : Hkv;
-    const int rtiles = cdiv(rows, 16);
     float* part = reinterpret_cast<float*>(ws);
-    const uint16_t* xh = reinterpret_cast<const uint16_t*>(hidden);
-    const uint16_t* w1 = reinterpret_cast<const uint16_t*>(sc->w1);
-    const dim3 g(cdiv(rtiles * ksplit, 4));
-    switch (cdiv(ntok, 16)) {
-      case 1: hipLaunchKernelGGL(score_small_gemm_kernel<1>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-      case 2: hipLaunchKernelGGL(score_small_gemm_kernel<2>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-      case 3: hipLaunchKernelGGL(score_small_gemm_kernel<3>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-      default: hipLaunchKernelGGL(score_small_gemm_kernel<4>, g, dim3(256), 0, stream, xh, w1, rows, ntok, H, rtiles, ksplit, part); break;
-    }
+    launch_small_gemm(small_gemm_of(sc, hidden, ntok, mlp ? sc->inner : Hkv, part), stream);
     KVP_LAUNCH_CHECK();
     if (mlp) {
       hipLaunchKernelGGL(score_small_mlp_epi_kernel, dim3(ntok), dim3(sc->inner), 0, stream, part, ksplit,
