@@ -348,10 +348,11 @@ size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
  * scores s_in[pair * ld_s]) followed by kvp_decode_attn with the same q: the cache, the
  * device position, the stored scores and s_out are bit-identical to that sequence's; out
  * agrees to fp32 rounding (the tokens are summed in another grouping).  The work runs in
- * the attention's two kernels (plus the MLP scorer's split-K first layer before them):
- * the streaming kernel reads the cache as the step will leave it (the token leaving its
- * ring slot counts iff it is retained; the new token is read from k_new/v_new) without
- * writing it, and the merge kernel applies the step.
+ * the attention's two kernels: the streaming kernel reads the cache as the step will
+ * leave it (the token leaving its ring slot counts iff it is retained; the new token is
+ * read from k_new/v_new) without writing it, and with an MLP scorer also computes the
+ * split-K partial sums of the new tokens' first layer; the merge kernel finishes the
+ * scores and applies the step.
  *   sc, hidden_new, hdtype  as kvp_score_step_delayed (sc->n_kv_heads = num_pairs / B), or
  *                sc == NULL: hidden_new unused, scores from s_in (ld_s >= 1)
  *   k_new, v_new [B*Hkv][d] bf16, 16-byte aligned; s_out NULL or [B*Hkv] fp32 (scorer)
