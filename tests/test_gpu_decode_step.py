@@ -81,6 +81,10 @@ def make_scorer(K, kind, H, inner, Hkv):
     ("mlp", 2, 4, 4, 128, 64, 250, 70, 0.0, 1024, 512, False),   # split-K MLP partials
     ("given", 4, 2, 8, 64, 48, 150, 60, 0.3, 0, 0, True),        # d 64, pairs with empty pools
     ("linear", 1, 8, 1, 64, 128, 400, 40, -0.1, 512, 0, False),  # g 1, ring of 128
+    # MLP slices taken inside the attention kernel: 40 tokens (three 16-token tiles) and
+    # 32 x 64 = 2048 slices of H 8192 / inner 1024, more than its waves (several each)
+    ("mlp", 40, 2, 2, 64, 32, 120, 20, 0.0, 8192, 1024, False),
+    ("mlp", 64, 1, 4, 128, 48, 160, 24, -0.2, 2048, 256, False),  # 64 tokens, inner 256
 ])
 def test_fused_step_matches_separate_calls(K, kind, B, Hkv, g, d, w, T0, steps, tau, H, inner,
                                            empty):
