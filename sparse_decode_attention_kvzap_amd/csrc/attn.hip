@@ -8,7 +8,7 @@
 // Work decomposition (split-K, evenly balanced), two kernels:
 //   Every pair (b, h_kv) contributes a "region A" of virtual pages (its pool pages,
 //   then its ring pages, padded to an even count) and, when a low-precision pool exists,
-//   a "region B" (its int8 or int4 pages, padded to even).  The A regions are
+//   a "region B" (its int8, int4 or fp8 pages, padded to even).  The A regions are
 //   concatenated into one page sequence and the B regions into another; each sequence
 //   is cut into one contiguous unit per wave.  A wave walks its units 32 tokens (two
 //   pages) at a time and writes one partial (max, sum, output) record per segment (the
@@ -19,6 +19,14 @@
 //   maintenance).  Record slot of segment (region s, unit u) = s + u: consecutive
 //   segments of a sequence advance s or u (or both), so slots are unique and a region's
 //   records are consecutive.
+//
+// Fused decode step (kvp_decode_step; DeInfer methodology (b): a fixed-address step
+// replayed from a graph): the stream kernel reads the cache as the delayed step will
+// leave it -- the token leaving the ring slot counts iff it is retained, the new token is
+// one more one-row virtual page -- without writing it; with an MLP scorer, waves 1..3 of
+// every work-group compute the split-K slices of the new tokens' first layer while wave 0
+// builds the plan; the merge kernel then finishes the scores and applies the step on
+// waves of its own, after every read of the ring is done.
 //
 // Per 32-token step (bf16, head dim D, g query heads of one KV head):
 //   S^T[32 tok x 16 heads] = K . Q^T on 16x16x32 bf16 MFMA (exact products, fp32
@@ -1424,8 +1432,9 @@ kvp_status kvp_launch_decode_attn(const void* q, int B, int Hq, const kvp_paged_
 }
 
 // The fused decode step: the delayed step's arguments (scores from s_in, or from the
-// scorer: x_new for a linear one, the split-K partial sums in part for an MLP) and the
-// attention, in the stream kernel plus the merge kernel.
+// scorer: x_new for a linear one; for an MLP, x_new's split-K first-layer slices, which
+// the stream kernel writes to part) and the attention, in the stream kernel plus the
+// merge kernel.
 kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, float* part,
                                   const kvp_paged_kv* kv, const kvp_ring* ring, const void* k_new,
                                   const void* v_new, const float* s_in, int64_t ld_s, float* s_out,
