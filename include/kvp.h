@@ -329,8 +329,10 @@ kvp_status kvp_score_step_delayed(const kvp_scorer* sc, const void* hidden_new, 
  * pages another), cut into one contiguous share per wave; each share is walked 32
  * tokens at a time and leaves one partial record per pair it touches; a second kernel
  * merges each pair's records in page order, so the output does not depend on timing
- * (bit-identical reruns).  Limits: num_pairs up to 13000 with a low-precision pool,
- * 20000 without (LDS plan; else KVP_E_UNSUPPORTED).
+ * (bit-identical reruns).  The split's page prefix lives in each work-group's LDS up to
+ * ~20000 pairs (~10000 with a low-precision pool); beyond that a third kernel (one
+ * work-group) writes it to the workspace first and the waves read it from there (slower
+ * per pair boundary, same results).
  * -------------------------------------------------------------------------- */
 kvp_status kvp_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t Hq,
                            const kvp_paged_kv* kv, const kvp_ring* ring, float sm_scale,
@@ -384,8 +386,8 @@ size_t kvp_decode_step_workspace_size(const kvp_scorer* sc, int32_t B, int32_t H
  *   Arguments, layouts, output and errors as kvp_decode_attn, and the same kernels, so
  *   the output is bit-identical to kvp_decode_attn's.  Additionally:
  *   KVP_E_WORKSPACE  kvp_decode_attn_workspace_size(B, Hq, num_pairs, head_dim) exceeds
- *                    KVP_NOALLOC_SCRATCH_BYTES (g = 4, d = 128 fits up to 14056 pairs,
- *                    g = 8 up to 6012, g = 16 up to 1984)
+ *                    KVP_NOALLOC_SCRATCH_BYTES (g = 4, d = 128 fits up to 14043 pairs,
+ *                    g = 8 up to 6009, g = 16 up to 1983)
  *   KVP_E_ARG        `stream` belongs to another device than the current one
  * The scratch is shared by every call on one GPU and keeps the last call's contents
  * (nothing in it needs to start at zero): calls that overlap in time on one GPU, on

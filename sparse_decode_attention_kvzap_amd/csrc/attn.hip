@@ -83,6 +83,10 @@ struct AttnArgs {
   // plan; the merge kernel's step waves add them up (st.part = gm.part).
   int fgemm;
   SmallGemm gm;
+  // Plan in global memory (gplan = 1, when P and Lens would not fit in LDS): written by
+  // decode_attn_plan_kernel before the stream kernel -- P[0..nseg] at plan, Lens at
+  // plan + nseg + 2 -- and read from there by every wave.
+  int gplan;
 };
 
 // -------------------------------------------------------------------------------
@@ -101,13 +105,12 @@ __device__ __forceinline__ int region_pages_of(int len, int extra) { return (cdi
 // Lens[s] says whether the token leaving pair s's ring slot `slot` is retained (its
 // position >= 0 and score >= tau), and each A region has one more page (the new token).
 constexpr int LEN_MASK = 0x7fffffff;
-__device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Lens, int nseg, int slot,
-                                             float tau) {
-  const int lane = threadIdx.x & 63;
+// Regions [s0, s1) of one thread: page counts to P[s + 1] (and pool lengths to Lens);
+// returns their sum.  Loads are requested eight regions at a time.
+__device__ __forceinline__ int plan_counts(const AttnArgs& a, int* P, int* Lens, int s0, int s1, int slot,
+                                           float tau) {
   const int np = a.kv.num_pairs;
   const int nring = a.has_ring ? a.ring.window / PAGE + a.fstep : 0;
-  const int per = cdiv(nseg, 64);
-  const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
   int sum = 0;
   for (int b = s0; b < s1; b += 8) {
     int v[8];
@@ -136,7 +139,11 @@ __device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Len
       }
     }
   }
-  int run = wave_incl_scan(sum) - sum;
+  return sum;
+}
+
+// Regions [s0, s1) of one thread: P[s + 1] = run + the counts up to s.
+__device__ __forceinline__ void plan_prefix(int* P, int s0, int s1, int run) {
   for (int b = s0; b < s1; b += 8) {
     int v[8];
 #pragma unroll
@@ -149,6 +156,15 @@ __device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Len
       }
     }
   }
+}
+
+__device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Lens, int nseg, int slot,
+                                             float tau) {
+  const int lane = threadIdx.x & 63;
+  const int per = cdiv(nseg, 64);
+  const int s0 = min(nseg, lane * per), s1 = min(nseg, s0 + per);
+  const int sum = plan_counts(a, P, Lens, s0, s1, slot, tau);
+  plan_prefix(P, s0, s1, wave_incl_scan(sum) - sum);
   if (lane == 0) P[0] = 0;
 }
 
@@ -1187,8 +1203,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   extern __shared__ int lds[];
   const int np = a.kv.num_pairs;
   const int nseg = plan_regions(a);
-  int* P = lds;
-  int* Lens = lds + nseg + 1;
+  int* P = a.gplan ? a.plan : lds;
+  int* Lens = a.gplan ? a.plan + nseg + 2 : lds + nseg + 1;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // fused step: the position being appended and the ring slot it turns over
   FStep fs{-1, 0};
@@ -1201,7 +1217,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     fs.rp = slot / PAGE;
     fs.rs = slot % PAGE;
   }
-  if (wid == 0) {
+  if (a.gplan) {
+    // the plan kernel wrote the plan; every wave may take first-layer slices
+    if constexpr (!F32 && !LP) {
+      if (a.fgemm) small_gemm_slices(a.gm, blockIdx.x * ATTN_WG_WAVES + wid, gridDim.x * ATTN_WG_WAVES);
+    }
+  } else if (wid == 0) {
     compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
   } else if constexpr (!F32 && !LP) {
     if (a.fgemm)
@@ -1209,7 +1230,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   }
   __syncthreads();
   // the merge kernel reads the prefix (and the position) from here
-  if (blockIdx.x == 0) {
+  if (!a.gplan && blockIdx.x == 0) {
     for (int s = threadIdx.x; s <= nseg; s += blockDim.x) a.plan[s] = P[s];
     if (threadIdx.x == 0) a.plan[nseg + 1] = p;
   }
@@ -1219,7 +1240,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
   const int gw = ((blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8) * ATTN_WG_WAVES + wid;
   const Plan pl = make_plan(P, np, gridDim.x * ATTN_WG_WAVES, LP);
   float* wlds = nullptr;
-  if constexpr (F32) wlds = reinterpret_cast<float*>(lds + 2 * nseg + 2) + wid * (16 * D + 16 * 32);
+  if constexpr (F32) wlds = reinterpret_cast<float*>(lds + (a.gplan ? 0 : 2 * nseg + 2)) + wid * (16 * D + 16 * 32);
   if constexpr (F32) {
     stream_segments<D, true, 8>(a, pl, false, gw, wlds);
   } else {
@@ -1229,6 +1250,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
       else if (a.kv.lp_bits == KVP_LP_FP8_E4M3) stream_segments<D, false, 8, true>(a, pl, true, gw, nullptr);
       else stream_segments<D, false, 8>(a, pl, true, gw, nullptr);
     }
+  }
+}
+
+// -------------------------------------------------------------------------------
+// Plan for caches whose P and Lens would not fit in LDS: one work-group computes them into
+// the workspace (and, for a fused step, the position the merge kernel applies), before
+// the stream kernel, whose waves then read them from global memory.
+// -------------------------------------------------------------------------------
+constexpr int PLAN_THREADS = 1024;
+__global__ __launch_bounds__(PLAN_THREADS) void decode_attn_plan_kernel(AttnArgs a) {
+  __shared__ int wsum[PLAN_THREADS / 64];
+  const int nseg = plan_regions(a);
+  int slot = 0, p = 0;
+  float tau = 0.f;
+  if (a.fstep) {
+    p = a.st.pos_dev[0];
+    tau = a.st.tau_dev[0];
+    slot = ((p % a.ring.window) + a.ring.window) % a.ring.window;
+  }
+  int* P = a.plan;
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int per = cdiv(nseg, PLAN_THREADS);
+  const int s0 = min(nseg, t * per), s1 = min(nseg, s0 + per);
+  const int sum = plan_counts(a, P, P + nseg + 2, s0, s1, slot, tau);
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += wsum[w];
+  plan_prefix(P, s0, s1, base + incl - sum);
+  if (t == 0) {
+    P[0] = 0;
+    P[nseg + 1] = p;
   }
 }
 
@@ -1360,7 +1414,9 @@ using namespace kvp;
 // Workspace: [plan: 2 num_pairs + 1 ints][records].  Record slots: per sequence, regions
 // + units (every segment is one (region, unit) pair and s + u is unique), for the
 // largest launch (two waves per SIMD).
-static size_t attn_plan_bytes(int num_pairs) { return (((size_t)(2 * num_pairs + 1) * sizeof(int)) + 255) & ~(size_t)255; }
+// Plan area: P[0..nseg] (nseg <= 2 num_pairs), the position, and Lens[num_pairs] when the
+// plan lives in global memory.
+static size_t attn_plan_bytes(int num_pairs) { return (((size_t)(3 * num_pairs + 2) * sizeof(int)) + 255) & ~(size_t)255; }
 static size_t attn_rec_floats(int g, int D) { return ((size_t)g * (D + 2) + 3) & ~(size_t)3; }
 static size_t attn_max_slots(int num_pairs) { return 2 * ((size_t)num_pairs + ATTN_MAX_NWAVES); }
 
@@ -1398,8 +1454,13 @@ static kvp_status launch_attn(const void* q, int B, int Hq, const kvp_paged_kv* 
   a.rec_floats = (int)attn_rec_floats(a.g, a.D);
   const bool f32 = kv->dtype == KVP_F32;
   const bool lp = kv->num_pages8 > 0;
-  const size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32, lp);
-  if (lds > 160 * 1024) return KVP_E_UNSUPPORTED;
+  size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32, lp);
+  a.gplan = lds > 160 * 1024;
+  if (a.gplan) {
+    lds = attn_lds_bytes(0, a.D, f32, lp) - 2 * sizeof(int);  // no plan in LDS
+    hipLaunchKernelGGL(decode_attn_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a);
+    KVP_LAUNCH_CHECK();
+  }
   const dim3 g1(ATTN_GRID), g2(ATTN_GRID * 2), b(256);
   a.nw = ATTN_GRID * ATTN_WG_WAVES;
   if (f32) {
@@ -1449,6 +1510,3 @@ kvp_status kvp_launch_decode_step(const kvp_scorer* sc, const void* x_new, float
   return launch_attn(q, B, Hq, kv, ring, sm_scale, out, ws, stream, &st);
 }
 
-size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32, bool lp) {
-  return attn_lds_bytes(num_pairs, D, f32, lp);
-}

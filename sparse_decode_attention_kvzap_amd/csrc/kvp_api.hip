@@ -40,7 +40,6 @@ kvp_status kvp_launch_prefill_attn(const void* q, const void* k, const void* v, 
                                    int window, float sm_scale, float* out, hipStream_t stream);
 kvp_status kvp_launch_reset(const kvp_paged_kv* kv, const kvp_ring* ring, hipStream_t stream);
 kvp_status kvp_launch_clear_error(const kvp_paged_kv* kv, hipStream_t stream);
-size_t kvp_attn_lds_bytes_host(int num_pairs, int D, bool f32, bool lp);
 
 namespace {
 
@@ -259,9 +258,6 @@ kvp_status check_decode_attn(const void* q, int32_t qdtype, int32_t B, int32_t H
   if (Hq / Hkv > 16) return KVP_E_UNSUPPORTED;
   if (qdtype != kv->dtype) return KVP_E_DTYPE;
   if (kv->num_pages8 > 0 && kv->dtype != KVP_BF16) return KVP_E_DTYPE;
-  if (kvp_attn_lds_bytes_host(kv->num_pairs, kv->head_dim, kv->dtype == KVP_F32, kv->num_pages8 > 0) >
-      160 * 1024)
-    return KVP_E_UNSUPPORTED;
   return KVP_OK;
 }
 
