@@ -90,8 +90,8 @@ struct AttnArgs {
 };
 
 // -------------------------------------------------------------------------------
-// Plan: page prefix P[] over the regions, computed by wave 0 of every work-group into
-// LDS (one load per region, one wave scan).
+// Plan: page prefix P[] over the regions, computed by every work-group into LDS (one load
+// per region, a wave or work-group scan).
 // -------------------------------------------------------------------------------
 __device__ __forceinline__ int plan_regions(const AttnArgs& a) {
   return (a.kv.num_pages8 > 0 ? 2 : 1) * a.kv.num_pairs;
@@ -166,6 +166,25 @@ __device__ __forceinline__ void compute_plan(const AttnArgs& a, int* P, int* Len
   const int sum = plan_counts(a, P, Lens, s0, s1, slot, tau);
   plan_prefix(P, s0, s1, wave_incl_scan(sum) - sum);
   if (lane == 0) P[0] = 0;
+}
+
+// The same plan by all NT threads of the work-group (every thread must call it): each
+// takes nseg / NT regions, so many pairs cost NT / 64 times fewer round trips.  wsum:
+// NT / 64 ints of LDS.
+template <int NT>
+__device__ __forceinline__ void compute_plan_wg(const AttnArgs& a, int* P, int* Lens, int nseg, int slot,
+                                                float tau, int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
+  const int per = cdiv(nseg, NT);
+  const int s0 = min(nseg, t * per), s1 = min(nseg, s0 + per);
+  const int sum = plan_counts(a, P, Lens, s0, s1, slot, tau);
+  const int incl = wave_incl_scan(sum);
+  if (lane == 63) wsum[wid] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wid; ++w) base += wsum[w];
+  plan_prefix(P, s0, s1, base + incl - sum);
+  if (t == 0) P[0] = 0;
 }
 
 // Largest s in [lo, hi) with P[s] <= x (P nondecreasing, P[lo] <= x): one LDS read and
@@ -1217,16 +1236,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
     fs.rp = slot / PAGE;
     fs.rs = slot % PAGE;
   }
+  __shared__ int wsum[ATTN_WG_WAVES];
   if (a.gplan) {
     // the plan kernel wrote the plan; every wave may take first-layer slices
     if constexpr (!F32 && !LP) {
       if (a.fgemm) small_gemm_slices(a.gm, blockIdx.x * ATTN_WG_WAVES + wid, gridDim.x * ATTN_WG_WAVES);
     }
-  } else if (wid == 0) {
-    compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
-  } else if constexpr (!F32 && !LP) {
-    if (a.fgemm)
+  } else if (a.fgemm) {
+    // wave 0 builds the plan while the other waves take first-layer slices
+    if (wid == 0) compute_plan(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau);
+    else if constexpr (!F32 && !LP)
       small_gemm_slices(a.gm, blockIdx.x * (ATTN_WG_WAVES - 1) + wid - 1, gridDim.x * (ATTN_WG_WAVES - 1));
+  } else {
+    compute_plan_wg<ATTN_WG_WAVES * 64>(a, P, Lens, nseg, fs.rp * PAGE + fs.rs, tau, wsum);
   }
   __syncthreads();
   // the merge kernel reads the prefix (and the position) from here
@@ -1269,21 +1291,8 @@ __global__ __launch_bounds__(PLAN_THREADS) void decode_attn_plan_kernel(AttnArgs
     tau = a.st.tau_dev[0];
     slot = ((p % a.ring.window) + a.ring.window) % a.ring.window;
   }
-  int* P = a.plan;
-  const int t = threadIdx.x, lane = t & 63, wid = t >> 6;
-  const int per = cdiv(nseg, PLAN_THREADS);
-  const int s0 = min(nseg, t * per), s1 = min(nseg, s0 + per);
-  const int sum = plan_counts(a, P, P + nseg + 2, s0, s1, slot, tau);
-  const int incl = wave_incl_scan(sum);
-  if (lane == 63) wsum[wid] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wid; ++w) base += wsum[w];
-  plan_prefix(P, s0, s1, base + incl - sum);
-  if (t == 0) {
-    P[0] = 0;
-    P[nseg + 1] = p;
-  }
+  compute_plan_wg<PLAN_THREADS>(a, a.plan, a.plan + nseg + 2, nseg, slot, tau, wsum);
+  if (threadIdx.x == 0) a.plan[nseg + 1] = p;
 }
 
 // -------------------------------------------------------------------------------
@@ -1455,7 +1464,7 @@ static kvp_status launch_attn(const void* q, int B, int Hq, const kvp_paged_kv* 
   const bool f32 = kv->dtype == KVP_F32;
   const bool lp = kv->num_pages8 > 0;
   size_t lds = attn_lds_bytes(kv->num_pairs, a.D, f32, lp);
-  a.gplan = lds > 160 * 1024;
+  a.gplan = lds > 160 * 1024 - 64;  // room for the kernel's static LDS
   if (a.gplan) {
     lds = attn_lds_bytes(0, a.D, f32, lp) - 2 * sizeof(int);  // no plan in LDS
     hipLaunchKernelGGL(decode_attn_plan_kernel, dim3(1), dim3(PLAN_THREADS), 0, stream, a);
