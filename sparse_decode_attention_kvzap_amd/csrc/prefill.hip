@@ -27,7 +27,9 @@
 // products, fp32 accumulation), with the K rows of the two 16-row MFMA tiles
 // interleaved so each lane holds the scores of 8 consecutive keys of one query row --
 // the B-operand layout of the P.V product that follows.  Online softmax in fp32 (log2
-// domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits).
+// domain); O^T += V^T P^T with P split into bf16 hi + lo parts (~16 significant bits),
+// both column tiles' P first so that each V^T fragment is read from LDS once for both
+// (LDS reads are what the kernel shares its time with the matrix pipe on).
 // Work-groups are numbered heavy-first (the last position blocks see the most keys);
 // the 32 blocks an XCD runs at a time are adjacent blocks of one pair, so the kept keys
 // they all read come from that XCD's L2; an XCD finishes a pair before the next, and
@@ -336,6 +338,9 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
         }
       }
 
+      // probabilities of both column tiles, then O^T += V^T P^T with each V^T fragment
+      // read from LDS once for both
+      bf16x8 phi[2], plo[2];
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         float sv[8];
@@ -383,15 +388,18 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
           ph[w] = hl[0];
           pl[w] = hl[1];
         }
-        const bf16x8 phi = as_bf16x8(ph), plo = as_bf16x8(pl);
-        // O^T += V^T P^T for this column tile
+        phi[cc] = as_bf16x8(ph);
+        plo[cc] = as_bf16x8(pl);
+      }
 #pragma unroll
-        for (int t = 0; t < D / 16; ++t) {
-          const int d = 16 * t + n;
-          const bf16x8 vf =
-              as_bf16x8(*reinterpret_cast<const u32x4*>(vt + d * PF_KT + 8 * ((4 * ch + G) ^ v_swz(d))));
-          o[t][cc] = mfma16x16x32(vf, phi, o[t][cc]);
-          o[t][cc] = mfma16x16x32(vf, plo, o[t][cc]);
+      for (int t = 0; t < D / 16; ++t) {
+        const int d = 16 * t + n;
+        const bf16x8 vf =
+            as_bf16x8(*reinterpret_cast<const u32x4*>(vt + d * PF_KT + 8 * ((4 * ch + G) ^ v_swz(d))));
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          o[t][cc] = mfma16x16x32(vf, phi[cc], o[t][cc]);
+          o[t][cc] = mfma16x16x32(vf, plo[cc], o[t][cc]);
         }
       }
     }
