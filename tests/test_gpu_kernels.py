@@ -101,13 +101,16 @@ def test_score_linear_bf16(K, B, T, H, Hkv, ld):
         assert torch.isnan(s[..., T:]).all()  # padding untouched
 
 
-@pytest.mark.parametrize("B,T,H,inner,Hkv", [(2, 300, 256, 512, 8), (1, 513, 128, 256, 4),
-                                             (3, 17, 64, 512, 16), (16, 1, 4096, 512, 8),
-                                             (5, 3, 512, 256, 3), (64, 1, 1024, 1024, 16)])
-def test_score_mlp_bf16(K, B, T, H, inner, Hkv):
+@pytest.mark.parametrize("B,T,H,inner,Hkv,bias", [
+    (2, 300, 256, 512, 8, True), (1, 513, 128, 256, 4, True), (3, 17, 64, 512, 16, True),
+    (16, 1, 4096, 512, 8, True), (5, 3, 512, 256, 3, True), (64, 1, 1024, 1024, 16, True),
+    (2, 77, 192, 768, 1, False),   # three K stages (the fewest with W2 / b1 staged in LDS), no bias
+    (1, 300, 320, 256, 16, True),  # 16 heads: every W2 copy block holds a row
+    (2, 200, 192, 256, 5, True)])
+def test_score_mlp_bf16(K, B, T, H, inner, Hkv, bias):
     x = seeded((B, T, H), 11, torch.bfloat16)
     W1 = seeded((inner, H), 12, torch.bfloat16, 1 / math.sqrt(H))
-    b1 = seeded((inner,), 13, scale=0.5)
+    b1 = seeded((inner,), 13, scale=0.5) if bias else None
     W2 = seeded((Hkv, inner), 14, scale=1 / math.sqrt(inner))
     b2 = seeded((Hkv,), 15)
     sc = K.Scorer(K.KVP_SCORER_MLP, W1, b1, W2, b2)
@@ -117,7 +120,7 @@ def test_score_mlp_bf16(K, B, T, H, inner, Hkv):
     s2 = torch.full((B, Hkv, T), float("nan"), device=DEV)
     K.kvp_score(sc, x, s2, ws)
     assert torch.equal(s, s2)  # deterministic
-    ref = oracle.score_mlp(f64(x), f64(W1), f64(b1), f64(W2), f64(b2))
+    ref = oracle.score_mlp(f64(x), f64(W1), f64(b1) if bias else None, f64(W2), f64(b2))
     err = np.abs(s.cpu().double().numpy() - ref).max()
     assert err < SCORE_ATOL, err
 
