@@ -268,6 +268,27 @@ def decode_run(ctx, q_keep, steps, warmup, stream, graph=False):
         assert ctx.cache.check(stream) == 0, "pool overflow"
         r["graph_ms_per_step"] = e0.elapsed_time(e1) / steps
         del g
+        # eight consecutive decode steps captured as one graph: the GPU's idle time before
+        # each replay (the same for any graph here) is paid once per eight steps
+        G = 8
+        reps = max(1, min(steps, 48) // G)
+        g8 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g8, stream=side):
+            for _ in range(G):
+                ctx.step(side)
+        torch.cuda.synchronize()
+        ctx.compress(q_keep, stream)
+        with torch.cuda.stream(stream):
+            g8.replay()
+            e0, e1 = new_event(), new_event()
+            e0.record(stream)
+            for _ in range(reps):
+                g8.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert ctx.cache.check(stream) == 0, "pool overflow"
+        r["graph8_ms_per_step"] = e0.elapsed_time(e1) / (reps * G)
+        del g8
     return r
 
 
@@ -599,6 +620,35 @@ def dms_loop(dev, stream):
     assert cache.check(stream) == 0
     same = bool(torch.equal(cache.out, out_fused))
     del graph
+    # 4. eight consecutive steps captured as one graph, each reading its slot of fixed
+    #    buffers that hold eight steps' inputs (refilled by four copies before each
+    #    replay, counted in its time): the GPU's idle time before a replay is paid once
+    #    per eight steps
+    G = 8
+    bufs = [torch.empty((G,) + tuple(X.shape[1:]), dtype=X.dtype, device=dev)
+            for X in (H_all, K_all, V_all, Q_all)]
+    prefill()
+    torch.cuda.synchronize()
+    graph8 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph8, stream=side):
+        for k in range(G):
+            cache.step(*(b[k] for b in bufs), stream=side)
+    torch.cuda.synchronize()
+    prefill()
+    torch.cuda.synchronize()
+    e0, e1 = new_event(), new_event()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for r8 in range(S // G):
+            for b, X in zip(bufs, (H_all, K_all, V_all, Q_all)):
+                b.copy_(X[r8 * G:(r8 + 1) * G])
+            graph8.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph8_ms = e0.elapsed_time(e1) * S / (G * (S // G))
+    assert cache.check(stream) == 0
+    same8 = bool(torch.equal(cache.out, out_fused)) if S % G == 0 else None
+    del graph8, bufs
     # the decode attention alone, back to back on the cache the loop left (the last step's
     # token-heads)
     for _ in range(2):
@@ -616,11 +666,12 @@ def dms_loop(dev, stream):
     r = {"workload": wl.name, "batch": B, "prompt": P0, "decode_steps": S, "delay_window": wl.w,
          "tau": wl.fixed_tau, "dtype": dtype_name(wl.kv_dtype),
          "eager_ms_per_step": eager_ms / S, "separate_calls_ms_per_step": separate_ms / S,
-         "graph_ms_per_step": graph_ms / S,
+         "graph_ms_per_step": graph_ms / S, "graph8_ms_per_step": graph8_ms / S,
          "token_heads_per_s_eager": th / (eager_ms * 1e-3),
          "token_heads_per_s_graph": th / (graph_ms * 1e-3),
+         "token_heads_per_s_graph8": th / (graph8_ms * 1e-3),
          "fused_vs_separate_max_abs": fused_vs_separate,
-         "graph_output_equals_eager": same,
+         "graph_output_equals_eager": same, "graph8_output_equals_eager": same8,
          "attn": {"ms": attn_ms, "bytes_per_call": last_bytes, "token_heads": visible[-1],
                   "gbs": achieved, "frac_of_peak": achieved / PEAK_HBM_GBS,
                   "token_heads_per_s": visible[-1] / (attn_ms * 1e-3),
@@ -630,9 +681,11 @@ def dms_loop(dev, stream):
                  "folded into the attention's stream and merge kernels) on that step's inputs "
                  "in place; separate_calls = kvp_score_step_delayed then kvp_decode_attn; the "
                  "graph holds the decode step and reads fixed buffers, refilled before each "
-                 "replay (4 small copies per step, in its time)"}
+                 "replay (4 small copies per step, in its time); graph8 holds eight steps, "
+                 "their inputs refilled by 4 copies per replay"}
     log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step (separate calls "
-        f"{separate_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step; attention "
+        f"{separate_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step, eight steps per "
+        f"graph {graph8_ms / S * 1e3:.1f} us/step (output equals eager: {same8}); attention "
         f"{attn_ms * 1e3:.1f} us at {achieved:.0f} GB/s on the last cache; token-heads "
         f"{visible[0]} -> {visible[-1]}; fused vs separate max diff {fused_vs_separate:.2e}")
     return r
@@ -746,7 +799,8 @@ def main():
             a = r["attn"]
             log(f"[bench] decode step {r['ms_per_step'] * 1e3:.1f} us (separate calls "
                 f"{r['separate_calls_ms_per_step'] * 1e3:.1f} us, graph replay "
-                f"{r['graph_ms_per_step'] * 1e3:.1f} us); attention {a['ms'] * 1e3:.1f} us = "
+                f"{r['graph_ms_per_step'] * 1e3:.1f} us, eight steps per graph "
+                f"{r['graph8_ms_per_step'] * 1e3:.1f} us); attention {a['ms'] * 1e3:.1f} us = "
                 f"{a['gbs']:.0f} GB/s ({100 * a['frac_of_peak']:.1f}% of peak); "
                 f"{r['token_heads_per_step']:.0f} token-heads per step")
             cpu = None if args.no_cpu else cpu_baseline(ctx, args.cpu_rows)
@@ -783,6 +837,7 @@ def main():
                              "launches_timed": a["launches"]},
                 "cpu_baseline": cpu,
                 "decode_step": {"ms": r["ms_per_step"], "graph_replay_ms": r["graph_ms_per_step"],
+                                "graph8_replay_ms": r["graph8_ms_per_step"],
                                 "separate_calls_ms": r["separate_calls_ms_per_step"],
                                 "steps_per_s": 1e3 / r["ms_per_step"],
                                 "sequence_steps_per_s": wl.B * 1e3 / r["ms_per_step"]},
