@@ -693,6 +693,26 @@ def dms_loop(dev, stream):
 
 # ------------------------------------------------------------------------------ CPU
 
+def blas_threads():
+    """Threads of the BLAS numpy calls into (None if threadpoolctl cannot tell)."""
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else None
+    except Exception:
+        return None
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(ctx, rows):
     """The oracle as it stands, on a bounded sample of the headline workload: for `rows`
     batch rows (all KV heads) the MLP scores of every position, tau by the oracle's own
@@ -737,6 +757,7 @@ def cpu_baseline(ctx, rows):
     return {"value": kept / dt, "unit": "kept token-heads/s",
             "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "threads": int(os.environ.get("OMP_NUM_THREADS", "0")) or None,
+            "blas_threads": blas_threads(), "host": host_cpu_model(),
             "sample": f"{rows} of {wl.B} batch rows, all {wl.Hkv} KV heads, context {wl.T}: "
                       f"MLP scores of every position, tau = oracle.threshold_quantile of the "
                       f"sample's prompt scores at q {wl.keep_quantiles[0]}, keep mask, decode "
