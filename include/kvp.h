@@ -354,7 +354,11 @@ size_t kvp_decode_attn_workspace_size(int32_t B, int32_t Hq, int32_t num_pairs,
  * leave it (the token leaving its ring slot counts iff it is retained; the new token is
  * read from k_new/v_new) without writing it, and with an MLP scorer also computes the
  * split-K partial sums of the new tokens' first layer; the merge kernel finishes the
- * scores and applies the step.
+ * scores and applies the step.  The call launches kernels only and takes tau and the
+ * position from device memory, so it can be captured in a HIP graph and replayed: one step
+ * per graph, or several consecutive steps in one graph (the position advances on the
+ * device from one to the next; each captured step reads its inputs at the addresses it
+ * was captured with), which pays the runtime's per-replay start-up once for all of them.
  *   sc, hidden_new, hdtype  as kvp_score_step_delayed (sc->n_kv_heads = num_pairs / B), or
  *                sc == NULL: hidden_new unused, scores from s_in (ld_s >= 1)
  *   k_new, v_new [B*Hkv][d] bf16, 16-byte aligned; s_out NULL or [B*Hkv] fp32 (scorer)
