@@ -3,7 +3,7 @@
 Sizes span several tiles and ragged tails; pools are poison-filled (NaN / sentinel
 ints) so unwritten or over-read elements show up.  Integer and byte results are
 compared bit-exactly; scores within a stated absolute bound; attention outputs with
-the benchmark spec's tolerances (max-abs 2e-3 for bf16 KV, 1e-5 relative per output vector
+the parity tolerances (max-abs 2e-3 for bf16 KV, 1e-5 relative per output vector
 for fp32 KV).
 """
 import math
