@@ -62,15 +62,17 @@ def same_cache(kvA, ringA, kvB, ringB):
 
 
 def make_scorer(K, kind, H, inner, Hkv):
-    if kind == "linear":
+    """kind: "linear" / "mlp" (with biases), "linear_nobias" / "mlp_nobias", or "given"."""
+    bias = not kind.endswith("_nobias")
+    if kind.startswith("linear"):
         W1 = seeded((Hkv, H), 201, torch.bfloat16, scale=1.0 / math.sqrt(H))
-        b1 = seeded((Hkv,), 202) * 0.1 - 1.0
+        b1 = seeded((Hkv,), 202) * 0.1 - 1.0 if bias else None
         return K.Scorer(K.KVP_SCORER_LINEAR, W1, b1)
-    if kind == "mlp":
+    if kind.startswith("mlp"):
         W1 = seeded((inner, H), 201, torch.bfloat16, scale=1.0 / math.sqrt(H))
-        b1 = seeded((inner,), 202, scale=0.5)
+        b1 = seeded((inner,), 202, scale=0.5) if bias else None
         W2 = seeded((Hkv, inner), 203, scale=1.0 / math.sqrt(inner))
-        b2 = seeded((Hkv,), 204) * 0.1 - 0.3
+        b2 = seeded((Hkv,), 204) * 0.1 - 0.3 if bias else None
         return K.Scorer(K.KVP_SCORER_MLP, W1, b1, W2, b2)
     return None  # scores given
 
@@ -85,6 +87,9 @@ def make_scorer(K, kind, H, inner, Hkv):
     # 32 x 64 = 2048 slices of H 8192 / inner 1024, more than its waves (several each)
     ("mlp", 40, 2, 2, 64, 32, 120, 20, 0.0, 8192, 1024, False),
     ("mlp", 64, 1, 4, 128, 48, 160, 24, -0.2, 2048, 256, False),  # 64 tokens, inner 256
+    ("linear_nobias", 2, 2, 16, 128, 32, 180, 40, 0.1, 512, 0, False),  # g 16, no bias
+    # g 16, d 64, no biases, inner 768: three first-layer slices, three 256-unit chunks
+    ("mlp_nobias", 3, 2, 16, 64, 32, 140, 30, 0.0, 768, 768, False),
 ])
 def test_fused_step_matches_separate_calls(K, kind, B, Hkv, g, d, w, T0, steps, tau, H, inner,
                                            empty):
