@@ -419,7 +419,7 @@ kvp_status kvp_decode_attn_noalloc(const void* q, int32_t qdtype, int32_t B, int
  *              positions ascending -- as written by kvp_select for the same keep bits
  *   out        [B][Hq][T][d] fp32: softmax(sm_scale * K q_i) V over the keys position
  *              i sees; a row that sees no key (window 0, nothing kept before it) is 0
- * g in {1, 2, 4, 8} and d in {64, 128} (else KVP_E_UNSUPPORTED); T >= 1, window >= 0,
+ * g in {1, 2, 4, 8, 16} and d in {64, 128} (else KVP_E_UNSUPPORTED); T >= 1, window >= 0,
  * sm_scale finite and > 0 (else KVP_E_ARG).
  * All buffers are caller-owned device memory; no workspace, no allocation.
  * -------------------------------------------------------------------------- */

@@ -388,7 +388,7 @@ extern "C" kvp_status kvp_prefill_attn(const void* q, const void* k, const void*
   if (!(sm_scale > 0.0f) || sm_scale == __builtin_huge_valf()) return KVP_E_ARG;
   if (Hq % Hkv != 0) return KVP_E_ARG;
   const int g = Hq / Hkv;
-  if (g != 1 && g != 2 && g != 4 && g != 8) return KVP_E_UNSUPPORTED;
+  if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return KVP_E_UNSUPPORTED;
   if (d != 64 && d != 128) return KVP_E_UNSUPPORTED;
   if ((int64_t)B * Hkv > 65535 || T > kMaxTokens) return KVP_E_UNSUPPORTED;
   return kvp_launch_prefill_attn(q, k, v, B, Hq, Hkv, T, d, keep_bits, kept_idx, window, sm_scale, out,

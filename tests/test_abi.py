@@ -227,7 +227,7 @@ def test_host_validation_without_device(L):
     assert pf(fake, fake, fake, L.KVP_F32, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
     assert pf(fake, fake, fake, 9, 1, 8, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_DTYPE
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 6, 4, 64, 128, fake, fake, 16, 0.1, fake, None) == E_ARG
-    assert pf(fake, fake, fake, L.KVP_BF16, 1, 32, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
+    assert pf(fake, fake, fake, L.KVP_BF16, 1, 64, 2, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 12, 4, 64, 128, fake, fake, 16, 0.1, fake, None) == E_UNSUP
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 96, fake, fake, 16, 0.1, fake, None) == E_UNSUP
     assert pf(fake, fake, fake, L.KVP_BF16, 1, 8, 2, 64, 128, fake, fake, -1, 0.1, fake, None) == E_ARG

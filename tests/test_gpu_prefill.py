@@ -80,6 +80,8 @@ def run(K, q, k, v, bits, idx, window):
     (2, 8, 8, 517, 128, 64, 0.25, 0.0),    # g 1, ragged
     (1, 16, 2, 300, 64, 16, 0.5, 0.0),     # g 8, d 64
     (2, 4, 2, 777, 64, 128, 0.1, 0.0),     # g 2
+    (1, 32, 2, 700, 128, 64, 0.3, 0.0),    # g 16: 16-position blocks, one head per column tile
+    (2, 16, 1, 301, 64, 128, 0.5, 0.0),    # g 16, d 64, ragged
     (1, 4, 1, 1, 128, 128, 0.5, 0.0),      # a one-token prompt
     (1, 8, 2, 200, 128, 0, 0.2, 0.0),      # W 0: rows with no kept key before them are 0
     (1, 8, 2, 450, 128, 1000, 0.0, 0.0),   # W > T: plain causal attention
