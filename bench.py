@@ -292,10 +292,11 @@ def decode_run(ctx, q_keep, steps, warmup, stream, graph=False):
     return r
 
 
-def flushed_attn_ms(ctx, stream, reps=8):
+def flushed_attn_ms(ctx, stream, reps=8, stats=False):
     """Median decode-attention time on the cache as it stands, each call right after a
     1 GiB READ that evicts the 256 MB MALL (a write flush would leave dirty lines draining
-    into the timed call); the flush and the call are queued back to back."""
+    into the timed call); the flush and the call are queued back to back.  With stats:
+    {"median_ms", "min_ms", "reps"}."""
     import numpy as np
     import torch
 
@@ -312,6 +313,8 @@ def flushed_attn_ms(ctx, stream, reps=8):
             torch.cuda.synchronize()
             if r >= 2:
                 out.append(e0.elapsed_time(e1))
+    if stats:
+        return {"median_ms": float(np.median(out)), "min_ms": float(np.min(out)), "reps": reps}
     return float(np.median(out))
 
 
@@ -818,11 +821,19 @@ def main():
                 f"scorer={wl.scorer} keep quantile {wl.keep_quantiles[0]}")
             r = decode_run(ctx, wl.keep_quantiles[0], args.steps, args.warmup, stream, graph=True)
             a = r["attn"]
+            # the same call timed one at a time after a 1 GiB read flush, 30 repetitions
+            fl = flushed_attn_ms(ctx, stream, reps=30, stats=True)
+            fl_bytes = ctx.attn_bytes(*ctx.read_split())
+            fl["gbs_median"] = gbs(fl_bytes, fl["median_ms"])
+            fl["frac_of_peak_median"] = fl["gbs_median"] / PEAK_HBM_GBS
+            fl["bytes_per_call"] = fl_bytes
+            a["flushed"] = fl
             log(f"[bench] decode step {r['ms_per_step'] * 1e3:.1f} us (separate calls "
                 f"{r['separate_calls_ms_per_step'] * 1e3:.1f} us, graph replay "
                 f"{r['graph_ms_per_step'] * 1e3:.1f} us, eight steps per graph "
                 f"{r['graph8_ms_per_step'] * 1e3:.1f} us); attention {a['ms'] * 1e3:.1f} us = "
-                f"{a['gbs']:.0f} GB/s ({100 * a['frac_of_peak']:.1f}% of peak); "
+                f"{a['gbs']:.0f} GB/s ({100 * a['frac_of_peak']:.1f}% of peak), after a flush "
+                f"{fl['median_ms'] * 1e3:.1f} us median / {fl['min_ms'] * 1e3:.1f} us min of 30; "
                 f"{r['token_heads_per_step']:.0f} token-heads per step")
             cpu = None if args.no_cpu else cpu_baseline(ctx, args.cpu_rows)
             line = {
