@@ -597,6 +597,19 @@ def dms_loop(dev, stream):
     out_separate = cache.out.clone()
     eager_ms = timed_loop(True)
     out_fused = cache.out.clone()
+    # the same eager steps reading fixed buffers refilled before each step (the four
+    # copies the one-step graph below also makes), for a like-for-like comparison
+    prefill()
+    torch.cuda.synchronize()
+    e0, e1 = new_event(), new_event()
+    e0.record(stream)
+    for i in range(S):
+        feed(i)
+        cache.step(hb, kb, vb, qb, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    eager_refill_ms = e0.elapsed_time(e1)
+    assert torch.equal(cache.out, out_fused)
     fused_vs_separate = float((out_fused - out_separate).abs().max())
 
     # 3. the same loop with the step captured once and replayed
@@ -669,6 +682,7 @@ def dms_loop(dev, stream):
     r = {"workload": wl.name, "batch": B, "prompt": P0, "decode_steps": S, "delay_window": wl.w,
          "tau": wl.fixed_tau, "dtype": dtype_name(wl.kv_dtype),
          "eager_ms_per_step": eager_ms / S, "separate_calls_ms_per_step": separate_ms / S,
+         "eager_refill_ms_per_step": eager_refill_ms / S,
          "graph_ms_per_step": graph_ms / S, "graph8_ms_per_step": graph8_ms / S,
          "token_heads_per_s_eager": th / (eager_ms * 1e-3),
          "token_heads_per_s_graph": th / (graph_ms * 1e-3),
@@ -687,7 +701,8 @@ def dms_loop(dev, stream):
                  "replay (4 small copies per step, in its time); graph8 holds eight steps, "
                  "their inputs refilled by 4 copies per replay"}
     log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step (separate calls "
-        f"{separate_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step, eight steps per "
+        f"{separate_ms / S * 1e3:.1f}; with the graph's input refills "
+        f"{eager_refill_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step, eight steps per "
         f"graph {graph8_ms / S * 1e3:.1f} us/step (output equals eager: {same8}); attention "
         f"{attn_ms * 1e3:.1f} us at {achieved:.0f} GB/s on the last cache; token-heads "
         f"{visible[0]} -> {visible[-1]}; fused vs separate max diff {fused_vs_separate:.2e}")
