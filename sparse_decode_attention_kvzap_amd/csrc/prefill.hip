@@ -107,8 +107,7 @@ struct PfRegs {
 // Positions of this thread's slots in a tile (-1: empty slot).  Prefix tiles read
 // kept_idx (the pair's kept positions, ascending).
 template <int D>
-__device__ __forceinline__ void pf_positions(const PrefillArgs& a, const int* kidx, const PfTile& t,
-                                             int s0, int (&pos)[pf_kg(D)]) {
+__device__ __forceinline__ void pf_positions(const int* kidx, const PfTile& t, int s0, int (&pos)[pf_kg(D)]) {
 #pragma unroll
   for (int r = 0; r < pf_kg(D); ++r) {
     const int slot = s0 + r;
@@ -266,17 +265,17 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
   // step before the previous barrier.
   PfRegs<D> R0, R1;
   int pos[KG];
-  pf_positions<D>(a, kidx, pf_tile(0, ntp, nk, lo64, hi, rev), s0, pos);
+  pf_positions<D>(kidx, pf_tile(0, ntp, nk, lo64, hi, rev), s0, pos);
   pf_load<D>(kp, vp, dc, pos, R0);
   if (ntiles > 1) {
-    pf_positions<D>(a, kidx, pf_tile(1, ntp, nk, lo64, hi, rev), s0, pos);
+    pf_positions<D>(kidx, pf_tile(1, ntp, nk, lo64, hi, rev), s0, pos);
     pf_load<D>(kp, vp, dc, pos, R1);
   }
   pf_store<D>(kbuf[0], vbuf[0], dc, s0, R0);
   if (ntiles > 2) {
-    pf_positions<D>(a, kidx, pf_tile(2, ntp, nk, lo64, hi, rev), s0, pos);
+    pf_positions<D>(kidx, pf_tile(2, ntp, nk, lo64, hi, rev), s0, pos);
     pf_load<D>(kp, vp, dc, pos, R0);
-    if (ntiles > 3) pf_positions<D>(a, kidx, pf_tile(3, ntp, nk, lo64, hi, rev), s0, pos);
+    if (ntiles > 3) pf_positions<D>(kidx, pf_tile(3, ntp, nk, lo64, hi, rev), s0, pos);
   }
   __syncthreads();
 
@@ -288,7 +287,7 @@ __global__ __launch_bounds__(PF_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
       pf_store<D>(kbuf[(tau + 1) & 1], vbuf[(tau + 1) & 1], dc, s0, Rn);
       if (tau + 3 < ntiles) {
         pf_load<D>(kp, vp, dc, pos, Rn);
-        if (tau + 4 < ntiles) pf_positions<D>(a, kidx, pf_tile(tau + 4, ntp, nk, lo64, hi, rev), s0, pos);
+        if (tau + 4 < ntiles) pf_positions<D>(kidx, pf_tile(tau + 4, ntp, nk, lo64, hi, rev), s0, pos);
       }
     }
     const uint16_t* const ks = kbuf[tau & 1];
