@@ -665,6 +665,32 @@ def dms_loop(dev, stream):
     assert cache.check(stream) == 0
     same8 = bool(torch.equal(cache.out, out_fused)) if S % G == 0 else None
     del graph8, bufs
+    # 5. one graph per window of eight steps, each step reading its inputs where they lie
+    #    (no refills): all windows captured before timing, then replayed in order
+    graphs = []
+    prefill()
+    torch.cuda.synchronize()
+    for r8 in range(S // G):
+        gw = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gw, stream=side):
+            for k in range(G):
+                i = r8 * G + k
+                cache.step(H_all[i], K_all[i], V_all[i], Q_all[i], stream=side)
+        graphs.append(gw)
+    torch.cuda.synchronize()
+    prefill()
+    torch.cuda.synchronize()
+    e0, e1 = new_event(), new_event()
+    e0.record(stream)
+    with torch.cuda.stream(stream):
+        for gw in graphs:
+            gw.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph8_inplace_ms = e0.elapsed_time(e1) * S / (G * (S // G))
+    assert cache.check(stream) == 0
+    same8_inplace = bool(torch.equal(cache.out, out_fused)) if S % G == 0 else None
+    del graphs
     # the decode attention alone, back to back on the cache the loop left (the last step's
     # token-heads)
     for _ in range(2):
@@ -684,6 +710,8 @@ def dms_loop(dev, stream):
          "eager_ms_per_step": eager_ms / S, "separate_calls_ms_per_step": separate_ms / S,
          "eager_refill_ms_per_step": eager_refill_ms / S,
          "graph_ms_per_step": graph_ms / S, "graph8_ms_per_step": graph8_ms / S,
+         "graph8_inplace_ms_per_step": graph8_inplace_ms / S,
+         "graph8_inplace_output_equals_eager": same8_inplace,
          "token_heads_per_s_eager": th / (eager_ms * 1e-3),
          "token_heads_per_s_graph": th / (graph_ms * 1e-3),
          "token_heads_per_s_graph8": th / (graph8_ms * 1e-3),
@@ -699,11 +727,14 @@ def dms_loop(dev, stream):
                  "in place; separate_calls = kvp_score_step_delayed then kvp_decode_attn; the "
                  "graph holds the decode step and reads fixed buffers, refilled before each "
                  "replay (4 small copies per step, in its time); graph8 holds eight steps, "
-                 "their inputs refilled by 4 copies per replay"}
+                 "their inputs refilled by 4 copies per replay; graph8_inplace: one graph per "
+                 "window of eight steps reading the inputs in place, captured before timing"}
     log(f"[bench] dms loop: eager {eager_ms / S * 1e3:.1f} us/step (separate calls "
         f"{separate_ms / S * 1e3:.1f}; with the graph's input refills "
         f"{eager_refill_ms / S * 1e3:.1f}), graph {graph_ms / S * 1e3:.1f} us/step, eight steps per "
-        f"graph {graph8_ms / S * 1e3:.1f} us/step (output equals eager: {same8}); attention "
+        f"graph {graph8_ms / S * 1e3:.1f} us/step (output equals eager: {same8}), one graph per "
+        f"eight-step window on the inputs in place {graph8_inplace_ms / S * 1e3:.1f} us/step "
+        f"(equal: {same8_inplace}); attention "
         f"{attn_ms * 1e3:.1f} us at {achieved:.0f} GB/s on the last cache; token-heads "
         f"{visible[0]} -> {visible[-1]}; fused vs separate max diff {fused_vs_separate:.2e}")
     return r
